@@ -1,0 +1,266 @@
+"""fp64 CPU oracle of the tensor-parallel MLP shard (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+may import this package.  It shares no code with the GPU library: the C
+loop nests live in ``tp_mlp_oracle.c`` (built by ``oracle/build.py`` with
+gcc), and this wrapper only converts storage arrays to float64, allocates
+outputs and loops over shards / experts.
+
+What each function computes, and the passage it follows:
+
+* ``mlp_fwd`` / ``mlp_bwd`` -- one shard of the paired column -> act -> row
+  MLP and its backward (Megatron-LM 源码精读——大模型并行训练全景, §三
+  3.1-3.4; SwiGLU: same page, §七).
+* ``sharded_fwd`` / ``sharded_bwd`` -- all T shards of a full weight pair,
+  plus the sums over shards (the forward all-reduce of Y_i and the backward
+  all-reduce of dX_i, same page §三 3.3 diagram), and the unsharded MLP.
+* ``partial_sum`` -- the all-reduce arithmetic over resident partials.
+* ``grouped_fwd`` / ``grouped_bwd`` -- each local expert runs the SwiGLU MLP
+  on its own routed rows (Megatron Core 带读 §09; Megatron-LM 源码精读
+  docs index, "MoE 层与 Expert Parallelism": grouped-GEMM expert compute).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from workloads import bf16_bits_to_f32, DT_BF16, ACT_SWIGLU, ACT_GELU_TANH
+
+ACT_IDENTITY = 99
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_d = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from oracle.build import build
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.orc_num_threads.restype = ctypes.c_int
+    for name in ("orc_gelu_tanh", "orc_gelu_tanh_grad", "orc_sigmoid",
+                 "orc_silu", "orc_silu_grad"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_double
+        f.argtypes = [ctypes.c_double]
+    for name in ("orc_matmul_nn", "orc_matmul_nt", "orc_matmul_tn"):
+        f = getattr(lib, name)
+        f.restype = None
+        f.argtypes = [_i64, _i64, _i64, _d, _d, _d]
+    lib.orc_mlp_fwd.restype = ctypes.c_int
+    lib.orc_mlp_fwd.argtypes = [_i64, _i64, _i64, ctypes.c_int] + [_d] * 8
+    lib.orc_mlp_bwd.restype = ctypes.c_int
+    lib.orc_mlp_bwd.argtypes = [_i64, _i64, _i64, ctypes.c_int] + [_d] * 14
+    lib.orc_partial_sum.restype = ctypes.c_int
+    lib.orc_partial_sum.argtypes = [ctypes.c_int, _i64, ctypes.POINTER(_d), _d]
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    return _load().orc_num_threads()
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_d)
+
+
+def to_f64(a, dtype=None) -> np.ndarray:
+    """Storage array (float32 or uint16 bf16 bits) -> float64, exactly."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(np.float64)
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# scalar activations (exposed for the closed-form pins)
+# ----------------------------------------------------------------------------
+def gelu_tanh(z: float) -> float:
+    return _load().orc_gelu_tanh(float(z))
+
+
+def gelu_tanh_grad(z: float) -> float:
+    return _load().orc_gelu_tanh_grad(float(z))
+
+
+def silu(g: float) -> float:
+    return _load().orc_silu(float(g))
+
+
+def silu_grad(g: float) -> float:
+    return _load().orc_silu_grad(float(g))
+
+
+def sigmoid(g: float) -> float:
+    return _load().orc_sigmoid(float(g))
+
+
+def matmul(kind: str, A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """The oracle's own product loops: 'nn' A@B, 'nt' A@B.T, 'tn' A.T@B."""
+    lib = _load()
+    A = np.ascontiguousarray(A, np.float64)
+    B = np.ascontiguousarray(B, np.float64)
+    if kind == "nn":
+        M, K = A.shape; N = B.shape[1]; f = lib.orc_matmul_nn
+    elif kind == "nt":
+        M, K = A.shape; N = B.shape[0]; f = lib.orc_matmul_nt
+    elif kind == "tn":
+        K, M = A.shape; N = B.shape[1]; f = lib.orc_matmul_tn
+    else:
+        raise ValueError(kind)
+    C = np.empty((M, N), np.float64)
+    f(M, N, K, _p(A), _p(B), _p(C))
+    return C
+
+
+# ----------------------------------------------------------------------------
+# one shard
+# ----------------------------------------------------------------------------
+def mlp_fwd(X, A, B, act, A_up=None) -> dict:
+    """One shard's forward.  Returns Z (gate G for SwiGLU), U (SwiGLU),
+    H (post-activation) and Y (the shard's partial output), all float64."""
+    lib = _load()
+    X, A, B, A_up = (to_f64(t) for t in (X, A, B, A_up))
+    N, Hd = X.shape
+    Ft = A.shape[1]
+    assert A.shape == (Hd, Ft) and B.shape == (Ft, Hd)
+    Z = np.empty((N, Ft)); Hact = np.empty((N, Ft)); Y = np.empty((N, Hd))
+    U = np.empty((N, Ft)) if act == ACT_SWIGLU else None
+    rc = lib.orc_mlp_fwd(N, Hd, Ft, act, _p(X), _p(A), _p(A_up), _p(B),
+                         _p(Z), _p(U), _p(Hact), _p(Y))
+    if rc != 0:
+        raise ValueError(f"orc_mlp_fwd failed ({rc})")
+    return {"Z": Z, "U": U, "H": Hact, "Y": Y}
+
+
+def mlp_bwd(X, A, B, act, dY, fwd: dict, A_up=None) -> dict:
+    """One shard's backward from the forward's saved tensors.  Returns dX
+    (the shard's partial), dA, dA_up (SwiGLU), dB, dZ (dG), dU (SwiGLU)."""
+    lib = _load()
+    X, A, B, A_up, dY = (to_f64(t) for t in (X, A, B, A_up, dY))
+    N, Hd = X.shape
+    Ft = A.shape[1]
+    sw = act == ACT_SWIGLU
+    dX = np.empty((N, Hd)); dA = np.empty((Hd, Ft)); dB = np.empty((Ft, Hd))
+    dAup = np.empty((Hd, Ft)) if sw else None
+    dZ = np.empty((N, Ft)); dU = np.empty((N, Ft)) if sw else None
+    rc = lib.orc_mlp_bwd(N, Hd, Ft, act, _p(X), _p(A), _p(A_up), _p(B),
+                         _p(fwd["Z"]), _p(fwd["U"]), _p(fwd["H"]), _p(dY),
+                         _p(dX), _p(dA), _p(dAup), _p(dB), _p(dZ), _p(dU))
+    if rc != 0:
+        raise ValueError(f"orc_mlp_bwd failed ({rc})")
+    return {"dX": dX, "dA": dA, "dA_up": dAup, "dB": dB, "dZ": dZ, "dU": dU}
+
+
+def partial_sum(parts) -> np.ndarray:
+    """Sum of T partial outputs, elementwise, fp64."""
+    lib = _load()
+    parts = [to_f64(p) for p in parts]
+    shape = parts[0].shape
+    flat = [np.ascontiguousarray(p.reshape(-1)) for p in parts]
+    arr = (_d * len(flat))(*[_p(p) for p in flat])
+    out = np.empty(flat[0].shape[0])
+    rc = lib.orc_partial_sum(len(flat), flat[0].shape[0], arr, _p(out))
+    if rc != 0:
+        raise ValueError(f"orc_partial_sum failed ({rc})")
+    return out.reshape(shape)
+
+
+# ----------------------------------------------------------------------------
+# all shards of a full weight pair, and the unsharded MLP
+# ----------------------------------------------------------------------------
+def shard_weights(A_full, B_full, T, A_up_full=None):
+    """Column split of A (and A_up) and row split of B into T shards; the
+    shard width is F/T and must divide exactly (§三 3.1: the per-partition
+    output size is the full size divided by the world size)."""
+    F = A_full.shape[1]
+    if F % T:
+        raise ValueError("F must be divisible by T")
+    Ft = F // T
+    shards = []
+    for i in range(T):
+        sl = slice(i * Ft, (i + 1) * Ft)
+        shards.append((np.ascontiguousarray(A_full[:, sl]),
+                       np.ascontiguousarray(B_full[sl, :]),
+                       None if A_up_full is None else np.ascontiguousarray(A_up_full[:, sl])))
+    return shards
+
+
+def sharded_fwd_bwd(X, A_full, B_full, T, act, dY=None, A_up_full=None) -> dict:
+    """Every shard's forward (+backward), the sums over shards, and the
+    unsharded MLP run on the full weights (T=1)."""
+    X64, A64, B64 = to_f64(X), to_f64(A_full), to_f64(B_full)
+    Au64 = to_f64(A_up_full)
+    dY64 = to_f64(dY)
+    out = {"shards": []}
+    for (Ai, Bi, Aui) in shard_weights(A64, B64, T, Au64):
+        f = mlp_fwd(X64, Ai, Bi, act, Aui)
+        rec = {"fwd": f}
+        if dY64 is not None:
+            rec["bwd"] = mlp_bwd(X64, Ai, Bi, act, dY64, f, Aui)
+        out["shards"].append(rec)
+    out["Y"] = partial_sum([r["fwd"]["Y"] for r in out["shards"]])
+    full_f = mlp_fwd(X64, A64, B64, act, Au64)
+    out["full_fwd"] = full_f
+    if dY64 is not None:
+        out["dX"] = partial_sum([r["bwd"]["dX"] for r in out["shards"]])
+        out["full_bwd"] = mlp_bwd(X64, A64, B64, act, dY64, full_f, Au64)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# grouped local experts
+# ----------------------------------------------------------------------------
+def grouped_fwd(X_perm, offsets, Wg, Wu, Wd) -> dict:
+    """Rows [o_e, o_{e+1}) of X_perm run expert e's SwiGLU MLP (expert
+    tensor-parallel size 1).  Returns G, U, H [R,F] and Y [R,H]."""
+    X = to_f64(X_perm)
+    R, Hd = X.shape
+    E, _, F = np.asarray(Wg).shape
+    G = np.zeros((R, F)); U = np.zeros((R, F)); Hh = np.zeros((R, F)); Y = np.zeros((R, Hd))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        f = mlp_fwd(np.ascontiguousarray(X[lo:hi]), to_f64(Wg[e]), to_f64(Wd[e]),
+                    ACT_SWIGLU, to_f64(Wu[e]))
+        G[lo:hi], U[lo:hi], Hh[lo:hi], Y[lo:hi] = f["Z"], f["U"], f["H"], f["Y"]
+    return {"G": G, "U": U, "H": Hh, "Y": Y}
+
+
+def grouped_bwd(X_perm, offsets, Wg, Wu, Wd, dY_perm, fwd: dict) -> dict:
+    """Backward of ``grouped_fwd``: dX [R,H], dWg/dWu [E,H,F], dWd [E,F,H]
+    (an expert with no rows has zero weight gradients)."""
+    X = to_f64(X_perm)
+    dY = to_f64(dY_perm)
+    R, Hd = X.shape
+    E, _, F = np.asarray(Wg).shape
+    dX = np.zeros((R, Hd))
+    dWg = np.zeros((E, Hd, F)); dWu = np.zeros((E, Hd, F)); dWd = np.zeros((E, F, Hd))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        sub = {"Z": np.ascontiguousarray(fwd["G"][lo:hi]),
+               "U": np.ascontiguousarray(fwd["U"][lo:hi]),
+               "H": np.ascontiguousarray(fwd["H"][lo:hi])}
+        b = mlp_bwd(np.ascontiguousarray(X[lo:hi]), to_f64(Wg[e]), to_f64(Wd[e]),
+                    ACT_SWIGLU, np.ascontiguousarray(dY[lo:hi]), sub, to_f64(Wu[e]))
+        dX[lo:hi] = b["dX"]
+        dWg[e], dWu[e], dWd[e] = b["dA"], b["dA_up"], b["dB"]
+    return {"dX": dX, "dWg": dWg, "dWu": dWu, "dWd": dWd}

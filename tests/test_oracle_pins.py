@@ -1,0 +1,334 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+The pages print no worked numeric example, so the oracle is pinned by
+closed forms, the sharding algebra the pages state, central finite
+differences of the scalar loss <dY, Y>, a library matmul, and exact
+power-of-two scaling.  Each test names the mistake it would catch.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import ACT_GELU_TANH, ACT_SWIGLU
+
+RNG = np.random.default_rng(12345)
+
+
+def rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+# ----------------------------------------------------------------------------
+# activations: closed forms
+# ----------------------------------------------------------------------------
+GRID = np.linspace(-8.0, 8.0, 3201)
+
+
+def test_gelu_closed_forms():
+    assert oracle.gelu_tanh(0.0) == 0.0
+    # gelu(z) - gelu(-z) = z for the tanh form (tanh is odd): catches a
+    # dropped 1/2 or a sign error inside the tanh argument.
+    for z in GRID:
+        assert abs(oracle.gelu_tanh(z) - oracle.gelu_tanh(-z) - z) <= 1e-14 * max(1.0, abs(z))
+    # derivative at 0 is exactly 1/2
+    assert oracle.gelu_tanh_grad(0.0) == 0.5
+    # second-order coefficient: (gelu(z) + gelu(-z)) / (2 z^2) -> phi(0) =
+    # 1/sqrt(2 pi), the Gaussian density at 0 (the tanh form matches the
+    # exact GeLU to second order).  Catches a wrong sqrt(2/pi).
+    z = 1e-4
+    even = (oracle.gelu_tanh(z) + oracle.gelu_tanh(-z)) / (2 * z * z)
+    assert abs(even - 1.0 / math.sqrt(2 * math.pi)) < 1e-7
+    # distance to the exact x*Phi(x) (Python's math.erf, independent of the
+    # oracle) stays within the tanh approximation's known error.
+    dev = max(abs(oracle.gelu_tanh(z) - z * 0.5 * (1 + math.erf(z / math.sqrt(2))))
+              for z in GRID)
+    assert dev < 4.8e-4
+    # asymptotes
+    assert abs(oracle.gelu_tanh(30.0) - 30.0) < 1e-12
+    assert abs(oracle.gelu_tanh(-30.0)) < 1e-12
+
+
+def test_gelu_grad_matches_central_difference():
+    for z in GRID:
+        h = 1e-5
+        fd = (oracle.gelu_tanh(z + h) - oracle.gelu_tanh(z - h)) / (2 * h)
+        assert abs(fd - oracle.gelu_tanh_grad(z)) < 1e-9
+
+
+def test_silu_closed_forms():
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.sigmoid(0.0) == 0.5
+    assert oracle.silu_grad(0.0) == 0.5
+    for z in GRID:
+        # silu(z) - silu(-z) = z (since sigmoid(z) + sigmoid(-z) = 1)
+        assert abs(oracle.silu(z) - oracle.silu(-z) - z) <= 1e-14 * max(1.0, abs(z))
+        assert abs(oracle.sigmoid(z) - 1.0 / (1.0 + math.exp(-z))) < 1e-15
+        h = 1e-5
+        fd = (oracle.silu(z + h) - oracle.silu(z - h)) / (2 * h)
+        assert abs(fd - oracle.silu_grad(z)) < 1e-9
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# product loops against a library matmul
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 1, 1), (3, 5, 7), (17, 9, 33), (64, 48, 40)])
+def test_matmul_loops_vs_numpy(shape):
+    M, N, K = shape
+    A = RNG.standard_normal((M, K)); B = RNG.standard_normal((K, N))
+    assert rel(oracle.matmul("nn", A, B), A @ B) < 1e-13
+    Bs = RNG.standard_normal((N, K))
+    assert rel(oracle.matmul("nt", A, Bs), A @ Bs.T) < 1e-13
+    As = RNG.standard_normal((K, M))
+    assert rel(oracle.matmul("tn", As, B), As.T @ B) < 1e-13
+
+
+def test_identity_activation_mlp_vs_numpy():
+    """With act = identity the MLP is linear: Y = X A B, dX = dY B^T A^T,
+    dA = X^T dY B^T, dB = (X A)^T dY.  Catches a transposed operand or a
+    swapped gradient anywhere in the shard's loops."""
+    N, H, Ft = 13, 24, 40
+    X = RNG.standard_normal((N, H)); A = RNG.standard_normal((H, Ft))
+    B = RNG.standard_normal((Ft, H)); dY = RNG.standard_normal((N, H))
+    f = oracle.mlp_fwd(X, A, B, oracle.ACT_IDENTITY)
+    assert rel(f["Y"], X @ A @ B) < 1e-13
+    b = oracle.mlp_bwd(X, A, B, oracle.ACT_IDENTITY, dY, f)
+    assert rel(b["dX"], dY @ B.T @ A.T) < 1e-13
+    assert rel(b["dA"], X.T @ (dY @ B.T)) < 1e-13
+    assert rel(b["dB"], (X @ A).T @ dY) < 1e-13
+
+
+# ----------------------------------------------------------------------------
+# finite differences of L = <dY, Y> on tiny shapes, every entry
+# ----------------------------------------------------------------------------
+def _loss(X, A, B, act, dY, Au=None):
+    return float(np.sum(oracle.mlp_fwd(X, A, B, act, Au)["Y"] * dY))
+
+
+def _fd_grad(fn, theta, idxs=None):
+    g = np.zeros_like(theta)
+    it = np.ndindex(theta.shape) if idxs is None else idxs
+    for ix in it:
+        old = theta[ix]
+        h = 1e-6 * max(1.0, abs(old))
+        theta[ix] = old + h; lp = fn()
+        theta[ix] = old - h; lm = fn()
+        theta[ix] = old
+        g[ix] = (lp - lm) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("act", [ACT_GELU_TANH, ACT_SWIGLU])
+def test_finite_differences_tiny_every_entry(act):
+    N, H, F, T = 4, 8, 16, 2
+    X = RNG.standard_normal((N, H))
+    A = RNG.standard_normal((H, F)) * 0.5
+    Au = RNG.standard_normal((H, F)) * 0.5 if act == ACT_SWIGLU else None
+    B = RNG.standard_normal((F, H)) * 0.5
+    dY = RNG.standard_normal((N, H))
+    res = oracle.sharded_fwd_bwd(X, A, B, T, act, dY, Au)
+    Ft = F // T
+    for i, rec in enumerate(res["shards"]):
+        sl = slice(i * Ft, (i + 1) * Ft)
+        Ai = np.ascontiguousarray(A[:, sl]); Bi = np.ascontiguousarray(B[sl, :])
+        Aui = None if Au is None else np.ascontiguousarray(Au[:, sl])
+        fn = lambda: _loss(X, Ai, Bi, act, dY, Aui)
+        b = rec["bwd"]
+        for theta, an in ((X, b["dX"]), (Ai, b["dA"]), (Bi, b["dB"])) + \
+                (((Aui, b["dA_up"]),) if Aui is not None else ()):
+            fd = _fd_grad(fn, theta)
+            assert rel(an, fd) < 1e-7
+            assert np.max(np.abs(an - fd)) < 1e-6 * max(1.0, np.max(np.abs(fd)))
+    # the input gradient of the unsharded MLP equals the sum of shard partials
+    fn_full = lambda: _loss(X, A, B, act, dY, Au)
+    fd_full = _fd_grad(fn_full, X)
+    assert rel(res["dX"], fd_full) < 1e-7
+
+
+def test_finite_differences_sampled_small_workload():
+    """256 sampled entries per tensor at the fp32 workload's full size."""
+    import workloads
+    w = workloads.WORKLOADS["c1_f32_gelu_t2"]
+    d = workloads.gen_mlp_inputs(w, shard=1)
+    X, A, B, dY = (oracle.to_f64(d[k]) for k in ("X", "A", "B", "dY"))
+    f = oracle.mlp_fwd(X, A, B, ACT_GELU_TANH)
+    b = oracle.mlp_bwd(X, A, B, ACT_GELU_TANH, dY, f)
+    fn = lambda: _loss(X, A, B, ACT_GELU_TANH, dY)
+    rng = np.random.default_rng(7)
+    for theta, an in ((X, b["dX"]), (A, b["dA"]), (B, b["dB"])):
+        flat = rng.choice(theta.size, size=256, replace=False)
+        idxs = [np.unravel_index(int(k), theta.shape) for k in flat]
+        fd = _fd_grad(fn, theta, idxs)
+        sel = tuple(np.array(idxs).T)
+        scale = np.max(np.abs(an))
+        assert np.max(np.abs(fd[sel] - an[sel])) < 1e-6 * scale
+
+
+# ----------------------------------------------------------------------------
+# sharding algebra the pages state
+# ----------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def c1_sharded():
+    import workloads
+    w = workloads.WORKLOADS["c1_f32_gelu_t2"]
+    d = workloads.gen_mlp_inputs(w)
+    res = oracle.sharded_fwd_bwd(d["X"], d["A_full"], d["B_full"], w.T, w.act, d["dY"])
+    return w, d, res
+
+
+def test_column_shards_concatenate_bitwise(c1_sharded):
+    """§三 3.1: each column shard computes its own block of output columns."""
+    w, d, res = c1_sharded
+    Zcat = np.concatenate([r["fwd"]["Z"] for r in res["shards"]], axis=1)
+    Hcat = np.concatenate([r["fwd"]["H"] for r in res["shards"]], axis=1)
+    assert np.array_equal(Zcat, res["full_fwd"]["Z"])
+    assert np.array_equal(Hcat, res["full_fwd"]["H"])
+
+
+def test_row_partials_sum_to_unsharded(c1_sharded):
+    """§三 3.2/3.3: the sum over shards of Y_i is the unsharded output."""
+    w, d, res = c1_sharded
+    assert rel(res["Y"], res["full_fwd"]["Y"]) < 1e-12
+    # and a single partial is not the full output (catches a sum that
+    # double-counts or a shard that silently used the full weights)
+    assert rel(res["shards"][0]["fwd"]["Y"], res["full_fwd"]["Y"]) > 0.1
+
+
+def test_dx_partials_sum_to_unsharded(c1_sharded):
+    """§三 3.1: dL/dX = sum_i dL/dZ_i A_i^T (the backward all-reduce)."""
+    w, d, res = c1_sharded
+    assert rel(res["dX"], res["full_bwd"]["dX"]) < 1e-12
+
+
+def test_weight_grads_are_slices_bitwise(c1_sharded):
+    w, d, res = c1_sharded
+    Ft = w.Ft
+    for i, rec in enumerate(res["shards"]):
+        sl = slice(i * Ft, (i + 1) * Ft)
+        assert np.array_equal(rec["bwd"]["dA"], res["full_bwd"]["dA"][:, sl])
+        assert np.array_equal(rec["bwd"]["dB"], res["full_bwd"]["dB"][sl, :])
+
+
+def test_indivisible_width_rejected():
+    A = np.zeros((4, 10)); B = np.zeros((10, 4))
+    with pytest.raises(ValueError):
+        oracle.shard_weights(A, B, 3)
+
+
+def test_t1_shard_is_full_mlp_bitwise():
+    N, H, F = 6, 16, 24
+    X = RNG.standard_normal((N, H)); A = RNG.standard_normal((H, F)) * 0.3
+    B = RNG.standard_normal((F, H)) * 0.3; dY = RNG.standard_normal((N, H))
+    res = oracle.sharded_fwd_bwd(X, A, B, 1, ACT_GELU_TANH, dY)
+    assert np.array_equal(res["Y"], res["full_fwd"]["Y"])
+    assert np.array_equal(res["dX"], res["full_bwd"]["dX"])
+
+
+@pytest.mark.parametrize("act", [ACT_GELU_TANH, ACT_SWIGLU])
+def test_power_of_two_scaling_exact(act):
+    """dY -> 2 dY doubles every gradient; B -> 2 B doubles Y: both exact in
+    binary floating point, so any data-dependent slip shows bitwise."""
+    N, H, Ft = 9, 16, 24
+    X = RNG.standard_normal((N, H)); A = RNG.standard_normal((H, Ft)) * 0.3
+    Au = RNG.standard_normal((H, Ft)) * 0.3 if act == ACT_SWIGLU else None
+    B = RNG.standard_normal((Ft, H)) * 0.3; dY = RNG.standard_normal((N, H))
+    f = oracle.mlp_fwd(X, A, B, act, Au)
+    b1 = oracle.mlp_bwd(X, A, B, act, dY, f, Au)
+    b2 = oracle.mlp_bwd(X, A, B, act, 2 * dY, f, Au)
+    for k in ("dX", "dA", "dB") + (("dA_up",) if Au is not None else ()):
+        assert np.array_equal(b2[k], 2 * b1[k])
+    f2 = oracle.mlp_fwd(X, A, 2 * B, act, Au)
+    assert np.array_equal(f2["Y"], 2 * f["Y"])
+
+
+def test_swiglu_matches_gate_up_definition():
+    """SwiGLU with the up projection replaced by a copy of the gate's
+    weights is silu(z) * z; and with up weights zero the output is zero."""
+    N, H, Ft = 5, 8, 12
+    X = RNG.standard_normal((N, H)); A = RNG.standard_normal((H, Ft))
+    B = RNG.standard_normal((Ft, H))
+    f = oracle.mlp_fwd(X, A, B, ACT_SWIGLU, A.copy())
+    Z = X @ A
+    assert rel(f["H"], Z * Z / (1 + np.exp(-Z))) < 1e-14
+    f0 = oracle.mlp_fwd(X, A, B, ACT_SWIGLU, np.zeros_like(A))
+    assert not np.any(f0["Y"])
+
+
+# ----------------------------------------------------------------------------
+# partial sum
+# ----------------------------------------------------------------------------
+def test_partial_sum_pins():
+    P = RNG.standard_normal((7, 5))
+    assert np.array_equal(oracle.partial_sum([P]), P)
+    # values with 8 significant bits: every running sum up to 8*P is exact
+    P = np.ldexp(np.round(np.ldexp(P, 7)), -7)
+    for T in (2, 4, 8):
+        assert np.array_equal(oracle.partial_sum([P] * T), T * P)
+    # integers: exact in fp64
+    parts = [RNG.integers(-1000, 1000, size=(11,)).astype(np.float64) for _ in range(5)]
+    assert np.array_equal(oracle.partial_sum(parts), np.sum(parts, axis=0))
+
+
+# ----------------------------------------------------------------------------
+# grouped experts
+# ----------------------------------------------------------------------------
+def _small_grouped(counts, H=16, F=24, seed=3):
+    rng = np.random.default_rng(seed)
+    E = len(counts)
+    offsets = np.zeros(E + 1, np.int64); offsets[1:] = np.cumsum(counts)
+    R = int(offsets[-1])
+    X = rng.standard_normal((R, H)); dY = rng.standard_normal((R, H))
+    Wg = rng.standard_normal((E, H, F)) * 0.3
+    Wu = rng.standard_normal((E, H, F)) * 0.3
+    Wd = rng.standard_normal((E, F, H)) * 0.3
+    return X, dY, offsets, Wg, Wu, Wd
+
+
+def test_grouped_rows_match_dense_on_gathered_tokens():
+    """Expert e's rows equal the dense SwiGLU MLP with expert e's weights run
+    over all tokens and then gathered, with numpy doing the gather and the
+    products (catches an offset or expert-index slip)."""
+    import workloads
+    w = workloads.WORKLOADS["c5_bf16_grouped_swiglu"]
+    d = workloads.gen_grouped_inputs(w, tokens=256, H=16, F=24)
+    n_tok = 256
+    Xtok = oracle.to_f64(workloads.normal_bf16(1000 * w.cid + workloads.K_X, (n_tok, 16), 1.0))
+    g = oracle.grouped_fwd(d["X_perm"], d["offsets"], d["Wg"], d["Wu"], d["Wd"])
+    for e in range(w.experts):
+        lo, hi = d["offsets"][e], d["offsets"][e + 1]
+        Gd = Xtok @ oracle.to_f64(d["Wg"][e]); Ud = Xtok @ oracle.to_f64(d["Wu"][e])
+        Hd = Gd / (1 + np.exp(-Gd)) * Ud
+        Yd = Hd @ oracle.to_f64(d["Wd"][e])
+        toks = d["token_ids"][lo:hi]
+        assert rel(g["Y"][lo:hi], Yd[toks]) < 1e-12
+
+
+def test_grouped_empty_expert_and_permutation():
+    counts = [3, 0, 5, 2]
+    X, dY, off, Wg, Wu, Wd = _small_grouped(counts)
+    f = oracle.grouped_fwd(X, off, Wg, Wu, Wd)
+    b = oracle.grouped_bwd(X, off, Wg, Wu, Wd, dY, f)
+    assert not np.any(b["dWg"][1]) and not np.any(b["dWu"][1]) and not np.any(b["dWd"][1])
+    # permuting rows inside a segment permutes the per-row outputs and
+    # leaves the weight gradients unchanged up to summation order
+    perm = np.arange(X.shape[0]); perm[3:8] = perm[3:8][::-1]
+    f2 = oracle.grouped_fwd(X[perm], off, Wg, Wu, Wd)
+    b2 = oracle.grouped_bwd(X[perm], off, Wg, Wu, Wd, dY[perm], f2)
+    assert np.array_equal(f2["Y"], f["Y"][perm])
+    assert np.array_equal(b2["dX"], b["dX"][perm])
+    assert rel(b2["dWg"], b["dWg"]) < 1e-14
+    assert rel(b2["dWd"], b["dWd"]) < 1e-14
+
+
+def test_grouped_weight_grad_finite_difference():
+    counts = [2, 3]
+    X, dY, off, Wg, Wu, Wd = _small_grouped(counts, H=6, F=8)
+    f = oracle.grouped_fwd(X, off, Wg, Wu, Wd)
+    b = oracle.grouped_bwd(X, off, Wg, Wu, Wd, dY, f)
+    fn = lambda: float(np.sum(oracle.grouped_fwd(X, off, Wg, Wu, Wd)["Y"] * dY))
+    for theta, an in ((Wg, b["dWg"]), (Wu, b["dWu"]), (Wd, b["dWd"]), (X, b["dX"])):
+        fd = _fd_grad(fn, theta)
+        assert rel(an, fd) < 1e-7
