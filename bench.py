@@ -1,0 +1,189 @@
+"""Throughput of one tensor-parallel rank's MLP shard, forward + backward.
+
+One step = the whole shard path on one batch, inputs resident in HBM:
+  forward   FC1 (+ activation epilogue) -> FC2             tp_mlp_shard_fwd
+  sum       Y = Y_0 + 7 stand-in partials of the other ranks  tp_partial_sum
+  backward  dH (+ activation-derivative epilogue), dB, dA, dX tp_mlp_shard_bwd
+  sum       dX = dX_0 + 7 stand-in partials                   tp_partial_sum
+The metric counts the GEMM FLOPs only (2 M N K per product: 9 products for
+SwiGLU, 6 for GeLU); the step time includes the two partial sums.
+
+Prints one JSON line.  Only one GPU is used: --gpus above 1 exits.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c4_bf16_swiglu_fwdbwd")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=0,
+                   help="tokens of the oracle sample (0: sized to ~15 s)")
+    return p.parse_args()
+
+
+def gemm_flops(w, N=None):
+    N = w.N if N is None else N
+    per = 2.0 * N * w.H * w.Ft
+    n_fwd = 3 if w.act == 1 else 2
+    return per * n_fwd * (3 if w.backward else 1)
+
+
+def cpu_baseline(w, tokens):
+    """The fp64 oracle, as it stands, on a token sample of the workload."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    d = wl.gen_mlp_inputs(w, n_rows=max(tokens, 1))
+    t0 = time.perf_counter()
+    f = oracle.mlp_fwd(d["X"], d["A"], d["B"], w.act, d["A_up"])
+    if w.backward:
+        oracle.mlp_bwd(d["X"], d["A"], d["B"], w.act, d["dY"], f, d["A_up"])
+    dt = time.perf_counter() - t0
+    return dt, gemm_flops(w, tokens)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs one tensor-parallel rank's shard on ONE GPU; multi-GPU runs "
+              "(collectives across GPUs) are not part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import tensor_transformer_mlp_02_amd as tp
+    from tensor_transformer_mlp_02_amd.tensors import to_device, ShardBuffers
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    assert w.dtype == wl.DT_BF16
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    d = wl.gen_mlp_inputs(w)
+    X, A, B = to_device(d["X"]), to_device(d["A"]), to_device(d["B"])
+    Au = to_device(d["A_up"]) if d["A_up"] is not None else None
+    dY = to_device(d["dY"]) if w.backward else None
+    desc = dict(S=w.S, B=w.B, H=w.H, F_shard=w.Ft, T=w.T, act=w.act, dtype=w.dtype)
+    buf = ShardBuffers(desc, backward=w.backward)
+    # the other T-1 ranks' partial outputs: seeded stand-ins of the same shape
+    stand = [to_device(p) for p in wl.gen_partials(w, w.T - 1, (w.N, w.H), 0.05)]
+    Ysum = torch.empty_like(buf.Y)
+    dXsum = torch.empty_like(buf.Y)
+    count = w.N * w.H
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        tp.tp_mlp_shard_fwd(desc, X, A, Au, B, buf.Z, buf.H, buf.Y)
+        if ev: ev[1].record(stream)
+        tp.tp_partial_sum(w.dtype, w.T, [buf.Y] + stand, count, Ysum)
+        if ev: ev[2].record(stream)
+        if w.backward:
+            tp.tp_mlp_shard_bwd(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
+                                buf.dA_up, buf.dB, buf.ws, buf.ws_bytes)
+            if ev: ev[3].record(stream)
+            tp.tp_partial_sum(w.dtype, w.T, [buf.dX] + stand, count, dXsum)
+            if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps between two events; per-call events inside
+    # each step split the time between the GEMM calls and the partial sums
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ps_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    bwd_ms = 0.0
+    if w.backward:
+        bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        ps_ms += [e[3].elapsed_time(e[4]) for e in evs]
+    ps_ms = float(np.mean(ps_ms))
+
+    flops = gemm_flops(w)
+    value = flops / (ms * 1e-3) / 1e12
+    gemm_ms = fwd_ms + bwd_ms
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    n_gemm = (2 + (4 if w.backward else 0))
+    ps_bytes = (w.T + 1) * count * 2
+    ps_gbs = ps_bytes / (ps_ms * 1e-3) / 1e9
+
+    line = {
+        "metric": "TP-shard MLP fwd+bwd TFLOP/s on 1 GPU + % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal draws, rounded to bf16)",
+        "config": {"workload": w.name, "S": w.S, "B": w.B, "H": w.H, "F": w.F, "T": w.T,
+                   "F_shard": w.Ft, "act": "swiglu" if w.act == 1 else "gelu_tanh",
+                   "rank": "one tensor-parallel rank; the other 7 ranks' partials are "
+                           "seeded stand-ins"},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "kernel": "bf16 MFMA GEMM with fused epilogues (%d launches per step)" % n_gemm,
+            "bound": "mfma",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "breakdown_ms": {"fwd_gemms": round(fwd_ms, 4), "bwd_gemms": round(bwd_ms, 4),
+                         "partial_sum_each": round(ps_ms, 4),
+                         "partial_sum_GBps": round(ps_gbs, 1),
+                         "partial_sum_hbm_frac": round(ps_gbs / PEAK_HBM_GBS, 4)},
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        tokens = args.cpu_tokens
+        if tokens <= 0:
+            dt, fl = cpu_baseline(w, 16)            # calibrate on 16 tokens
+            rate = fl / max(dt, 1e-6)
+            tokens = int(max(16, min(w.N, 15.0 * rate / gemm_flops(w, 1))))
+        dt, fl = cpu_baseline(w, tokens)
+        line["cpu_baseline"] = {
+            "value": round(fl / dt / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle, forward+backward of the same shard on {tokens} of "
+                      f"{w.N} tokens ({fl / 1e9:.1f} GFLOP in {dt:.1f} s)",
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * tpmlp.h -- C ABI of the tensor-parallel MLP shard library (libtpmlp.so).
+ *
+ * One tensor-parallel rank's share of the paired column-parallel ->
+ * activation -> row-parallel MLP, on one gfx950 (MI355X) GPU:
+ *
+ *   forward   Z_i = X A_i,  H_i = act(Z_i),  Y_i = H_i B_i
+ *   backward  dB_i = H_i^T dY,  dZ_i = (dY B_i^T) * act'(Z_i),
+ *             dA_i = X^T dZ_i,  dX_i = dZ_i A_i^T
+ *
+ * The column split of A and the row split of B, and where the two sums
+ * over shards sit (Y after the row-parallel product, dX before the
+ * column-parallel one), follow "Megatron-LM 源码精读——大模型并行训练全景",
+ * §三 3.1 (ColumnParallelLinear), 3.2 (RowParallelLinear), 3.3 (the MLP's
+ * column/row pairing and its diagram) and 3.4 (the forward-identity /
+ * backward-all-reduce and forward-all-reduce / backward-identity
+ * mappings).  Shapes follow "Megatron Core 带读" §02: hidden [S,B,H],
+ * column output [S,B,O/p], row input [S,B,I/p], row partial [S,B,O].
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout:    every matrix is row-major and contiguous.  [S,B,H] hidden
+ *            states are the [N,H] matrix with N = S*B and row n = s*B + b.
+ *            Weights use the mathematical layout: A_i [H, F_shard],
+ *            B_i [F_shard, H] (not PyTorch's transposed [out,in] storage).
+ * Types:     TP_BF16 tensors are bfloat16 bit patterns (2 bytes); TP_F32
+ *            tensors are IEEE float.  Products accumulate in fp32.  bf16
+ *            outputs are rounded to nearest even.  Weight gradients are
+ *            always fp32.
+ * Ownership: the caller owns every buffer.  The library never allocates,
+ *            frees or synchronizes; inputs are never written.  Kernels are
+ *            enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *            and the call returns without waiting for them.
+ * Pointers:  device pointers, 16-byte aligned.  Outputs must not overlap
+ *            inputs or each other (tp_partial_sum's in-place form aside).
+ * Errors:    a nonzero tp_status is returned and nothing is enqueued when
+ *            an argument check fails; tp_last_error() then holds a message
+ *            (per thread).  Argument checks touch no GPU state, so they
+ *            run on machines without a GPU.  A launch failure returns
+ *            TP_ERR_HIP.  Faults inside kernels surface at the caller's
+ *            next synchronization, as HIP errors.  The library never
+ *            aborts and never prints.
+ * Threads:   all entry points are reentrant; the only global state is a
+ *            per-device "is this a gfx950" cache filled on first use.
+ */
+#ifndef TPMLP_H
+#define TPMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* GeLU in its tanh form (Hendrycks & Gimpel); SwiGLU = silu(X Ag) * (X Au)
+ * (Shazeer, "GLU Variants Improve Transformer").  The pages name GeLU for
+ * the MLP (§三 3.3 diagram) and SwiGLU, "three matrices", for Llama-style
+ * models (§七 mlp.py) without printing either formula. */
+typedef enum tp_act { TP_ACT_GELU_TANH = 0, TP_ACT_SWIGLU = 1 } tp_act;
+
+typedef enum tp_status {
+    TP_OK = 0,
+    TP_ERR_NULL = 1,      /* a required pointer is NULL                     */
+    TP_ERR_SHAPE = 2,     /* a dimension is out of range or indivisible     */
+    TP_ERR_DTYPE = 3,     /* unknown dtype / activation, or unsupported mix */
+    TP_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned               */
+    TP_ERR_WORKSPACE = 5, /* workspace missing or too small                 */
+    TP_ERR_DEVICE = 6,    /* no current HIP device, or it is not gfx950     */
+    TP_ERR_HIP = 7,       /* a HIP launch failed                            */
+    TP_ERR_ALIAS = 8      /* an output overlaps an input or another output  */
+} tp_status;
+
+/* Largest shard count accepted (pointers of tp_partial_sum travel by value
+ * in the kernel's argument block). */
+#define TP_MAX_SHARDS 64
+/* Largest number of local experts of one grouped call. */
+#define TP_MAX_EXPERTS 64
+
+/*
+ * One shard's problem.  N = S*B tokens (may be 0: empty batch), hidden H,
+ * shard width F_shard = F/T (the full width divided by the shard count:
+ * §三 3.1, the per-partition output size is output size / world size).
+ * T (1..TP_MAX_SHARDS) is recorded for checks only: a shard's arithmetic
+ * does not depend on it.  act is a tp_act, dtype a tp_dtype.
+ * H and F_shard must be positive multiples of 8 (bf16) or 4 (fp32).
+ */
+typedef struct tp_mlp_desc {
+    int64_t S, B, H, F_shard;
+    int32_t T, act, dtype;
+} tp_mlp_desc;
+
+/*
+ * tp_mlp_shard_fwd -- forward of one shard (§三 3.1-3.3).
+ *   X         [N,H]        input hidden states (replicated on every shard)
+ *   A         [H,F_shard]  column shard of FC1 (the gate projection for
+ *                          SwiGLU)
+ *   A_up      [H,F_shard]  SwiGLU up projection; must be NULL for GeLU
+ *   B         [F_shard,H]  row shard of FC2
+ *   Z_save    GeLU: [N,F_shard] pre-activation Z;  SwiGLU: [N,2*F_shard],
+ *             row n = [G(n,:) | U(n,:)].  Saved for the backward; NULL =
+ *             forward only (nothing saved).
+ *   H_act     [N,F_shard]  post-activation (also saved for the backward)
+ *   Y_partial [N,H]        this shard's partial output; the full output
+ *                          is the sum over shards (tp_partial_sum)
+ * The activation is applied in the FC1 kernel's epilogue: Z is never
+ * re-read to compute H.
+ */
+int tp_mlp_shard_fwd(const tp_mlp_desc *desc, const void *X, const void *A,
+                     const void *A_up, const void *B, void *Z_save,
+                     void *H_act, void *Y_partial, void *stream);
+
+/* Bytes of device workspace tp_mlp_shard_bwd needs: the activation-side
+ * gradient dZ ([N,F_shard], SwiGLU [N,2*F_shard], in the dtype).  Returns
+ * 0 and sets tp_last_error() for an invalid descriptor (and for N = 0). */
+size_t tp_mlp_shard_bwd_workspace(const tp_mlp_desc *desc);
+
+/*
+ * tp_mlp_shard_bwd -- backward of one shard.
+ *   X, A, A_up, B   as in the forward
+ *   Z_save, H_act   the forward's saved tensors (Z_save required)
+ *   dY [N,H]        the FULL output gradient: the backward of the sum over
+ *                   shards is the identity, so every shard receives all of
+ *                   it (§三 3.4, the reduce mapping's backward)
+ *   dX_partial [N,H]  this shard's partial input gradient; the input
+ *                   gradient is the sum over shards (§三 3.1: dL/dX =
+ *                   sum_i dL/dY_i W_i^T), i.e. tp_partial_sum
+ *   dA  [H,F_shard] fp32   gradient of A (the gate projection for SwiGLU)
+ *   dA_up [H,F_shard] fp32 SwiGLU only, else NULL
+ *   dB  [F_shard,H] fp32
+ *   workspace, ws_bytes    at least tp_mlp_shard_bwd_workspace(desc) bytes
+ * The activation derivative is applied inside the kernel that forms
+ * dY B_i^T (in its epilogue); no separate elementwise pass runs.
+ * With N = 0 the weight gradients are written as zeros.
+ */
+int tp_mlp_shard_bwd(const tp_mlp_desc *desc, const void *X, const void *A,
+                     const void *A_up, const void *B, const void *Z_save,
+                     const void *H_act, const void *dY, void *dX_partial,
+                     float *dA, float *dA_up, float *dB, void *workspace,
+                     size_t ws_bytes, void *stream);
+
+/*
+ * tp_partial_sum -- out = sum_{i=0}^{T-1} partials[i], elementwise: the
+ * arithmetic the all-reduce performs over the T shards' partial outputs
+ * (§三 3.2/3.3: forward sum of Y_i; backward sum of dX_i), here over
+ * partials already resident in one GPU's memory.
+ *   dtype     TP_BF16 or TP_F32 (every buffer has this type)
+ *   T         1..TP_MAX_SHARDS
+ *   partials  HOST array of T device pointers, `count` elements each
+ *   out       `count` elements; may be exactly one of the partials
+ *             (in-place), must not otherwise overlap them
+ * Each element is summed in fp32 in the fixed order i = 0..T-1 and then
+ * rounded once to the output type.  count may be 0 (nothing is launched).
+ */
+int tp_partial_sum(int32_t dtype, int32_t T, const void *const *partials,
+                   int64_t count, void *out, void *stream);
+
+/*
+ * Grouped local experts: E experts, each a full SwiGLU MLP of width F
+ * (expert tensor parallelism 1), over rows already sorted by expert
+ * ("Megatron Core 带读" §09: the dispatcher brings each token to the rank
+ * that holds its expert, the local experts compute, combine returns the
+ * results; the docs index of "Megatron-LM 源码精读", "MoE 层与 Expert
+ * Parallelism": grouped-GEMM expert compute).  bf16 only.
+ * H and F must be positive multiples of 8; 1 <= E <= TP_MAX_EXPERTS.
+ */
+typedef struct tp_expert_desc {
+    int64_t H, F;
+    int32_t E, dtype;
+} tp_expert_desc;
+
+/*
+ * tp_grouped_expert_fwd
+ *   offsets  HOST array of E+1 row offsets: expert e owns rows
+ *            [offsets[e], offsets[e+1]); offsets[0] = 0, non-decreasing;
+ *            R = offsets[E] (experts may own no rows; R may be 0)
+ *   X_perm   [R,H]      routed token rows in (expert, token) order
+ *   Wg, Wu   [E,H,F]    gate / up projections of each expert
+ *   Wd       [E,F,H]    down projection of each expert
+ *   Z_save   [R,2F]     row r = [G(r,:) | U(r,:)]; NULL = forward only
+ *   H_act    [R,F]
+ *   Y_perm   [R,H]      expert outputs, unweighted (the router's weighted
+ *                       combine is outside this call)
+ */
+int tp_grouped_expert_fwd(const tp_expert_desc *desc, const int64_t *offsets,
+                          const void *X_perm, const void *Wg, const void *Wu,
+                          const void *Wd, void *Z_save, void *H_act,
+                          void *Y_perm, void *stream);
+
+/* Bytes of workspace tp_grouped_expert_bwd needs ([R,2F] bf16). */
+size_t tp_grouped_expert_bwd_workspace(const tp_expert_desc *desc,
+                                       const int64_t *offsets);
+
+/*
+ * tp_grouped_expert_bwd -- backward of tp_grouped_expert_fwd.
+ *   dY_perm [R,H]   gradient of Y_perm
+ *   dX_perm [R,H]   gradient of X_perm
+ *   dWg, dWu [E,H,F] fp32, dWd [E,F,H] fp32 (zeros for an expert with no
+ *                   rows)
+ */
+int tp_grouped_expert_bwd(const tp_expert_desc *desc, const int64_t *offsets,
+                          const void *X_perm, const void *Wg, const void *Wu,
+                          const void *Wd, const void *Z_save,
+                          const void *H_act, const void *dY_perm,
+                          void *dX_perm, float *dWg, float *dWu, float *dWd,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *tp_last_error(void);
+
+/* Fixed name of a tp_status value. */
+const char *tp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPMLP_H */

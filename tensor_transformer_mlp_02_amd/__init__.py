@@ -1,0 +1,192 @@
+"""Python binding of libtpmlp.so, the tensor-parallel MLP shard library.
+
+Argument marshalling only: each function has the name of the C entry point
+it calls (declared in include/tpmlp.h), takes device tensors (or raw
+integer device addresses) and passes their pointers and the current HIP
+stream.  No arithmetic of the method happens here: every step runs in the
+library's HIP kernels.  A nonzero status raises ``TpError``.  When the
+library has not been built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU", "TpError",
+    "tp_mlp_desc", "tp_expert_desc", "lib", "library_path",
+    "tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_mlp_shard_bwd_workspace",
+    "tp_partial_sum", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
+    "tp_grouped_expert_bwd_workspace", "tp_last_error", "tp_status_string",
+]
+
+TP_F32, TP_BF16 = 0, 1
+TP_ACT_GELU_TANH, TP_ACT_SWIGLU = 0, 1
+STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_DTYPE",
+                4: "TP_ERR_ALIGN", 5: "TP_ERR_WORKSPACE", 6: "TP_ERR_DEVICE",
+                7: "TP_ERR_HIP", 8: "TP_ERR_ALIAS"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libtpmlp.so")
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class tp_mlp_desc(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_int64), ("B", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("F_shard", ctypes.c_int64), ("T", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class tp_expert_desc(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int64), ("F", ctypes.c_int64), ("E", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(
+            f"{library_path} is missing: build it with __graft_entry__.build() "
+            "(python tensor_transformer_mlp_02_amd/build.py)")
+    L = ctypes.CDLL(library_path)
+    D = ctypes.POINTER(tp_mlp_desc)
+    ED = ctypes.POINTER(tp_expert_desc)
+    I64P = ctypes.POINTER(ctypes.c_int64)
+    L.tp_mlp_shard_fwd.argtypes = [D] + [_vp] * 8
+    L.tp_mlp_shard_fwd.restype = ctypes.c_int
+    L.tp_mlp_shard_bwd_workspace.argtypes = [D]
+    L.tp_mlp_shard_bwd_workspace.restype = ctypes.c_size_t
+    L.tp_mlp_shard_bwd.argtypes = [D] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+    L.tp_mlp_shard_bwd.restype = ctypes.c_int
+    L.tp_partial_sum.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_vp),
+                                 ctypes.c_int64, _vp, _vp]
+    L.tp_partial_sum.restype = ctypes.c_int
+    L.tp_grouped_expert_fwd.argtypes = [ED, I64P] + [_vp] * 8
+    L.tp_grouped_expert_fwd.restype = ctypes.c_int
+    L.tp_grouped_expert_bwd_workspace.argtypes = [ED, I64P]
+    L.tp_grouped_expert_bwd_workspace.restype = ctypes.c_size_t
+    L.tp_grouped_expert_bwd.argtypes = [ED, I64P] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+    L.tp_grouped_expert_bwd.restype = ctypes.c_int
+    L.tp_last_error.argtypes = []
+    L.tp_last_error.restype = ctypes.c_char_p
+    L.tp_status_string.argtypes = [ctypes.c_int]
+    L.tp_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor (must be contiguous), an int, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    if torch.cuda.is_available():
+        return torch.cuda.current_stream().cuda_stream
+    return None
+
+
+def _check(rc: int) -> int:
+    if rc != 0:
+        raise TpError(rc, tp_last_error())
+    return rc
+
+
+def tp_last_error() -> str:
+    return lib().tp_last_error().decode()
+
+
+def tp_status_string(status: int) -> str:
+    return lib().tp_status_string(int(status)).decode()
+
+
+def _desc(desc) -> tp_mlp_desc:
+    if isinstance(desc, tp_mlp_desc):
+        return desc
+    return tp_mlp_desc(**desc)
+
+
+def _edesc(desc) -> tp_expert_desc:
+    if isinstance(desc, tp_expert_desc):
+        return desc
+    return tp_expert_desc(**desc)
+
+
+def _offsets(offsets: Sequence[int]):
+    vals = [int(v) for v in offsets]
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def tp_mlp_shard_fwd(desc, X, A, A_up, B, Z_save, H_act, Y_partial, stream=None) -> int:
+    d = _desc(desc)
+    return _check(lib().tp_mlp_shard_fwd(
+        ctypes.byref(d), _ptr(X), _ptr(A), _ptr(A_up), _ptr(B), _ptr(Z_save),
+        _ptr(H_act), _ptr(Y_partial), _stream(stream)))
+
+
+def tp_mlp_shard_bwd_workspace(desc) -> int:
+    d = _desc(desc)
+    return int(lib().tp_mlp_shard_bwd_workspace(ctypes.byref(d)))
+
+
+def tp_mlp_shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up, dB,
+                     workspace, ws_bytes: int, stream=None) -> int:
+    d = _desc(desc)
+    return _check(lib().tp_mlp_shard_bwd(
+        ctypes.byref(d), _ptr(X), _ptr(A), _ptr(A_up), _ptr(B), _ptr(Z_save), _ptr(H_act),
+        _ptr(dY), _ptr(dX_partial), _ptr(dA), _ptr(dA_up), _ptr(dB), _ptr(workspace),
+        int(ws_bytes), _stream(stream)))
+
+
+def tp_partial_sum(dtype: int, T: int, partials, count: int, out, stream=None) -> int:
+    arr = None
+    if partials is not None:
+        arr = (_vp * max(1, len(partials)))(*[_ptr(p) for p in partials])
+    return _check(lib().tp_partial_sum(int(dtype), int(T), arr, int(count), _ptr(out),
+                                       _stream(stream)))
+
+
+def tp_grouped_expert_fwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, Y_perm,
+                          stream=None) -> int:
+    d = _edesc(desc)
+    return _check(lib().tp_grouped_expert_fwd(
+        ctypes.byref(d), _offsets(offsets), _ptr(X_perm), _ptr(Wg), _ptr(Wu), _ptr(Wd),
+        _ptr(Z_save), _ptr(H_act), _ptr(Y_perm), _stream(stream)))
+
+
+def tp_grouped_expert_bwd_workspace(desc, offsets) -> int:
+    d = _edesc(desc)
+    return int(lib().tp_grouped_expert_bwd_workspace(ctypes.byref(d), _offsets(offsets)))
+
+
+def tp_grouped_expert_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm,
+                          dX_perm, dWg, dWu, dWd, workspace, ws_bytes: int,
+                          stream=None) -> int:
+    d = _edesc(desc)
+    return _check(lib().tp_grouped_expert_bwd(
+        ctypes.byref(d), _offsets(offsets), _ptr(X_perm), _ptr(Wg), _ptr(Wu), _ptr(Wd),
+        _ptr(Z_save), _ptr(H_act), _ptr(dY_perm), _ptr(dX_perm), _ptr(dWg), _ptr(dWu),
+        _ptr(dWd), _ptr(workspace), int(ws_bytes), _stream(stream)))

@@ -1,0 +1,522 @@
+// extern "C" entry points of libtpmlp.so: argument checks (host only, no
+// GPU call until every check has passed), then kernel launches on the
+// caller's stream.  Declarations and the contract live in include/tpmlp.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <atomic>
+#include <string>
+
+#include "common.h"
+#include "launch.h"
+
+using namespace tpmlp;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return TP_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Buf& a, const Buf& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// every output against every input and every other output
+int check_alias(const Buf* ins, int nin, const Buf* outs, int nout) {
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i)
+      if (overlap(outs[o], ins[i]))
+        return fail(TP_ERR_ALIAS, "output %s overlaps input %s", outs[o].name, ins[i].name);
+    for (int p = o + 1; p < nout; ++p)
+      if (overlap(outs[o], outs[p]))
+        return fail(TP_ERR_ALIAS, "outputs %s and %s overlap", outs[o].name, outs[p].name);
+  }
+  return TP_OK;
+}
+
+int check_ptrs(const Buf* bufs, int n, bool required) {
+  for (int i = 0; i < n; ++i) {
+    if (!bufs[i].p) {
+      if (required) return fail(TP_ERR_NULL, "%s is NULL", bufs[i].name);
+      continue;
+    }
+    if (!aligned16(bufs[i].p))
+      return fail(TP_ERR_ALIGN, "%s is not 16-byte aligned", bufs[i].name);
+  }
+  return TP_OK;
+}
+
+// per-device gfx950 check, cached: 0 unknown, 1 yes, 2 no
+std::atomic<int> g_arch[64];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(TP_ERR_DEVICE, "no current HIP device");
+  if (dev < 64) {
+    int s = g_arch[dev].load(std::memory_order_relaxed);
+    if (s == 1) return TP_OK;
+    if (s == 2) return fail(TP_ERR_DEVICE, "device %d is not a gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(TP_ERR_DEVICE, "hipGetDeviceProperties failed on device %d", dev);
+  bool yes = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_arch[dev].store(yes ? 1 : 2, std::memory_order_relaxed);
+  if (!yes) return fail(TP_ERR_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  return TP_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+struct Shard {
+  int64_t N, H, Ft;
+  int act, dtype;
+  size_t elt;
+};
+
+int check_desc(const tp_mlp_desc* d, Shard& s) {
+  if (!d) return fail(TP_ERR_NULL, "desc is NULL");
+  if (d->dtype != TP_F32 && d->dtype != TP_BF16)
+    return fail(TP_ERR_DTYPE, "unknown dtype %d", d->dtype);
+  if (d->act != TP_ACT_GELU_TANH && d->act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_DTYPE, "unknown activation %d", d->act);
+  if (d->S < 0 || d->B < 0) return fail(TP_ERR_SHAPE, "S and B must be >= 0");
+  if (d->H <= 0 || d->F_shard <= 0) return fail(TP_ERR_SHAPE, "H and F_shard must be > 0");
+  if (d->T < 1 || d->T > TP_MAX_SHARDS)
+    return fail(TP_ERR_SHAPE, "T must be in 1..%d", TP_MAX_SHARDS);
+  if (d->S > kMaxDim || d->B > kMaxDim || d->S * d->B > kMaxDim || d->H > kMaxDim ||
+      d->F_shard > kMaxDim / 2)
+    return fail(TP_ERR_SHAPE, "dimension too large");
+  const int vec = d->dtype == TP_BF16 ? 8 : 4;
+  if (d->H % vec || d->F_shard % vec)
+    return fail(TP_ERR_SHAPE, "H and F_shard must be multiples of %d for this dtype", vec);
+  s.N = d->S * d->B;
+  s.H = d->H;
+  s.Ft = d->F_shard;
+  s.act = d->act;
+  s.dtype = d->dtype;
+  s.elt = d->dtype == TP_BF16 ? 2 : 4;
+  return TP_OK;
+}
+
+GemmArgs dense_args(int M, int N, int K) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.M = M; g.N = N; g.K = K;
+  g.ragged = RAGGED_NONE;
+  g.E = 1;
+  return g;
+}
+
+hipError_t run_gemm(int dtype, GemmKind kind, GemmArgs& g, hipStream_t st) {
+  return dtype == TP_BF16 ? gemm_bf16(kind, g, st) : gemm_f32(kind, g, st);
+}
+
+size_t dz_bytes(const Shard& s) {
+  return (size_t)s.N * (size_t)s.Ft * (s.act == TP_ACT_SWIGLU ? 2 : 1) * s.elt;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+const char* tp_status_string(int status) {
+  switch (status) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_NULL: return "TP_ERR_NULL";
+    case TP_ERR_SHAPE: return "TP_ERR_SHAPE";
+    case TP_ERR_DTYPE: return "TP_ERR_DTYPE";
+    case TP_ERR_ALIGN: return "TP_ERR_ALIGN";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE";
+    case TP_ERR_DEVICE: return "TP_ERR_DEVICE";
+    case TP_ERR_HIP: return "TP_ERR_HIP";
+    case TP_ERR_ALIAS: return "TP_ERR_ALIAS";
+  }
+  return "TP_ERR_UNKNOWN";
+}
+
+int tp_mlp_shard_fwd(const tp_mlp_desc* desc, const void* X, const void* A, const void* A_up,
+                     const void* B, void* Z_save, void* H_act, void* Y_partial, void* stream) {
+  Shard s;
+  int rc = check_desc(desc, s);
+  if (rc) return rc;
+  const bool sw = s.act == TP_ACT_SWIGLU;
+  const size_t e = s.elt;
+  Buf req[] = {{X, (size_t)(s.N * s.H) * e, "X"},
+               {A, (size_t)(s.H * s.Ft) * e, "A"},
+               {B, (size_t)(s.Ft * s.H) * e, "B"},
+               {H_act, (size_t)(s.N * s.Ft) * e, "H_act"},
+               {Y_partial, (size_t)(s.N * s.H) * e, "Y_partial"}};
+  if ((rc = check_ptrs(req, 5, true))) return rc;
+  if (sw && !A_up) return fail(TP_ERR_NULL, "A_up is required for SwiGLU");
+  if (!sw && A_up) return fail(TP_ERR_SHAPE, "A_up must be NULL for GeLU");
+  Buf opt[] = {{A_up, (size_t)(s.H * s.Ft) * e, "A_up"},
+               {Z_save, (size_t)(s.N * s.Ft) * (sw ? 2 : 1) * e, "Z_save"}};
+  if ((rc = check_ptrs(opt, 2, false))) return rc;
+  Buf ins[] = {req[0], req[1], req[2], opt[0]};
+  Buf outs[] = {req[3], req[4], opt[1]};
+  if ((rc = check_alias(ins, 4, outs, 3))) return rc;
+  if ((rc = check_device())) return rc;
+  if (s.N == 0) return ok();
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int N = (int)s.N, H = (int)s.H, Ft = (int)s.Ft;
+
+  GemmArgs g1 = dense_args(N, Ft, H);
+  g1.a = {X, nullptr, H, 0, 0};
+  g1.b = {A, A_up, Ft, 0, sw ? Ft : 0};
+  g1.epi.out0 = Z_save;
+  g1.epi.out1 = H_act;
+  g1.epi.ld0 = sw ? 2 * (int64_t)Ft : Ft;
+  g1.epi.ld1 = Ft;
+  g1.epi.split = Ft;
+  hipError_t he = run_gemm(s.dtype, sw ? GK_FC1_SWIGLU : GK_FC1_GELU, g1, st);
+  if (he != hipSuccess) return hip_fail(he, "FC1 launch");
+
+  GemmArgs g2 = dense_args(N, H, Ft);
+  g2.a = {H_act, nullptr, Ft, 0, 0};
+  g2.b = {B, nullptr, H, 0, 0};
+  g2.epi.out0 = Y_partial;
+  g2.epi.ld0 = H;
+  he = run_gemm(s.dtype, GK_FC2, g2, st);
+  if (he != hipSuccess) return hip_fail(he, "FC2 launch");
+  return ok();
+}
+
+size_t tp_mlp_shard_bwd_workspace(const tp_mlp_desc* desc) {
+  Shard s;
+  if (check_desc(desc, s)) return 0;
+  return dz_bytes(s);
+}
+
+int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void* A_up,
+                     const void* B, const void* Z_save, const void* H_act, const void* dY,
+                     void* dX_partial, float* dA, float* dA_up, float* dB, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  Shard s;
+  int rc = check_desc(desc, s);
+  if (rc) return rc;
+  const bool sw = s.act == TP_ACT_SWIGLU;
+  const size_t e = s.elt;
+  Buf in_req[] = {{X, (size_t)(s.N * s.H) * e, "X"},
+                  {A, (size_t)(s.H * s.Ft) * e, "A"},
+                  {B, (size_t)(s.Ft * s.H) * e, "B"},
+                  {Z_save, (size_t)(s.N * s.Ft) * (sw ? 2 : 1) * e, "Z_save"},
+                  {H_act, (size_t)(s.N * s.Ft) * e, "H_act"},
+                  {dY, (size_t)(s.N * s.H) * e, "dY"}};
+  Buf out_req[] = {{dX_partial, (size_t)(s.N * s.H) * e, "dX_partial"},
+                   {dA, (size_t)(s.H * s.Ft) * 4, "dA"},
+                   {dB, (size_t)(s.Ft * s.H) * 4, "dB"}};
+  if ((rc = check_ptrs(in_req, 6, true))) return rc;
+  if ((rc = check_ptrs(out_req, 3, true))) return rc;
+  if (sw && (!A_up || !dA_up)) return fail(TP_ERR_NULL, "A_up and dA_up are required for SwiGLU");
+  if (!sw && (A_up || dA_up)) return fail(TP_ERR_SHAPE, "A_up and dA_up must be NULL for GeLU");
+  Buf in_opt[] = {{A_up, (size_t)(s.H * s.Ft) * e, "A_up"}};
+  Buf out_opt[] = {{dA_up, (size_t)(s.H * s.Ft) * 4, "dA_up"}};
+  if ((rc = check_ptrs(in_opt, 1, false))) return rc;
+  if ((rc = check_ptrs(out_opt, 1, false))) return rc;
+  const size_t need = dz_bytes(s);
+  if (need > 0) {
+    if (!workspace) return fail(TP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned16(workspace)) return fail(TP_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (ws_bytes < need)
+      return fail(TP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  }
+  Buf ws = {workspace, need, "workspace"};
+  Buf ins[] = {in_req[0], in_req[1], in_req[2], in_req[3], in_req[4], in_req[5], in_opt[0]};
+  Buf outs[] = {out_req[0], out_req[1], out_req[2], out_opt[0], ws};
+  if ((rc = check_alias(ins, 7, outs, 5))) return rc;
+  if ((rc = check_device())) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int N = (int)s.N, H = (int)s.H, Ft = (int)s.Ft;
+  const int64_t zld = sw ? 2 * (int64_t)Ft : Ft;
+  hipError_t he;
+
+  // 1. dZ = (dY B^T) * act'(Z): the activation derivative in the epilogue
+  if (N > 0) {
+    GemmArgs g = dense_args(N, Ft, H);
+    g.a = {dY, nullptr, H, 0, 0};
+    g.b = {B, nullptr, H, 0, 0};
+    g.epi.aux = Z_save;
+    g.epi.ldaux = zld;
+    g.epi.out0 = workspace;
+    g.epi.ld0 = zld;
+    g.epi.split = Ft;
+    he = run_gemm(s.dtype, sw ? GK_DH_SWIGLU : GK_DH_GELU, g, st);
+    if (he != hipSuccess) return hip_fail(he, "dH launch");
+  }
+  // 2. dB = H^T dY   (K = N; N = 0 writes zeros)
+  {
+    GemmArgs g = dense_args(Ft, H, N);
+    g.a = {H_act, nullptr, Ft, 0, 0};
+    g.b = {dY, nullptr, H, 0, 0};
+    g.epi.out0 = dB;
+    g.epi.ld0 = H;
+    he = run_gemm(s.dtype, GK_WGRAD, g, st);
+    if (he != hipSuccess) return hip_fail(he, "dB launch");
+  }
+  // 3. dA (| dA_up) = X^T dZ
+  {
+    GemmArgs g = dense_args(H, sw ? 2 * Ft : Ft, N);
+    g.a = {X, nullptr, H, 0, 0};
+    g.b = {workspace, nullptr, zld, 0, 0};
+    g.epi.out0 = dA;
+    g.epi.out1 = dA_up;
+    g.epi.ld0 = Ft;
+    g.epi.ld1 = Ft;
+    g.epi.split = Ft;
+    he = run_gemm(s.dtype, sw ? GK_WGRAD_SPLIT : GK_WGRAD, g, st);
+    if (he != hipSuccess) return hip_fail(he, "dA launch");
+  }
+  // 4. dX_partial = dZ A^T  (SwiGLU: [dG|dU] [Ag|Au]^T)
+  if (N > 0) {
+    GemmArgs g = dense_args(N, H, sw ? 2 * Ft : Ft);
+    g.a = {workspace, nullptr, zld, 0, 0};
+    g.b = {A, A_up, Ft, 0, Ft};
+    g.epi.out0 = dX_partial;
+    g.epi.ld0 = H;
+    he = run_gemm(s.dtype, sw ? GK_DX_KSPLIT : GK_DX, g, st);
+    if (he != hipSuccess) return hip_fail(he, "dX launch");
+  }
+  return ok();
+}
+
+int tp_partial_sum(int32_t dtype, int32_t T, const void* const* partials, int64_t count,
+                   void* out, void* stream) {
+  if (dtype != TP_F32 && dtype != TP_BF16) return fail(TP_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (T < 1 || T > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "T must be in 1..%d", TP_MAX_SHARDS);
+  if (count < 0) return fail(TP_ERR_SHAPE, "count must be >= 0");
+  if (!partials) return fail(TP_ERR_NULL, "partials is NULL");
+  const size_t bytes = (size_t)count * (dtype == TP_BF16 ? 2 : 4);
+  Buf ob = {out, bytes, "out"};
+  if (int rc = check_ptrs(&ob, 1, true)) return rc;
+  for (int i = 0; i < T; ++i) {
+    if (!partials[i]) return fail(TP_ERR_NULL, "partials[%d] is NULL", i);
+    if (!aligned16(partials[i])) return fail(TP_ERR_ALIGN, "partials[%d] is not 16-byte aligned", i);
+    Buf pb = {partials[i], bytes, "partial"};
+    if (partials[i] != out && overlap(ob, pb))
+      return fail(TP_ERR_ALIAS, "out overlaps partials[%d] without being equal to it", i);
+  }
+  if (int rc = check_device()) return rc;
+  if (count == 0) return ok();
+  hipError_t he = partial_sum_launch(dtype, T, partials, count, out,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "partial-sum launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// grouped local experts
+// ---------------------------------------------------------------------------
+namespace {
+
+struct Experts {
+  int64_t H, F, R;
+  int E;
+};
+
+int check_experts(const tp_expert_desc* d, const int64_t* offsets, Experts& x) {
+  if (!d) return fail(TP_ERR_NULL, "desc is NULL");
+  if (d->dtype != TP_BF16) return fail(TP_ERR_DTYPE, "grouped experts support bf16 only");
+  if (d->E < 1 || d->E > TP_MAX_EXPERTS)
+    return fail(TP_ERR_SHAPE, "E must be in 1..%d", TP_MAX_EXPERTS);
+  if (d->H <= 0 || d->F <= 0 || d->H % 8 || d->F % 8)
+    return fail(TP_ERR_SHAPE, "H and F must be positive multiples of 8");
+  if (d->H > kMaxDim || d->F > kMaxDim / 2) return fail(TP_ERR_SHAPE, "dimension too large");
+  if (!offsets) return fail(TP_ERR_NULL, "offsets is NULL");
+  if (offsets[0] != 0) return fail(TP_ERR_SHAPE, "offsets[0] must be 0");
+  for (int e = 0; e < d->E; ++e)
+    if (offsets[e + 1] < offsets[e]) return fail(TP_ERR_SHAPE, "offsets must be non-decreasing");
+  if (offsets[d->E] > kMaxDim) return fail(TP_ERR_SHAPE, "too many rows");
+  x.H = d->H;
+  x.F = d->F;
+  x.E = d->E;
+  x.R = offsets[d->E];
+  return TP_OK;
+}
+
+void set_rows(GemmArgs& g, const Experts& x, const int64_t* offsets, int ragged) {
+  g.E = x.E;
+  g.ragged = ragged;
+  for (int e = 0; e <= x.E; ++e) g.row_off[e] = (int)offsets[e];
+}
+
+}  // namespace
+
+int tp_grouped_expert_fwd(const tp_expert_desc* desc, const int64_t* offsets, const void* X_perm,
+                          const void* Wg, const void* Wu, const void* Wd, void* Z_save,
+                          void* H_act, void* Y_perm, void* stream) {
+  Experts x;
+  int rc = check_experts(desc, offsets, x);
+  if (rc) return rc;
+  const size_t wbytes = (size_t)(x.E * x.H * x.F) * 2;
+  Buf req[] = {{X_perm, (size_t)(x.R * x.H) * 2, "X_perm"},
+               {Wg, wbytes, "Wg"},
+               {Wu, wbytes, "Wu"},
+               {Wd, wbytes, "Wd"},
+               {H_act, (size_t)(x.R * x.F) * 2, "H_act"},
+               {Y_perm, (size_t)(x.R * x.H) * 2, "Y_perm"}};
+  if ((rc = check_ptrs(req, 6, true))) return rc;
+  Buf zs = {Z_save, (size_t)(x.R * x.F) * 4, "Z_save"};
+  if ((rc = check_ptrs(&zs, 1, false))) return rc;
+  Buf ins[] = {req[0], req[1], req[2], req[3]};
+  Buf outs[] = {req[4], req[5], zs};
+  if ((rc = check_alias(ins, 4, outs, 3))) return rc;
+  if ((rc = check_device())) return rc;
+  if (x.R == 0) return ok();
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int H = (int)x.H, F = (int)x.F;
+  GemmArgs g1 = dense_args(0, 2 * F, H);
+  set_rows(g1, x, offsets, RAGGED_M);
+  g1.a = {X_perm, nullptr, H, 0, 0};
+  g1.b = {Wg, Wu, F, (int64_t)H * F, F};
+  g1.epi.out0 = Z_save;
+  g1.epi.out1 = H_act;
+  g1.epi.ld0 = 2 * (int64_t)F;
+  g1.epi.ld1 = F;
+  g1.epi.split = F;
+  hipError_t he = gemm_bf16(GK_FC1_SWIGLU, g1, st);
+  if (he != hipSuccess) return hip_fail(he, "grouped FC1 launch");
+
+  GemmArgs g2 = dense_args(0, H, F);
+  set_rows(g2, x, offsets, RAGGED_M);
+  g2.a = {H_act, nullptr, F, 0, 0};
+  g2.b = {Wd, nullptr, H, (int64_t)F * H, 0};
+  g2.epi.out0 = Y_perm;
+  g2.epi.ld0 = H;
+  he = gemm_bf16(GK_FC2, g2, st);
+  if (he != hipSuccess) return hip_fail(he, "grouped FC2 launch");
+  return ok();
+}
+
+size_t tp_grouped_expert_bwd_workspace(const tp_expert_desc* desc, const int64_t* offsets) {
+  Experts x;
+  if (check_experts(desc, offsets, x)) return 0;
+  return (size_t)(x.R * x.F) * 2 * 2;
+}
+
+int tp_grouped_expert_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* X_perm,
+                          const void* Wg, const void* Wu, const void* Wd, const void* Z_save,
+                          const void* H_act, const void* dY_perm, void* dX_perm, float* dWg,
+                          float* dWu, float* dWd, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  Experts x;
+  int rc = check_experts(desc, offsets, x);
+  if (rc) return rc;
+  const size_t wbytes = (size_t)(x.E * x.H * x.F) * 2;
+  const size_t gbytes = (size_t)(x.E * x.H * x.F) * 4;
+  Buf in_req[] = {{X_perm, (size_t)(x.R * x.H) * 2, "X_perm"},
+                  {Wg, wbytes, "Wg"},
+                  {Wu, wbytes, "Wu"},
+                  {Wd, wbytes, "Wd"},
+                  {Z_save, (size_t)(x.R * x.F) * 4, "Z_save"},
+                  {H_act, (size_t)(x.R * x.F) * 2, "H_act"},
+                  {dY_perm, (size_t)(x.R * x.H) * 2, "dY_perm"}};
+  Buf out_req[] = {{dX_perm, (size_t)(x.R * x.H) * 2, "dX_perm"},
+                   {dWg, gbytes, "dWg"},
+                   {dWu, gbytes, "dWu"},
+                   {dWd, gbytes, "dWd"}};
+  if ((rc = check_ptrs(in_req, 7, true))) return rc;
+  if ((rc = check_ptrs(out_req, 4, true))) return rc;
+  const size_t need = (size_t)(x.R * x.F) * 4;
+  if (need > 0) {
+    if (!workspace) return fail(TP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned16(workspace)) return fail(TP_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (ws_bytes < need)
+      return fail(TP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  }
+  Buf ws = {workspace, need, "workspace"};
+  Buf outs[] = {out_req[0], out_req[1], out_req[2], out_req[3], ws};
+  if ((rc = check_alias(in_req, 7, outs, 5))) return rc;
+  if ((rc = check_device())) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int H = (int)x.H, F = (int)x.F;
+  const int64_t HF = (int64_t)H * F;
+  hipError_t he;
+  if (x.R > 0) {
+    GemmArgs g = dense_args(0, F, H);
+    set_rows(g, x, offsets, RAGGED_M);
+    g.a = {dY_perm, nullptr, H, 0, 0};
+    g.b = {Wd, nullptr, H, HF, 0};
+    g.epi.aux = Z_save;
+    g.epi.ldaux = 2 * (int64_t)F;
+    g.epi.out0 = workspace;
+    g.epi.ld0 = 2 * (int64_t)F;
+    g.epi.split = F;
+    he = gemm_bf16(GK_DH_SWIGLU, g, st);
+    if (he != hipSuccess) return hip_fail(he, "grouped dH launch");
+  }
+  {
+    GemmArgs g = dense_args(F, H, 0);
+    set_rows(g, x, offsets, RAGGED_K);
+    g.a = {H_act, nullptr, F, 0, 0};
+    g.b = {dY_perm, nullptr, H, 0, 0};
+    g.epi.out0 = dWd;
+    g.epi.ld0 = H;
+    g.epi.bstride = HF;
+    he = gemm_bf16(GK_WGRAD, g, st);
+    if (he != hipSuccess) return hip_fail(he, "grouped dWd launch");
+  }
+  {
+    GemmArgs g = dense_args(H, 2 * F, 0);
+    set_rows(g, x, offsets, RAGGED_K);
+    g.a = {X_perm, nullptr, H, 0, 0};
+    g.b = {workspace, nullptr, 2 * (int64_t)F, 0, 0};
+    g.epi.out0 = dWg;
+    g.epi.out1 = dWu;
+    g.epi.ld0 = F;
+    g.epi.ld1 = F;
+    g.epi.split = F;
+    g.epi.bstride = HF;
+    he = gemm_bf16(GK_WGRAD_SPLIT, g, st);
+    if (he != hipSuccess) return hip_fail(he, "grouped dWg/dWu launch");
+  }
+  if (x.R > 0) {
+    GemmArgs g = dense_args(0, H, 2 * F);
+    set_rows(g, x, offsets, RAGGED_M);
+    g.a = {workspace, nullptr, 2 * (int64_t)F, 0, 0};
+    g.b = {Wg, Wu, F, HF, F};
+    g.epi.out0 = dX_perm;
+    g.epi.ld0 = H;
+    he = gemm_bf16(GK_DX_KSPLIT, g, st);
+    if (he != hipSuccess) return hip_fail(he, "grouped dX launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

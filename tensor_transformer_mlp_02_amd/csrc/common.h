@@ -1,0 +1,254 @@
+// Shared device-side pieces of the shard kernels: storage types, the
+// activation functions, the GEMM argument block and the fused epilogues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tpmlp.h"
+
+namespace tpmlp {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Round to nearest, ties to even.  NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// activations (fp32)
+//
+// GeLU, tanh form: gelu(z) = z/2 (1 + tanh(u)), u = c (z + k z^3),
+// c = sqrt(2/pi), k = 0.044715.  Since (1 + tanh(u))/2 = sigmoid(2u),
+// gelu(z) = z * s with s = sigmoid(2u), and
+// gelu'(z) = s + z * 2 s (1 - s) * c (1 + 3 k z^2).
+// SwiGLU pieces: silu(g) = g sigmoid(g), silu'(g) = s (1 + g (1 - s)).
+// sigmoid(x) = 1 / (1 + exp(-x)); exp via the hardware exp2 (__expf).
+// Large |x| saturate correctly: exp -> inf gives 0, exp -> 0 gives 1.
+// ---------------------------------------------------------------------------
+#define TP_GELU_C 0.7978845608028654f
+#define TP_GELU_K 0.044715f
+
+__device__ __forceinline__ float sigmoid_f(float x) {
+  return 1.0f / (1.0f + __expf(-x));
+}
+
+__device__ __forceinline__ float gelu_f(float z) {
+  float u = TP_GELU_C * (z + TP_GELU_K * z * z * z);
+  return z * sigmoid_f(2.0f * u);
+}
+
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  float z2 = z * z;
+  float u = TP_GELU_C * (z + TP_GELU_K * z2 * z);
+  float s = sigmoid_f(2.0f * u);
+  return s + z * 2.0f * s * (1.0f - s) * TP_GELU_C * (1.0f + 3.0f * TP_GELU_K * z2);
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
+
+__device__ __forceinline__ float silu_grad_f(float g) {
+  float s = sigmoid_f(g);
+  return s * (1.0f + g * (1.0f - s));
+}
+
+// ---------------------------------------------------------------------------
+// GEMM arguments
+//
+// C[M,N] = opA[M,K] * opB[K,N], fp32 accumulate.  An operand is
+// "K-major" when its K index is the contiguous one in memory.
+//   opA K-major:  element (m,k) at a.p0[m*a.ld + k]
+//   opA MN-major: element (m,k) at a.p0[k*a.ld + m]
+//   opB K-major:  element (k,n) at b.p0[n*b.ld + k]
+//                 (BMODE_KSPLIT: k >= b.split reads b.p1 at k - b.split)
+//   opB MN-major: element (k,n) at b.p0[k*b.ld + n]
+//                 (BMODE_PAIR32: logical column n = 64 g + 32 h + j maps to
+//                  matrix h (p0 gate / p1 up), column f = 32 g + j; this
+//                  puts the gate and up values of one f in the same lanes)
+//
+// Grouped problems: E independent problems share every operand; problem e
+// covers the rows [row_off[e], row_off[e+1]) of its ragged dimension
+// (M for RAGGED_M, K for RAGGED_K; unused for RAGGED_NONE), and its
+// "batched" operands/outputs are offset by e * bstride elements.  Row
+// indices of the ragged dimension are global (no per-expert rebasing).
+// Problem e owns blocks [tile_off[e], tile_off[e+1]).
+// ---------------------------------------------------------------------------
+enum { BMODE_PLAIN = 0, BMODE_KSPLIT = 1, BMODE_PAIR32 = 2 };
+enum { RAGGED_NONE = 0, RAGGED_M = 1, RAGGED_K = 2 };
+
+enum {
+  EPI_STORE = 0,        // out0[m,n] = c
+  EPI_GELU_FWD = 1,     // out0[m,n] = z (if out0), out1[m,n] = gelu(z)
+  EPI_SWIGLU_FWD = 2,   // out0[m,f] = g, out0[m,split+f] = u (if out0),
+                        // out1[m,f] = silu(g) u
+  EPI_GELU_BWD = 3,     // out0[m,n] = c * gelu'(aux[m,n])
+  EPI_SWIGLU_BWD = 4,   // g = aux[m,n], u = aux[m,split+n]:
+                        // out0[m,n] = c u silu'(g), out0[m,split+n] = c silu(g)
+  EPI_STORE_SPLIT = 5,  // n < split: out0[m,n]; else out1[m,n-split]
+};
+
+struct OpArgs {
+  const void* p0;
+  const void* p1;
+  int64_t ld;
+  int64_t bstride;  // per-problem element offset (0: shared by all problems)
+  int64_t split;
+};
+
+struct EpiArgs {
+  void* out0;
+  void* out1;
+  const void* aux;
+  int64_t ld0, ld1, ldaux;
+  int64_t bstride;  // per-problem element offset of out0/out1 (weight grads)
+  int64_t split;
+};
+
+struct GemmArgs {
+  OpArgs a, b;
+  EpiArgs epi;
+  int M, N, K;
+  int ragged;
+  int E;
+  int tiles_n;
+  int row_off[TP_MAX_EXPERTS + 1];
+  int tile_off[TP_MAX_EXPERTS + 1];
+};
+
+// Problem lookup shared by the GEMM kernels.
+struct TileCoord {
+  int e, tm, tn;
+  int m_begin, m_end, k_begin, k_end;
+};
+
+__device__ __forceinline__ TileCoord locate_tile(const GemmArgs& g, int tile,
+                                                 int BM) {
+  TileCoord t;
+  int e = 0;
+  while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
+  int local = tile - g.tile_off[e];
+  t.e = e;
+  t.tm = local / g.tiles_n;
+  t.tn = local - t.tm * g.tiles_n;
+  int lo = g.row_off[e], hi = g.row_off[e + 1];
+  if (g.ragged == RAGGED_M) {
+    t.m_begin = lo + t.tm * BM; t.m_end = hi; t.k_begin = 0; t.k_end = g.K;
+  } else if (g.ragged == RAGGED_K) {
+    t.m_begin = t.tm * BM; t.m_end = g.M; t.k_begin = lo; t.k_end = hi;
+  } else {
+    t.m_begin = t.tm * BM; t.m_end = g.M; t.k_begin = 0; t.k_end = g.K;
+  }
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// storage access for 4 consecutive elements
+// ---------------------------------------------------------------------------
+template <typename T> struct Store4;
+
+template <> struct Store4<bf16_t> {
+  static __device__ __forceinline__ void store(void* base, int64_t off,
+                                               const float v[4]) {
+    uint2 p;
+    p.x = pack_bf16x2(v[0], v[1]);
+    p.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(base) + off) = p;
+  }
+  static __device__ __forceinline__ void load(const void* base, int64_t off,
+                                              float v[4]) {
+    uint2 p = *reinterpret_cast<const uint2*>(
+        reinterpret_cast<const bf16_t*>(base) + off);
+    v[0] = __uint_as_float(p.x << 16);
+    v[1] = __uint_as_float(p.x & 0xffff0000u);
+    v[2] = __uint_as_float(p.y << 16);
+    v[3] = __uint_as_float(p.y & 0xffff0000u);
+  }
+};
+
+template <> struct Store4<float> {
+  static __device__ __forceinline__ void store(void* base, int64_t off,
+                                               const float v[4]) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  }
+  static __device__ __forceinline__ void load(const void* base, int64_t off,
+                                              float v[4]) {
+    float4 p = *reinterpret_cast<const float4*>(
+        reinterpret_cast<const float*>(base) + off);
+    v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fused epilogues: 4 consecutive columns n..n+3 of row m
+// (T = activation storage type, OutT = type of out0/out1 for EPI_STORE /
+//  EPI_STORE_SPLIT)
+// ---------------------------------------------------------------------------
+template <int EPI, typename T, typename OutT>
+__device__ __forceinline__ void epilogue4(const EpiArgs& ea, int e, int64_t m,
+                                          int64_t n, const float c[4]) {
+  if constexpr (EPI == EPI_STORE) {
+    Store4<OutT>::store(ea.out0, e * ea.bstride + m * ea.ld0 + n, c);
+  } else if constexpr (EPI == EPI_STORE_SPLIT) {
+    if (n < ea.split)
+      Store4<OutT>::store(ea.out0, e * ea.bstride + m * ea.ld0 + n, c);
+    else
+      Store4<OutT>::store(ea.out1, e * ea.bstride + m * ea.ld1 + (n - ea.split), c);
+  } else if constexpr (EPI == EPI_GELU_FWD) {
+    float h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = gelu_f(c[i]);
+    if (ea.out0) Store4<T>::store(ea.out0, m * ea.ld0 + n, c);
+    Store4<T>::store(ea.out1, m * ea.ld1 + n, h);
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    float z[4], d[4];
+    Store4<T>::load(ea.aux, m * ea.ldaux + n, z);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = c[i] * gelu_grad_f(z[i]);
+    Store4<T>::store(ea.out0, m * ea.ld0 + n, d);
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    float g[4], u[4], dg[4], du[4];
+    Store4<T>::load(ea.aux, m * ea.ldaux + n, g);
+    Store4<T>::load(ea.aux, m * ea.ldaux + ea.split + n, u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float s = sigmoid_f(g[i]);
+      dg[i] = c[i] * u[i] * (s * (1.0f + g[i] * (1.0f - s)));
+      du[i] = c[i] * (g[i] * s);
+    }
+    Store4<T>::store(ea.out0, m * ea.ld0 + n, dg);
+    Store4<T>::store(ea.out0, m * ea.ld0 + ea.split + n, du);
+  }
+}
+
+// SwiGLU forward epilogue: gate and up values of columns f..f+3.
+template <typename T>
+__device__ __forceinline__ void epilogue_swiglu4(const EpiArgs& ea, int64_t m,
+                                                 int64_t f, const float g[4],
+                                                 const float u[4]) {
+  float h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = silu_f(g[i]) * u[i];
+  if (ea.out0) {
+    Store4<T>::store(ea.out0, m * ea.ld0 + f, g);
+    Store4<T>::store(ea.out0, m * ea.ld0 + ea.split + f, u);
+  }
+  Store4<T>::store(ea.out1, m * ea.ld1 + f, h);
+}
+
+}  // namespace tpmlp

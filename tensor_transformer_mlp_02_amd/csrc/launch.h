@@ -1,0 +1,31 @@
+// Host-side launchers shared between the entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace tpmlp {
+
+// The GEMMs of one shard's forward and backward.
+enum GemmKind {
+  GK_FC1_GELU,     // Z = X A; epilogue: save Z, H = gelu(Z)
+  GK_FC1_SWIGLU,   // [G|U] = X [Ag|Au]; epilogue: save G|U, H = silu(G) U
+  GK_FC2,          // Y_partial = H B
+  GK_DH_GELU,      // dZ = (dY B^T) * gelu'(Z)
+  GK_DH_SWIGLU,    // [dG|dU] from dH = dY B^T and the saved G|U
+  GK_WGRAD,        // dW = L^T R  (both operands M/N-contiguous), fp32 out
+  GK_WGRAD_SPLIT,  // as GK_WGRAD with the columns split over two outputs
+  GK_DX,           // dX_partial = dZ A^T
+  GK_DX_KSPLIT,    // dX_partial = [dG|dU] [Ag|Au]^T
+};
+
+// bf16 storage, MFMA path.
+hipError_t gemm_bf16(GemmKind kind, GemmArgs& g, hipStream_t stream);
+// fp32 storage, fp32 FMA path.
+hipError_t gemm_f32(GemmKind kind, GemmArgs& g, hipStream_t stream);
+
+hipError_t partial_sum_launch(int dtype, int T, const void* const* parts,
+                              int64_t count, void* out, hipStream_t stream);
+
+}  // namespace tpmlp

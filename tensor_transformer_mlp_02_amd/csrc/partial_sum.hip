@@ -1,0 +1,114 @@
+// Partial-output sum over T shard outputs resident in one GPU's memory:
+// out = sum_{i<T} P_i, summed in fp32 in the fixed order i = 0..T-1 and
+// rounded once.  Bandwidth-bound: every byte is read or written once.
+//
+// Each thread owns UNROLL chunks of 8 elements (16 bytes of bf16, 32 bytes
+// of fp32) spaced one grid-width apart, so a wavefront's loads cover 1 KiB
+// contiguous per instruction and UNROLL independent loads of each partial
+// are in flight at once.  The T partial pointers travel by value.
+#include "common.h"
+#include "launch.h"
+
+namespace tpmlp {
+
+struct PartialPtrs {
+  const void* p[TP_MAX_SHARDS];
+};
+
+constexpr int PS_NT = 256;
+constexpr int PS_UNROLL = 4;
+
+__device__ __forceinline__ void load8(const bf16_t* p, int64_t c, float v[8]) {
+  uint4 q = *reinterpret_cast<const uint4*>(p + c * 8);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, int64_t c, float v[8]) {
+  float4 a = *reinterpret_cast<const float4*>(p + c * 8);
+  float4 b = *reinterpret_cast<const float4*>(p + c * 8 + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16_t* p, int64_t c, const float v[8]) {
+  uint4 q;
+  q.x = pack_bf16x2(v[0], v[1]);
+  q.y = pack_bf16x2(v[2], v[3]);
+  q.z = pack_bf16x2(v[4], v[5]);
+  q.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p + c * 8) = q;
+}
+__device__ __forceinline__ void store8(float* p, int64_t c, const float v[8]) {
+  *reinterpret_cast<float4*>(p + c * 8) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + c * 8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ float load1(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float load1(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ void store1(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+__device__ __forceinline__ void store1(float* p, int64_t i, float v) { p[i] = v; }
+
+template <typename T>
+__global__ __launch_bounds__(PS_NT) void partial_sum_kernel(PartialPtrs ptrs, int nparts,
+                                                            int64_t nchunks, int64_t count,
+                                                            void* out_) {
+  T* out = reinterpret_cast<T*>(out_);
+  const int64_t stride = (int64_t)gridDim.x * PS_NT;
+  const int64_t t0 = (int64_t)blockIdx.x * PS_NT + threadIdx.x;
+  for (int64_t base = t0; base < nchunks; base += stride * PS_UNROLL) {
+    float s[PS_UNROLL][8];
+    bool ok[PS_UNROLL];
+#pragma unroll
+    for (int u = 0; u < PS_UNROLL; ++u) {
+      int64_t c = base + u * stride;
+      ok[u] = c < nchunks;
+      if (ok[u]) load8(reinterpret_cast<const T*>(ptrs.p[0]), c, s[u]);
+    }
+    for (int i = 1; i < nparts; ++i) {
+      const T* p = reinterpret_cast<const T*>(ptrs.p[i]);
+      float v[PS_UNROLL][8];
+#pragma unroll
+      for (int u = 0; u < PS_UNROLL; ++u)
+        if (ok[u]) load8(p, base + u * stride, v[u]);
+#pragma unroll
+      for (int u = 0; u < PS_UNROLL; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[u][e] += v[u][e];
+    }
+#pragma unroll
+    for (int u = 0; u < PS_UNROLL; ++u)
+      if (ok[u]) store8(out, base + u * stride, s[u]);
+  }
+  // elements past the last whole chunk
+  if (blockIdx.x == 0) {
+    int64_t i = nchunks * 8 + threadIdx.x;
+    if (i < count) {
+      float s = load1(reinterpret_cast<const T*>(ptrs.p[0]), i);
+      for (int k = 1; k < nparts; ++k) s += load1(reinterpret_cast<const T*>(ptrs.p[k]), i);
+      store1(out, i, s);
+    }
+  }
+}
+
+hipError_t partial_sum_launch(int dtype, int T, const void* const* parts,
+                              int64_t count, void* out, hipStream_t stream) {
+  if (count == 0) return hipSuccess;
+  PartialPtrs ptrs;
+  for (int i = 0; i < TP_MAX_SHARDS; ++i) ptrs.p[i] = i < T ? parts[i] : nullptr;
+  const int64_t nchunks = count / 8;
+  int64_t threads = (nchunks + PS_UNROLL - 1) / PS_UNROLL;
+  int64_t blocks = (threads + PS_NT - 1) / PS_NT;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  if (dtype == TP_BF16)
+    hipLaunchKernelGGL(partial_sum_kernel<bf16_t>, dim3((unsigned)blocks), dim3(PS_NT), 0,
+                       stream, ptrs, T, nchunks, count, out);
+  else
+    hipLaunchKernelGGL(partial_sum_kernel<float>, dim3((unsigned)blocks), dim3(PS_NT), 0,
+                       stream, ptrs, T, nchunks, count, out);
+  return hipGetLastError();
+}
+
+}  // namespace tpmlp

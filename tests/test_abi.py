@@ -1,0 +1,174 @@
+"""The C ABI on the CPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status
+before touching any GPU state (so these run without a GPU; no call here
+reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_transformer_mlp_02_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpmlp.h")
+
+# Fake device addresses: 16-byte aligned, 1 TiB apart (never dereferenced:
+# every call below fails its argument checks first).
+BASE = 1 << 44
+def addr(k, off=0):
+    return BASE + (k << 40) + off
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(tp_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 9, names
+    L = tp.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_status_strings():
+    for k, v in tp.STATUS_NAMES.items():
+        assert tp.tp_status_string(k) == v
+    assert tp.tp_status_string(99) == "TP_ERR_UNKNOWN"
+
+
+def gelu_desc(**kw):
+    d = dict(S=64, B=2, H=256, F_shard=128, T=8, act=tp.TP_ACT_GELU_TANH, dtype=tp.TP_BF16)
+    d.update(kw)
+    return d
+
+
+def fwd(desc, X=addr(1), A=addr(2), A_up=None, B=addr(3), Z=addr(4), H=addr(5), Y=addr(6)):
+    try:
+        tp.tp_mlp_shard_fwd(desc, X, A, A_up, B, Z, H, Y)
+    except tp.TpError as e:
+        return e.status
+    return 0
+
+
+def bwd(desc, A_up=None, dA_up=None, ws=addr(14), ws_bytes=None, **kw):
+    p = dict(X=addr(1), A=addr(2), B=addr(3), Z=addr(4), H=addr(5), dY=addr(7),
+             dX=addr(8), dA=addr(9), dB=addr(10))
+    p.update(kw)
+    if ws_bytes is None:
+        ws_bytes = tp.tp_mlp_shard_bwd_workspace(desc)
+    try:
+        tp.tp_mlp_shard_bwd(desc, p["X"], p["A"], A_up, p["B"], p["Z"], p["H"], p["dY"],
+                            p["dX"], p["dA"], dA_up, p["dB"], ws, ws_bytes)
+    except tp.TpError as e:
+        return e.status
+    return 0
+
+
+E_NULL, E_SHAPE, E_DTYPE, E_ALIGN, E_WS, E_DEV, E_HIP, E_ALIAS = range(1, 9)
+
+
+def test_forward_argument_checks():
+    assert fwd(gelu_desc(dtype=7)) == E_DTYPE
+    assert fwd(gelu_desc(act=5)) == E_DTYPE
+    assert fwd(gelu_desc(H=0)) == E_SHAPE
+    assert fwd(gelu_desc(H=12)) == E_SHAPE             # bf16 needs multiples of 8
+    assert fwd(gelu_desc(F_shard=20)) == E_SHAPE
+    assert fwd(gelu_desc(T=0)) == E_SHAPE
+    assert fwd(gelu_desc(T=65)) == E_SHAPE
+    assert fwd(gelu_desc(S=-1)) == E_SHAPE
+    assert fwd(gelu_desc(S=1 << 20, B=1 << 20)) == E_SHAPE
+    assert fwd(gelu_desc(), X=None) == E_NULL
+    assert fwd(gelu_desc(), H=None) == E_NULL
+    assert fwd(gelu_desc(), X=addr(1, 2)) == E_ALIGN
+    assert fwd(gelu_desc(), Y=addr(6, 8)) == E_ALIGN
+    assert fwd(gelu_desc(), A_up=addr(11)) == E_SHAPE  # GeLU takes no up projection
+    assert fwd(gelu_desc(act=tp.TP_ACT_SWIGLU)) == E_NULL
+    assert fwd(gelu_desc(), Y=addr(1)) == E_ALIAS       # output over an input
+    assert fwd(gelu_desc(), Y=addr(1, 64 * 2 * 256)) == E_ALIAS  # X ends at 64*2*256*2 bytes
+    assert fwd(gelu_desc(), Z=addr(5)) == E_ALIAS       # two outputs overlap
+    assert "overlap" in tp.tp_last_error()
+
+
+def test_forward_f32_vector_width():
+    # multiples of 4 pass the shape checks (the NULL X is what stops the call)
+    assert fwd(gelu_desc(dtype=tp.TP_F32, H=12, F_shard=20), X=None) == E_NULL
+    assert fwd(gelu_desc(dtype=tp.TP_F32, H=10)) == E_SHAPE
+
+
+def test_backward_argument_checks():
+    d = gelu_desc()
+    need = tp.tp_mlp_shard_bwd_workspace(d)
+    assert need == 128 * 128 * 2
+    assert bwd(d, ws=None) == E_WS
+    assert bwd(d, ws_bytes=need - 1) == E_WS
+    assert bwd(d, ws=addr(14, 4)) == E_ALIGN
+    assert bwd(d, dA=None) == E_NULL
+    assert bwd(d, Z=None) == E_NULL
+    assert bwd(d, A_up=addr(11)) == E_SHAPE
+    assert bwd(gelu_desc(act=tp.TP_ACT_SWIGLU), A_up=addr(11)) == E_NULL  # dA_up missing
+    assert bwd(d, dX=addr(7)) == E_ALIAS               # dX over dY
+    assert bwd(d, ws=addr(9)) == E_ALIAS               # workspace over dA
+    s = gelu_desc(act=tp.TP_ACT_SWIGLU)
+    assert tp.tp_mlp_shard_bwd_workspace(s) == 128 * 2 * 128 * 2
+    assert tp.tp_mlp_shard_bwd_workspace(gelu_desc(dtype=9)) == 0
+
+
+def test_workspace_of_the_llama_shard():
+    d = dict(S=4096, B=1, H=8192, F_shard=3584, T=8, act=tp.TP_ACT_SWIGLU, dtype=tp.TP_BF16)
+    assert tp.tp_mlp_shard_bwd_workspace(d) == 4096 * 2 * 3584 * 2
+
+
+def ps(dtype=tp.TP_BF16, T=2, parts=(addr(1), addr(2)), count=1000, out=addr(3)):
+    try:
+        tp.tp_partial_sum(dtype, T, list(parts) if parts is not None else None, count, out)
+    except tp.TpError as e:
+        return e.status
+    return 0
+
+
+def test_partial_sum_argument_checks():
+    assert ps(dtype=3) == E_DTYPE
+    assert ps(T=0, parts=()) == E_SHAPE
+    assert ps(T=65, parts=[addr(1)] * 65) == E_SHAPE
+    assert ps(count=-1) == E_SHAPE
+    assert ps(parts=None) == E_NULL
+    assert ps(parts=(addr(1), None)) == E_NULL
+    assert ps(parts=(addr(1), addr(2, 2))) == E_ALIGN
+    assert ps(out=None) == E_NULL
+    assert ps(out=addr(3, 8)) == E_ALIGN
+    assert ps(out=addr(1, 16)) == E_ALIAS              # overlaps partials[0], not equal
+
+
+def gfwd(desc, offsets, **kw):
+    p = dict(X=addr(1), Wg=addr(2), Wu=addr(3), Wd=addr(4), Z=addr(5), H=addr(6), Y=addr(7))
+    p.update(kw)
+    try:
+        tp.tp_grouped_expert_fwd(desc, offsets, p["X"], p["Wg"], p["Wu"], p["Wd"], p["Z"],
+                                 p["H"], p["Y"])
+    except tp.TpError as e:
+        return e.status
+    return 0
+
+
+def test_grouped_argument_checks():
+    d = dict(H=256, F=128, E=4, dtype=tp.TP_BF16)
+    off = [0, 10, 10, 30, 31]
+    assert gfwd(dict(d, dtype=tp.TP_F32), off) == E_DTYPE
+    assert gfwd(dict(d, E=0), [0]) == E_SHAPE
+    assert gfwd(dict(d, E=65), [0] * 66) == E_SHAPE
+    assert gfwd(dict(d, F=100), off) == E_SHAPE
+    assert gfwd(d, [1, 10, 10, 30, 31]) == E_SHAPE     # must start at 0
+    assert gfwd(d, [0, 10, 9, 30, 31]) == E_SHAPE      # must not decrease
+    assert gfwd(d, off, Wd=None) == E_NULL
+    assert gfwd(d, off, Y=addr(2)) == E_ALIAS
+    assert tp.tp_grouped_expert_bwd_workspace(d, off) == 31 * 2 * 128 * 2
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="with a GPU visible these fake addresses would reach a launch")
+def test_valid_arguments_without_gpu_report_no_device():
+    assert fwd(gelu_desc()) == E_DEV
+    assert "device" in tp.tp_last_error()

@@ -1,0 +1,402 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64
+oracle on the same seeded inputs.
+
+Small shapes are compared element by element over whole tensors (several
+256-wide tiles plus ragged tails in every dimension).  The full workloads
+are compared on sampled rows (per-token outputs: Z, H, Y, dX) and sampled
+weight-gradient columns, which the oracle computes exactly by running the
+same shard narrowed to those columns (a narrower column/row split of the
+same weights, so every sampled entry is the full-length sum).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_transformer_mlp_02_amd as tp
+import workloads as wl
+from tensor_transformer_mlp_02_amd.tensors import to_device, to_host, ShardBuffers, ExpertBuffers
+from parity import TOL, assert_close, f64, sample_idx
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _desc(w, N=None):
+    S, B = (w.S, w.B) if N is None else (N, 1)
+    return dict(S=S, B=B, H=w.H, F_shard=w.Ft, T=w.T, act=w.act, dtype=w.dtype)
+
+
+def _run_shard(w, d, save=True, backward=True, desc=None):
+    desc = desc or _desc(w, d["X"].shape[0])
+    dev = {k: (to_device(d[k]) if d.get(k) is not None else None)
+           for k in ("X", "A", "A_up", "B", "dY")}
+    buf = ShardBuffers(desc, save=save, backward=backward)
+    print(f"[gpu] shard fwd {desc}", flush=True)
+    tp.tp_mlp_shard_fwd(desc, dev["X"], dev["A"], dev["A_up"], dev["B"], buf.Z, buf.H, buf.Y)
+    if backward:
+        print(f"[gpu] shard bwd {desc}", flush=True)
+        tp.tp_mlp_shard_bwd(desc, dev["X"], dev["A"], dev["A_up"], dev["B"], buf.Z, buf.H,
+                            dev["dY"], buf.dX, buf.dA, buf.dA_up, buf.dB, buf.ws, buf.ws_bytes)
+    _sync()
+    return dev, buf
+
+
+def _check_full(w, d, buf, backward=True, tol=None):
+    tol = TOL[w.dtype] if tol is None else tol
+    f = oracle.mlp_fwd(d["X"], d["A"], d["B"], w.act, d["A_up"])
+    Ft = w.Ft if d["A"].shape[1] == w.Ft else d["A"].shape[1]
+    Z = f64(to_host(buf.Z))
+    if w.act == wl.ACT_SWIGLU:
+        assert_close("G", Z[:, :Ft], f["Z"], tol)
+        assert_close("U", Z[:, Ft:], f["U"], tol)
+    else:
+        assert_close("Z", Z, f["Z"], tol)
+    assert_close("H", f64(to_host(buf.H)), f["H"], tol)
+    assert_close("Y", f64(to_host(buf.Y)), f["Y"], tol)
+    if backward:
+        b = oracle.mlp_bwd(d["X"], d["A"], d["B"], w.act, d["dY"], f, d["A_up"])
+        assert_close("dX", f64(to_host(buf.dX)), b["dX"], tol)
+        assert_close("dA", to_host(buf.dA), b["dA"], tol)
+        assert_close("dB", to_host(buf.dB), b["dB"], tol)
+        if w.act == wl.ACT_SWIGLU:
+            assert_close("dA_up", to_host(buf.dA_up), b["dA_up"], tol)
+    return f
+
+
+# ----------------------------------------------------------------------------
+# fp32 GeLU(tanh), both shards of T=2, sums vs the unsharded MLP
+# ----------------------------------------------------------------------------
+def test_c1_fp32_both_shards_and_sums():
+    w = wl.WORKLOADS["c1_f32_gelu_t2"]
+    full = wl.gen_mlp_inputs(w, shard=0)
+    ref = oracle.sharded_fwd_bwd(full["X"], full["A_full"], full["B_full"], w.T, w.act,
+                                 full["dY"])
+    Ys, dXs = [], []
+    for i in range(w.T):
+        d = wl.gen_mlp_inputs(w, shard=i)
+        dev, buf = _run_shard(w, d)
+        r = ref["shards"][i]
+        assert_close(f"Z{i}", to_host(buf.Z), r["fwd"]["Z"], 1e-5)
+        assert_close(f"H{i}", to_host(buf.H), r["fwd"]["H"], 1e-5)
+        assert_close(f"Y{i}", to_host(buf.Y), r["fwd"]["Y"], 1e-5)
+        assert_close(f"dX{i}", to_host(buf.dX), r["bwd"]["dX"], 1e-5)
+        assert_close(f"dA{i}", to_host(buf.dA), r["bwd"]["dA"], 1e-5)
+        assert_close(f"dB{i}", to_host(buf.dB), r["bwd"]["dB"], 1e-5)
+        Ys.append(buf.Y)
+        dXs.append(buf.dX)
+    N, H = w.N, w.H
+    Y = torch.empty_like(Ys[0]); dX = torch.empty_like(dXs[0])
+    tp.tp_partial_sum(tp.TP_F32, w.T, Ys, N * H, Y)
+    tp.tp_partial_sum(tp.TP_F32, w.T, dXs, N * H, dX)
+    _sync()
+    assert_close("Y = sum_i Y_i", to_host(Y), ref["Y"], 1e-5)
+    assert_close("Y vs unsharded", to_host(Y), ref["full_fwd"]["Y"], 1e-5)
+    assert_close("dX = sum_i dX_i", to_host(dX), ref["dX"], 1e-5)
+    assert_close("dX vs unsharded", to_host(dX), ref["full_bwd"]["dX"], 1e-5)
+
+
+# ----------------------------------------------------------------------------
+# small shapes spanning several tiles with ragged tails, whole tensors
+# ----------------------------------------------------------------------------
+SMALL = [
+    # (dtype, act, N, H, Ft)
+    (wl.DT_BF16, wl.ACT_GELU_TANH, 300, 520, 392),
+    (wl.DT_BF16, wl.ACT_SWIGLU, 300, 520, 392),
+    (wl.DT_BF16, wl.ACT_GELU_TANH, 513, 264, 136),
+    (wl.DT_BF16, wl.ACT_SWIGLU, 1, 8, 8),
+    (wl.DT_BF16, wl.ACT_GELU_TANH, 77, 8, 600),
+    (wl.DT_F32, wl.ACT_GELU_TANH, 300, 132, 100),
+    (wl.DT_F32, wl.ACT_SWIGLU, 70, 68, 36),
+    (wl.DT_F32, wl.ACT_SWIGLU, 1, 4, 4),
+]
+
+
+@pytest.mark.parametrize("dtype,act,N,H,Ft", SMALL)
+def test_small_shapes_full_tensors(dtype, act, N, H, Ft):
+    w = wl.Workload(60 + SMALL.index((dtype, act, N, H, Ft)), "small", dtype, act,
+                    S=N, B=1, H=H, F=Ft, T=1, w_std=0.05)
+    d = wl.gen_mlp_inputs(w)
+    dev, buf = _run_shard(w, d)
+    _check_full(w, d, buf)
+
+
+def test_empty_batch():
+    """N = 0: the forward enqueues nothing; the weight gradients are sums
+    over no tokens, i.e. zeros (the buffers start as NaN)."""
+    for dt, act in ((wl.DT_BF16, wl.ACT_SWIGLU), (wl.DT_F32, wl.ACT_GELU_TANH)):
+        H, Ft = 64, 32
+        desc = dict(S=0, B=4, H=H, F_shard=Ft, T=1, act=act, dtype=dt)
+        tdt = torch.bfloat16 if dt == wl.DT_BF16 else torch.float32
+        X = torch.empty((0, H), dtype=tdt, device="cuda")
+        A = torch.randn((H, Ft), device="cuda").to(tdt)
+        Au = torch.randn((H, Ft), device="cuda").to(tdt) if act == wl.ACT_SWIGLU else None
+        B = torch.randn((Ft, H), device="cuda").to(tdt)
+        buf = ShardBuffers(desc)
+        buf.dA.fill_(float("nan")); buf.dB.fill_(float("nan"))
+        if buf.dA_up is not None:
+            buf.dA_up.fill_(float("nan"))
+        # empty tensors may share an address; give them distinct 16-byte aligned ones
+        e = torch.empty(64 * 16, dtype=torch.uint8, device="cuda")
+        ptr = [e.data_ptr() + 16 * k for k in range(8)]
+        tp.tp_mlp_shard_fwd(desc, ptr[0], A, Au, B, ptr[1], ptr[2], ptr[3])
+        tp.tp_mlp_shard_bwd(desc, ptr[0], A, Au, B, ptr[1], ptr[2], ptr[4], ptr[5],
+                            buf.dA, buf.dA_up, buf.dB, None, 0)
+        _sync()
+        assert torch.count_nonzero(buf.dA).item() == 0 and not torch.isnan(buf.dA).any()
+        assert torch.count_nonzero(buf.dB).item() == 0 and not torch.isnan(buf.dB).any()
+        if buf.dA_up is not None:
+            assert torch.count_nonzero(buf.dA_up).item() == 0
+
+
+# ----------------------------------------------------------------------------
+# partial sum
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [wl.DT_F32, wl.DT_BF16])
+@pytest.mark.parametrize("T,count", [(1, 1), (2, 7), (3, 4099), (8, 65536 + 5), (64, 1000)])
+def test_partial_sum_vs_oracle(dtype, T, count):
+    w = wl.WORKLOADS["c3_bf16_gelu_fwdbwd"]
+    parts = wl.gen_partials(w, T, (count,), 0.5, dtype=dtype)
+    dev = [to_device(p) for p in parts]
+    out = torch.empty_like(dev[0])
+    tp.tp_partial_sum(dtype, T, dev, count, out)
+    _sync()
+    ref = oracle.partial_sum(parts)
+    got = f64(to_host(out))
+    # fp32 running sum then one rounding to the storage type
+    absum = sum(np.abs(f64(p)) for p in parts)
+    eps_store = 2.0 ** -8 if dtype == wl.DT_BF16 else 2.0 ** -23
+    bound = eps_store * np.abs(ref) + T * 2.0 ** -23 * absum
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+@pytest.mark.parametrize("dtype", [wl.DT_F32, wl.DT_BF16])
+def test_partial_sum_exact_pins(dtype):
+    w = wl.WORKLOADS["c3_bf16_gelu_fwdbwd"]
+    # values with 8 significant bits (bf16-representable, also for the fp32
+    # case): every fp32 running sum up to 8 P is then exact
+    P = wl.gen_partials(w, 1, (8192 * 3 + 3,), 1.0, dtype=wl.DT_BF16)[0]
+    if dtype == wl.DT_F32:
+        P = wl.bf16_bits_to_f32(P)
+    p = to_device(P)
+    count = P.size
+    out = torch.empty_like(p)
+    tp.tp_partial_sum(dtype, 1, [p], count, out)             # T = 1: a copy
+    _sync()
+    assert np.array_equal(to_host(out), P)
+    for T in (2, 4, 8):                                        # T equal buffers: T * P
+        tp.tp_partial_sum(dtype, T, [p] * T, count, out)
+        _sync()
+        assert np.array_equal(f64(to_host(out)), T * f64(P))
+    # in place: out == partials[0]
+    q = p.clone()
+    tp.tp_partial_sum(dtype, 2, [q, p], count, q)
+    _sync()
+    assert np.array_equal(f64(to_host(q)), 2 * f64(P))
+
+
+# ----------------------------------------------------------------------------
+# exact GPU pins
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("act", [wl.ACT_GELU_TANH, wl.ACT_SWIGLU])
+def test_dy_doubling_doubles_grads_bitwise(act):
+    w = wl.Workload(70 + act, "pin", wl.DT_BF16, act, S=300, B=1, H=520, F=392, T=1, w_std=0.05)
+    d = wl.gen_mlp_inputs(w)
+    dev, buf = _run_shard(w, d)
+    d2 = dict(d)
+    d2["dY"] = wl.f32_to_bf16_bits(2 * wl.bf16_bits_to_f32(d["dY"]))
+    dev2, buf2 = _run_shard(w, d2)
+    assert torch.equal(buf2.Y, buf.Y)
+    assert torch.equal(buf2.dX.float(), 2 * buf.dX.float())
+    assert torch.equal(buf2.dA, 2 * buf.dA)
+    assert torch.equal(buf2.dB, 2 * buf.dB)
+    if buf.dA_up is not None:
+        assert torch.equal(buf2.dA_up, 2 * buf.dA_up)
+
+
+def test_run_to_run_bitwise_determinism():
+    w = wl.Workload(75, "det", wl.DT_BF16, wl.ACT_SWIGLU, S=700, B=1, H=1032, F=520, T=1,
+                    w_std=0.03)
+    d = wl.gen_mlp_inputs(w)
+    _, b1 = _run_shard(w, d)
+    _, b2 = _run_shard(w, d)
+    for k in ("Z", "H", "Y", "dX", "dA", "dA_up", "dB"):
+        assert torch.equal(getattr(b1, k), getattr(b2, k)), k
+
+
+# ----------------------------------------------------------------------------
+# full workloads on sampled outputs
+# ----------------------------------------------------------------------------
+def _sampled_full(name, n_rows=128, n_cols=64):
+    w = wl.WORKLOADS[name]
+    d = wl.gen_mlp_inputs(w)
+    dev, buf = _run_shard(w, d, backward=w.backward)
+    tol = TOL[w.dtype]
+    rows = sample_idx(w.N, n_rows)
+    # per-token outputs: the oracle on the sampled tokens only
+    sub = {k: (d[k][rows] if k in ("X", "dY") and d[k] is not None else d[k]) for k in d}
+    f = oracle.mlp_fwd(sub["X"], d["A"], d["B"], w.act, d["A_up"])
+    Z = f64(to_host(buf.Z[rows]))
+    Ft = w.Ft
+    if w.act == wl.ACT_SWIGLU:
+        assert_close("G rows", Z[:, :Ft], f["Z"], tol)
+        assert_close("U rows", Z[:, Ft:], f["U"], tol)
+    else:
+        assert_close("Z rows", Z, f["Z"], tol)
+    assert_close("H rows", f64(to_host(buf.H[rows])), f["H"], tol)
+    assert_close("Y rows", f64(to_host(buf.Y[rows])), f["Y"], tol)
+    if not w.backward:
+        return
+    b = oracle.mlp_bwd(sub["X"], d["A"], d["B"], w.act, sub["dY"], f, d["A_up"])
+    assert_close("dX rows", f64(to_host(buf.dX[rows])), b["dX"], tol)
+    # weight gradients: the shard narrowed to sampled columns, all tokens
+    cols = sample_idx(Ft, n_cols)
+    An = np.ascontiguousarray(d["A"][:, cols]); Bn = np.ascontiguousarray(d["B"][cols, :])
+    Aun = np.ascontiguousarray(d["A_up"][:, cols]) if d["A_up"] is not None else None
+    fn = oracle.mlp_fwd(d["X"], An, Bn, w.act, Aun)
+    bn = oracle.mlp_bwd(d["X"], An, Bn, w.act, d["dY"], fn, Aun)
+    assert_close("dA cols", to_host(buf.dA[:, cols]), bn["dA"], tol)
+    assert_close("dB rows", to_host(buf.dB[cols, :]), bn["dB"], tol)
+    if w.act == wl.ACT_SWIGLU:
+        assert_close("dA_up cols", to_host(buf.dA_up[:, cols]), bn["dA_up"], tol)
+
+
+def test_c2_full_size_sampled():
+    _sampled_full("c2_bf16_gelu_fwd")
+
+
+def test_c2_forward_only_without_saving_z():
+    """Z_save = NULL: the forward-only variant writes H and Y identically."""
+    w = wl.WORKLOADS["c2_bf16_gelu_fwd"]
+    d = wl.gen_mlp_inputs(w)
+    _, b1 = _run_shard(w, d, save=True, backward=False)
+    _, b2 = _run_shard(w, d, save=False, backward=False)
+    assert torch.equal(b1.H, b2.H) and torch.equal(b1.Y, b2.Y)
+
+
+def test_c3_full_size_sampled():
+    _sampled_full("c3_bf16_gelu_fwdbwd")
+
+
+def test_c4_full_size_sampled():
+    _sampled_full("c4_bf16_swiglu_fwdbwd")
+
+
+# ----------------------------------------------------------------------------
+# grouped experts
+# ----------------------------------------------------------------------------
+def _grouped_inputs(counts, H, F, seed=80):
+    w = wl.Workload(seed, "grp", wl.DT_BF16, wl.ACT_SWIGLU, S=1, B=1, H=H, F=F, T=1,
+                    w_std=0.05, experts=len(counts))
+    E = len(counts)
+    off = np.zeros(E + 1, np.int64); off[1:] = np.cumsum(counts)
+    R = int(off[-1])
+    return w, {
+        "offsets": off,
+        "X_perm": wl.normal_bf16(1000 * seed + 1, (R, H), 1.0),
+        "Wg": wl.normal_bf16(1000 * seed + 2, (E, H, F), 0.05),
+        "Wu": wl.normal_bf16(1000 * seed + 3, (E, H, F), 0.05),
+        "Wd": wl.normal_bf16(1000 * seed + 4, (E, F, H), 0.05),
+        "dY_perm": wl.normal_bf16(1000 * seed + 5, (R, H), 1e-2),
+    }
+
+
+def _run_grouped(d, H, F, backward=True):
+    E = len(d["offsets"]) - 1
+    desc = dict(H=H, F=F, E=E, dtype=wl.DT_BF16)
+    dev = {k: to_device(d[k]) for k in ("X_perm", "Wg", "Wu", "Wd", "dY_perm")}
+    buf = ExpertBuffers(desc, d["offsets"], backward=backward)
+    print(f"[gpu] grouped fwd H={H} F={F} offsets={list(d['offsets'])}", flush=True)
+    tp.tp_grouped_expert_fwd(desc, d["offsets"], dev["X_perm"], dev["Wg"], dev["Wu"],
+                             dev["Wd"], buf.Z, buf.H, buf.Y)
+    if backward:
+        for t in (buf.dWg, buf.dWu, buf.dWd):
+            t.fill_(float("nan"))
+        print("[gpu] grouped bwd", flush=True)
+        tp.tp_grouped_expert_bwd(desc, d["offsets"], dev["X_perm"], dev["Wg"], dev["Wu"],
+                                 dev["Wd"], buf.Z, buf.H, dev["dY_perm"], buf.dX, buf.dWg,
+                                 buf.dWu, buf.dWd, buf.ws, buf.ws_bytes)
+    _sync()
+    return dev, buf
+
+
+def test_grouped_small_ragged_with_empty_expert():
+    counts = [37, 0, 300, 5]
+    H, F = 264, 136
+    w, d = _grouped_inputs(counts, H, F)
+    dev, buf = _run_grouped(d, H, F)
+    f = oracle.grouped_fwd(d["X_perm"], d["offsets"], d["Wg"], d["Wu"], d["Wd"])
+    b = oracle.grouped_bwd(d["X_perm"], d["offsets"], d["Wg"], d["Wu"], d["Wd"],
+                           d["dY_perm"], f)
+    tol = TOL[wl.DT_BF16]
+    Z = f64(to_host(buf.Z))
+    assert_close("G", Z[:, :F], f["G"], tol)
+    assert_close("U", Z[:, F:], f["U"], tol)
+    assert_close("H", f64(to_host(buf.H)), f["H"], tol)
+    assert_close("Y", f64(to_host(buf.Y)), f["Y"], tol)
+    assert_close("dX", f64(to_host(buf.dX)), b["dX"], tol)
+    for k in ("dWg", "dWu", "dWd"):
+        g = to_host(getattr(buf, k))
+        for e in range(len(counts)):
+            assert_close(f"{k}[{e}]", g[e], b[k][e], tol)   # expert 1: exact zeros
+
+
+def test_grouped_rows_equal_dense_shard_bitwise():
+    """Expert e's rows through the grouped call equal tp_mlp_shard_fwd/bwd
+    (SwiGLU, T = 1) on those rows alone, bit for bit: the same tiles run the
+    same sums."""
+    counts = [200, 0, 333, 64]
+    H, F = 264, 136
+    w, d = _grouped_inputs(counts, H, F, seed=81)
+    dev, buf = _run_grouped(d, H, F)
+    off = d["offsets"]
+    for e in range(len(counts)):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        desc = dict(S=hi - lo, B=1, H=H, F_shard=F, T=1, act=wl.ACT_SWIGLU, dtype=wl.DT_BF16)
+        sb = ShardBuffers(desc)
+        X = dev["X_perm"][lo:hi].contiguous(); dY = dev["dY_perm"][lo:hi].contiguous()
+        tp.tp_mlp_shard_fwd(desc, X, dev["Wg"][e], dev["Wu"][e], dev["Wd"][e], sb.Z, sb.H, sb.Y)
+        tp.tp_mlp_shard_bwd(desc, X, dev["Wg"][e], dev["Wu"][e], dev["Wd"][e], sb.Z, sb.H, dY,
+                            sb.dX, sb.dA, sb.dA_up, sb.dB, sb.ws, sb.ws_bytes)
+        _sync()
+        assert torch.equal(sb.Z, buf.Z[lo:hi])
+        assert torch.equal(sb.Y, buf.Y[lo:hi])
+        assert torch.equal(sb.dX, buf.dX[lo:hi])
+        assert torch.equal(sb.dA, buf.dWg[e]) and torch.equal(sb.dA_up, buf.dWu[e])
+        assert torch.equal(sb.dB, buf.dWd[e])
+
+
+def test_c5_grouped_full_size_sampled():
+    w = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
+    d = wl.gen_grouped_inputs(w)
+    H, F, E = w.H, w.F, w.experts
+    dev, buf = _run_grouped(d, H, F)
+    tol = TOL[wl.DT_BF16]
+    off = d["offsets"]
+    # per-row outputs on 16 sampled rows of every expert
+    rows, sub_off = [], [0]
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        r = lo + sample_idx(hi - lo, 16)
+        rows.extend(r.tolist()); sub_off.append(sub_off[-1] + len(r))
+    rows = np.array(rows)
+    f = oracle.grouped_fwd(d["X_perm"][rows], sub_off, d["Wg"], d["Wu"], d["Wd"])
+    b = oracle.grouped_bwd(d["X_perm"][rows], sub_off, d["Wg"], d["Wu"], d["Wd"],
+                           d["dY_perm"][rows], f)
+    assert_close("Y rows", f64(to_host(buf.Y[rows])), f["Y"], tol)
+    assert_close("H rows", f64(to_host(buf.H[rows])), f["H"], tol)
+    assert_close("dX rows", f64(to_host(buf.dX[rows])), b["dX"], tol)
+    # weight gradients on 32 sampled columns f of every expert, all rows
+    cols = sample_idx(F, 32)
+    Wg = np.ascontiguousarray(d["Wg"][:, :, cols]); Wu = np.ascontiguousarray(d["Wu"][:, :, cols])
+    Wd = np.ascontiguousarray(d["Wd"][:, cols, :])
+    fn = oracle.grouped_fwd(d["X_perm"], off, Wg, Wu, Wd)
+    bn = oracle.grouped_bwd(d["X_perm"], off, Wg, Wu, Wd, d["dY_perm"], fn)
+    assert_close("dWg cols", to_host(buf.dWg[:, :, cols]), bn["dWg"], tol)
+    assert_close("dWu cols", to_host(buf.dWu[:, :, cols]), bn["dWu"], tol)
+    assert_close("dWd rows", to_host(buf.dWd[:, cols, :]), bn["dWd"], tol)
