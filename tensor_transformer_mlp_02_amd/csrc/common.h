@@ -5,11 +5,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/tpmlp.h"
 
 namespace tpmlp {
 
 typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+// Register arrays indexed inside stay register arrays whatever the body's
+// size (a large unrolled body can otherwise defeat unrolling and push the
+// array to scratch memory).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // bf16 <-> f32

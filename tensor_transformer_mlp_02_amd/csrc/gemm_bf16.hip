@@ -57,122 +57,129 @@ __device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8]) {
   }
 }
 
+// Buffer resource over an operand: out-of-range offsets read as zero, so a
+// load needs no branch.  Offsets stay below 2^31 (dimensions are capped by
+// the entry points); OOB_OFF marks a masked-off load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OOB_OFF = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// K-contiguous operand tile straight from memory into shared memory: 256 rows
+// x 64 k, 8 x 1 KiB per wavefront.  Within each 1 KiB block lane l fills
+// the 16 bytes at l*16, i.e. row 8*blk + l/8 at physical chunk l%8, which
+// holds logical chunk (l%8) ^ swz(row).  `rs` is based at (row 0, k 0) of
+// the tile's row range; rows >= rows_valid and k >= k_lim read as zeros.
+__device__ __forceinline__ void direct_kmajor(rsrc_t rs, int64_t ld, int rows_valid,
+                                              int k0, int k_lim, bf16_t* tile,
+                                              int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;
+    const int r = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    const int k = k0 + c * 8;
+    const uint32_t off = (r < rows_valid && k < k_lim)
+                             ? (uint32_t)(((int64_t)r * ld + k) * 2) : OOB_OFF;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + blk * 512), 16, off,
+                                             0, 0, 0);
+  }
+}
+
 // Staging registers of one operand tile for one thread: 8 x 16 bytes.
 struct Stage {
   uint4 v[8];
 };
 
-// ---- opA -----------------------------------------------------------------
-template <bool KMAJOR>
-__device__ __forceinline__ void load_a(const GemmArgs& g, const bf16_t* a0,
-                                       const TileCoord& tc, int k0, int tid,
-                                       Stage& s) {
-  if constexpr (KMAJOR) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int c = tid + NT * i;
-      int r = c >> 3, kc = c & 7;
-      int m = tc.m_begin + r;
-      int k = k0 + kc * 8;
-      if (m < tc.m_end && k < tc.k_end)
-        s.v[i] = *reinterpret_cast<const uint4*>(a0 + (int64_t)m * g.a.ld + k);
-      else
-        s.v[i] = make_uint4(0, 0, 0, 0);
-    }
+__device__ __forceinline__ uint4 load16_or_zero(const bf16_t* p, const bf16_t* safe, bool ok) {
+  uint4 v = *reinterpret_cast<const uint4*>(ok ? p : safe);
+  return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
+// M/N-contiguous operand tile (64 k rows x 256 m) through registers: thread
+// (kb, rb) loads the 8 x 8 block k = 8 kb .. 8 kb + 7, m = 8 rb .. 8 rb + 7.
+// `base` points at (k 0, m 0) of the tile's m range; BMODE_PAIR32 maps the
+// logical column to one of two matrices (see GemmArgs).
+template <int BMODE>
+__device__ __forceinline__ void load_mn(const bf16_t* p0, const bf16_t* p1, int64_t ld,
+                                        int m_base, int m_lim, int k0, int k_lim, int tid,
+                                        Stage& s) {
+  const int kb = tid & 7, rb = tid >> 3;
+  const int n = m_base + rb * 8;
+  const bf16_t* base;
+  int col;
+  bool okc;
+  if constexpr (BMODE == BMODE_PAIR32) {
+    const int grp = n >> 6, w = n & 63;
+    col = grp * 32 + (w & 31);
+    base = (w < 32) ? p0 : p1;
+    okc = col < m_lim;
   } else {
-    int kb = tid & 7, rb = tid >> 3;
-    int m = tc.m_begin + rb * 8;
+    col = n;
+    base = p0;
+    okc = n < m_lim;
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int k = k0 + kb * 8 + i;
-      if (m < tc.m_end && k < tc.k_end)
-        s.v[i] = *reinterpret_cast<const uint4*>(a0 + (int64_t)k * g.a.ld + m);
-      else
-        s.v[i] = make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int k = k0 + kb * 8 + i;
+    const bool ok = okc && k < k_lim;
+    s.v[i] = load16_or_zero(base + (int64_t)k * ld + col, p0, ok);
   }
 }
 
-template <bool KMAJOR>
-__device__ __forceinline__ void store_a(bf16_t* lds, int tid, const Stage& s) {
-  if constexpr (KMAJOR) {
+__device__ __forceinline__ void store_mn(bf16_t* tile, int tid, const Stage& s) {
+  uint4 t[8];
+  transpose8x8(s.v, t);
+  const int kb = tid & 7, rb = tid >> 3;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int c = tid + NT * i;
-      int r = c >> 3, kc = c & 7;
-      *reinterpret_cast<uint4*>(lds + lds_off(r, kc)) = s.v[i];
-    }
-  } else {
-    uint4 t[8];
-    transpose8x8(s.v, t);
-    int kb = tid & 7, rb = tid >> 3;
+  for (int j = 0; j < 8; ++j)
+    *reinterpret_cast<uint4*>(tile + lds_off(rb * 8 + j, kb)) = t[j];
+}
+
+// K-contiguous operand through registers (used when one tile would need
+// two source matrices: a k split that is not a multiple of 64).
+template <int BMODE>
+__device__ __forceinline__ void load_k(const bf16_t* p0, const bf16_t* p1, int64_t ld,
+                                       int64_t split, int r_base, int r_lim, int k0,
+                                       int k_lim, int tid, Stage& s) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<uint4*>(lds + lds_off(rb * 8 + j, kb)) = t[j];
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + NT * i;
+    const int r = c >> 3, kc = c & 7;
+    const int n = r_base + r;
+    const int k = k0 + kc * 8;
+    const bool ok = n < r_lim && k < k_lim;
+    const bf16_t* p;
+    if constexpr (BMODE == BMODE_KSPLIT)
+      p = (k < split) ? p0 + (int64_t)n * ld + k : p1 + (int64_t)n * ld + (k - split);
+    else
+      p = p0 + (int64_t)n * ld + k;
+    s.v[i] = load16_or_zero(p, p0, ok);
   }
 }
 
-// ---- opB -----------------------------------------------------------------
-template <bool KMAJOR, int BMODE>
-__device__ __forceinline__ void load_b(const GemmArgs& g, const bf16_t* b0,
-                                       const bf16_t* b1, const TileCoord& tc,
-                                       int k0, int tid, Stage& s) {
-  const int n_base = tc.tn * BN;
-  if constexpr (KMAJOR) {
+__device__ __forceinline__ void store_k(bf16_t* tile, int tid, const Stage& s) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int c = tid + NT * i;
-      int r = c >> 3, kc = c & 7;
-      int n = n_base + r;
-      int k = k0 + kc * 8;
-      if (n < g.N && k < tc.k_end) {
-        const bf16_t* p;
-        if constexpr (BMODE == BMODE_KSPLIT)
-          p = (k < g.b.split) ? b0 + (int64_t)n * g.b.ld + k
-                              : b1 + (int64_t)n * g.b.ld + (k - g.b.split);
-        else
-          p = b0 + (int64_t)n * g.b.ld + k;
-        s.v[i] = *reinterpret_cast<const uint4*>(p);
-      } else {
-        s.v[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  } else {
-    int kb = tid & 7, rb = tid >> 3;
-    int n = n_base + rb * 8;
-    const bf16_t* base;
-    int col;
-    bool ok;
-    if constexpr (BMODE == BMODE_PAIR32) {
-      int grp = n >> 6, w = n & 63;
-      col = grp * 32 + (w & 31);
-      base = (w < 32) ? b0 : b1;
-      ok = col < g.b.split;  // split = width of each of the two matrices
-    } else {
-      col = n;
-      base = b0;
-      ok = n < g.N;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int k = k0 + kb * 8 + i;
-      if (ok && k < tc.k_end)
-        s.v[i] = *reinterpret_cast<const uint4*>(base + (int64_t)k * g.b.ld + col);
-      else
-        s.v[i] = make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + NT * i;
+    const int r = c >> 3, kc = c & 7;
+    *reinterpret_cast<uint4*>(tile + lds_off(r, kc)) = s.v[i];
   }
-}
-
-template <bool KMAJOR>
-__device__ __forceinline__ void store_b(bf16_t* lds, int tid, const Stage& s) {
-  store_a<KMAJOR>(lds, tid, s);  // same tile geometry (256 rows x 64 k)
 }
 
 // ---- kernel ----------------------------------------------------------------
-template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT>
+// A_KMAJOR: opA K-contiguous (loaded straight into shared memory) or M-
+// contiguous (through registers, transposed).  B likewise; B_DIRECT selects
+// the direct path for a K-contiguous opB (a k split must then be a multiple
+// of 64 so each k tile comes from one matrix).
+template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT, bool B_DIRECT>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[2 * TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -183,102 +190,149 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
   const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
   const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
   const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
+  // scalar copies of the argument block: helpers never see its address
+  const int64_t lda = g.a.ld, ldb = g.b.ld, bsplit = g.b.split;
+  const int Ncols = g.N, Ktot = g.K;
+  const EpiArgs ea = g.epi;
+  const int n_base = tc.tn * BN;
+  const int m_rows = tc.m_end - tc.m_begin;
+  // opB's valid extent along N: PAIR32 masks on the per-matrix column
+  const int n_lim = (BMODE == BMODE_PAIR32) ? (int)bsplit : Ncols;
+
+  // buffer resources based at the tile's first row (K-contiguous operands)
+  const rsrc_t rs_a = make_rsrc(A_KMAJOR ? a0 + (int64_t)tc.m_begin * lda : a0);
+  const rsrc_t rs_b0 = make_rsrc(B_KMAJOR ? b0 + (int64_t)n_base * ldb : b0);
+  const rsrc_t rs_b1 = make_rsrc(B_KMAJOR && BMODE == BMODE_KSPLIT ? b1 + (int64_t)n_base * ldb
+                                                                   : b0);
 
   f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  static_for<0, 4>([&](auto I) {
+    static_for<0, 4>([&](auto J) { acc[I][J] = (f32x16_t)(0.0f); });
+  });
 
   const int nk = (tc.k_end > tc.k_begin) ? (tc.k_end - tc.k_begin + BK - 1) / BK : 0;
 
   Stage sa, sb;
-  if (nk > 0) {
-    load_a<A_KMAJOR>(g, a0, tc, tc.k_begin, tid, sa);
-    load_b<B_KMAJOR, BMODE>(g, b0, b1, tc, tc.k_begin, tid, sb);
-    store_a<A_KMAJOR>(lds, tid, sa);
-    store_b<B_KMAJOR>(lds + BM * BK, tid, sb);
-  }
-  __syncthreads();
+  // issue the loads of k tile starting at k0 into buffer `buf`; register-
+  // staged parts land in sa / sb and are written by `commit`
+  auto issue = [&](int k0, bf16_t* buf) {
+    if constexpr (A_KMAJOR) {
+      direct_kmajor(rs_a, lda, m_rows, k0, tc.k_end, buf, wave, lane);
+    } else {
+      load_mn<BMODE_PLAIN>(a0, a0, lda, tc.m_begin, tc.m_end, k0, tc.k_end, tid, sa);
+    }
+    bf16_t* tb = buf + BM * BK;
+    if constexpr (B_KMAJOR && B_DIRECT) {
+      if constexpr (BMODE == BMODE_KSPLIT) {
+        if (k0 < bsplit)
+          direct_kmajor(rs_b0, ldb, Ncols - n_base, k0, (int)bsplit, tb, wave, lane);
+        else
+          direct_kmajor(rs_b1, ldb, Ncols - n_base, k0 - (int)bsplit, Ktot - (int)bsplit, tb,
+                        wave, lane);
+      } else {
+        direct_kmajor(rs_b0, ldb, Ncols - n_base, k0, tc.k_end, tb, wave, lane);
+      }
+    } else if constexpr (B_KMAJOR) {
+      load_k<BMODE>(b0, b1, ldb, bsplit, n_base, Ncols, k0, tc.k_end, tid, sb);
+    } else {
+      load_mn<BMODE>(b0, b1, ldb, n_base, n_lim, k0, tc.k_end, tid, sb);
+    }
+  };
+  auto commit = [&](bf16_t* buf) {
+    if constexpr (!A_KMAJOR) store_mn(buf, tid, sa);
+    if constexpr (!B_KMAJOR) store_mn(buf + BM * BK, tid, sb);
+    else if constexpr (!B_DIRECT) store_k(buf + BM * BK, tid, sb);
+  };
 
   const int r_lane = lane & 31;
   const int c_lane = lane >> 5;
+  bf16x8_t fa[2][4], fb[2][4];
+  auto frags = [&](const bf16_t* buf, int s, int slot) {
+    const int c = 2 * s + c_lane;
+    const bf16_t* la = buf;
+    const bf16_t* lb = buf + BM * BK;
+    static_for<0, 4>([&](auto I) {
+      fa[slot][I] = *reinterpret_cast<const bf16x8_t*>(la + lds_off(wm * 128 + I * 32 + r_lane, c));
+    });
+    static_for<0, 4>([&](auto J) {
+      fb[slot][J] = *reinterpret_cast<const bf16x8_t*>(lb + lds_off(wn * 128 + J * 32 + r_lane, c));
+    });
+  };
+
+  if (nk > 0) {
+    issue(tc.k_begin, lds);
+    commit(lds);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  if (nk > 0) frags(lds, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = tc.k_begin + (kt + 1) * BK;
-      load_a<A_KMAJOR>(g, a0, tc, k0, tid, sa);
-      load_b<B_KMAJOR, BMODE>(g, b0, b1, tc, k0, tid, sb);
-    }
-    const bf16_t* la = lds + (kt & 1) * TILE_ELEMS;
-    const bf16_t* lb = la + BM * BK;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8_t af[4], bfr[4];
-      const int c = 2 * s + c_lane;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(
-            la + lds_off(wm * 128 + i * 32 + r_lane, c));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-            lb + lds_off(wn * 128 + j * 32 + r_lane, c));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i],
-                                                              acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      bf16_t* nxt = lds + ((kt + 1) & 1) * TILE_ELEMS;
-      store_a<A_KMAJOR>(nxt, tid, sa);
-      store_b<B_KMAJOR>(nxt + BM * BK, tid, sb);
-    }
+    bf16_t* cur = lds + (kt & 1) * TILE_ELEMS;
+    bf16_t* nxt = lds + ((kt + 1) & 1) * TILE_ELEMS;
+    if (more) issue(tc.k_begin + (kt + 1) * BK, nxt);
+    static_for<0, BK / 16>([&](auto S) {
+      constexpr int s = decltype(S)::value;
+      if constexpr (s + 1 < BK / 16) frags(cur, s + 1, (s + 1) & 1);
+      static_for<0, 4>([&](auto I) {
+        static_for<0, 4>([&](auto J) {
+          acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][J], fa[s & 1][I],
+                                                              acc[I][J], 0, 0, 0);
+        });
+      });
+    });
+    if (more) commit(nxt);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (more) frags(nxt, 0, 0);
   }
 
   // ---- epilogue: lane holds rows m, columns n0 + 8 q + 4 c_lane + (0..3)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  static_for<0, 4>([&](auto I) {
+    constexpr int i = decltype(I)::value;
     const int64_t m = tc.m_begin + wm * 128 + i * 32 + r_lane;
-    if (m >= tc.m_end) continue;
-    if constexpr (EPI == EPI_SWIGLU_FWD) {
-#pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t f = (int64_t)tc.tn * (BN / 2) + wn * 64 + jp * 32 +
-                            q * 8 + c_lane * 4;
-          if (f >= g.epi.split) continue;
-          float gv[4], uv[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            gv[v] = acc[i][2 * jp][q * 4 + v];
-            uv[v] = acc[i][2 * jp + 1][q * 4 + v];
-          }
-          epilogue_swiglu4<bf16_t>(g.epi, m, f, gv, uv);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = (int64_t)tc.tn * BN + wn * 128 + j * 32 + q * 8 + c_lane * 4;
-          if (n >= g.N) continue;
-          float cv[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) cv[v] = acc[i][j][q * 4 + v];
-          epilogue4<EPI, bf16_t, OutT>(g.epi, tc.e, m, n, cv);
-        }
+    if (m < tc.m_end) {
+      if constexpr (EPI == EPI_SWIGLU_FWD) {
+        static_for<0, 2>([&](auto JP) {
+          constexpr int jp = decltype(JP)::value;
+          static_for<0, 4>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+            const int64_t f = (int64_t)tc.tn * (BN / 2) + wn * 64 + jp * 32 + q * 8 + c_lane * 4;
+            if (f < ea.split) {
+              float gv[4], uv[4];
+              static_for<0, 4>([&](auto V) {
+                constexpr int v = decltype(V)::value;
+                gv[v] = acc[i][2 * jp][q * 4 + v];
+                uv[v] = acc[i][2 * jp + 1][q * 4 + v];
+              });
+              epilogue_swiglu4<bf16_t>(ea, m, f, gv, uv);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        });
+      } else {
+        static_for<0, 4>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          static_for<0, 4>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+            const int64_t n = (int64_t)tc.tn * BN + wn * 128 + j * 32 + q * 8 + c_lane * 4;
+            if (n < Ncols) {
+              float cv[4];
+              static_for<0, 4>([&](auto V) {
+                constexpr int v = decltype(V)::value;
+                cv[v] = acc[i][j][q * 4 + v];
+              });
+              epilogue4<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
+            }
+            // keep each group's loads and stores local: hoisting all of
+            // them would exceed the register file
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        });
       }
     }
-  }
+  });
 }
 
 }  // namespace mfma256
@@ -302,8 +356,7 @@ static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols) {
 
 template <bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
-  // PAIR32 covers 2 * split logical columns
-  int n_cols = (BMODE == BMODE_PAIR32) ? 2 * (int)g.b.split : g.N;
+  int n_cols = g.N;
   if (BMODE == BMODE_PAIR32) {
     // logical columns are laid out in 64-wide (gate 32 | up 32) groups
     n_cols = ((int)((g.b.split + 31) / 32)) * 64;
@@ -312,8 +365,15 @@ static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   fill_tiles(g, mfma256::BM, mfma256::BN, n_cols);
   int blocks = g.tile_off[g.E];
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((mfma256::gemm_kernel<AK, BK_, BMODE, EPI, OutT>),
-                     dim3(blocks), dim3(mfma256::NT), 0, stream, g);
+  // a K-contiguous opB goes straight to shared memory unless a 64-wide k
+  // tile could straddle its two source matrices
+  const bool b_direct = BK_ && (BMODE != BMODE_KSPLIT || g.b.split % mfma256::BK == 0);
+  if (b_direct)
+    hipLaunchKernelGGL((mfma256::gemm_kernel<AK, BK_, BMODE, EPI, OutT, BK_>),
+                       dim3(blocks), dim3(mfma256::NT), 0, stream, g);
+  else
+    hipLaunchKernelGGL((mfma256::gemm_kernel<AK, BK_, BMODE, EPI, OutT, false>),
+                       dim3(blocks), dim3(mfma256::NT), 0, stream, g);
   return hipGetLastError();
 }
 
