@@ -91,6 +91,57 @@ __device__ __forceinline__ void direct_kmajor(rsrc_t rs, int64_t ld, int rows_va
   }
 }
 
+// M/N-contiguous operand tiles (64 k rows x 256 columns) live in shared
+// memory as two halves of 128 columns, [half][k][16 granules of 8], with
+// granule q of row k stored at q ^ 4 (k % 4).  A 1 KiB direct load then
+// covers 4 rows of one half (so it has one source matrix, which the gate /
+// up pair needs), and the transposed fragment reads below touch 16
+// distinct 16-byte bank slots per 4 rows.
+__device__ __forceinline__ int mn_off(int k, int c) {
+  const int h = c >> 7, q = (c >> 3) & 15, e = c & 7;
+  return h * (BK * 128) + k * 128 + ((q ^ ((k & 3) << 2)) << 3) + e;
+}
+
+// Direct load of an M/N-contiguous tile.  rs[h] is based at (k row 0 of the
+// tile, column 0 of the source matrix of half h); half h covers columns
+// col0[h] .. col0[h] + 127 of it, valid below col_lim, rows below k_valid.
+__device__ __forceinline__ void direct_mn(rsrc_t rs0, rsrc_t rs1, int64_t ld, int col00,
+                                          int col01, int col_lim, int k_valid, bf16_t* tile,
+                                          int wave, int lane) {
+  const int half = wave >> 1;
+  const rsrc_t rs = half ? rs1 : rs0;
+  const int col0 = half ? col01 : col00;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int b = (wave & 1) * 8 + i;
+    const int k = 4 * b + (lane >> 4);
+    const int q = (lane & 15) ^ ((k & 3) << 2);
+    const int col = col0 + 8 * q;
+    const uint32_t off = (k < k_valid && col < col_lim)
+                             ? (uint32_t)(((int64_t)k * ld + col) * 2) : OOB_OFF;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + half * (BK * 128) + b * 512),
+                                             16, off, 0, 0, 0);
+  }
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// MFMA fragment (32 columns from c0, 16 k from k0) of an M/N-contiguous
+// tile: lane l gets column c0 + l % 32, k = k0 + 8 (l / 32) + 0..7, the
+// same order as a 16-byte read of a K-contiguous row.
+__device__ __forceinline__ bf16x8_t frag_mn(const bf16_t* tile, int c0, int k0, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  const int c = c0 + 16 * (g & 1) + 4 * (r & 3);
+  const int k = k0 + 8 * (g >> 1) + (r >> 2);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)(tile + mn_off(k, c)));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)(tile + mn_off(k + 4, c)));
+  const auto v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
 // Staging registers of one operand tile for one thread: 8 x 16 bytes.
 struct Stage {
   uint4 v[8];
@@ -199,11 +250,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
   // opB's valid extent along N: PAIR32 masks on the per-matrix column
   const int n_lim = (BMODE == BMODE_PAIR32) ? (int)bsplit : Ncols;
 
-  // buffer resources based at the tile's first row (K-contiguous operands)
-  const rsrc_t rs_a = make_rsrc(A_KMAJOR ? a0 + (int64_t)tc.m_begin * lda : a0);
-  const rsrc_t rs_b0 = make_rsrc(B_KMAJOR ? b0 + (int64_t)n_base * ldb : b0);
-  const rsrc_t rs_b1 = make_rsrc(B_KMAJOR && BMODE == BMODE_KSPLIT ? b1 + (int64_t)n_base * ldb
-                                                                   : b0);
+  // buffer resources: K-contiguous operands are based at the tile's first
+  // row (fixed for the whole k loop); M/N-contiguous ones are re-based at
+  // each k tile's first row (see issue)
+  const rsrc_t rs_a = make_rsrc(a0 + (A_KMAJOR ? (int64_t)tc.m_begin * lda : 0));
+  const rsrc_t rs_b0 = make_rsrc(b0 + (B_KMAJOR ? (int64_t)n_base * ldb : 0));
+  const rsrc_t rs_b1 = make_rsrc((BMODE != BMODE_PLAIN ? b1 : b0) +
+                                 (B_KMAJOR ? (int64_t)n_base * ldb : 0));
 
   f32x16_t acc[4][4];
   static_for<0, 4>([&](auto I) {
@@ -212,14 +265,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
 
   const int nk = (tc.k_end > tc.k_begin) ? (tc.k_end - tc.k_begin + BK - 1) / BK : 0;
 
-  Stage sa, sb;
-  // issue the loads of k tile starting at k0 into buffer `buf`; register-
-  // staged parts land in sa / sb and are written by `commit`
+  Stage sb;  // only for a K-contiguous opB whose k split is not 64-aligned
+  // issue the loads of the k tile starting at k0 into buffer `buf`
   auto issue = [&](int k0, bf16_t* buf) {
     if constexpr (A_KMAJOR) {
       direct_kmajor(rs_a, lda, m_rows, k0, tc.k_end, buf, wave, lane);
     } else {
-      load_mn<BMODE_PLAIN>(a0, a0, lda, tc.m_begin, tc.m_end, k0, tc.k_end, tid, sa);
+      const rsrc_t r = make_rsrc(a0 + (int64_t)k0 * lda);
+      direct_mn(r, r, lda, tc.m_begin, tc.m_begin + 128, tc.m_end, tc.k_end - k0, buf, wave,
+                lane);
     }
     bf16_t* tb = buf + BM * BK;
     if constexpr (B_KMAJOR && B_DIRECT) {
@@ -234,28 +288,44 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
       }
     } else if constexpr (B_KMAJOR) {
       load_k<BMODE>(b0, b1, ldb, bsplit, n_base, Ncols, k0, tc.k_end, tid, sb);
+    } else if constexpr (BMODE == BMODE_PAIR32) {
+      // half 0: gate columns, half 1: up columns, both f = 128 tn ..
+      const rsrc_t r0 = make_rsrc(b0 + (int64_t)k0 * ldb);
+      const rsrc_t r1 = make_rsrc(b1 + (int64_t)k0 * ldb);
+      direct_mn(r0, r1, ldb, tc.tn * 128, tc.tn * 128, (int)bsplit, tc.k_end - k0, tb, wave,
+                lane);
     } else {
-      load_mn<BMODE>(b0, b1, ldb, n_base, n_lim, k0, tc.k_end, tid, sb);
+      const rsrc_t r = make_rsrc(b0 + (int64_t)k0 * ldb);
+      direct_mn(r, r, ldb, n_base, n_base + 128, Ncols, tc.k_end - k0, tb, wave, lane);
     }
   };
   auto commit = [&](bf16_t* buf) {
-    if constexpr (!A_KMAJOR) store_mn(buf, tid, sa);
-    if constexpr (!B_KMAJOR) store_mn(buf + BM * BK, tid, sb);
-    else if constexpr (!B_DIRECT) store_k(buf + BM * BK, tid, sb);
+    if constexpr (B_KMAJOR && !B_DIRECT) store_k(buf + BM * BK, tid, sb);
   };
 
   const int r_lane = lane & 31;
   const int c_lane = lane >> 5;
+  // tile column of opB block j of this wavefront
+  auto b_col = [&](int j) {
+    if constexpr (BMODE == BMODE_PAIR32) return (j & 1) * 128 + wn * 64 + (j >> 1) * 32;
+    else return wn * 128 + j * 32;
+  };
   bf16x8_t fa[2][4], fb[2][4];
   auto frags = [&](const bf16_t* buf, int s, int slot) {
     const int c = 2 * s + c_lane;
     const bf16_t* la = buf;
     const bf16_t* lb = buf + BM * BK;
     static_for<0, 4>([&](auto I) {
-      fa[slot][I] = *reinterpret_cast<const bf16x8_t*>(la + lds_off(wm * 128 + I * 32 + r_lane, c));
+      if constexpr (A_KMAJOR)
+        fa[slot][I] = *reinterpret_cast<const bf16x8_t*>(la + lds_off(wm * 128 + I * 32 + r_lane, c));
+      else
+        fa[slot][I] = frag_mn(la, wm * 128 + I * 32, 16 * s, lane);
     });
     static_for<0, 4>([&](auto J) {
-      fb[slot][J] = *reinterpret_cast<const bf16x8_t*>(lb + lds_off(wn * 128 + J * 32 + r_lane, c));
+      if constexpr (B_KMAJOR)
+        fb[slot][J] = *reinterpret_cast<const bf16x8_t*>(lb + lds_off(wn * 128 + J * 32 + r_lane, c));
+      else
+        fb[slot][J] = frag_mn(lb, b_col(J), 16 * s, lane);
     });
   };
 
