@@ -145,21 +145,43 @@ struct GemmArgs {
 };
 
 // Problem lookup shared by the GEMM kernels.
+//
+// Block placement: consecutive workgroup ids are dispatched round-robin to
+// the 8 XCDs (each with its own L2), so block b runs on XCD b % 8.  The
+// logical tile order gives each XCD a contiguous range of tiles, and
+// within a problem tiles are rastered in groups of RASTER_G tile rows
+// (column by column inside a group), so the blocks that run together on
+// one XCD share a few operand panels instead of touching all of them.
+constexpr int RASTER_G = 4;
+
 struct TileCoord {
   int e, tm, tn;
   int m_begin, m_end, k_begin, k_end;
 };
 
-__device__ __forceinline__ TileCoord locate_tile(const GemmArgs& g, int tile,
+__device__ __forceinline__ int xcd_logical_block(int b, int nb) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int q = nb >> 3, r = nb & 7;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+__device__ __forceinline__ TileCoord locate_tile(const GemmArgs& g, int block, int nblocks,
                                                  int BM) {
+  const int tile = xcd_logical_block(block, nblocks);
   TileCoord t;
   int e = 0;
   while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
-  int local = tile - g.tile_off[e];
+  const int local = tile - g.tile_off[e];
+  const int lo = g.row_off[e], hi = g.row_off[e + 1];
+  const int rows = (g.ragged == RAGGED_M) ? hi - lo : g.M;
+  const int tiles_m = (rows + BM - 1) / BM;
+  const int group = local / (RASTER_G * g.tiles_n);
+  const int first_m = group * RASTER_G;
+  const int gm = min(RASTER_G, tiles_m - first_m);
+  const int li = local - group * RASTER_G * g.tiles_n;
   t.e = e;
-  t.tm = local / g.tiles_n;
-  t.tn = local - t.tm * g.tiles_n;
-  int lo = g.row_off[e], hi = g.row_off[e + 1];
+  t.tm = first_m + li % gm;
+  t.tn = li / gm;
   if (g.ragged == RAGGED_M) {
     t.m_begin = lo + t.tm * BM; t.m_end = hi; t.k_begin = 0; t.k_end = g.K;
   } else if (g.ragged == RAGGED_K) {

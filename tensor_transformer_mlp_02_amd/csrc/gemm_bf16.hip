@@ -1,21 +1,23 @@
 // bf16 MFMA GEMM for gfx950 with the shard's fused epilogues.
 //
-// Block tile 256 x 256 x 64, 256 threads = 4 wavefronts in a 2 x 2 grid,
-// each wavefront owning a 128 x 128 sub-tile computed as 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulators: 256 per lane).
+// Block tile 256 x 256 x 64 (one block per CU: two 64 KiB shared-memory
+// tile buffers), 8 wavefronts in a 2 x 4 grid, each owning 128 x 64
+// outputs computed as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.
 //
-// Shared memory holds both operand tiles "K-contiguous": row r (an m of
-// opA or an n of opB) stores its 64 k values as eight 16-byte chunks, chunk
-// c at position c ^ swz(r), so that the per-lane 16-byte MFMA operand
-// reads of 8 or 16 consecutive rows fall in distinct banks.  Two tile
-// buffers alternate: while the MFMAs consume one, the next tile's global
-// loads are in flight in registers and are written to the other buffer
-// afterwards (one barrier per 64-wide k step).
+// Operand tiles go from memory straight into shared memory (buffer loads
+// with the LDS destination; out-of-range offsets read as zeros, so tile
+// edges need no branches).  A K-contiguous operand is stored row by row
+// (64 k = eight 16-byte chunks, chunk c of row r at c ^ swz(r)) and its
+// MFMA fragments are 16-byte reads; an M/N-contiguous operand keeps its
+// memory orientation ([half][k][granule], XOR-swizzled by k) and its
+// fragments come from transposing LDS reads (ds_read_b64_tr_b16).  Either
+// way each lane receives 8 consecutive k of one row or column, so the
+// MFMA sees the same operand order for every memory layout.
 //
-// Operands stored K-contiguous in memory are copied 16 bytes at a time.
-// Operands stored M/N-contiguous are loaded as 8 x 8 blocks (8 k rows of 8
-// consecutive m/n) and transposed in registers before the shared-memory
-// write, so the MFMA read path is the same for every operand layout.
+// Two tile buffers alternate: while the MFMAs consume one, the next k
+// tile's loads are in flight into the other (spread over the k steps),
+// and the next k step's fragments are read while the current step's MFMAs
+// run.  One barrier per 64-wide k tile.
 //
 // The MFMA is issued with the B fragment as its first operand, which
 // yields C^T blocks: each lane then holds 4 consecutive output columns of
@@ -31,30 +33,33 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 namespace mfma256 {
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NT = 256;
+// Wavefront layouts of the block tile:
+//  NW = 4: 2 x 2 wavefronts of 128 x 128 (4 x 4 MFMA blocks, 256 fp32
+//          accumulators each, one wavefront per SIMD): fragment reads need
+//          0.5 KiB of shared memory per MFMA.
+//  NW = 8: 2 x 4 wavefronts of 128 x 64 (two per SIMD: one issues MFMAs
+//          while the other waits), 0.75 KiB per MFMA.
+// Shared memory serves ~128 B/clk per CU, and the direct loads write 0.25
+// KiB per MFMA more, so NW = 8 runs close to that limit; fragment reads
+// that transpose cost more than plain ones.
+template <int NW>
+struct Cfg {
+  static constexpr int NWAVES = NW;
+  static constexpr int WAVES_N = NW == 8 ? 4 : 2;
+  static constexpr int WTM = 128, WTN = NW == 8 ? 64 : 128;  // wavefront tile
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int NT = 64 * NW;
+  // 1 KiB direct loads per wavefront and operand tile (32 per tile)
+  static constexpr int LDW = (BM * BK * 2 / 1024) / NW;
+  // 16-byte register-staged chunks per thread and operand tile
+  static constexpr int STAGE_N = BM * BK / 8 / NT;
+};
 constexpr int TILE_ELEMS = (BM + BN) * BK;  // one buffer: A then B
 
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ int lds_off(int r, int c) {
   return r * BK + ((c ^ swz(r)) << 3);
-}
-
-// 8 x 8 transpose of 16-bit elements: in[i] holds row i (8 elements),
-// out[j] receives column j (element i of out[j] = element j of in[i]).
-__device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8]) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(in);  // w[i*4 + q]
-  uint32_t* o = reinterpret_cast<uint32_t*>(out);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t lo = w[(2 * q) * 4 + (j >> 1)];
-      uint32_t hi = w[(2 * q + 1) * 4 + (j >> 1)];
-      o[j * 4 + q] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                             : ((lo & 0xffffu) | (hi << 16));
-    }
-  }
 }
 
 // Buffer resource over an operand: out-of-range offsets read as zero, so a
@@ -71,16 +76,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // K-contiguous operand tile straight from memory into shared memory: 256 rows
-// x 64 k, 8 x 1 KiB per wavefront.  Within each 1 KiB block lane l fills
+// x 64 k, LDW x 1 KiB per wavefront (instructions I0..I1-1 of them here).  Within each 1 KiB block lane l fills
 // the 16 bytes at l*16, i.e. row 8*blk + l/8 at physical chunk l%8, which
 // holds logical chunk (l%8) ^ swz(row).  `rs` is based at (row 0, k 0) of
 // the tile's row range; rows >= rows_valid and k >= k_lim read as zeros.
+template <int NW, int I0, int I1>
 __device__ __forceinline__ void direct_kmajor(rsrc_t rs, int64_t ld, int rows_valid,
                                               int k0, int k_lim, bf16_t* tile,
                                               int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = wave * 8 + i;
+  for (int i = I0; i < I1; ++i) {
+    const int blk = wave * Cfg<NW>::LDW + i;
     const int r = blk * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
     const int k = k0 + c * 8;
@@ -102,18 +108,17 @@ __device__ __forceinline__ int mn_off(int k, int c) {
   return h * (BK * 128) + k * 128 + ((q ^ ((k & 3) << 2)) << 3) + e;
 }
 
-// Direct load of an M/N-contiguous tile.  rs[h] is based at (k row 0 of the
-// tile, column 0 of the source matrix of half h); half h covers columns
-// col0[h] .. col0[h] + 127 of it, valid below col_lim, rows below k_valid.
-__device__ __forceinline__ void direct_mn(rsrc_t rs0, rsrc_t rs1, int64_t ld, int col00,
-                                          int col01, int col_lim, int k_valid, bf16_t* tile,
-                                          int wave, int lane) {
-  const int half = wave >> 1;
-  const rsrc_t rs = half ? rs1 : rs0;
-  const int col0 = half ? col01 : col00;
+// Direct load of an M/N-contiguous tile (instructions I0..I1-1 of LDW per
+// wavefront; the first half of the wavefronts fills half 0).  rs is based at (k row
+// 0 of the tile, column 0 of this half's source matrix); the half covers
+// columns col0 .. col0 + 127, valid below col_lim, rows below k_valid.
+template <int NW, int I0, int I1>
+__device__ __forceinline__ void direct_mn(rsrc_t rs, int64_t ld, int col0, int col_lim,
+                                          int k_valid, bf16_t* tile, int wave, int lane) {
+  const int half = wave / (NW / 2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int b = (wave & 1) * 8 + i;
+  for (int i = I0; i < I1; ++i) {
+    const int b = (wave % (NW / 2)) * Cfg<NW>::LDW + i;
     const int k = 4 * b + (lane >> 4);
     const int q = (lane & 15) ^ ((k & 3) << 2);
     const int col = col0 + 8 * q;
@@ -142,9 +147,60 @@ __device__ __forceinline__ bf16x8_t frag_mn(const bf16_t* tile, int c0, int k0, 
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// Staging registers of one operand tile for one thread: 8 x 16 bytes.
+// ---- in-order main-loop primitives ----------------------------------------
+// The k loop is written with these so that the compiler keeps the order
+// chosen here: the LDS reads of the next k step are issued ahead of the
+// current step's MFMAs, and a step waits for its own fragments only.  An
+// LDS read issued here completes asynchronously: its registers are only
+// used after lds_wait() has passed them through fence().
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// fragment of a K-contiguous tile: one 16-byte read
+struct FragK {
+  bf16x8_t v;
+  __device__ __forceinline__ void read(uint32_t addr) {
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+  }
+  __device__ __forceinline__ void fence() { asm volatile("" : "+v"(v)); }
+  __device__ __forceinline__ bf16x8_t op() const { return v; }
+};
+
+// fragment of an M/N-contiguous tile: two transposing 8-byte reads
+struct FragMN {
+  i16x4_t lo, hi;
+  __device__ __forceinline__ void read(uint32_t a_lo, uint32_t a_hi) {
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a_lo));
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a_hi));
+  }
+  __device__ __forceinline__ void fence() { asm volatile("" : "+v"(lo), "+v"(hi)); }
+  __device__ __forceinline__ bf16x8_t op() const {
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
+
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void mfma_32x32x16(f32x16_t& acc, const bf16x8_t& a,
+                                              const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// addresses of the two transposing reads of an M/N-contiguous fragment
+__device__ __forceinline__ void frag_mn_addr(const bf16_t* tile, int c0, int k0, int lane,
+                                             uint32_t& a_lo, uint32_t& a_hi) {
+  const int g = lane >> 4, r = lane & 15;
+  const int c = c0 + 16 * (g & 1) + 4 * (r & 3);
+  const int k = k0 + 8 * (g >> 1) + (r >> 2);
+  a_lo = lds_u32(tile + mn_off(k, c));
+  a_hi = lds_u32(tile + mn_off(k + 4, c));
+}
+
+// Staging registers of one operand tile for one thread.
+template <int NW>
 struct Stage {
-  uint4 v[8];
+  uint4 v[Cfg<NW>::STAGE_N];
 };
 
 __device__ __forceinline__ uint4 load16_or_zero(const bf16_t* p, const bf16_t* safe, bool ok) {
@@ -152,55 +208,15 @@ __device__ __forceinline__ uint4 load16_or_zero(const bf16_t* p, const bf16_t* s
   return ok ? v : make_uint4(0, 0, 0, 0);
 }
 
-// M/N-contiguous operand tile (64 k rows x 256 m) through registers: thread
-// (kb, rb) loads the 8 x 8 block k = 8 kb .. 8 kb + 7, m = 8 rb .. 8 rb + 7.
-// `base` points at (k 0, m 0) of the tile's m range; BMODE_PAIR32 maps the
-// logical column to one of two matrices (see GemmArgs).
-template <int BMODE>
-__device__ __forceinline__ void load_mn(const bf16_t* p0, const bf16_t* p1, int64_t ld,
-                                        int m_base, int m_lim, int k0, int k_lim, int tid,
-                                        Stage& s) {
-  const int kb = tid & 7, rb = tid >> 3;
-  const int n = m_base + rb * 8;
-  const bf16_t* base;
-  int col;
-  bool okc;
-  if constexpr (BMODE == BMODE_PAIR32) {
-    const int grp = n >> 6, w = n & 63;
-    col = grp * 32 + (w & 31);
-    base = (w < 32) ? p0 : p1;
-    okc = col < m_lim;
-  } else {
-    col = n;
-    base = p0;
-    okc = n < m_lim;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k = k0 + kb * 8 + i;
-    const bool ok = okc && k < k_lim;
-    s.v[i] = load16_or_zero(base + (int64_t)k * ld + col, p0, ok);
-  }
-}
-
-__device__ __forceinline__ void store_mn(bf16_t* tile, int tid, const Stage& s) {
-  uint4 t[8];
-  transpose8x8(s.v, t);
-  const int kb = tid & 7, rb = tid >> 3;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    *reinterpret_cast<uint4*>(tile + lds_off(rb * 8 + j, kb)) = t[j];
-}
-
 // K-contiguous operand through registers (used when one tile would need
 // two source matrices: a k split that is not a multiple of 64).
-template <int BMODE>
+template <int NW, int BMODE>
 __device__ __forceinline__ void load_k(const bf16_t* p0, const bf16_t* p1, int64_t ld,
                                        int64_t split, int r_base, int r_lim, int k0,
-                                       int k_lim, int tid, Stage& s) {
+                                       int k_lim, int tid, Stage<NW>& s) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + NT * i;
+  for (int i = 0; i < Cfg<NW>::STAGE_N; ++i) {
+    const int c = tid + Cfg<NW>::NT * i;
     const int r = c >> 3, kc = c & 7;
     const int n = r_base + r;
     const int k = k0 + kc * 8;
@@ -214,10 +230,11 @@ __device__ __forceinline__ void load_k(const bf16_t* p0, const bf16_t* p1, int64
   }
 }
 
-__device__ __forceinline__ void store_k(bf16_t* tile, int tid, const Stage& s) {
+template <int NW>
+__device__ __forceinline__ void store_k(bf16_t* tile, int tid, const Stage<NW>& s) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + NT * i;
+  for (int i = 0; i < Cfg<NW>::STAGE_N; ++i) {
+    const int c = tid + Cfg<NW>::NT * i;
     const int r = c >> 3, kc = c & 7;
     *reinterpret_cast<uint4*>(tile + lds_off(r, kc)) = s.v[i];
   }
@@ -228,16 +245,21 @@ __device__ __forceinline__ void store_k(bf16_t* tile, int tid, const Stage& s) {
 // contiguous (through registers, transposed).  B likewise; B_DIRECT selects
 // the direct path for a K-contiguous opB (a k split must then be a multiple
 // of 64 so each k tile comes from one matrix).
-template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT, bool B_DIRECT>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
+template <int NW, bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT, bool B_DIRECT>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
+  using C = Cfg<NW>;
+  constexpr int NWAVES = C::NWAVES, WAVES_N = C::WAVES_N, WTM = C::WTM, WTN = C::WTN;
+  constexpr int FM = C::FM, FN = C::FN, LDW = C::LDW;
   __shared__ __attribute__((aligned(1024))) bf16_t lds[2 * TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  // the wavefront index is uniform: keep it (and what derives from it) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int half_w = wave / (NWAVES / 2);  // tile half this wavefront loads
 
-  const TileCoord tc = locate_tile(g, blockIdx.x, BM);
+  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BM);
   const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
   const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
   const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
@@ -247,56 +269,53 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
   const EpiArgs ea = g.epi;
   const int n_base = tc.tn * BN;
   const int m_rows = tc.m_end - tc.m_begin;
-  // opB's valid extent along N: PAIR32 masks on the per-matrix column
-  const int n_lim = (BMODE == BMODE_PAIR32) ? (int)bsplit : Ncols;
 
-  // buffer resources: K-contiguous operands are based at the tile's first
-  // row (fixed for the whole k loop); M/N-contiguous ones are re-based at
-  // each k tile's first row (see issue)
-  const rsrc_t rs_a = make_rsrc(a0 + (A_KMAJOR ? (int64_t)tc.m_begin * lda : 0));
-  const rsrc_t rs_b0 = make_rsrc(b0 + (B_KMAJOR ? (int64_t)n_base * ldb : 0));
-  const rsrc_t rs_b1 = make_rsrc((BMODE != BMODE_PLAIN ? b1 : b0) +
-                                 (B_KMAJOR ? (int64_t)n_base * ldb : 0));
-
-  f32x16_t acc[4][4];
-  static_for<0, 4>([&](auto I) {
-    static_for<0, 4>([&](auto J) { acc[I][J] = (f32x16_t)(0.0f); });
+  f32x16_t acc[FM][FN];
+  static_for<0, FM>([&](auto I) {
+    static_for<0, FN>([&](auto J) { acc[I][J] = (f32x16_t)(0.0f); });
   });
 
   const int nk = (tc.k_end > tc.k_begin) ? (tc.k_end - tc.k_begin + BK - 1) / BK : 0;
 
-  Stage sb;  // only for a K-contiguous opB whose k split is not 64-aligned
-  // issue the loads of the k tile starting at k0 into buffer `buf`
-  auto issue = [&](int k0, bf16_t* buf) {
+  Stage<NW> sb;  // only for a K-contiguous opB whose k split is not 64-aligned
+  // Loads of the k tile starting at k0 into buffer `buf`, instructions
+  // I0..I1-1 of each wavefront's 8 per operand.  k0 >= k_end masks every
+  // load (the tile past the last one reads as zeros and is never used).
+  auto issue = [&](auto I0c, auto I1c, int k0, bf16_t* buf) {
+    constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
     if constexpr (A_KMAJOR) {
-      direct_kmajor(rs_a, lda, m_rows, k0, tc.k_end, buf, wave, lane);
+      direct_kmajor<NW, I0, I1>(make_rsrc(a0 + (int64_t)tc.m_begin * lda), lda, m_rows, k0,
+                            tc.k_end, buf, wave, lane);
     } else {
-      const rsrc_t r = make_rsrc(a0 + (int64_t)k0 * lda);
-      direct_mn(r, r, lda, tc.m_begin, tc.m_begin + 128, tc.m_end, tc.k_end - k0, buf, wave,
-                lane);
+      direct_mn<NW, I0, I1>(make_rsrc(a0 + (int64_t)k0 * lda), lda,
+                        tc.m_begin + half_w * 128, tc.m_end, tc.k_end - k0, buf, wave,
+                        lane);
     }
     bf16_t* tb = buf + BM * BK;
     if constexpr (B_KMAJOR && B_DIRECT) {
       if constexpr (BMODE == BMODE_KSPLIT) {
-        if (k0 < bsplit)
-          direct_kmajor(rs_b0, ldb, Ncols - n_base, k0, (int)bsplit, tb, wave, lane);
-        else
-          direct_kmajor(rs_b1, ldb, Ncols - n_base, k0 - (int)bsplit, Ktot - (int)bsplit, tb,
-                        wave, lane);
+        // a 64-aligned split: the whole k tile comes from one matrix
+        const bool first = k0 < bsplit;
+        const bf16_t* bp = first ? b0 : b1;
+        const int kl = first ? k0 : k0 - (int)bsplit;
+        const int lim = first ? (int)bsplit : Ktot - (int)bsplit;
+        direct_kmajor<NW, I0, I1>(make_rsrc(bp + (int64_t)n_base * ldb), ldb, Ncols - n_base, kl,
+                              k0 < tc.k_end ? lim : 0, tb, wave, lane);
       } else {
-        direct_kmajor(rs_b0, ldb, Ncols - n_base, k0, tc.k_end, tb, wave, lane);
+        direct_kmajor<NW, I0, I1>(make_rsrc(b0 + (int64_t)n_base * ldb), ldb, Ncols - n_base, k0,
+                              tc.k_end, tb, wave, lane);
       }
     } else if constexpr (B_KMAJOR) {
-      load_k<BMODE>(b0, b1, ldb, bsplit, n_base, Ncols, k0, tc.k_end, tid, sb);
+      if constexpr (I0 == 0)
+        load_k<NW, BMODE>(b0, b1, ldb, bsplit, n_base, Ncols, k0, tc.k_end, tid, sb);
     } else if constexpr (BMODE == BMODE_PAIR32) {
       // half 0: gate columns, half 1: up columns, both f = 128 tn ..
-      const rsrc_t r0 = make_rsrc(b0 + (int64_t)k0 * ldb);
-      const rsrc_t r1 = make_rsrc(b1 + (int64_t)k0 * ldb);
-      direct_mn(r0, r1, ldb, tc.tn * 128, tc.tn * 128, (int)bsplit, tc.k_end - k0, tb, wave,
-                lane);
+      const bf16_t* bp = half_w ? b1 : b0;
+      direct_mn<NW, I0, I1>(make_rsrc(bp + (int64_t)k0 * ldb), ldb, tc.tn * 128, (int)bsplit,
+                        tc.k_end - k0, tb, wave, lane);
     } else {
-      const rsrc_t r = make_rsrc(b0 + (int64_t)k0 * ldb);
-      direct_mn(r, r, ldb, n_base, n_base + 128, Ncols, tc.k_end - k0, tb, wave, lane);
+      direct_mn<NW, I0, I1>(make_rsrc(b0 + (int64_t)k0 * ldb), ldb, n_base + half_w * 128,
+                        Ncols, tc.k_end - k0, tb, wave, lane);
     }
   };
   auto commit = [&](bf16_t* buf) {
@@ -307,68 +326,101 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
   const int c_lane = lane >> 5;
   // tile column of opB block j of this wavefront
   auto b_col = [&](int j) {
-    if constexpr (BMODE == BMODE_PAIR32) return (j & 1) * 128 + wn * 64 + (j >> 1) * 32;
-    else return wn * 128 + j * 32;
+    if constexpr (BMODE == BMODE_PAIR32) return (j & 1) * 128 + wn * (WTN / 2) + (j >> 1) * 32;
+    else return wn * WTN + j * 32;
   };
-  bf16x8_t fa[2][4], fb[2][4];
-  auto frags = [&](const bf16_t* buf, int s, int slot) {
+  using FA = typename std::conditional<A_KMAJOR, FragK, FragMN>::type;
+  using FB = typename std::conditional<B_KMAJOR, FragK, FragMN>::type;
+  FA fa[2][FM];
+  FB fb[2][FN];
+  // issue the LDS reads of k step s of tile `buf` into fragment slot `slot`
+  auto read_frags = [&](const bf16_t* buf, int s, int slot) {
     const int c = 2 * s + c_lane;
     const bf16_t* la = buf;
     const bf16_t* lb = buf + BM * BK;
-    static_for<0, 4>([&](auto I) {
-      if constexpr (A_KMAJOR)
-        fa[slot][I] = *reinterpret_cast<const bf16x8_t*>(la + lds_off(wm * 128 + I * 32 + r_lane, c));
-      else
-        fa[slot][I] = frag_mn(la, wm * 128 + I * 32, 16 * s, lane);
+    static_for<0, FM>([&](auto I) {
+      if constexpr (A_KMAJOR) {
+        fa[slot][I].read(lds_u32(la + lds_off(wm * WTM + I * 32 + r_lane, c)));
+      } else {
+        uint32_t lo, hi;
+        frag_mn_addr(la, wm * WTM + I * 32, 16 * s, lane, lo, hi);
+        fa[slot][I].read(lo, hi);
+      }
     });
-    static_for<0, 4>([&](auto J) {
-      if constexpr (B_KMAJOR)
-        fb[slot][J] = *reinterpret_cast<const bf16x8_t*>(lb + lds_off(wn * 128 + J * 32 + r_lane, c));
-      else
-        fb[slot][J] = frag_mn(lb, b_col(J), 16 * s, lane);
+    static_for<0, FN>([&](auto J) {
+      if constexpr (B_KMAJOR) {
+        fb[slot][J].read(lds_u32(lb + lds_off(wn * WTN + J * 32 + r_lane, c)));
+      } else {
+        uint32_t lo, hi;
+        frag_mn_addr(lb, b_col(J), 16 * s, lane, lo, hi);
+        fb[slot][J].read(lo, hi);
+      }
     });
   };
+  auto fence_frags = [&](int slot) {
+    lds_wait();
+    static_for<0, FM>([&](auto I) { fa[slot][I].fence(); });
+    static_for<0, FN>([&](auto J) { fb[slot][J].fence(); });
+  };
+  constexpr int NSTEP = BK / 16;
 
   if (nk > 0) {
-    issue(tc.k_begin, lds);
+    issue(std::integral_constant<int, 0>{}, std::integral_constant<int, LDW>{}, tc.k_begin, lds);
     commit(lds);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-  if (nk > 0) frags(lds, 0, 0);
+  if (nk > 0) read_frags(lds, 0, 0);
+  // accumulators were zeroed by VALU writes: cover the write-to-MFMA gap
+  asm volatile("s_nop 4");
 
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
     bf16_t* cur = lds + (kt & 1) * TILE_ELEMS;
     bf16_t* nxt = lds + ((kt + 1) & 1) * TILE_ELEMS;
-    if (more) issue(tc.k_begin + (kt + 1) * BK, nxt);
-    static_for<0, BK / 16>([&](auto S) {
+    // next tile's start; past the end on the last iteration (masked loads)
+    const int kn = tc.k_begin + (kt + 1) * BK;
+    static_for<0, NSTEP>([&](auto S) {
       constexpr int s = decltype(S)::value;
-      if constexpr (s + 1 < BK / 16) frags(cur, s + 1, (s + 1) & 1);
-      static_for<0, 4>([&](auto I) {
-        static_for<0, 4>([&](auto J) {
-          acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][J], fa[s & 1][I],
-                                                              acc[I][J], 0, 0, 0);
+      constexpr int slot = s & 1;
+      fence_frags(slot);
+      if constexpr (s == 0) {
+        issue(std::integral_constant<int, 0>{}, std::integral_constant<int, LDW>{}, kn, nxt);
+      }
+      if constexpr (s + 1 < NSTEP) {
+        read_frags(cur, s + 1, slot ^ 1);
+      } else {
+        // every wavefront is done reading `cur` and its loads into `nxt`
+        // have landed: after the barrier, read the next tile's first step
+        // while this step's MFMAs run
+        commit(nxt);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        read_frags(nxt, 0, slot ^ 1);
+      }
+      static_for<0, FM>([&](auto I) {
+        static_for<0, FN>([&](auto J) {
+          mfma_32x32x16(acc[I][J], fb[slot][J].op(), fa[slot][I].op());
         });
       });
     });
-    if (more) commit(nxt);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (more) frags(nxt, 0, 0);
   }
+  // the last iteration's reads of the (unused) next tile may still be in
+  // flight into fragment registers, and the last MFMAs' results are read by
+  // the epilogue's VALU code: drain both before the registers are reused
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 
   // ---- epilogue: lane holds rows m, columns n0 + 8 q + 4 c_lane + (0..3)
-  static_for<0, 4>([&](auto I) {
+  static_for<0, FM>([&](auto I) {
     constexpr int i = decltype(I)::value;
-    const int64_t m = tc.m_begin + wm * 128 + i * 32 + r_lane;
+    const int64_t m = tc.m_begin + wm * WTM + i * 32 + r_lane;
     if (m < tc.m_end) {
       if constexpr (EPI == EPI_SWIGLU_FWD) {
-        static_for<0, 2>([&](auto JP) {
+        static_for<0, FN / 2>([&](auto JP) {
           constexpr int jp = decltype(JP)::value;
           static_for<0, 4>([&](auto Q) {
             constexpr int q = decltype(Q)::value;
-            const int64_t f = (int64_t)tc.tn * (BN / 2) + wn * 64 + jp * 32 + q * 8 + c_lane * 4;
+            const int64_t f = (int64_t)tc.tn * (BN / 2) + wn * (WTN / 2) + jp * 32 + q * 8 +
+                              c_lane * 4;
             if (f < ea.split) {
               float gv[4], uv[4];
               static_for<0, 4>([&](auto V) {
@@ -382,11 +434,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs g) {
           });
         });
       } else {
-        static_for<0, 4>([&](auto J) {
+        static_for<0, FN>([&](auto J) {
           constexpr int j = decltype(J)::value;
           static_for<0, 4>([&](auto Q) {
             constexpr int q = decltype(Q)::value;
-            const int64_t n = (int64_t)tc.tn * BN + wn * 128 + j * 32 + q * 8 + c_lane * 4;
+            const int64_t n = (int64_t)tc.tn * BN + wn * WTN + j * 32 + q * 8 + c_lane * 4;
             if (n < Ncols) {
               float cv[4];
               static_for<0, 4>([&](auto V) {
@@ -424,7 +476,7 @@ static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols) {
   }
 }
 
-template <bool AK, bool BK_, int BMODE, int EPI, typename OutT>
+template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   int n_cols = g.N;
   if (BMODE == BMODE_PAIR32) {
@@ -439,34 +491,37 @@ static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   // tile could straddle its two source matrices
   const bool b_direct = BK_ && (BMODE != BMODE_KSPLIT || g.b.split % mfma256::BK == 0);
   if (b_direct)
-    hipLaunchKernelGGL((mfma256::gemm_kernel<AK, BK_, BMODE, EPI, OutT, BK_>),
-                       dim3(blocks), dim3(mfma256::NT), 0, stream, g);
+    hipLaunchKernelGGL((mfma256::gemm_kernel<NW, AK, BK_, BMODE, EPI, OutT, BK_>),
+                       dim3(blocks), dim3(64 * NW), 0, stream, g);
   else
-    hipLaunchKernelGGL((mfma256::gemm_kernel<AK, BK_, BMODE, EPI, OutT, false>),
-                       dim3(blocks), dim3(mfma256::NT), 0, stream, g);
+    hipLaunchKernelGGL((mfma256::gemm_kernel<NW, AK, BK_, BMODE, EPI, OutT, false>),
+                       dim3(blocks), dim3(64 * NW), 0, stream, g);
   return hipGetLastError();
 }
 
+#ifndef TP_NW_DEFAULT
+#define TP_NW_DEFAULT 8
+#endif
 hipError_t gemm_bf16(GemmKind kind, GemmArgs& g, hipStream_t stream) {
   switch (kind) {
     case GK_FC1_GELU:
-      return launch_mfma<true, false, BMODE_PLAIN, EPI_GELU_FWD, bf16_t>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, true, false, BMODE_PLAIN, EPI_GELU_FWD, bf16_t>(g, stream);
     case GK_FC1_SWIGLU:
-      return launch_mfma<true, false, BMODE_PAIR32, EPI_SWIGLU_FWD, bf16_t>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, true, false, BMODE_PAIR32, EPI_SWIGLU_FWD, bf16_t>(g, stream);
     case GK_FC2:
-      return launch_mfma<true, false, BMODE_PLAIN, EPI_STORE, bf16_t>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, true, false, BMODE_PLAIN, EPI_STORE, bf16_t>(g, stream);
     case GK_DH_GELU:
-      return launch_mfma<true, true, BMODE_PLAIN, EPI_GELU_BWD, bf16_t>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, true, true, BMODE_PLAIN, EPI_GELU_BWD, bf16_t>(g, stream);
     case GK_DH_SWIGLU:
-      return launch_mfma<true, true, BMODE_PLAIN, EPI_SWIGLU_BWD, bf16_t>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, true, true, BMODE_PLAIN, EPI_SWIGLU_BWD, bf16_t>(g, stream);
     case GK_WGRAD:
-      return launch_mfma<false, false, BMODE_PLAIN, EPI_STORE, float>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, false, false, BMODE_PLAIN, EPI_STORE, float>(g, stream);
     case GK_WGRAD_SPLIT:
-      return launch_mfma<false, false, BMODE_PLAIN, EPI_STORE_SPLIT, float>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, false, false, BMODE_PLAIN, EPI_STORE_SPLIT, float>(g, stream);
     case GK_DX:
-      return launch_mfma<true, true, BMODE_PLAIN, EPI_STORE, bf16_t>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, true, true, BMODE_PLAIN, EPI_STORE, bf16_t>(g, stream);
     case GK_DX_KSPLIT:
-      return launch_mfma<true, true, BMODE_KSPLIT, EPI_STORE, bf16_t>(g, stream);
+      return launch_mfma<TP_NW_DEFAULT, true, true, BMODE_KSPLIT, EPI_STORE, bf16_t>(g, stream);
   }
   return hipErrorInvalidValue;
 }

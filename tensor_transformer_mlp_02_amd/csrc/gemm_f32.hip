@@ -20,7 +20,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
-  const TileCoord tc = locate_tile(g, blockIdx.x, BM);
+  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BM);
   const float* a0 = reinterpret_cast<const float*>(g.a.p0) + tc.e * g.a.bstride;
   const float* b0 = reinterpret_cast<const float*>(g.b.p0) + tc.e * g.b.bstride;
   const float* b1 = reinterpret_cast<const float*>(g.b.p1) + tc.e * g.b.bstride;
