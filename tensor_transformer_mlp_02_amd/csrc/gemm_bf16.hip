@@ -240,6 +240,59 @@ __device__ __forceinline__ void store_k(bf16_t* tile, int tid, const Stage<NW>& 
   }
 }
 
+// ---- epilogue: lane holds rows m, columns n0 + 8 q + 4 c_lane + (0..3) of
+// each of its FM x FN accumulator blocks
+template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN>
+__device__ __forceinline__ void write_tile(const f32x16_t (&acc)[FM][FN], const EpiArgs& ea,
+                                           const TileCoord& tc, int wm, int wn, int r_lane,
+                                           int c_lane, int Ncols) {
+  static_for<0, FM>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const int64_t m = tc.m_begin + wm * WTM + i * 32 + r_lane;
+    if (m < tc.m_end) {
+      if constexpr (EPI == EPI_SWIGLU_FWD) {
+        static_for<0, FN / 2>([&](auto JP) {
+          constexpr int jp = decltype(JP)::value;
+          static_for<0, 4>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+            const int64_t f = (int64_t)tc.tn * (BN / 2) + wn * (WTN / 2) + jp * 32 + q * 8 +
+                              c_lane * 4;
+            if (f < ea.split) {
+              float gv[4], uv[4];
+              static_for<0, 4>([&](auto V) {
+                constexpr int v = decltype(V)::value;
+                gv[v] = acc[i][2 * jp][q * 4 + v];
+                uv[v] = acc[i][2 * jp + 1][q * 4 + v];
+              });
+              epilogue_swiglu4<bf16_t>(ea, m, f, gv, uv);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        });
+      } else {
+        static_for<0, FN>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          static_for<0, 4>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+            const int64_t n = (int64_t)tc.tn * BN + wn * WTN + j * 32 + q * 8 + c_lane * 4;
+            if (n < Ncols) {
+              float cv[4];
+              static_for<0, 4>([&](auto V) {
+                constexpr int v = decltype(V)::value;
+                cv[v] = acc[i][j][q * 4 + v];
+              });
+              epilogue4<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
+            }
+            // keep each group's loads and stores local: hoisting all of
+            // them would exceed the register file
+            __builtin_amdgcn_sched_barrier(0);
+          });
+        });
+      }
+    }
+  });
+}
+
 // ---- kernel ----------------------------------------------------------------
 // A_KMAJOR: opA K-contiguous (loaded straight into shared memory) or M-
 // contiguous (through registers, transposed).  B likewise; B_DIRECT selects
@@ -409,52 +462,292 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
   // the epilogue's VALU code: drain both before the registers are reused
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 
-  // ---- epilogue: lane holds rows m, columns n0 + 8 q + 4 c_lane + (0..3)
-  static_for<0, FM>([&](auto I) {
-    constexpr int i = decltype(I)::value;
-    const int64_t m = tc.m_begin + wm * WTM + i * 32 + r_lane;
-    if (m < tc.m_end) {
-      if constexpr (EPI == EPI_SWIGLU_FWD) {
-        static_for<0, FN / 2>([&](auto JP) {
-          constexpr int jp = decltype(JP)::value;
-          static_for<0, 4>([&](auto Q) {
-            constexpr int q = decltype(Q)::value;
-            const int64_t f = (int64_t)tc.tn * (BN / 2) + wn * (WTN / 2) + jp * 32 + q * 8 +
-                              c_lane * 4;
-            if (f < ea.split) {
-              float gv[4], uv[4];
-              static_for<0, 4>([&](auto V) {
-                constexpr int v = decltype(V)::value;
-                gv[v] = acc[i][2 * jp][q * 4 + v];
-                uv[v] = acc[i][2 * jp + 1][q * 4 + v];
-              });
-              epilogue_swiglu4<bf16_t>(ea, m, f, gv, uv);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          });
-        });
+  write_tile<EPI, BMODE, OutT, FM, FN, WTM, WTN>(acc, ea, tc, wm, wn, r_lane, c_lane, Ncols);
+}
+
+// ---- lean kernel: 4 wavefronts of 128 x 128, hand-ordered k loop ----------
+//
+// One wavefront per SIMD owns 128 x 128 outputs (4 x 4 MFMA blocks, 256
+// accumulators): fragment reads cost 0.5 KiB of shared memory per MFMA, so
+// reads plus the direct-load writes stay near 75 % of the LDS bandwidth at
+// full MFMA rate.  With a single wavefront per SIMD nothing hides a stall,
+// so every instruction of the k loop is placed by hand: each MFMA is
+// followed by at most three memory instructions (LDS reads for the k step
+// two ahead, and at the third k step the direct loads of the tile after
+// next); the barrier sits before the third k step, so reads get two steps
+// of latency and loads a whole tile.  All per-lane offsets are loop invariant: k
+// advances through the buffer load's scalar offset (K-contiguous operands)
+// or the buffer base (M/N-contiguous, whose k tail the buffer range masks),
+// and k step / buffer parity are immediate offsets of the LDS reads.
+// Shared memory: [A buffer 0 | A buffer 1 | B buffer 0 | B buffer 1].
+// Requirements (checked by the launcher): a K-contiguous operand has K a
+// multiple of 64, and a k split is a multiple of 64.
+
+constexpr int LEAN_NT = 256;
+constexpr int TILE_BYTES = BM * BK * 2;  // one operand tile, 32 KiB
+
+template <int OFF>
+__device__ __forceinline__ void ds_read_b128_at(bf16x8_t& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_read_tr_at(i16x4_t& v, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+// MFMA that also orders memory: direct loads issued between two of these
+// stay where they were written
+__device__ __forceinline__ void mfma_ordered(f32x16_t& acc, const bf16x8_t& a,
+                                             const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b) : "memory");
+}
+
+__device__ __forceinline__ rsrc_t make_rsrc_n(const void* p, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)nbytes,
+                                           0x00020000);
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT>
+__global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
+  constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[4 * BM * BK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r_lane = lane & 31, c_lane = lane >> 5;
+
+  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BM);
+  const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
+  const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
+  const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
+  const int64_t lda = g.a.ld, ldb = g.b.ld, bsplit = g.b.split;
+  const int Ncols = g.N;
+  const EpiArgs ea = g.epi;
+  const int n_base = tc.tn * BN;
+  const int m_rows = tc.m_end - tc.m_begin;
+  const int nk = (tc.k_end > tc.k_begin) ? (tc.k_end - tc.k_begin + BK - 1) / BK : 0;
+
+  const uint32_t lds0 = lds_u32(lds);
+  const uint32_t ldsA = lds0, ldsB = lds0 + 2 * TILE_BYTES;
+
+  // ---- loop-invariant direct-load offsets (bytes) and LDS destinations
+  uint32_t voffA[8], voffB[8];
+  uint32_t dstA[8], dstB[8];  // relative to the buffer (0 or TILE_BYTES)
+  static_for<0, 8>([&](auto Ic) {
+    constexpr int i = decltype(Ic)::value;
+    if constexpr (A_KMAJOR) {
+      const int blk = wave * 8 + i;
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      voffA[i] = r < m_rows ? (uint32_t)(((int64_t)r * lda + c * 8) * 2) : OOB_OFF;
+      dstA[i] = blk * 1024;
+    } else {
+      const int half = wave >> 1, b = (wave & 1) * 8 + i;
+      const int k = 4 * b + (lane >> 4);
+      const int q = (lane & 15) ^ ((k & 3) << 2);
+      const int col = tc.m_begin + half * 128 + 8 * q;
+      voffA[i] = col < tc.m_end ? (uint32_t)(((int64_t)k * lda + col) * 2) : OOB_OFF;
+      dstA[i] = half * (TILE_BYTES / 2) + b * 1024;
+    }
+    if constexpr (B_KMAJOR) {
+      const int blk = wave * 8 + i;
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      voffB[i] = r < Ncols - n_base ? (uint32_t)(((int64_t)r * ldb + c * 8) * 2) : OOB_OFF;
+      dstB[i] = blk * 1024;
+    } else {
+      const int half = wave >> 1, b = (wave & 1) * 8 + i;
+      const int k = 4 * b + (lane >> 4);
+      const int q = (lane & 15) ^ ((k & 3) << 2);
+      int col, lim;
+      if constexpr (BMODE == BMODE_PAIR32) {
+        col = tc.tn * 128 + 8 * q;
+        lim = (int)bsplit;
       } else {
-        static_for<0, FN>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          static_for<0, 4>([&](auto Q) {
-            constexpr int q = decltype(Q)::value;
-            const int64_t n = (int64_t)tc.tn * BN + wn * WTN + j * 32 + q * 8 + c_lane * 4;
-            if (n < Ncols) {
-              float cv[4];
-              static_for<0, 4>([&](auto V) {
-                constexpr int v = decltype(V)::value;
-                cv[v] = acc[i][j][q * 4 + v];
-              });
-              epilogue4<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
-            }
-            // keep each group's loads and stores local: hoisting all of
-            // them would exceed the register file
-            __builtin_amdgcn_sched_barrier(0);
-          });
-        });
+        col = n_base + half * 128 + 8 * q;
+        lim = Ncols;
       }
+      voffB[i] = col < lim ? (uint32_t)(((int64_t)k * ldb + col) * 2) : OOB_OFF;
+      dstB[i] = half * (TILE_BYTES / 2) + b * 1024;
     }
   });
+  // buffer resources of the k tile starting at k0 (a past-the-end tile gets
+  // an empty range: its loads read zeros)
+  rsrc_t rsA, rsB;
+  int soA = 0, soB = 0;
+  auto set_tile = [&](int k0, bool valid) {
+    if constexpr (A_KMAJOR) {
+      rsA = make_rsrc_n(a0 + (int64_t)tc.m_begin * lda, valid ? 0x7fffffffu : 0u);
+      soA = k0 * 2;
+    } else {
+      const int64_t rem = (int64_t)(tc.k_end - k0) * lda * 2;
+      rsA = make_rsrc_n(a0 + (int64_t)k0 * lda,
+                        valid ? (uint32_t)min<int64_t>(rem, 0x7fffffff) : 0u);
+    }
+    if constexpr (B_KMAJOR) {
+      const bool first = BMODE != BMODE_KSPLIT || k0 < bsplit;
+      const bf16_t* bp = first ? b0 : b1;
+      rsB = make_rsrc_n(bp + (int64_t)n_base * ldb, valid ? 0x7fffffffu : 0u);
+      soB = (first ? k0 : k0 - (int)bsplit) * 2;
+    } else {
+      const bf16_t* bp = (BMODE == BMODE_PAIR32 && (wave >> 1)) ? b1 : b0;
+      const int64_t rem = (int64_t)(tc.k_end - k0) * ldb * 2;
+      rsB = make_rsrc_n(bp + (int64_t)k0 * ldb,
+                        valid ? (uint32_t)min<int64_t>(rem, 0x7fffffff) : 0u);
+    }
+  };
+  auto load_op = [&](auto Lc, uint32_t buf_off) {
+    constexpr int l = decltype(Lc)::value;
+    if constexpr (l < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsA, (lds_void_t*)(lds + (ldsA - lds0 + buf_off + dstA[l]) / 2), 16, voffA[l], soA, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsB, (lds_void_t*)(lds + (ldsB - lds0 + buf_off + dstB[l - 8]) / 2), 16, voffB[l - 8],
+          soB, 0, 0);
+  };
+
+  // ---- loop-invariant LDS read addresses (bytes)
+  // K-contiguous: one per k step s (the chunk XOR is not affine in s);
+  // blocks add 4 KiB each, buffer parity adds TILE_BYTES.
+  // M/N-contiguous: one per block (the granule XOR is not affine in the
+  // block); k steps add 4 KiB, the second transposing read 1 KiB.
+  uint32_t rdA[4], rdB[4];
+  const int sw = swz(r_lane);
+  static_for<0, 4>([&](auto Xc) {
+    constexpr int x = decltype(Xc)::value;
+    if constexpr (A_KMAJOR)
+      rdA[x] = ldsA + (wm * 128 + r_lane) * 128 + (((2 * x + c_lane) ^ sw) << 4);
+    else {
+      uint32_t lo, hi;
+      frag_mn_addr(lds, wm * 128 + x * 32, 0, lane, lo, hi);
+      rdA[x] = lo;
+    }
+    if constexpr (B_KMAJOR)
+      rdB[x] = ldsB + (wn * 128 + r_lane) * 128 + (((2 * x + c_lane) ^ sw) << 4);
+    else {
+      const int c0 = (BMODE == BMODE_PAIR32) ? (x & 1) * 128 + wn * 64 + (x >> 1) * 32
+                                             : wn * 128 + x * 32;
+      uint32_t lo, hi;
+      frag_mn_addr(lds + 2 * BM * BK, c0, 0, lane, lo, hi);
+      rdB[x] = lo;
+    }
+  });
+
+  using FA = typename std::conditional<A_KMAJOR, FragK, FragMN>::type;
+  using FB = typename std::conditional<B_KMAJOR, FragK, FragMN>::type;
+  // one fragment slot per k step: reads run two steps ahead of the MFMAs
+  FA fa[4][FM];
+  FB fb[4][FN];
+  constexpr int RA = A_KMAJOR ? 4 : 8, RB = B_KMAJOR ? 4 : 8;
+  constexpr int NREAD = RA + RB;
+  // LDS reads complete in order, so waiting until at most this many are
+  // outstanding lets the most recent step's reads stay in flight
+  constexpr int KEEP = NREAD < 15 ? NREAD : 15;
+  // read op r of k step S from the buffer at byte offset `boff`, into slot S
+  auto read_op = [&](auto Rc, auto Sc, uint32_t boff) {
+    constexpr int r = decltype(Rc)::value, S = decltype(Sc)::value;
+    if constexpr (r < RA) {
+      if constexpr (A_KMAJOR) {
+        ds_read_b128_at<r * 4096>(fa[S][r].v, rdA[S] + boff);
+      } else {
+        constexpr int blk = r >> 1, part = r & 1;
+        if constexpr (part == 0)
+          ds_read_tr_at<S * 4096>(fa[S][blk].lo, rdA[blk] + boff);
+        else
+          ds_read_tr_at<S * 4096 + 1024>(fa[S][blk].hi, rdA[blk] + boff);
+      }
+    } else {
+      constexpr int rr = r - RA;
+      if constexpr (B_KMAJOR) {
+        ds_read_b128_at<rr * 4096>(fb[S][rr].v, rdB[S] + boff);
+      } else {
+        constexpr int blk = rr >> 1, part = rr & 1;
+        if constexpr (part == 0)
+          ds_read_tr_at<S * 4096>(fb[S][blk].lo, rdB[blk] + boff);
+        else
+          ds_read_tr_at<S * 4096 + 1024>(fb[S][blk].hi, rdB[blk] + boff);
+      }
+    }
+  };
+  auto fence_slot = [&](auto SLc, auto ALLc) {
+    constexpr int SL = decltype(SLc)::value;
+    if constexpr (decltype(ALLc)::value)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    else
+      asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(KEEP) : "memory");
+    static_for<0, FM>([&](auto I) { fa[SL][I].fence(); });
+    static_for<0, FN>([&](auto J) { fb[SL][J].fence(); });
+  };
+
+  f32x16_t acc[FM][FN];
+  static_for<0, FM>([&](auto I) {
+    static_for<0, FN>([&](auto J) { acc[I][J] = (f32x16_t)(0.0f); });
+  });
+
+  // prologue: tiles 0 and 1 in flight, wait for tile 0 only
+  if (nk > 0) {
+    set_tile(tc.k_begin, true);
+    static_for<0, 16>([&](auto L) { load_op(L, 0u); });
+    set_tile(tc.k_begin + BK, nk > 1);
+    static_for<0, 16>([&](auto L) { load_op(L, (uint32_t)TILE_BYTES); });
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  }
+  __syncthreads();
+  if (nk > 0) {
+    static_for<0, NREAD>([&](auto R) { read_op(R, std::integral_constant<int, 0>{}, 0u); });
+    static_for<0, NREAD>([&](auto R) { read_op(R, std::integral_constant<int, 1>{}, 0u); });
+  }
+  asm volatile("s_nop 4");
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // byte offsets of the buffer being consumed and of the other one
+    const uint32_t cur = (uint32_t)(kt & 1) * TILE_BYTES;
+    const uint32_t nxt = cur ^ TILE_BYTES;
+    // tile kt + 2 goes into this buffer once everyone has finished with it
+    set_tile(tc.k_begin + (kt + 2) * BK, kt + 2 < nk);
+    static_for<0, 4>([&](auto Sc) {
+      constexpr int S = decltype(Sc)::value;
+      // step 2 drains every read: with the barrier this makes the whole
+      // buffer free and (after vmcnt) the next tile readable
+      fence_slot(std::integral_constant<int, S>{}, std::integral_constant<bool, S == 2>{});
+      if constexpr (S == 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+      // side operations: reads for the step two ahead (steps 2, 3 read the
+      // next tile's steps 0, 1), within the first 8 MFMAs; at step 2 the
+      // direct loads of tile kt + 2, one per MFMA
+      constexpr int NLOAD = (S >= 2) ? 8 : 0;
+      constexpr int LOFF = (S == 3) ? 8 : 0;  // first direct load of this step
+      static_for<0, 16>([&](auto Mc) {
+        constexpr int m = decltype(Mc)::value;
+        constexpr int i = m >> 2, j = m & 3;
+        mfma_ordered(acc[i][j], fb[S][j].op(), fa[S][i].op());
+        constexpr int r0 = m < 8 ? (m * NREAD) / 8 : NREAD;
+        constexpr int r1 = m < 8 ? ((m + 1) * NREAD) / 8 : NREAD;
+        constexpr int l0 = NREAD + (m * NLOAD) / 16, l1 = NREAD + ((m + 1) * NLOAD) / 16;
+        auto side = [&](auto Oc) {
+          constexpr int o = decltype(Oc)::value;
+          if constexpr (o < NREAD) {
+            constexpr int T = (S + 2) & 3;  // k step being read
+            read_op(std::integral_constant<int, o>{}, std::integral_constant<int, T>{},
+                    S < 2 ? cur : nxt);
+          } else {
+            // interleave A and B: A0 B0 A1 B1 ...
+            constexpr int idx = o - NREAD + LOFF;
+            load_op(std::integral_constant<int, (idx & 1) * 8 + (idx >> 1)>{}, cur);
+          }
+        };
+        static_for<r0, r1>(side);
+        static_for<l0, l1>(side);
+      });
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+
+  write_tile<EPI, BMODE, OutT, FM, FN, WTM, WTN>(acc, ea, tc, wm, wn, r_lane, c_lane, Ncols);
 }
 
 }  // namespace mfma256
@@ -462,6 +755,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// general kernel's wavefront layout; hand-ordered kernel on/off
+#ifndef TP_NW_DEFAULT
+#define TP_NW_DEFAULT 8
+#endif
+#ifndef TP_USE_LEAN
+#define TP_USE_LEAN 1
+#endif
+
 static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols) {
   g.tiles_n = (n_cols + BN - 1) / BN;
   g.tile_off[0] = 0;
@@ -487,9 +788,18 @@ static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   fill_tiles(g, mfma256::BM, mfma256::BN, n_cols);
   int blocks = g.tile_off[g.E];
   if (blocks == 0) return hipSuccess;
+  // the hand-ordered kernel needs whole 64-wide k tiles of K-contiguous
+  // operands and a 64-aligned k split
+  const bool k_whole = (!AK && !BK_) || g.K % mfma256::BK == 0;
+  const bool split_ok = BMODE != BMODE_KSPLIT || g.b.split % mfma256::BK == 0;
+  if (TP_USE_LEAN && k_whole && split_ok) {
+    hipLaunchKernelGGL((mfma256::gemm_lean<AK, BK_, BMODE, EPI, OutT>), dim3(blocks),
+                       dim3(mfma256::LEAN_NT), 0, stream, g);
+    return hipGetLastError();
+  }
   // a K-contiguous opB goes straight to shared memory unless a 64-wide k
   // tile could straddle its two source matrices
-  const bool b_direct = BK_ && (BMODE != BMODE_KSPLIT || g.b.split % mfma256::BK == 0);
+  const bool b_direct = BK_ && split_ok;
   if (b_direct)
     hipLaunchKernelGGL((mfma256::gemm_kernel<NW, AK, BK_, BMODE, EPI, OutT, BK_>),
                        dim3(blocks), dim3(64 * NW), 0, stream, g);
@@ -499,9 +809,6 @@ static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-#ifndef TP_NW_DEFAULT
-#define TP_NW_DEFAULT 8
-#endif
 hipError_t gemm_bf16(GemmKind kind, GemmArgs& g, hipStream_t stream) {
   switch (kind) {
     case GK_FC1_GELU:
