@@ -85,7 +85,9 @@ typedef enum tp_status {
  * §三 3.1, the per-partition output size is output size / world size).
  * T (1..TP_MAX_SHARDS) is recorded for checks only: a shard's arithmetic
  * does not depend on it.  act is a tp_act, dtype a tp_dtype.
- * H and F_shard must be positive multiples of 8 (bf16) or 4 (fp32).
+ * H and F_shard must be positive multiples of 8 (bf16) or 4 (fp32), with
+ * H <= 2^21 and F_shard <= 2^20 (row strides are addressed with 32-bit
+ * offsets), and N <= 2^30.
  */
 typedef struct tp_mlp_desc {
     int64_t S, B, H, F_shard;
@@ -164,7 +166,8 @@ int tp_partial_sum(int32_t dtype, int32_t T, const void *const *partials,
  * that holds its expert, the local experts compute, combine returns the
  * results; the docs index of "Megatron-LM 源码精读", "MoE 层与 Expert
  * Parallelism": grouped-GEMM expert compute).  bf16 only.
- * H and F must be positive multiples of 8; 1 <= E <= TP_MAX_EXPERTS.
+ * H and F must be positive multiples of 8, H <= 2^21, F <= 2^20;
+ * 1 <= E <= TP_MAX_EXPERTS.
  */
 typedef struct tp_expert_desc {
     int64_t H, F;

@@ -97,6 +97,10 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// Largest leading dimension (H, and the Z_save width 2 F_shard): the bf16
+// kernels address one 256-row tile through 32-bit buffer offsets, so
+// 256 rows x ld x 2 bytes must stay below 2^31.
+constexpr int64_t kMaxLd = (int64_t)1 << 21;
 
 struct Shard {
   int64_t N, H, Ft;
@@ -114,8 +118,8 @@ int check_desc(const tp_mlp_desc* d, Shard& s) {
   if (d->H <= 0 || d->F_shard <= 0) return fail(TP_ERR_SHAPE, "H and F_shard must be > 0");
   if (d->T < 1 || d->T > TP_MAX_SHARDS)
     return fail(TP_ERR_SHAPE, "T must be in 1..%d", TP_MAX_SHARDS);
-  if (d->S > kMaxDim || d->B > kMaxDim || d->S * d->B > kMaxDim || d->H > kMaxDim ||
-      d->F_shard > kMaxDim / 2)
+  if (d->S > kMaxDim || d->B > kMaxDim || d->S * d->B > kMaxDim || d->H > kMaxLd ||
+      d->F_shard > kMaxLd / 2)
     return fail(TP_ERR_SHAPE, "dimension too large");
   const int vec = d->dtype == TP_BF16 ? 8 : 4;
   if (d->H % vec || d->F_shard % vec)
@@ -355,7 +359,7 @@ int check_experts(const tp_expert_desc* d, const int64_t* offsets, Experts& x) {
     return fail(TP_ERR_SHAPE, "E must be in 1..%d", TP_MAX_EXPERTS);
   if (d->H <= 0 || d->F <= 0 || d->H % 8 || d->F % 8)
     return fail(TP_ERR_SHAPE, "H and F must be positive multiples of 8");
-  if (d->H > kMaxDim || d->F > kMaxDim / 2) return fail(TP_ERR_SHAPE, "dimension too large");
+  if (d->H > kMaxLd || d->F > kMaxLd / 2) return fail(TP_ERR_SHAPE, "dimension too large");
   if (!offsets) return fail(TP_ERR_NULL, "offsets is NULL");
   if (offsets[0] != 0) return fail(TP_ERR_SHAPE, "offsets[0] must be 0");
   for (int e = 0; e < d->E; ++e)

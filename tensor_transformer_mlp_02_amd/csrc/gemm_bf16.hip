@@ -506,6 +506,13 @@ __device__ __forceinline__ rsrc_t make_rsrc_n(const void* p, uint32_t nbytes) {
                                            0x00020000);
 }
 
+// byte count of a buffer resource, capped to the largest the kernels use
+// (integer compare: keeps the resource in scalar registers)
+__device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
+  return bytes > (int64_t)0x7fffffff ? 0x7fffffffu : (uint32_t)bytes;
+}
+
+
 template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT>
 __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
@@ -583,7 +590,7 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
     } else {
       const int64_t rem = (int64_t)(tc.k_end - k0) * lda * 2;
       rsA = make_rsrc_n(a0 + (int64_t)k0 * lda,
-                        valid ? (uint32_t)min<int64_t>(rem, 0x7fffffff) : 0u);
+                        valid ? clamp_records(rem) : 0u);
     }
     if constexpr (B_KMAJOR) {
       const bool first = BMODE != BMODE_KSPLIT || k0 < bsplit;
@@ -594,7 +601,7 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
       const bf16_t* bp = (BMODE == BMODE_PAIR32 && (wave >> 1)) ? b1 : b0;
       const int64_t rem = (int64_t)(tc.k_end - k0) * ldb * 2;
       rsB = make_rsrc_n(bp + (int64_t)k0 * ldb,
-                        valid ? (uint32_t)min<int64_t>(rem, 0x7fffffff) : 0u);
+                        valid ? clamp_records(rem) : 0u);
     }
   };
   auto load_op = [&](auto Lc, uint32_t buf_off) {
@@ -750,6 +757,267 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   write_tile<EPI, BMODE, OutT, FM, FN, WTM, WTN>(acc, ea, tc, wm, wn, r_lane, c_lane, Ncols);
 }
 
+// ---- ring kernel: 4-stage shared-memory ring of 32-wide k tiles ------------
+//
+// Same wavefront layout and hand-ordered k loop as gemm_lean, but the k
+// tiles are 32 wide and four of them live in shared memory at once
+// ([A stage 0..3 | B stage 0..3], 16 KiB each).  Every k step issues half
+// of the direct loads of the tile three ahead (4 per wavefront, one after
+// every fourth MFMA), so load issue is spread evenly over the loop and each load
+// has two tiles of latency budget; LDS reads run two k steps (one tile)
+// ahead; one barrier per tile, at its first step.
+constexpr int RBK = 32;
+#ifndef RING_STAGES
+#define RING_STAGES 4
+#endif
+constexpr int RTILE = BM * RBK * 2;  // one operand stage, 16 KiB
+
+__device__ __forceinline__ int swz4(int r) { return (r & 3) ^ ((r >> 2) & 3); }
+
+// M/N-contiguous stage tile: [half][k 0..31][16 granules], granule q of row
+// k at q ^ 4 (k % 4)
+__device__ __forceinline__ int mn_off32(int k, int c) {
+  const int h = c >> 7, q = (c >> 3) & 15, e = c & 7;
+  return h * (RBK * 128) + k * 128 + ((q ^ ((k & 3) << 2)) << 3) + e;
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT>
+__global__ __launch_bounds__(LEAN_NT, 1) void gemm_ring(GemmArgs g) {
+  constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
+  constexpr int NS = RING_STAGES;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[2 * NS * BM * RBK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r_lane = lane & 31, c_lane = lane >> 5;
+
+  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BM);
+  const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
+  const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
+  const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
+  const int64_t lda = g.a.ld, ldb = g.b.ld, bsplit = g.b.split;
+  const int Ncols = g.N;
+  const EpiArgs ea = g.epi;
+  const int n_base = tc.tn * BN;
+  const int m_rows = tc.m_end - tc.m_begin;
+  const int nk = (tc.k_end > tc.k_begin) ? (tc.k_end - tc.k_begin + RBK - 1) / RBK : 0;
+
+  const uint32_t lds0 = lds_u32(lds);
+  const uint32_t ldsA = lds0, ldsB = lds0 + NS * RTILE;
+
+  // ---- loop-invariant direct-load offsets (bytes) and destinations
+  uint32_t voffA[4], voffB[4], dstA[4], dstB[4];
+  static_for<0, 4>([&](auto Ic) {
+    constexpr int i = decltype(Ic)::value;
+    if constexpr (A_KMAJOR) {
+      const int blk = wave * 4 + i;
+      const int r = blk * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz4(r);
+      voffA[i] = r < m_rows ? (uint32_t)(((int64_t)r * lda + c * 8) * 2) : OOB_OFF;
+      dstA[i] = blk * 1024;
+    } else {
+      const int half = wave >> 1, b = (wave & 1) * 4 + i;
+      const int k = 4 * b + (lane >> 4);
+      const int q = (lane & 15) ^ ((k & 3) << 2);
+      const int col = tc.m_begin + half * 128 + 8 * q;
+      voffA[i] = col < tc.m_end ? (uint32_t)(((int64_t)k * lda + col) * 2) : OOB_OFF;
+      dstA[i] = half * (RTILE / 2) + b * 1024;
+    }
+    if constexpr (B_KMAJOR) {
+      const int blk = wave * 4 + i;
+      const int r = blk * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz4(r);
+      voffB[i] = r < Ncols - n_base ? (uint32_t)(((int64_t)r * ldb + c * 8) * 2) : OOB_OFF;
+      dstB[i] = blk * 1024;
+    } else {
+      const int half = wave >> 1, b = (wave & 1) * 4 + i;
+      const int k = 4 * b + (lane >> 4);
+      const int q = (lane & 15) ^ ((k & 3) << 2);
+      int col, lim;
+      if constexpr (BMODE == BMODE_PAIR32) {
+        col = tc.tn * 128 + 8 * q;
+        lim = (int)bsplit;
+      } else {
+        col = n_base + half * 128 + 8 * q;
+        lim = Ncols;
+      }
+      voffB[i] = col < lim ? (uint32_t)(((int64_t)k * ldb + col) * 2) : OOB_OFF;
+      dstB[i] = half * (RTILE / 2) + b * 1024;
+    }
+  });
+  rsrc_t rsA, rsB;
+  int soA = 0, soB = 0;
+  // buffer resources of the k tile starting at k0 (past the end: empty)
+  auto set_tile = [&](int k0, bool valid) {
+    if constexpr (A_KMAJOR) {
+      rsA = make_rsrc_n(a0 + (int64_t)tc.m_begin * lda, valid ? 0x7fffffffu : 0u);
+      soA = k0 * 2;
+    } else {
+      const int64_t rem = (int64_t)(tc.k_end - k0) * lda * 2;
+      rsA = make_rsrc_n(a0 + (int64_t)k0 * lda,
+                        valid ? clamp_records(rem) : 0u);
+    }
+    if constexpr (B_KMAJOR) {
+      const bool first = BMODE != BMODE_KSPLIT || k0 < bsplit;
+      const bf16_t* bp = first ? b0 : b1;
+      rsB = make_rsrc_n(bp + (int64_t)n_base * ldb, valid ? 0x7fffffffu : 0u);
+      soB = (first ? k0 : k0 - (int)bsplit) * 2;
+    } else {
+      const bf16_t* bp = (BMODE == BMODE_PAIR32 && (wave >> 1)) ? b1 : b0;
+      const int64_t rem = (int64_t)(tc.k_end - k0) * ldb * 2;
+      rsB = make_rsrc_n(bp + (int64_t)k0 * ldb,
+                        valid ? clamp_records(rem) : 0u);
+    }
+  };
+  // direct load l of a tile (A0 B0 A1 B1 ...) into the stage at `soff`
+  auto load_op = [&](auto Lc, uint32_t soff) {
+    constexpr int l = decltype(Lc)::value, i = l >> 1;
+    if constexpr ((l & 1) == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsA, (lds_void_t*)(lds + (soff + dstA[i]) / 2), 16, voffA[i], soA, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsB, (lds_void_t*)(lds + (NS * RTILE + soff + dstB[i]) / 2), 16, voffB[i], soB, 0, 0);
+  };
+
+  // ---- loop-invariant LDS read addresses (bytes, stage 0)
+  uint32_t rdA[4], rdB[4];
+  const int sw = swz4(r_lane);
+  static_for<0, 4>([&](auto Xc) {
+    constexpr int x = decltype(Xc)::value;
+    if constexpr (A_KMAJOR) {
+      if constexpr (x < 2) rdA[x] = ldsA + (wm * 128 + r_lane) * 64 + (((2 * x + c_lane) ^ sw) << 4);
+    } else {
+      const int gg = lane >> 4, rr = lane & 15;
+      const int c = wm * 128 + x * 32 + 16 * (gg & 1) + 4 * (rr & 3);
+      const int k = 8 * (gg >> 1) + (rr >> 2);
+      rdA[x] = ldsA + 2 * mn_off32(k, c);
+    }
+    if constexpr (B_KMAJOR) {
+      if constexpr (x < 2) rdB[x] = ldsB + (wn * 128 + r_lane) * 64 + (((2 * x + c_lane) ^ sw) << 4);
+    } else {
+      const int c0 = (BMODE == BMODE_PAIR32) ? (x & 1) * 128 + wn * 64 + (x >> 1) * 32
+                                             : wn * 128 + x * 32;
+      const int gg = lane >> 4, rr = lane & 15;
+      const int c = c0 + 16 * (gg & 1) + 4 * (rr & 3);
+      const int k = 8 * (gg >> 1) + (rr >> 2);
+      rdB[x] = ldsB + 2 * mn_off32(k, c);
+    }
+  });
+
+  using FA = typename std::conditional<A_KMAJOR, FragK, FragMN>::type;
+  using FB = typename std::conditional<B_KMAJOR, FragK, FragMN>::type;
+  FA fa[4][FM];
+  FB fb[4][FN];
+  constexpr int RA = A_KMAJOR ? 4 : 8, RB = B_KMAJOR ? 4 : 8;
+  constexpr int NREAD = RA + RB;
+  constexpr int KEEP = NREAD < 15 ? NREAD : 15;
+  // read op r of step SP (0/1) of the stage at `soff`, into slot SL
+  auto read_op = [&](auto Rc, auto SPc, uint32_t soff, auto SLc) {
+    constexpr int r = decltype(Rc)::value, SP = decltype(SPc)::value;
+    constexpr int SL = decltype(SLc)::value;
+    if constexpr (r < RA) {
+      if constexpr (A_KMAJOR) {
+        ds_read_b128_at<r * 2048>(fa[SL][r].v, rdA[SP] + soff);
+      } else {
+        constexpr int blk = r >> 1, part = r & 1;
+        ds_read_tr_at<SP * 4096 + part * 1024>(part ? fa[SL][blk].hi : fa[SL][blk].lo,
+                                               rdA[blk] + soff);
+      }
+    } else {
+      constexpr int rr = r - RA;
+      if constexpr (B_KMAJOR) {
+        ds_read_b128_at<rr * 2048>(fb[SL][rr].v, rdB[SP] + soff);
+      } else {
+        constexpr int blk = rr >> 1, part = rr & 1;
+        ds_read_tr_at<SP * 4096 + part * 1024>(part ? fb[SL][blk].hi : fb[SL][blk].lo,
+                                               rdB[blk] + soff);
+      }
+    }
+  };
+  auto fence_slot = [&](auto SLc) {
+    constexpr int SL = decltype(SLc)::value;
+    asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(KEEP) : "memory");
+    static_for<0, FM>([&](auto I) { fa[SL][I].fence(); });
+    static_for<0, FN>([&](auto J) { fb[SL][J].fence(); });
+  };
+
+  f32x16_t acc[FM][FN];
+  static_for<0, FM>([&](auto I) {
+    static_for<0, FN>([&](auto J) { acc[I][J] = (f32x16_t)(0.0f); });
+  });
+
+  // prologue: tiles 0 .. NS-2 in flight, wait for tile 0, read its two steps
+  if (nk > 0) {
+    static_for<0, NS - 1>([&](auto Tc) {
+      constexpr int T = decltype(Tc)::value;
+      set_tile(tc.k_begin + T * RBK, T < nk);
+      static_for<0, 8>([&](auto L) { load_op(L, (uint32_t)(T * RTILE)); });
+    });
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * 8) : "memory");
+  }
+  // a plain s_barrier: __syncthreads() would also drain the loads of tiles
+  // 1 and 2 (the explicit vmcnt waits order the shared-memory traffic)
+  __builtin_amdgcn_s_barrier();
+  if (nk > 0) {
+    static_for<0, NREAD>([&](auto R) {
+      read_op(R, std::integral_constant<int, 0>{}, 0u, std::integral_constant<int, 0>{});
+    });
+    static_for<0, NREAD>([&](auto R) {
+      read_op(R, std::integral_constant<int, 1>{}, 0u, std::integral_constant<int, 1>{});
+    });
+  }
+  asm volatile("s_nop 4");
+
+  // two tiles (four k steps) per trip so the fragment slot is a constant; an
+  // odd tile count runs one more tile, loaded as zeros (both operands lie
+  // past the end), which leaves the sums unchanged
+  const int nk2 = (nk + 1) & ~1;
+  int st_next = 1 % NS, st_load = NS - 1;  // stages of tiles t + 1 and t + NS - 1
+  for (int t0 = 0; t0 < nk2; t0 += 2) {
+    static_for<0, 2>([&](auto TPc) {
+      constexpr int TP = decltype(TPc)::value;
+      const int t = t0 + TP;
+      {
+        const uint32_t s_next = (uint32_t)st_next * RTILE;  // stage read ahead
+        const uint32_t s_load = (uint32_t)st_load * RTILE;  // stage being refilled
+        st_next = st_next == NS - 1 ? 0 : st_next + 1;
+        st_load = st_load == NS - 1 ? 0 : st_load + 1;
+        set_tile(tc.k_begin + (t + NS - 1) * RBK, t + NS - 1 < nk);
+        static_for<0, 2>([&](auto SPc) {
+          constexpr int SP = decltype(SPc)::value;
+          constexpr int S = TP * 2 + SP;  // fragment slot of this step
+          fence_slot(std::integral_constant<int, S>{});
+          if constexpr (SP == 0) {
+            // tile t + 1 has landed everywhere, and everyone has finished
+            // reading tile t - 1, whose stage tile t + NS - 1 now refills
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 3) * 8) : "memory");
+            __builtin_amdgcn_s_barrier();
+          }
+          static_for<0, 16>([&](auto Mc) {
+            constexpr int m = decltype(Mc)::value;
+            constexpr int i = m >> 2, j = m & 3;
+            mfma_ordered(acc[i][j], fb[S][j].op(), fa[S][i].op());
+            constexpr int r0 = m < 8 ? (m * NREAD) / 8 : NREAD;
+            constexpr int r1 = m < 8 ? ((m + 1) * NREAD) / 8 : NREAD;
+            static_for<r0, r1>([&](auto Oc) {
+              read_op(Oc, std::integral_constant<int, SP>{}, s_next,
+                      std::integral_constant<int, (S + 2) & 3>{});
+            });
+            if constexpr (m % 4 == 1)
+              load_op(std::integral_constant<int, SP * 4 + m / 4>{}, s_load);
+          });
+        });
+      }
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+
+  write_tile<EPI, BMODE, OutT, FM, FN, WTM, WTN>(acc, ea, tc, wm, wn, r_lane, c_lane, Ncols);
+}
+
 }  // namespace mfma256
 
 // ---------------------------------------------------------------------------
@@ -761,6 +1029,9 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
 #endif
 #ifndef TP_USE_LEAN
 #define TP_USE_LEAN 1
+#endif
+#ifndef TP_USE_RING
+#define TP_USE_RING 1
 #endif
 
 static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols) {
@@ -792,8 +1063,16 @@ static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   // operands and a 64-aligned k split
   const bool k_whole = (!AK && !BK_) || g.K % mfma256::BK == 0;
   const bool split_ok = BMODE != BMODE_KSPLIT || g.b.split % mfma256::BK == 0;
+  // the ring kernel needs whole 32-wide k tiles and a 32-aligned k split
+  const bool ring_ok = ((!AK && !BK_) || g.K % mfma256::RBK == 0) &&
+                       (BMODE != BMODE_KSPLIT || g.b.split % mfma256::RBK == 0);
   if (TP_USE_LEAN && k_whole && split_ok) {
     hipLaunchKernelGGL((mfma256::gemm_lean<AK, BK_, BMODE, EPI, OutT>), dim3(blocks),
+                       dim3(mfma256::LEAN_NT), 0, stream, g);
+    return hipGetLastError();
+  }
+  if (TP_USE_RING && ring_ok) {
+    hipLaunchKernelGGL((mfma256::gemm_ring<AK, BK_, BMODE, EPI, OutT>), dim3(blocks),
                        dim3(mfma256::LEAN_NT), 0, stream, g);
     return hipGetLastError();
   }

@@ -80,6 +80,9 @@ def test_forward_argument_checks():
     assert fwd(gelu_desc(T=65)) == E_SHAPE
     assert fwd(gelu_desc(S=-1)) == E_SHAPE
     assert fwd(gelu_desc(S=1 << 20, B=1 << 20)) == E_SHAPE
+    # row strides must fit the kernels' 32-bit tile offsets
+    assert fwd(gelu_desc(H=1 << 22)) == E_SHAPE
+    assert fwd(gelu_desc(F_shard=(1 << 20) + 8)) == E_SHAPE
     assert fwd(gelu_desc(), X=None) == E_NULL
     assert fwd(gelu_desc(), H=None) == E_NULL
     assert fwd(gelu_desc(), X=addr(1, 2)) == E_ALIGN
@@ -160,6 +163,7 @@ def test_grouped_argument_checks():
     assert gfwd(dict(d, E=0), [0]) == E_SHAPE
     assert gfwd(dict(d, E=65), [0] * 66) == E_SHAPE
     assert gfwd(dict(d, F=100), off) == E_SHAPE
+    assert gfwd(dict(d, H=1 << 22), off) == E_SHAPE
     assert gfwd(d, [1, 10, 10, 30, 31]) == E_SHAPE     # must start at 0
     assert gfwd(d, [0, 10, 9, 30, 31]) == E_SHAPE      # must not decrease
     assert gfwd(d, off, Wd=None) == E_NULL

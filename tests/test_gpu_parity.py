@@ -109,6 +109,10 @@ SMALL = [
     (wl.DT_BF16, wl.ACT_GELU_TANH, 513, 264, 136),
     (wl.DT_BF16, wl.ACT_SWIGLU, 1, 8, 8),
     (wl.DT_BF16, wl.ACT_GELU_TANH, 77, 8, 600),
+    # k extents that are multiples of 32 but not of 64 (the 32-wide k-tile
+    # kernel), including the SwiGLU split of [dG | dU] at Ft = 416
+    (wl.DT_BF16, wl.ACT_SWIGLU, 300, 544, 416),
+    (wl.DT_BF16, wl.ACT_GELU_TANH, 130, 96, 160),
     (wl.DT_F32, wl.ACT_GELU_TANH, 300, 132, 100),
     (wl.DT_F32, wl.ACT_SWIGLU, 70, 68, 36),
     (wl.DT_F32, wl.ACT_SWIGLU, 1, 4, 4),
