@@ -64,6 +64,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c4_bf16_swiglu_fwdbwd")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--overlap", type=int, default=0,
+                   help="1: partial sums on a second stream, overlapping the GEMMs")
+    p.add_argument("--sum-workgroups", type=int, default=256,
+                   help="workgroup cap of the overlapped partial sums")
     p.add_argument("--cpu-tokens", type=int, default=0,
                    help="tokens of the oracle sample (0: sized to ~15 s)")
     return p.parse_args()
@@ -120,18 +124,48 @@ def main():
     count = w.N * w.H
     stream = torch.cuda.current_stream()
 
+    # The partial sums stand in for the all-reduces of a real rank, so they
+    # run on a second stream (default priority) like communication would:
+    # sum(Y) overlaps the backward GEMMs and sum(dX) the next forward, on the
+    # compute units the GEMM grids leave idle.  Events keep every dependency:
+    # a sum starts after the GEMM that wrote its input, and the next write of
+    # Y (forward) or dX (backward) waits for the sum that reads it.
+    side = torch.cuda.Stream(device=dev) if args.overlap else stream
+
+    def psum(*a, stream):
+        # overlapped: a few workgroups, so the sum takes only the compute
+        # units the GEMM grids leave free
+        if args.overlap:
+            return tp.tp_partial_sum_capped(*a, args.sum_workgroups, stream=stream)
+        return tp.tp_partial_sum(*a, stream=stream)
+    y_ready, dx_ready = torch.cuda.Event(), torch.cuda.Event()
+    y_read, dx_read = torch.cuda.Event(), torch.cuda.Event()
+    y_read.record(side)
+    dx_read.record(side)
+
     def step(ev=None):
         if ev: ev[0].record(stream)
-        tp.tp_mlp_shard_fwd(desc, X, A, Au, B, buf.Z, buf.H, buf.Y)
+        stream.wait_event(y_read)
+        tp.tp_mlp_shard_fwd(desc, X, A, Au, B, buf.Z, buf.H, buf.Y, stream=stream)
         if ev: ev[1].record(stream)
-        tp.tp_partial_sum(w.dtype, w.T, [buf.Y] + stand, count, Ysum)
-        if ev: ev[2].record(stream)
+        y_ready.record(stream)
+        side.wait_event(y_ready)
+        if ev: ev[5].record(side)
+        psum(w.dtype, w.T, [buf.Y] + stand, count, Ysum, stream=side)
+        if ev: ev[6].record(side)
+        y_read.record(side)
         if w.backward:
+            if ev: ev[2].record(stream)
+            stream.wait_event(dx_read)
             tp.tp_mlp_shard_bwd(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
-                                buf.dA_up, buf.dB, buf.ws, buf.ws_bytes)
+                                buf.dA_up, buf.dB, buf.ws, buf.ws_bytes, stream=stream)
             if ev: ev[3].record(stream)
-            tp.tp_partial_sum(w.dtype, w.T, [buf.dX] + stand, count, dXsum)
-            if ev: ev[4].record(stream)
+            dx_ready.record(stream)
+            side.wait_event(dx_ready)
+            if ev: ev[7].record(side)
+            psum(w.dtype, w.T, [buf.dX] + stand, count, dXsum, stream=side)
+            if ev: ev[8].record(side)
+            dx_read.record(side)
 
     # calibration copy (one partial sum of a single buffer = a copy)
     n_calib = CALIB_COPY_BYTES // 2
@@ -145,25 +179,30 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps between two events; per-call events inside
-    # each step split the time between the GEMM calls and the partial sums
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: K whole steps between two events on the compute stream
+    # (the last one after it has waited for the side stream); per-call events
+    # on each stream split the time between the GEMM calls and the sums
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
+    side.wait_event(t_start)
     for k in range(args.steps):
         step(evs[k])
+    done = torch.cuda.Event()
+    done.record(side)
+    stream.wait_event(done)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms = total_ms / args.steps
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ps_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ps_ms = [e[5].elapsed_time(e[6]) for e in evs]
     bwd_ms = 0.0
     if w.backward:
         bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-        ps_ms += [e[3].elapsed_time(e[4]) for e in evs]
+        ps_ms += [e[7].elapsed_time(e[8]) for e in evs]
     ps_ms = float(np.mean(ps_ms))
 
     flops = gemm_flops(w)
@@ -205,7 +244,10 @@ def main():
         "config": {"workload": w.name, "S": w.S, "B": w.B, "H": w.H, "F": w.F, "T": w.T,
                    "F_shard": w.Ft, "act": "swiglu" if w.act == 1 else "gelu_tanh",
                    "rank": "one tensor-parallel rank; the other 7 ranks' partials are "
-                           "seeded stand-ins"},
+                           "seeded stand-ins",
+                   "partial_sums": ("second stream, overlapping the GEMMs, at most %d "
+                                    "workgroups" % args.sum_workgroups) if args.overlap
+                                   else "in order on the compute stream"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "kernel": "bf16 MFMA GEMM with fused epilogues (%d launches per step)" % n_gemm,

@@ -160,6 +160,20 @@ int tp_partial_sum(int32_t dtype, int32_t T, const void *const *partials,
                    int64_t count, void *out, void *stream);
 
 /*
+ * tp_partial_sum_capped -- tp_partial_sum on at most `max_workgroups`
+ * workgroups of 256 threads (which stride over the whole tensor), so the
+ * sum occupies only a few compute units and can run on a second stream
+ * beside the shard's GEMMs, the way the all-reduce it stands in for
+ * overlaps computation (§三 3.4 places the reduce between the shard's
+ * forward and the next layer, and its backward twin after dX_i).
+ *   max_workgroups  >= 1; other arguments as in tp_partial_sum
+ * The result is bitwise identical to tp_partial_sum's (same order).
+ */
+int tp_partial_sum_capped(int32_t dtype, int32_t T, const void *const *partials,
+                          int64_t count, void *out, int32_t max_workgroups,
+                          void *stream);
+
+/*
  * Grouped local experts: E experts, each a full SwiGLU MLP of width F
  * (expert tensor parallelism 1), over rows already sorted by expert
  * ("Megatron Core 带读" §09: the dispatcher brings each token to the rank

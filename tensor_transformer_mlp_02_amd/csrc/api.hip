@@ -318,8 +318,9 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, cons
   return ok();
 }
 
-int tp_partial_sum(int32_t dtype, int32_t T, const void* const* partials, int64_t count,
-                   void* out, void* stream) {
+namespace {
+int partial_sum_common(int32_t dtype, int32_t T, const void* const* partials, int64_t count,
+                       void* out, int32_t max_blocks, void* stream) {
   if (dtype != TP_F32 && dtype != TP_BF16) return fail(TP_ERR_DTYPE, "unknown dtype %d", dtype);
   if (T < 1 || T > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "T must be in 1..%d", TP_MAX_SHARDS);
   if (count < 0) return fail(TP_ERR_SHAPE, "count must be >= 0");
@@ -336,10 +337,22 @@ int tp_partial_sum(int32_t dtype, int32_t T, const void* const* partials, int64_
   }
   if (int rc = check_device()) return rc;
   if (count == 0) return ok();
-  hipError_t he = partial_sum_launch(dtype, T, partials, count, out,
+  hipError_t he = partial_sum_launch(dtype, T, partials, count, out, max_blocks,
                                      reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "partial-sum launch");
   return ok();
+}
+}  // namespace
+
+int tp_partial_sum(int32_t dtype, int32_t T, const void* const* partials, int64_t count,
+                   void* out, void* stream) {
+  return partial_sum_common(dtype, T, partials, count, out, 0, stream);
+}
+
+int tp_partial_sum_capped(int32_t dtype, int32_t T, const void* const* partials,
+                          int64_t count, void* out, int32_t max_workgroups, void* stream) {
+  if (max_workgroups < 1) return fail(TP_ERR_SHAPE, "max_workgroups must be >= 1");
+  return partial_sum_common(dtype, T, partials, count, out, max_workgroups, stream);
 }
 
 // ---------------------------------------------------------------------------

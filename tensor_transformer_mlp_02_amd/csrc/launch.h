@@ -25,7 +25,8 @@ hipError_t gemm_bf16(GemmKind kind, GemmArgs& g, hipStream_t stream);
 // fp32 storage, fp32 FMA path.
 hipError_t gemm_f32(GemmKind kind, GemmArgs& g, hipStream_t stream);
 
-hipError_t partial_sum_launch(int dtype, int T, const void* const* parts,
-                              int64_t count, void* out, hipStream_t stream);
+// max_blocks > 0 caps the grid (the kernel strides over the tensor).
+hipError_t partial_sum_launch(int dtype, int T, const void* const* parts, int64_t count,
+                              void* out, int max_blocks, hipStream_t stream);
 
 }  // namespace tpmlp

@@ -2,10 +2,14 @@
 // out = sum_{i<T} P_i, summed in fp32 in the fixed order i = 0..T-1 and
 // rounded once.  Bandwidth-bound: every byte is read or written once.
 //
-// Each thread owns UNROLL chunks of 8 elements (16 bytes of bf16, 32 bytes
-// of fp32) spaced one grid-width apart, so a wavefront's loads cover 1 KiB
-// contiguous per instruction and UNROLL independent loads of each partial
-// are in flight at once.  The T partial pointers travel by value.
+// A thread owns PS_U chunks of 8 elements (16 bytes of bf16, 32 bytes of
+// fp32) spaced one grid-width apart, so a wavefront's loads cover 1 KiB
+// contiguous per instruction.  The partials are taken in groups of PS_G:
+// all PS_G x PS_U loads of a group are issued before the first add, which
+// keeps 256 bytes (bf16) per lane in flight; the adds then run in partial
+// order.  The grid strides over the chunks, so any workgroup count covers
+// the whole tensor (the capped variant runs on a few compute units beside
+// other kernels).  The T partial pointers travel by value.
 #include "common.h"
 #include "launch.h"
 
@@ -16,34 +20,53 @@ struct PartialPtrs {
 };
 
 constexpr int PS_NT = 256;
-constexpr int PS_UNROLL = 4;
+constexpr int PS_G = 8;  // partials whose loads are in flight together
+constexpr int PS_U = 2;  // chunks per thread per pass
 
-__device__ __forceinline__ void load8(const bf16_t* p, int64_t c, float v[8]) {
-  uint4 q = *reinterpret_cast<const uint4*>(p + c * 8);
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// one chunk of 8 elements as loaded (raw bits; converted when added).
+// Loads and stores are non-temporal: every byte is touched once.
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16_t> {
+  u32x4_t q;
+  __device__ __forceinline__ void load(const bf16_t* p, int64_t c) {
+    q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + c * 8));
   }
-}
-__device__ __forceinline__ void load8(const float* p, int64_t c, float v[8]) {
-  float4 a = *reinterpret_cast<const float4*>(p + c * 8);
-  float4 b = *reinterpret_cast<const float4*>(p + c * 8 + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
+  __device__ __forceinline__ void get(float v[8]) const {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Chunk<float> {
+  f32x4_t a, b;
+  __device__ __forceinline__ void load(const float* p, int64_t c) {
+    a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + c * 8));
+    b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + c * 8 + 4));
+  }
+  __device__ __forceinline__ void get(float v[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
 __device__ __forceinline__ void store8(bf16_t* p, int64_t c, const float v[8]) {
-  uint4 q;
+  u32x4_t q;
   q.x = pack_bf16x2(v[0], v[1]);
   q.y = pack_bf16x2(v[2], v[3]);
   q.z = pack_bf16x2(v[4], v[5]);
   q.w = pack_bf16x2(v[6], v[7]);
-  *reinterpret_cast<uint4*>(p + c * 8) = q;
+  __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t*>(p + c * 8));
 }
 __device__ __forceinline__ void store8(float* p, int64_t c, const float v[8]) {
-  *reinterpret_cast<float4*>(p + c * 8) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + c * 8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  const f32x4_t a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+  __builtin_nontemporal_store(a, reinterpret_cast<f32x4_t*>(p + c * 8));
+  __builtin_nontemporal_store(b, reinterpret_cast<f32x4_t*>(p + c * 8 + 4));
 }
 __device__ __forceinline__ float load1(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
 __device__ __forceinline__ float load1(const float* p, int64_t i) { return p[i]; }
@@ -57,28 +80,42 @@ __global__ __launch_bounds__(PS_NT) void partial_sum_kernel(PartialPtrs ptrs, in
   T* out = reinterpret_cast<T*>(out_);
   const int64_t stride = (int64_t)gridDim.x * PS_NT;
   const int64_t t0 = (int64_t)blockIdx.x * PS_NT + threadIdx.x;
-  for (int64_t base = t0; base < nchunks; base += stride * PS_UNROLL) {
-    float s[PS_UNROLL][8];
-    bool ok[PS_UNROLL];
+  for (int64_t base = t0; base < nchunks; base += stride * PS_U) {
+    float s[PS_U][8];
+    bool ok[PS_U];
 #pragma unroll
-    for (int u = 0; u < PS_UNROLL; ++u) {
-      int64_t c = base + u * stride;
-      ok[u] = c < nchunks;
-      if (ok[u]) load8(reinterpret_cast<const T*>(ptrs.p[0]), c, s[u]);
+    for (int u = 0; u < PS_U; ++u) ok[u] = base + u * stride < nchunks;
+    for (int g0 = 0; g0 < nparts; g0 += PS_G) {
+      Chunk<T> raw[PS_G][PS_U];
+#pragma unroll
+      for (int i = 0; i < PS_G; ++i) {
+        if (g0 + i < nparts) {
+          const T* p = reinterpret_cast<const T*>(ptrs.p[g0 + i]);
+#pragma unroll
+          for (int u = 0; u < PS_U; ++u)
+            if (ok[u]) raw[i][u].load(p, base + u * stride);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PS_G; ++i) {
+        if (g0 + i < nparts) {
+#pragma unroll
+          for (int u = 0; u < PS_U; ++u) {
+            float v[8];
+            raw[i][u].get(v);
+            if (g0 + i == 0) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) s[u][e] = v[e];
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) s[u][e] += v[e];
+            }
+          }
+        }
+      }
     }
-    for (int i = 1; i < nparts; ++i) {
-      const T* p = reinterpret_cast<const T*>(ptrs.p[i]);
-      float v[PS_UNROLL][8];
 #pragma unroll
-      for (int u = 0; u < PS_UNROLL; ++u)
-        if (ok[u]) load8(p, base + u * stride, v[u]);
-#pragma unroll
-      for (int u = 0; u < PS_UNROLL; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s[u][e] += v[u][e];
-    }
-#pragma unroll
-    for (int u = 0; u < PS_UNROLL; ++u)
+    for (int u = 0; u < PS_U; ++u)
       if (ok[u]) store8(out, base + u * stride, s[u]);
   }
   // elements past the last whole chunk
@@ -92,16 +129,17 @@ __global__ __launch_bounds__(PS_NT) void partial_sum_kernel(PartialPtrs ptrs, in
   }
 }
 
-hipError_t partial_sum_launch(int dtype, int T, const void* const* parts,
-                              int64_t count, void* out, hipStream_t stream) {
+hipError_t partial_sum_launch(int dtype, int T, const void* const* parts, int64_t count,
+                              void* out, int max_blocks, hipStream_t stream) {
   if (count == 0) return hipSuccess;
   PartialPtrs ptrs;
   for (int i = 0; i < TP_MAX_SHARDS; ++i) ptrs.p[i] = i < T ? parts[i] : nullptr;
   const int64_t nchunks = count / 8;
-  int64_t threads = (nchunks + PS_UNROLL - 1) / PS_UNROLL;
+  int64_t threads = (nchunks + PS_U - 1) / PS_U;
   int64_t blocks = (threads + PS_NT - 1) / PS_NT;
   if (blocks < 1) blocks = 1;
   if (blocks > 8192) blocks = 8192;
+  if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
   if (dtype == TP_BF16)
     hipLaunchKernelGGL(partial_sum_kernel<bf16_t>, dim3((unsigned)blocks), dim3(PS_NT), 0,
                        stream, ptrs, T, nchunks, count, out);

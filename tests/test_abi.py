@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -143,6 +143,22 @@ def test_partial_sum_argument_checks():
     assert ps(out=None) == E_NULL
     assert ps(out=addr(3, 8)) == E_ALIGN
     assert ps(out=addr(1, 16)) == E_ALIAS              # overlaps partials[0], not equal
+
+
+def test_capped_partial_sum_argument_checks():
+    def psc(cap, **kw):
+        a = dict(dtype=tp.TP_BF16, T=2, parts=[addr(1), addr(2)], count=1000, out=addr(3))
+        a.update(kw)
+        try:
+            tp.tp_partial_sum_capped(a["dtype"], a["T"], a["parts"], a["count"], a["out"], cap)
+        except tp.TpError as e:
+            return e.status
+        return 0
+    assert psc(0) == E_SHAPE
+    assert psc(-4) == E_SHAPE
+    assert psc(8, dtype=5) == E_DTYPE
+    assert psc(8, parts=None) == E_NULL
+    assert psc(8, out=addr(1, 16)) == E_ALIAS
 
 
 def gfwd(desc, offsets, **kw):

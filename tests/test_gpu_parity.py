@@ -202,6 +202,30 @@ def test_partial_sum_exact_pins(dtype):
     assert np.array_equal(f64(to_host(q)), 2 * f64(P))
 
 
+@pytest.mark.parametrize("dtype", [wl.DT_F32, wl.DT_BF16])
+def test_capped_partial_sum_matches_uncapped(dtype):
+    """The workgroup-capped sum strides over the tensor in the same summation
+    order, so it must equal the uncapped sum bit for bit, for any cap, with
+    a ragged tail (count not a multiple of 8) and for T above one load group."""
+    w = wl.WORKLOADS["c3_bf16_gelu_fwdbwd"]
+    for T, count in ((8, 1_000_003), (13, 65_541), (1, 777)):
+        parts = wl.gen_partials(w, T, (count,), 0.5, dtype=dtype)
+        dev = [to_device(p) for p in parts]
+        ref = torch.empty_like(dev[0])
+        tp.tp_partial_sum(dtype, T, dev, count, ref)
+        for cap in (1, 7, 32, 100000):
+            print(f"[gpu] capped sum dtype={dtype} T={T} count={count} cap={cap}", flush=True)
+            out = torch.full_like(dev[0], 0)
+            tp.tp_partial_sum_capped(dtype, T, dev, count, out, cap)
+            _sync()
+            assert np.array_equal(to_host(out), to_host(ref)), (T, count, cap)
+        got = f64(to_host(ref))
+        exp = oracle.partial_sum(parts)
+        absum = sum(np.abs(f64(p)) for p in parts)
+        eps_store = 2.0 ** -8 if dtype == wl.DT_BF16 else 2.0 ** -23
+        assert np.all(np.abs(got - exp) <= eps_store * np.abs(exp) + T * 2.0 ** -23 * absum)
+
+
 # ----------------------------------------------------------------------------
 # exact GPU pins
 # ----------------------------------------------------------------------------
