@@ -26,6 +26,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # its FETCH_SIZE / WRITE_SIZE calibrate the GEMM kernels' byte counts
 CALIB_COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_c4_swiglu.txt")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "gemm_clock_c4_swiglu.txt")
 KERNEL_SOURCES = ["gemm_bf16.hip", "common.h", "api.hip"]
 
 
@@ -40,21 +41,26 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per GEMM launch from the committed counter summary, or
-    None when it is missing or was taken on other kernel sources."""
+def recorded_field(path, key):
+    """A figure from a committed counter summary, or None when the file is
+    missing or was taken on other kernel sources."""
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     fields[k.strip()] = v.strip()
         if fields.get("kernel_source_hash") != kernel_source_hash():
             return None
-        return float(fields["hbm_bytes_per_gemm_launch"])
+        return float(fields[key])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def recorded_traffic():
+    """HBM bytes per GEMM launch (FETCH_SIZE + WRITE_SIZE, calibrated)."""
+    return recorded_field(TRAFFIC_FILE, "hbm_bytes_per_gemm_launch")
 
 
 def parse():
@@ -227,6 +233,9 @@ def main():
             + (nz * N * Ft + nz * Hd * Ft) * e2 + N * Hd * e2
     algo_bytes = fwd_bytes + bwd_bytes
     ps_gbs = ps_bytes / (ps_ms * 1e-3) / 1e9
+    # the shader clock the GEMMs ran at under load (counter summary of the
+    # same kernels): the MFMA peak at that clock is what the silicon offered
+    sclk = recorded_field(CLOCK_FILE, "sclk_ghz_gemm_mean")
 
     line = {
         "metric": "TP-shard MLP fwd+bwd TFLOP/s on 1 GPU + % of bf16 MFMA peak",
@@ -259,6 +268,11 @@ def main():
             "traffic": recorded_traffic(),
             "algorithmic_bytes_per_launch": round(algo_bytes / n_gemm),
         },
+        "clock_under_load": None if sclk is None else {
+            "sclk_ghz": sclk,
+            "peak_at_sclk": round(PEAK_BF16_TFLOPS * sclk / 2.4, 1),
+            "frac_at_sclk": round(gemm_tflops / (PEAK_BF16_TFLOPS * sclk / 2.4), 4),
+            "source": "profiles/gemm_clock_c4_swiglu.txt (rocprofv3 SQ_BUSY_CYCLES)"},
         "breakdown_ms": {"fwd_gemms": round(fwd_ms, 4), "bwd_gemms": round(bwd_ms, 4),
                          "partial_sum_each": round(ps_ms, 4),
                          "partial_sum_GBps": round(ps_gbs, 1),

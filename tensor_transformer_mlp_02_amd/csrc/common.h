@@ -32,16 +32,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// Round to nearest, ties to even.  NaN stays a (quiet) NaN.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// Round to nearest, ties to even, NaN stays a NaN: gfx950's packed
+// conversion (v_cvt_pk_bf16_f32) does this in one instruction per pair.
+typedef float f32x2_cvt_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const f32x2_cvt_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt_t));
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return (bf16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
 }
 
 // ---------------------------------------------------------------------------
@@ -285,6 +287,98 @@ __device__ __forceinline__ void epilogue_swiglu4(const EpiArgs& ea, int64_t m,
     Store4<T>::store(ea.out0, m * ea.ld0 + ea.split + f, u);
   }
   Store4<T>::store(ea.out1, m * ea.ld1 + f, h);
+}
+
+
+// ---------------------------------------------------------------------------
+// the same fused epilogues on 8 consecutive columns n..n+7 (one 16-byte
+// piece of a bf16 row): used when a tile's sums are read back row-major
+// ---------------------------------------------------------------------------
+template <typename T> struct Vec8;
+
+template <> struct Vec8<bf16_t> {
+  static __device__ __forceinline__ void store(void* base, int64_t off, const float v[8]) {
+    uint4 p;
+    p.x = pack_bf16x2(v[0], v[1]);
+    p.y = pack_bf16x2(v[2], v[3]);
+    p.z = pack_bf16x2(v[4], v[5]);
+    p.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(base) + off) = p;
+  }
+  static __device__ __forceinline__ void load(const void* base, int64_t off, float v[8]) {
+    const uint4 p = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(base) + off);
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void store(void* base, int64_t off, const float v[8]) {
+    float* q = reinterpret_cast<float*>(base) + off;
+    *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(q + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  static __device__ __forceinline__ void load(const void* base, int64_t off, float v[8]) {
+    const float* q = reinterpret_cast<const float*>(base) + off;
+    const float4 a = *reinterpret_cast<const float4*>(q);
+    const float4 b = *reinterpret_cast<const float4*>(q + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+template <int EPI, typename T, typename OutT>
+__device__ __forceinline__ void epilogue8(const EpiArgs& ea, int e, int64_t m, int64_t n,
+                                          const float c[8]) {
+  if constexpr (EPI == EPI_STORE) {
+    Vec8<OutT>::store(ea.out0, e * ea.bstride + m * ea.ld0 + n, c);
+  } else if constexpr (EPI == EPI_STORE_SPLIT) {
+    if (n < ea.split)
+      Vec8<OutT>::store(ea.out0, e * ea.bstride + m * ea.ld0 + n, c);
+    else
+      Vec8<OutT>::store(ea.out1, e * ea.bstride + m * ea.ld1 + (n - ea.split), c);
+  } else if constexpr (EPI == EPI_GELU_FWD) {
+    float h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = gelu_f(c[i]);
+    if (ea.out0) Vec8<T>::store(ea.out0, m * ea.ld0 + n, c);
+    Vec8<T>::store(ea.out1, m * ea.ld1 + n, h);
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    float z[8], d[8];
+    Vec8<T>::load(ea.aux, m * ea.ldaux + n, z);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = c[i] * gelu_grad_f(z[i]);
+    Vec8<T>::store(ea.out0, m * ea.ld0 + n, d);
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    float g[8], u[8], dg[8], du[8];
+    Vec8<T>::load(ea.aux, m * ea.ldaux + n, g);
+    Vec8<T>::load(ea.aux, m * ea.ldaux + ea.split + n, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float s = sigmoid_f(g[i]);
+      dg[i] = c[i] * u[i] * (s * (1.0f + g[i] * (1.0f - s)));
+      du[i] = c[i] * (g[i] * s);
+    }
+    Vec8<T>::store(ea.out0, m * ea.ld0 + n, dg);
+    Vec8<T>::store(ea.out0, m * ea.ld0 + ea.split + n, du);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void epilogue_swiglu8(const EpiArgs& ea, int64_t m, int64_t f,
+                                                 const float g[8], const float u[8]) {
+  float h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = silu_f(g[i]) * u[i];
+  if (ea.out0) {
+    Vec8<T>::store(ea.out0, m * ea.ld0 + f, g);
+    Vec8<T>::store(ea.out0, m * ea.ld0 + ea.split + f, u);
+  }
+  Vec8<T>::store(ea.out1, m * ea.ld1 + f, h);
 }
 
 }  // namespace tpmlp

@@ -240,56 +240,83 @@ __device__ __forceinline__ void store_k(bf16_t* tile, int tid, const Stage<NW>& 
   }
 }
 
-// ---- epilogue: lane holds rows m, columns n0 + 8 q + 4 c_lane + (0..3) of
-// each of its FM x FN accumulator blocks
-template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN>
-__device__ __forceinline__ void write_tile(const f32x16_t (&acc)[FM][FN], const EpiArgs& ea,
-                                           const TileCoord& tc, int wm, int wn, int r_lane,
-                                           int c_lane, int Ncols) {
-  static_for<0, FM>([&](auto I) {
-    constexpr int i = decltype(I)::value;
-    const int64_t m = tc.m_begin + wm * WTM + i * 32 + r_lane;
-    if (m < tc.m_end) {
-      if constexpr (EPI == EPI_SWIGLU_FWD) {
-        static_for<0, FN / 2>([&](auto JP) {
-          constexpr int jp = decltype(JP)::value;
-          static_for<0, 4>([&](auto Q) {
-            constexpr int q = decltype(Q)::value;
-            const int64_t f = (int64_t)tc.tn * (BN / 2) + wn * (WTN / 2) + jp * 32 + q * 8 +
-                              c_lane * 4;
-            if (f < ea.split) {
-              float gv[4], uv[4];
-              static_for<0, 4>([&](auto V) {
-                constexpr int v = decltype(V)::value;
-                gv[v] = acc[i][2 * jp][q * 4 + v];
-                uv[v] = acc[i][2 * jp + 1][q * 4 + v];
-              });
-              epilogue_swiglu4<bf16_t>(ea, m, f, gv, uv);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+// ---- epilogue through shared memory ----------------------------------------
+// The tile is written out in four passes of 64 rows.  In each pass the two
+// wavefronts holding those rows store their fp32 sums row-major in shared
+// memory (rows padded by 16 bytes, so a wavefront's 16-byte writes spread
+// over all banks), then every thread takes 8 consecutive columns of a row:
+// saved activations are loaded and outputs stored as 16-byte pieces of
+// contiguous rows.  For the paired SwiGLU forward the gate sums go to
+// columns 0..127 and the up sums to 128..255 of the staged rows.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int EQ_ROWS = 64;
+constexpr int EQ_PITCH = BN + 4;  // floats
+constexpr int EQ_BYTES = EQ_ROWS * EQ_PITCH * 4;
+
+template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN, int NT>
+__device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
+                                                  const EpiArgs& ea, const TileCoord& tc,
+                                                  int wm, int wn, int lane, int tid, int Ncols,
+                                                  float* stage) {
+  static_assert(WTM == 128 && FM == 4, "passes of 64 rows take two 32-row fragment rows");
+  constexpr bool PAIR = EPI == EPI_SWIGLU_FWD;
+  const int r_lane = lane & 31, c_lane = lane >> 5;
+  static_for<0, 4>([&](auto Qc) {
+    constexpr int q = decltype(Qc)::value;
+    if (wm == q / 2) {
+      static_for<0, 2>([&](auto Ic) {
+        constexpr int ii = decltype(Ic)::value, i = 2 * (q % 2) + ii;
+        const int row = ii * 32 + r_lane;
+        static_for<0, FN>([&](auto Jc) {
+          constexpr int j = decltype(Jc)::value;
+          const int col0 = PAIR ? (j & 1) * (BN / 2) + wn * (WTN / 2) + (j >> 1) * 32
+                                : wn * WTN + j * 32;
+          static_for<0, 4>([&](auto Gc) {
+            constexpr int gq = decltype(Gc)::value;
+            const f32x4_t v = {acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                               acc[i][j][4 * gq + 3]};
+            *reinterpret_cast<f32x4_t*>(stage + row * EQ_PITCH + col0 + 8 * gq + 4 * c_lane) = v;
           });
         });
-      } else {
-        static_for<0, FN>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          static_for<0, 4>([&](auto Q) {
-            constexpr int q = decltype(Q)::value;
-            const int64_t n = (int64_t)tc.tn * BN + wn * WTN + j * 32 + q * 8 + c_lane * 4;
-            if (n < Ncols) {
-              float cv[4];
-              static_for<0, 4>([&](auto V) {
-                constexpr int v = decltype(V)::value;
-                cv[v] = acc[i][j][q * 4 + v];
-              });
-              epilogue4<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
-            }
-            // keep each group's loads and stores local: hoisting all of
-            // them would exceed the register file
-            __builtin_amdgcn_sched_barrier(0);
-          });
-        });
-      }
+      });
     }
+    __syncthreads();
+    const int64_t m0 = tc.m_begin + EQ_ROWS * q;
+    if constexpr (PAIR) {
+      constexpr int CH = EQ_ROWS * (BN / 2) / 8;
+      static_for<0, CH / NT>([&](auto Kc) {
+        const int k = decltype(Kc)::value * NT + tid;
+        const int row = k >> 4, cc = (k & 15) * 8;
+        const int64_t m = m0 + row;
+        const int64_t f = (int64_t)tc.tn * (BN / 2) + cc;
+        if (m < tc.m_end && f < ea.split) {
+          float gv[8], uv[8];
+          const float* src = stage + row * EQ_PITCH + cc;
+          *reinterpret_cast<f32x4_t*>(gv) = *reinterpret_cast<const f32x4_t*>(src);
+          *reinterpret_cast<f32x4_t*>(gv + 4) = *reinterpret_cast<const f32x4_t*>(src + 4);
+          *reinterpret_cast<f32x4_t*>(uv) = *reinterpret_cast<const f32x4_t*>(src + BN / 2);
+          *reinterpret_cast<f32x4_t*>(uv + 4) = *reinterpret_cast<const f32x4_t*>(src + BN / 2 + 4);
+          epilogue_swiglu8<bf16_t>(ea, m, f, gv, uv);
+        }
+      });
+    } else {
+      constexpr int CH = EQ_ROWS * BN / 8;
+      static_for<0, CH / NT>([&](auto Kc) {
+        const int k = decltype(Kc)::value * NT + tid;
+        const int row = k >> 5, cc = (k & 31) * 8;
+        const int64_t m = m0 + row;
+        const int64_t n = (int64_t)tc.tn * BN + cc;
+        if (m < tc.m_end && n < Ncols) {
+          float cv[8];
+          const float* src = stage + row * EQ_PITCH + cc;
+          *reinterpret_cast<f32x4_t*>(cv) = *reinterpret_cast<const f32x4_t*>(src);
+          *reinterpret_cast<f32x4_t*>(cv + 4) = *reinterpret_cast<const f32x4_t*>(src + 4);
+          epilogue8<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
+        }
+      });
+    }
+    // the next pass rewrites the staging rows
+    __syncthreads();
   });
 }
 
@@ -462,7 +489,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
   // the epilogue's VALU code: drain both before the registers are reused
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 
-  write_tile<EPI, BMODE, OutT, FM, FN, WTM, WTN>(acc, ea, tc, wm, wn, r_lane, c_lane, Ncols);
+  // every wavefront is past its last shared-memory read before the tile
+  // is staged through shared memory
+  static_assert(EQ_BYTES <= (int)sizeof(lds), "staging rows exceed shared memory");
+  __syncthreads();
+  write_tile_staged<EPI, BMODE, OutT, FM, FN, WTM, WTN, 64 * NW>(
+      acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
 // ---- lean kernel: 4 wavefronts of 128 x 128, hand-ordered k loop ----------
@@ -754,7 +786,12 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 
-  write_tile<EPI, BMODE, OutT, FM, FN, WTM, WTN>(acc, ea, tc, wm, wn, r_lane, c_lane, Ncols);
+  // every wavefront's loads have landed and its reads are done before the
+  // tile is staged through shared memory
+  static_assert(EQ_BYTES <= (int)sizeof(lds), "staging rows exceed shared memory");
+  __syncthreads();
+  write_tile_staged<EPI, BMODE, OutT, FM, FN, WTM, WTN, LEAN_NT>(
+      acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
 // ---- ring kernel: 4-stage shared-memory ring of 32-wide k tiles ------------
@@ -1015,7 +1052,12 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_ring(GemmArgs g) {
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 
-  write_tile<EPI, BMODE, OutT, FM, FN, WTM, WTN>(acc, ea, tc, wm, wn, r_lane, c_lane, Ncols);
+  // every wavefront's loads have landed and its reads are done before the
+  // tile is staged through shared memory
+  static_assert(EQ_BYTES <= (int)sizeof(lds), "staging rows exceed shared memory");
+  __syncthreads();
+  write_tile_staged<EPI, BMODE, OutT, FM, FN, WTM, WTN, LEAN_NT>(
+      acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
 }  // namespace mfma256
