@@ -516,6 +516,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
 // multiple of 64, and a k split is a multiple of 64.
 
 constexpr int LEAN_NT = 256;
+constexpr int W16_NT = 256;
 constexpr int TILE_BYTES = BM * BK * 2;  // one operand tile, 32 KiB
 
 template <int OFF>
@@ -1060,6 +1061,326 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_ring(GemmArgs g) {
       acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
+
+// ---- 16x16x32 kernel: tiles of BMT x BNT, each 224 or 256 ---------------------
+//
+// Tiles 224 wide let a GEMM whose extent is a multiple of 224 but not 256
+// (F/T = 3584 = 16 x 224) fill every compute unit in whole waves, where
+// 256 x 256 tiles leave a partial last wave.  Four wavefronts, 2 x 2, each
+// own a (BMT/2) x (BNT/2) block of 16 x 16 accumulators; a 16-wide fragment
+// grid is what lets a wavefront cover 112 columns.  k tiles are 64 wide
+// (two 32-wide MFMA steps) in two shared-memory buffers, laid out as in
+// gemm_lean except that M/N-contiguous tiles also XOR granules with bit 3
+// of k: the four k groups of a 16 x 32 fragment read the same 16 columns,
+// and this keeps two neighbouring groups on different banks.  For the
+// paired SwiGLU forward, gate columns fill buffer half 0 and up columns
+// half 1 (one source matrix per direct load); the wavefronts of column 0
+// compute gate sums and those of column 1 up sums for the same 112 logical
+// columns, re-paired by the staged epilogue.
+__device__ __forceinline__ int sw16(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
+__device__ __forceinline__ int mn16_off(int k, int c) {
+  const int h = c >> 7, q = (c >> 3) & 15, e = c & 7;
+  return h * (BK * 128) + k * 128 + ((q ^ sw16(k)) << 3) + e;
+}
+__device__ __forceinline__ void mfma16_ordered(f32x4_t& acc, const bf16x8_t& a,
+                                               const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b) : "memory");
+}
+
+// staged epilogue for 16 x 16 accumulators: passes of up to 64 rows (four
+// fragment rows of one wavefront row); lane l holds row 16 i + l % 16 and
+// columns 16 j + 4 (l / 16) + (0..3) of its wavefront block
+template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN, int BNT>
+__device__ __forceinline__ void write_tile_staged16(const f32x4_t (&acc)[FM][FN],
+                                                    const EpiArgs& ea, const TileCoord& tc,
+                                                    int wm, int wn, int lane, int tid,
+                                                    int Ncols, float* stage) {
+  constexpr bool PAIR = EPI == EPI_SWIGLU_FWD;
+  constexpr int HALF = (FM + 1) / 2;  // fragment rows of the first pass of a wavefront row
+  const int r16 = lane & 15, c16 = lane >> 4;
+  static_for<0, 4>([&](auto Pc) {
+    constexpr int p = decltype(Pc)::value;
+    constexpr int lo = (p & 1) ? HALF : 0, hi = (p & 1) ? FM : HALF;
+    constexpr int R = (hi - lo) * 16;
+    if (wm == (p >> 1)) {
+      static_for<lo, hi>([&](auto Ic) {
+        constexpr int i = decltype(Ic)::value;
+        const int row = (i - lo) * 16 + r16;
+        static_for<0, FN>([&](auto Jc) {
+          constexpr int j = decltype(Jc)::value;
+          const int col = (PAIR ? wn * 128 : wn * WTN) + 16 * j + 4 * c16;
+          *reinterpret_cast<f32x4_t*>(stage + row * EQ_PITCH + col) = acc[i][j];
+        });
+      });
+    }
+    __syncthreads();
+    const int64_t m0 = tc.m_begin + (p >> 1) * WTM + lo * 16;
+    constexpr int CPR = PAIR ? WTN / 8 : BNT / 8;  // 8-column chunks per row
+    constexpr int NCH = R * CPR;
+    static_for<0, (NCH + W16_NT - 1) / W16_NT>([&](auto Kc) {
+      const int k = decltype(Kc)::value * W16_NT + tid;
+      if (NCH % W16_NT == 0 || k < NCH) {
+        const int row = k / CPR, cc = (k % CPR) * 8;
+        const int64_t m = m0 + row;
+        const float* src = stage + row * EQ_PITCH + cc;
+        if constexpr (PAIR) {
+          const int64_t f = (int64_t)tc.tn * WTN + cc;
+          if (m < tc.m_end && f < ea.split) {
+            float gv[8], uv[8];
+            *reinterpret_cast<f32x4_t*>(gv) = *reinterpret_cast<const f32x4_t*>(src);
+            *reinterpret_cast<f32x4_t*>(gv + 4) = *reinterpret_cast<const f32x4_t*>(src + 4);
+            *reinterpret_cast<f32x4_t*>(uv) = *reinterpret_cast<const f32x4_t*>(src + 128);
+            *reinterpret_cast<f32x4_t*>(uv + 4) = *reinterpret_cast<const f32x4_t*>(src + 132);
+            epilogue_swiglu8<bf16_t>(ea, m, f, gv, uv);
+          }
+        } else {
+          const int64_t n = (int64_t)tc.tn * BNT + cc;
+          if (m < tc.m_end && n < Ncols) {
+            float cv[8];
+            *reinterpret_cast<f32x4_t*>(cv) = *reinterpret_cast<const f32x4_t*>(src);
+            *reinterpret_cast<f32x4_t*>(cv + 4) = *reinterpret_cast<const f32x4_t*>(src + 4);
+            epilogue8<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
+          }
+        }
+      }
+    });
+    __syncthreads();
+  });
+}
+
+template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT, int BMT, int BNT>
+__global__ __launch_bounds__(W16_NT, 1) void gemm_w16(GemmArgs g) {
+  static_assert(BMT == 224 || BMT == 256, "tile rows");
+  static_assert(BNT == 224 || BNT == 256, "tile columns");
+  constexpr bool PAIR = BMODE == BMODE_PAIR32;
+  static_assert(!PAIR || (!B_KMAJOR && BNT == 224), "paired tiles: 112 gate + 112 up columns");
+  static_assert(BMODE != BMODE_KSPLIT, "k split not supported here");
+  constexpr int WTM = BMT / 2, WTN = BNT / 2;
+  constexpr int FM = WTM / 16, FN = WTN / 16;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[4 * BM * BK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r16 = lane & 15, c16 = lane >> 4;
+
+  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BMT);
+  const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
+  const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
+  const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
+  const int64_t lda = g.a.ld, ldb = g.b.ld, bsplit = g.b.split;
+  const int Ncols = g.N;
+  const EpiArgs ea = g.epi;
+  const int n_base = tc.tn * BNT;
+  // rows / columns of this tile that exist
+  const int m_rows = min(BMT, tc.m_end - tc.m_begin);
+  const int n_cols = min(BNT, Ncols - n_base);
+  const int nk = (tc.k_end > tc.k_begin) ? (tc.k_end - tc.k_begin + BK - 1) / BK : 0;
+
+  const uint32_t lds0 = lds_u32(lds);
+  const uint32_t ldsA = lds0, ldsB = lds0 + 2 * TILE_BYTES;
+
+  // ---- loop-invariant direct-load offsets (bytes) and LDS destinations
+  uint32_t voffA[8], voffB[8];
+  uint32_t dstA[8], dstB[8];
+  static_for<0, 8>([&](auto Ic) {
+    constexpr int i = decltype(Ic)::value;
+    if constexpr (A_KMAJOR) {
+      const int blk = wave * 8 + i;
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      voffA[i] = r < m_rows ? (uint32_t)(((int64_t)r * lda + c * 8) * 2) : OOB_OFF;
+      dstA[i] = blk * 1024;
+    } else {
+      const int half = wave >> 1, b = (wave & 1) * 8 + i;
+      const int k = 4 * b + (lane >> 4);
+      const int q = (lane & 15) ^ sw16(k);
+      const int cl = half * 128 + 8 * q;
+      voffA[i] = cl < m_rows ? (uint32_t)(((int64_t)k * lda + tc.m_begin + cl) * 2) : OOB_OFF;
+      dstA[i] = half * (TILE_BYTES / 2) + b * 1024;
+    }
+    if constexpr (B_KMAJOR) {
+      const int blk = wave * 8 + i;
+      const int r = blk * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      voffB[i] = r < n_cols ? (uint32_t)(((int64_t)r * ldb + c * 8) * 2) : OOB_OFF;
+      dstB[i] = blk * 1024;
+    } else {
+      const int half = wave >> 1, b = (wave & 1) * 8 + i;
+      const int k = 4 * b + (lane >> 4);
+      const int q = (lane & 15) ^ sw16(k);
+      bool ok;
+      int64_t col;
+      if constexpr (PAIR) {
+        // half 0: gate columns, half 1: up columns, 112 of each
+        col = (int64_t)tc.tn * WTN + 8 * q;
+        ok = q < WTN / 8 && col < bsplit;
+      } else {
+        const int cl = half * 128 + 8 * q;
+        col = n_base + cl;
+        ok = cl < n_cols;
+      }
+      voffB[i] = ok ? (uint32_t)(((int64_t)k * ldb + col) * 2) : OOB_OFF;
+      dstB[i] = half * (TILE_BYTES / 2) + b * 1024;
+    }
+  });
+  rsrc_t rsA, rsB;
+  int soA = 0, soB = 0;
+  auto set_tile = [&](int k0, bool valid) {
+    if constexpr (A_KMAJOR) {
+      rsA = make_rsrc_n(a0 + (int64_t)tc.m_begin * lda, valid ? 0x7fffffffu : 0u);
+      soA = k0 * 2;
+    } else {
+      const int64_t rem = (int64_t)(tc.k_end - k0) * lda * 2;
+      rsA = make_rsrc_n(a0 + (int64_t)k0 * lda, valid ? clamp_records(rem) : 0u);
+    }
+    if constexpr (B_KMAJOR) {
+      rsB = make_rsrc_n(b0 + (int64_t)n_base * ldb, valid ? 0x7fffffffu : 0u);
+      soB = k0 * 2;
+    } else {
+      const bf16_t* bp = (PAIR && (wave >> 1)) ? b1 : b0;
+      const int64_t rem = (int64_t)(tc.k_end - k0) * ldb * 2;
+      rsB = make_rsrc_n(bp + (int64_t)k0 * ldb, valid ? clamp_records(rem) : 0u);
+    }
+  };
+  auto load_op = [&](auto Lc, uint32_t buf_off) {
+    constexpr int l = decltype(Lc)::value;
+    if constexpr (l < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsA, (lds_void_t*)(lds + (ldsA - lds0 + buf_off + dstA[l]) / 2), 16, voffA[l], soA, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsB, (lds_void_t*)(lds + (ldsB - lds0 + buf_off + dstB[l - 8]) / 2), 16, voffB[l - 8],
+          soB, 0, 0);
+  };
+
+  // ---- loop-invariant LDS read addresses (bytes, buffer 0)
+  // K-contiguous: one per 32-wide k step (fragment i adds 2 KiB);
+  // M/N-contiguous: one per fragment (k step s adds 8 KiB, the second
+  // transposing read 1 KiB)
+  uint32_t rdA[FM], rdB[FN];
+  const int sw = swz(r16);
+  static_for<0, FM>([&](auto Xc) {
+    constexpr int x = decltype(Xc)::value;
+    if constexpr (A_KMAJOR) {
+      if constexpr (x < 2) rdA[x] = ldsA + (wm * WTM + r16) * 128 + (((4 * x + c16) ^ sw) << 4);
+    } else {
+      const int c = wm * WTM + 16 * x + 4 * (r16 & 3);
+      const int k = 8 * c16 + (r16 >> 2);
+      rdA[x] = ldsA + 2 * mn16_off(k, c);
+    }
+  });
+  static_for<0, FN>([&](auto Xc) {
+    constexpr int x = decltype(Xc)::value;
+    if constexpr (B_KMAJOR) {
+      if constexpr (x < 2) rdB[x] = ldsB + (wn * WTN + r16) * 128 + (((4 * x + c16) ^ sw) << 4);
+    } else {
+      const int c = (PAIR ? wn * 128 : wn * WTN) + 16 * x + 4 * (r16 & 3);
+      const int k = 8 * c16 + (r16 >> 2);
+      rdB[x] = ldsB + 2 * mn16_off(k, c);
+    }
+  });
+
+  using FA = typename std::conditional<A_KMAJOR, FragK, FragMN>::type;
+  using FB = typename std::conditional<B_KMAJOR, FragK, FragMN>::type;
+  FA fa[2][FM];
+  FB fb[2][FN];
+  constexpr int RA = A_KMAJOR ? FM : 2 * FM, RB = B_KMAJOR ? FN : 2 * FN;
+  constexpr int NREAD = RA + RB;
+  auto read_op = [&](auto Rc, auto Sc, uint32_t boff) {
+    constexpr int r = decltype(Rc)::value, S = decltype(Sc)::value;
+    if constexpr (r < RA) {
+      if constexpr (A_KMAJOR) {
+        ds_read_b128_at<r * 2048>(fa[S][r].v, rdA[S] + boff);
+      } else {
+        constexpr int blk = r >> 1, part = r & 1;
+        if constexpr (part == 0)
+          ds_read_tr_at<S * 8192>(fa[S][blk].lo, rdA[blk] + boff);
+        else
+          ds_read_tr_at<S * 8192 + 1024>(fa[S][blk].hi, rdA[blk] + boff);
+      }
+    } else {
+      constexpr int rr = r - RA;
+      if constexpr (B_KMAJOR) {
+        ds_read_b128_at<rr * 2048>(fb[S][rr].v, rdB[S] + boff);
+      } else {
+        constexpr int blk = rr >> 1, part = rr & 1;
+        if constexpr (part == 0)
+          ds_read_tr_at<S * 8192>(fb[S][blk].lo, rdB[blk] + boff);
+        else
+          ds_read_tr_at<S * 8192 + 1024>(fb[S][blk].hi, rdB[blk] + boff);
+      }
+    }
+  };
+  auto fence_slot = [&](auto SLc) {
+    constexpr int SL = decltype(SLc)::value;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    static_for<0, FM>([&](auto I) { fa[SL][I].fence(); });
+    static_for<0, FN>([&](auto J) { fb[SL][J].fence(); });
+  };
+
+  f32x4_t acc[FM][FN];
+  static_for<0, FM>([&](auto I) {
+    static_for<0, FN>([&](auto J) { acc[I][J] = (f32x4_t)(0.0f); });
+  });
+
+  // prologue: tiles 0 and 1 in flight, wait for tile 0, read its first step
+  if (nk > 0) {
+    set_tile(tc.k_begin, true);
+    static_for<0, 16>([&](auto L) { load_op(L, 0u); });
+    set_tile(tc.k_begin + BK, nk > 1);
+    static_for<0, 16>([&](auto L) { load_op(L, (uint32_t)TILE_BYTES); });
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
+  if (nk > 0) {
+    static_for<0, NREAD>([&](auto R) { read_op(R, std::integral_constant<int, 0>{}, 0u); });
+  }
+  asm volatile("s_nop 4");
+
+  constexpr int NMF = FM * FN;  // MFMAs per step
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint32_t cur = (uint32_t)(kt & 1) * TILE_BYTES;
+    const uint32_t nxt = cur ^ TILE_BYTES;
+    set_tile(tc.k_begin + (kt + 2) * BK, kt + 2 < nk);
+    static_for<0, 2>([&](auto Sc) {
+      constexpr int S = decltype(Sc)::value;
+      fence_slot(std::integral_constant<int, S>{});
+      if constexpr (S == 1) {
+        // tile kt + 1 has landed everywhere and every wavefront has read
+        // all of this tile: the buffer takes tile kt + 2
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+      }
+      constexpr int NLOAD = S == 1 ? 16 : 0;
+      static_for<0, NMF>([&](auto Mc) {
+        constexpr int m = decltype(Mc)::value;
+        constexpr int i = m / FN, j = m % FN;
+        mfma16_ordered(acc[i][j], fb[S][j].op(), fa[S][i].op());
+        // reads of the next step within the first half of the MFMAs
+        constexpr int H = NMF / 2;
+        constexpr int r0 = m < H ? (m * NREAD) / H : NREAD;
+        constexpr int r1 = m < H ? ((m + 1) * NREAD) / H : NREAD;
+        static_for<r0, r1>([&](auto Oc) {
+          read_op(Oc, std::integral_constant<int, S ^ 1>{}, S == 0 ? cur : nxt);
+        });
+        constexpr int l0 = (m * NLOAD) / NMF, l1 = ((m + 1) * NLOAD) / NMF;
+        static_for<l0, l1>([&](auto Oc) {
+          constexpr int idx = decltype(Oc)::value;
+          load_op(std::integral_constant<int, (idx & 1) * 8 + (idx >> 1)>{}, cur);
+        });
+      });
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+
+  static_assert(EQ_BYTES <= (int)sizeof(lds), "staging rows exceed shared memory");
+  __syncthreads();
+  write_tile_staged16<EPI, BMODE, OutT, FM, FN, WTM, WTN, BNT>(
+      acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
+}
+
 }  // namespace mfma256
 
 // ---------------------------------------------------------------------------
@@ -1074,6 +1395,9 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_ring(GemmArgs g) {
 #endif
 #ifndef TP_USE_RING
 #define TP_USE_RING 1
+#endif
+#ifndef TP_USE_W16
+#define TP_USE_W16 1
 #endif
 
 static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols) {
@@ -1090,8 +1414,93 @@ static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols) {
   }
 }
 
+// compute units of the current device (cached per device)
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// tiles of a BMT x BNT grid (n_cols: columns as tiled)
+static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols) {
+  const int tn = (n_cols + BNT - 1) / BNT;
+  int t = 0;
+  for (int e = 0; e < g.E; ++e) {
+    const int rows = g.ragged == RAGGED_M ? g.row_off[e + 1] - g.row_off[e] : g.M;
+    t += ((rows + BMT - 1) / BMT) * tn;
+  }
+  return t;
+}
+
+// Tile shape for the bf16 GEMM: 256 x 256 unless a 224-wide shape fills
+// the compute units in fewer tile-area waves (whole waves x tile area).  The
+// 16 x 16 x 32 MFMA of the 224-wide kernel takes about 9 % more cycles per
+// FLOP than 32 x 32 x 16 (measured on an MFMA-only loop and on the GEMM
+// k loop), so its cost is scaled by that.
+// Returns 0 (256 x 256), 1 (256 x 224) or 2 (224 x 256).
+constexpr double W16_CYCLE_FACTOR = 1.09;
+static int pick_shape(const GemmArgs& g, int bmode, bool w16_ok) {
+  if (!TP_USE_W16 || !w16_ok) return 0;
+  const int cus = device_cus();
+  auto cost = [&](int BMT, int BNT, int tiles) {
+    const double f = (BMT == 256 && BNT == 256) ? 1.0 : W16_CYCLE_FACTOR;
+    return f * (double)((tiles + cus - 1) / cus) * BMT * BNT;
+  };
+  if (bmode == BMODE_PAIR32) {
+    const int split = (int)g.b.split;
+    const double c0 = cost(256, 256, count_tiles(g, 256, 128, split));
+    const double c1 = cost(256, 224, count_tiles(g, 256, 112, split));
+    return c1 < c0 ? 1 : 0;
+  }
+  const double c0 = cost(256, 256, count_tiles(g, 256, 256, g.N));
+  const double c1 = cost(256, 224, count_tiles(g, 256, 224, g.N));
+  const double c2 = cost(224, 256, count_tiles(g, 224, 256, g.N));
+  if (c1 < c0 && c1 <= c2) return 1;
+  if (c2 < c0) return 2;
+  return 0;
+}
+
+template <bool AK, bool BK_, int BMODE, int EPI, typename OutT, int BMT, int BNT>
+static hipError_t launch_w16(GemmArgs& g, hipStream_t stream) {
+  if constexpr (BMODE == BMODE_KSPLIT || (BMODE == BMODE_PAIR32 && (BK_ || BNT != 224))) {
+    return hipErrorInvalidValue;
+  } else {
+    if (BMODE == BMODE_PAIR32) {
+      // 112 gate + 112 up columns per tile
+      const int tiles_n = (int)((g.b.split + 111) / 112);
+      g.N = tiles_n * 224;
+    }
+    fill_tiles(g, BMT, BNT, g.N);
+    const int blocks = g.tile_off[g.E];
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((mfma256::gemm_w16<AK, BK_, BMODE, EPI, OutT, BMT, BNT>), dim3(blocks),
+                       dim3(mfma256::W16_NT), 0, stream, g);
+    return hipGetLastError();
+  }
+}
+
 template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
+  {
+    const bool k_whole = (!AK && !BK_) || g.K % mfma256::BK == 0;
+    const bool w16_ok = k_whole && BMODE != BMODE_KSPLIT && !(BMODE == BMODE_PAIR32 && BK_);
+    switch (pick_shape(g, BMODE, w16_ok)) {
+      case 1: return launch_w16<AK, BK_, BMODE, EPI, OutT, 256, 224>(g, stream);
+      case 2:
+        if constexpr (BMODE != BMODE_PAIR32)
+          return launch_w16<AK, BK_, BMODE, EPI, OutT, 224, 256>(g, stream);
+        break;
+      default: break;
+    }
+  }
   int n_cols = g.N;
   if (BMODE == BMODE_PAIR32) {
     // logical columns are laid out in 64-wide (gate 32 | up 32) groups
