@@ -211,6 +211,26 @@ def main():
         ps_ms += [e[7].elapsed_time(e[8]) for e in evs]
     ps_ms = float(np.mean(ps_ms))
 
+    # sequence-parallel form of the same exchange (outside the timed step):
+    # rank 0's [S/T,B,H] slice of the sum, the reduce-scatter arithmetic
+    rs = None
+    if w.S % w.T == 0:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        slice_out = torch.empty((w.S // w.T) * w.B * w.H, dtype=Ysum.dtype, device=dev)
+        for _ in range(3):
+            tp.tp_partial_sum_scatter(w.dtype, w.T, [buf.Y] + stand, w.S, w.B, w.H, 0, slice_out)
+        reps = 20
+        e0.record(stream)
+        for _ in range(reps):
+            tp.tp_partial_sum_scatter(w.dtype, w.T, [buf.Y] + stand, w.S, w.B, w.H, 0, slice_out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rs_ms = e0.elapsed_time(e1) / reps
+        rs_bytes = (w.T + 1) * slice_out.numel() * 2
+        rs = {"us": round(rs_ms * 1e3, 2), "GBps": round(rs_bytes / (rs_ms * 1e-3) / 1e9, 1),
+              "hbm_frac": round(rs_bytes / (rs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+              "bytes": rs_bytes}
+
     flops = gemm_flops(w)
     value = flops / (ms * 1e-3) / 1e12
     gemm_ms = fwd_ms + bwd_ms
@@ -277,6 +297,7 @@ def main():
                          "partial_sum_each": round(ps_ms, 4),
                          "partial_sum_GBps": round(ps_gbs, 1),
                          "partial_sum_hbm_frac": round(ps_gbs / PEAK_HBM_GBS, 4)},
+        "reduce_scatter_rank0": rs,
     }
 
     if not args.no_cpu_baseline:

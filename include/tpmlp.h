@@ -160,6 +160,27 @@ int tp_partial_sum(int32_t dtype, int32_t T, const void *const *partials,
                    int64_t count, void *out, void *stream);
 
 /*
+ * tp_partial_sum_scatter -- the reduce-scatter form of tp_partial_sum used
+ * with sequence parallelism ([P1] §三 3.5; [P3] §06 Sequence Parallel):
+ * each of the T ranks keeps only its slice of the sequence, so this rank's
+ * output is rows s = rank*S/T .. (rank+1)*S/T - 1 of the summed [S,B,H]
+ * tensor (with n = s*B + b these rows are one contiguous range):
+ *   out[j] = sum_{i<T} partials[i][rank*(S/T)*B*H + j],  j < (S/T)*B*H
+ *   partials  HOST array of T device pointers to full [S,B,H] partials
+ *   S, B, H   the full shape; S must be a multiple of T; H a multiple of 8
+ *             (bf16) or 4 (fp32)
+ *   rank      0..T-1
+ *   out       [S/T,B,H]; must not overlap any partial
+ * Each element is summed in fp32 in the order i = 0..T-1 and rounded once:
+ * the result equals the same rows of tp_partial_sum's output bit for bit.
+ * The backward of the sequence all-gather in front of FC1 is this same
+ * reduce-scatter applied to the dX partials.
+ */
+int tp_partial_sum_scatter(int32_t dtype, int32_t T, const void *const *partials,
+                           int64_t S, int64_t B, int64_t H, int32_t rank, void *out,
+                           void *stream);
+
+/*
  * tp_partial_sum_capped -- tp_partial_sum on at most `max_workgroups`
  * workgroups of 256 threads (which stride over the whole tensor), so the
  * sum occupies only a few compute units and can run on a second stream

@@ -181,6 +181,19 @@ def partial_sum(parts) -> np.ndarray:
     return out.reshape(shape)
 
 
+def reduce_scatter(parts, S, B, H, rank) -> np.ndarray:
+    """Sequence-parallel reduce-scatter ([P1] §三 3.5; [P3] §06): the sum of
+    the T partial [S,B,H] outputs, of which rank keeps sequence rows
+    rank*S/T .. (rank+1)*S/T - 1.  Written as its definition: the full sum,
+    then the rank's slice."""
+    T = len(parts)
+    if S % T:
+        raise ValueError("S must be divisible by T")
+    full = partial_sum([np.asarray(p).reshape(S, B, H) for p in parts])
+    m = S // T
+    return full[rank * m:(rank + 1) * m]
+
+
 # ----------------------------------------------------------------------------
 # all shards of a full weight pair, and the unsharded MLP
 # ----------------------------------------------------------------------------

@@ -17,7 +17,7 @@ __all__ = [
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU", "TpError",
     "tp_mlp_desc", "tp_expert_desc", "lib", "library_path",
     "tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_mlp_shard_bwd_workspace",
-    "tp_partial_sum", "tp_partial_sum_capped", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
+    "tp_partial_sum", "tp_partial_sum_capped", "tp_partial_sum_scatter", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
     "tp_grouped_expert_bwd_workspace", "tp_last_error", "tp_status_string",
 ]
 
@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
     L.tp_partial_sum_capped.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_vp),
                                         ctypes.c_int64, _vp, ctypes.c_int32, _vp]
     L.tp_partial_sum_capped.restype = ctypes.c_int
+    L.tp_partial_sum_scatter.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_vp),
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int32, _vp, _vp]
+    L.tp_partial_sum_scatter.restype = ctypes.c_int
     L.tp_grouped_expert_fwd.argtypes = [ED, I64P] + [_vp] * 8
     L.tp_grouped_expert_fwd.restype = ctypes.c_int
     L.tp_grouped_expert_bwd_workspace.argtypes = [ED, I64P]
@@ -179,6 +183,15 @@ def tp_partial_sum_capped(dtype: int, T: int, partials, count: int, out, max_wor
         arr = (_vp * max(1, len(partials)))(*[_ptr(p) for p in partials])
     return _check(lib().tp_partial_sum_capped(int(dtype), int(T), arr, int(count), _ptr(out),
                                               int(max_workgroups), _stream(stream)))
+
+
+def tp_partial_sum_scatter(dtype: int, T: int, partials, S: int, B: int, H: int, rank: int,
+                           out, stream=None) -> int:
+    arr = None
+    if partials is not None:
+        arr = (_vp * max(1, len(partials)))(*[_ptr(p) for p in partials])
+    return _check(lib().tp_partial_sum_scatter(int(dtype), int(T), arr, int(S), int(B), int(H),
+                                               int(rank), _ptr(out), _stream(stream)))
 
 
 def tp_grouped_expert_fwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, Y_perm,

@@ -349,6 +349,38 @@ int tp_partial_sum(int32_t dtype, int32_t T, const void* const* partials, int64_
   return partial_sum_common(dtype, T, partials, count, out, 0, stream);
 }
 
+int tp_partial_sum_scatter(int32_t dtype, int32_t T, const void* const* partials, int64_t S,
+                           int64_t B, int64_t H, int32_t rank, void* out, void* stream) {
+  if (dtype != TP_F32 && dtype != TP_BF16) return fail(TP_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (T < 1 || T > TP_MAX_SHARDS) return fail(TP_ERR_SHAPE, "T must be in 1..%d", TP_MAX_SHARDS);
+  if (S < 0 || B < 0 || H <= 0 || S > kMaxDim || B > kMaxDim || H > kMaxLd || S * B > kMaxDim)
+    return fail(TP_ERR_SHAPE, "S, B must be >= 0 and H > 0 within range");
+  if (S % T) return fail(TP_ERR_SHAPE, "S must be a multiple of T");
+  const int vec = dtype == TP_BF16 ? 8 : 4;
+  if (H % vec) return fail(TP_ERR_SHAPE, "H must be a multiple of %d for this dtype", vec);
+  if (rank < 0 || rank >= T) return fail(TP_ERR_SHAPE, "rank must be in 0..T-1");
+  if (!partials) return fail(TP_ERR_NULL, "partials is NULL");
+  const size_t elt = dtype == TP_BF16 ? 2 : 4;
+  const int64_t slice = (S / T) * B * H;
+  const size_t full_bytes = (size_t)(S * B * H) * elt;
+  Buf ob = {out, (size_t)slice * elt, "out"};
+  if (int rc = check_ptrs(&ob, 1, true)) return rc;
+  const void* sl[TP_MAX_SHARDS];
+  for (int i = 0; i < T; ++i) {
+    if (!partials[i]) return fail(TP_ERR_NULL, "partials[%d] is NULL", i);
+    if (!aligned16(partials[i])) return fail(TP_ERR_ALIGN, "partials[%d] is not 16-byte aligned", i);
+    Buf pb = {partials[i], full_bytes, "partial"};
+    if (overlap(ob, pb)) return fail(TP_ERR_ALIAS, "out overlaps partials[%d]", i);
+    sl[i] = static_cast<const char*>(partials[i]) + (size_t)rank * (size_t)slice * elt;
+  }
+  if (int rc = check_device()) return rc;
+  if (slice == 0) return ok();
+  hipError_t he = partial_sum_launch(dtype, T, sl, slice, out, 0,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "partial-sum launch");
+  return ok();
+}
+
 int tp_partial_sum_capped(int32_t dtype, int32_t T, const void* const* partials,
                           int64_t count, void* out, int32_t max_workgroups, void* stream) {
   if (max_workgroups < 1) return fail(TP_ERR_SHAPE, "max_workgroups must be >= 1");

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -143,6 +143,28 @@ def test_partial_sum_argument_checks():
     assert ps(out=None) == E_NULL
     assert ps(out=addr(3, 8)) == E_ALIGN
     assert ps(out=addr(1, 16)) == E_ALIAS              # overlaps partials[0], not equal
+
+
+def test_scatter_partial_sum_argument_checks():
+    def pss(**kw):
+        a = dict(dtype=tp.TP_BF16, T=2, parts=[addr(1), addr(2)], S=64, B=2, H=128, rank=1,
+                 out=addr(3))
+        a.update(kw)
+        try:
+            tp.tp_partial_sum_scatter(a["dtype"], a["T"], a["parts"], a["S"], a["B"], a["H"],
+                                      a["rank"], a["out"])
+        except tp.TpError as e:
+            return e.status
+        return 0
+    assert pss(dtype=7) == E_DTYPE
+    assert pss(S=63) == E_SHAPE                         # S not a multiple of T
+    assert pss(rank=2) == E_SHAPE
+    assert pss(rank=-1) == E_SHAPE
+    assert pss(H=12) == E_SHAPE                         # bf16 needs multiples of 8
+    assert pss(parts=None) == E_NULL
+    assert pss(parts=[addr(1), None]) == E_NULL
+    assert pss(parts=[addr(1), addr(2, 4)]) == E_ALIGN
+    assert pss(out=addr(1, 4096)) == E_ALIAS             # inside partials[0]
 
 
 def test_capped_partial_sum_argument_checks():

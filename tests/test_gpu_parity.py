@@ -226,6 +226,34 @@ def test_capped_partial_sum_matches_uncapped(dtype):
         assert np.all(np.abs(got - exp) <= eps_store * np.abs(exp) + T * 2.0 ** -23 * absum)
 
 
+@pytest.mark.parametrize("dtype", [wl.DT_F32, wl.DT_BF16])
+def test_reduce_scatter_slices(dtype):
+    """Sequence-parallel reduce-scatter: every rank's slice equals the same
+    rows of the full partial sum bit for bit, and the oracle's slice within
+    the partial-sum bound."""
+    w = wl.WORKLOADS["c3_bf16_gelu_fwdbwd"]
+    for T, S, B, H in ((8, 64, 3, 264), (3, 9, 2, 8), (8, 2048, 1, 4096)):
+        parts = wl.gen_partials(w, T, (S, B, H), 0.5, dtype=dtype)
+        dev = [to_device(p) for p in parts]
+        full = torch.empty_like(dev[0])
+        tp.tp_partial_sum(dtype, T, dev, S * B * H, full)
+        m = S // T
+        small = S * B * H <= 200_000
+        for rank in range(T):
+            print(f"[gpu] reduce-scatter dtype={dtype} T={T} S={S} B={B} H={H} rank={rank}",
+                  flush=True)
+            out = torch.empty_like(dev[0][:m])
+            tp.tp_partial_sum_scatter(dtype, T, dev, S, B, H, rank, out)
+            _sync()
+            assert np.array_equal(to_host(out), to_host(full[rank * m:(rank + 1) * m]))
+            if small:
+                exp = oracle.reduce_scatter(parts, S, B, H, rank)
+                got = f64(to_host(out))
+                absum = sum(np.abs(f64(p[rank * m:(rank + 1) * m])) for p in parts)
+                eps = 2.0 ** -8 if dtype == wl.DT_BF16 else 2.0 ** -23
+                assert np.all(np.abs(got - exp) <= eps * np.abs(exp) + T * 2.0 ** -23 * absum)
+
+
 # ----------------------------------------------------------------------------
 # exact GPU pins
 # ----------------------------------------------------------------------------

@@ -272,6 +272,28 @@ def test_partial_sum_pins():
     assert np.array_equal(oracle.partial_sum(parts), np.sum(parts, axis=0))
 
 
+def test_reduce_scatter_pins():
+    """Sequence-parallel slices: the T ranks' slices, stacked in rank order
+    along the sequence, are the full sum (numpy's, on integer data where
+    fp64 is exact); rank r's slice holds sequence rows r*S/T onwards (a
+    shifted index or a slice taken along B instead of S fails); T = 1 keeps
+    everything; S must divide by T."""
+    S, B, H, T = 12, 3, 8, 4
+    parts = [RNG.integers(-500, 500, size=(S, B, H)).astype(np.float64) for _ in range(T)]
+    full = np.sum(parts, axis=0)
+    slices = [oracle.reduce_scatter(parts, S, B, H, r) for r in range(T)]
+    assert all(sl.shape == (S // T, B, H) for sl in slices)
+    assert np.array_equal(np.concatenate(slices, axis=0), full)
+    # sequence row s of rank 2's slice is global row 2*S/T + s
+    marker = [np.zeros((S, B, H)) for _ in range(T)]
+    marker[1][7, 2, 5] = 1.0
+    assert oracle.reduce_scatter(marker, S, B, H, 2)[1, 2, 5] == 1.0
+    assert not np.any(oracle.reduce_scatter(marker, S, B, H, 1))
+    assert np.array_equal(oracle.reduce_scatter(parts[:1], S, B, H, 0), parts[0])
+    with pytest.raises(ValueError):
+        oracle.reduce_scatter(parts[:3] + parts[:2], S, B, H, 0)   # T = 5 does not divide 12
+
+
 # ----------------------------------------------------------------------------
 # grouped experts
 # ----------------------------------------------------------------------------
