@@ -231,6 +231,25 @@ def main():
               "hbm_frac": round(rs_bytes / (rs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
               "bytes": rs_bytes}
 
+    # gradient-accumulation form of the backward (weight gradients added
+    # into the fp32 buffers), timed beside the plain backward
+    acc_cmp = None
+    if w.backward:
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            tp.tp_mlp_shard_bwd(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
+                                buf.dA_up, buf.dB, buf.ws, buf.ws_bytes, stream=stream)
+        e1.record(stream)
+        for _ in range(reps):
+            tp.tp_mlp_shard_bwd_accum(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
+                                      buf.dA_up, buf.dB, buf.ws, buf.ws_bytes, stream=stream)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        acc_cmp = {"bwd_ms": round(e0.elapsed_time(e1) / reps, 4),
+                   "bwd_accum_ms": round(e1.elapsed_time(e2) / reps, 4)}
+
     flops = gemm_flops(w)
     value = flops / (ms * 1e-3) / 1e12
     gemm_ms = fwd_ms + bwd_ms
@@ -298,6 +317,7 @@ def main():
                          "partial_sum_GBps": round(ps_gbs, 1),
                          "partial_sum_hbm_frac": round(ps_gbs / PEAK_HBM_GBS, 4)},
         "reduce_scatter_rank0": rs,
+        "grad_accumulation": acc_cmp,
     }
 
     if not args.no_cpu_baseline:

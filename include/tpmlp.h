@@ -245,6 +245,31 @@ int tp_grouped_expert_bwd(const tp_expert_desc *desc, const int64_t *offsets,
                           void *dX_perm, float *dWg, float *dWu, float *dWd,
                           void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Gradient-accumulation fusion ([P1] §五 5.2: the weight gradients of the
+ * M microbatches of one iteration are added straight into the fp32 grad
+ * buffer by the weight-gradient kernel, with no intermediate tensor).
+ * tp_mlp_shard_bwd_accum and tp_grouped_expert_bwd_accum take the same
+ * arguments as tp_mlp_shard_bwd / tp_grouped_expert_bwd, but the weight
+ * gradients are in/out: dA += X^T dZ, dA_up += ..., dB += H^T dY (grouped:
+ * dWg, dWu, dWd likewise), each element read, added to in fp32 and written
+ * once by the one tile that owns it, so the result is deterministic (no
+ * atomics).  dX_partial is written as in the plain call.  The caller zeroes
+ * the buffers before the first microbatch.  With N = 0 (or an expert with no
+ * rows) the buffers are left unchanged.
+ */
+int tp_mlp_shard_bwd_accum(const tp_mlp_desc *desc, const void *X, const void *A,
+                           const void *A_up, const void *B, const void *Z_save,
+                           const void *H_act, const void *dY, void *dX_partial,
+                           float *dA, float *dA_up, float *dB, void *workspace,
+                           size_t ws_bytes, void *stream);
+int tp_grouped_expert_bwd_accum(const tp_expert_desc *desc, const int64_t *offsets,
+                                const void *X_perm, const void *Wg, const void *Wu,
+                                const void *Wd, const void *Z_save,
+                                const void *H_act, const void *dY_perm,
+                                void *dX_perm, float *dWg, float *dWu, float *dWd,
+                                void *workspace, size_t ws_bytes, void *stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char *tp_last_error(void);
 

@@ -16,9 +16,9 @@ from typing import Optional, Sequence
 __all__ = [
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU", "TpError",
     "tp_mlp_desc", "tp_expert_desc", "lib", "library_path",
-    "tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_mlp_shard_bwd_workspace",
+    "tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_mlp_shard_bwd_accum", "tp_mlp_shard_bwd_workspace",
     "tp_partial_sum", "tp_partial_sum_capped", "tp_partial_sum_scatter", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
-    "tp_grouped_expert_bwd_workspace", "tp_last_error", "tp_status_string",
+    "tp_grouped_expert_bwd_workspace", "tp_grouped_expert_bwd_accum", "tp_last_error", "tp_status_string",
 ]
 
 TP_F32, TP_BF16 = 0, 1
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.tp_mlp_shard_bwd_workspace.restype = ctypes.c_size_t
     L.tp_mlp_shard_bwd.argtypes = [D] + [_vp] * 12 + [ctypes.c_size_t, _vp]
     L.tp_mlp_shard_bwd.restype = ctypes.c_int
+    L.tp_mlp_shard_bwd_accum.argtypes = [D] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+    L.tp_mlp_shard_bwd_accum.restype = ctypes.c_int
     L.tp_partial_sum.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_vp),
                                  ctypes.c_int64, _vp, _vp]
     L.tp_partial_sum.restype = ctypes.c_int
@@ -88,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.tp_grouped_expert_bwd_workspace.restype = ctypes.c_size_t
     L.tp_grouped_expert_bwd.argtypes = [ED, I64P] + [_vp] * 12 + [ctypes.c_size_t, _vp]
     L.tp_grouped_expert_bwd.restype = ctypes.c_int
+    L.tp_grouped_expert_bwd_accum.argtypes = [ED, I64P] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+    L.tp_grouped_expert_bwd_accum.restype = ctypes.c_int
     L.tp_last_error.argtypes = []
     L.tp_last_error.restype = ctypes.c_char_p
     L.tp_status_string.argtypes = [ctypes.c_int]
@@ -160,9 +164,11 @@ def tp_mlp_shard_bwd_workspace(desc) -> int:
 
 
 def tp_mlp_shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up, dB,
-                     workspace, ws_bytes: int, stream=None) -> int:
+                     workspace, ws_bytes: int, stream=None, accumulate: bool = False) -> int:
+    """accumulate=True calls tp_mlp_shard_bwd_accum (dA, dA_up, dB += ...)."""
     d = _desc(desc)
-    return _check(lib().tp_mlp_shard_bwd(
+    fn = lib().tp_mlp_shard_bwd_accum if accumulate else lib().tp_mlp_shard_bwd
+    return _check(fn(
         ctypes.byref(d), _ptr(X), _ptr(A), _ptr(A_up), _ptr(B), _ptr(Z_save), _ptr(H_act),
         _ptr(dY), _ptr(dX_partial), _ptr(dA), _ptr(dA_up), _ptr(dB), _ptr(workspace),
         int(ws_bytes), _stream(stream)))
@@ -209,9 +215,19 @@ def tp_grouped_expert_bwd_workspace(desc, offsets) -> int:
 
 def tp_grouped_expert_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm,
                           dX_perm, dWg, dWu, dWd, workspace, ws_bytes: int,
-                          stream=None) -> int:
+                          stream=None, accumulate: bool = False) -> int:
+    """accumulate=True calls tp_grouped_expert_bwd_accum (dW* += ...)."""
     d = _edesc(desc)
-    return _check(lib().tp_grouped_expert_bwd(
+    fn = lib().tp_grouped_expert_bwd_accum if accumulate else lib().tp_grouped_expert_bwd
+    return _check(fn(
         ctypes.byref(d), _offsets(offsets), _ptr(X_perm), _ptr(Wg), _ptr(Wu), _ptr(Wd),
         _ptr(Z_save), _ptr(H_act), _ptr(dY_perm), _ptr(dX_perm), _ptr(dWg), _ptr(dWu),
         _ptr(dWd), _ptr(workspace), int(ws_bytes), _stream(stream)))
+
+
+def tp_mlp_shard_bwd_accum(*args, **kw) -> int:
+    return tp_mlp_shard_bwd(*args, accumulate=True, **kw)
+
+
+def tp_grouped_expert_bwd_accum(*args, **kw) -> int:
+    return tp_grouped_expert_bwd(*args, accumulate=True, **kw)

@@ -225,10 +225,11 @@ size_t tp_mlp_shard_bwd_workspace(const tp_mlp_desc* desc) {
   return dz_bytes(s);
 }
 
-int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void* A_up,
-                     const void* B, const void* Z_save, const void* H_act, const void* dY,
-                     void* dX_partial, float* dA, float* dA_up, float* dB, void* workspace,
-                     size_t ws_bytes, void* stream) {
+namespace {
+int shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void* A_up,
+              const void* B, const void* Z_save, const void* H_act, const void* dY,
+              void* dX_partial, float* dA, float* dA_up, float* dB, void* workspace,
+              size_t ws_bytes, void* stream, bool accumulate) {
   Shard s;
   int rc = check_desc(desc, s);
   if (rc) return rc;
@@ -289,7 +290,7 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, cons
     g.b = {dY, nullptr, H, 0, 0};
     g.epi.out0 = dB;
     g.epi.ld0 = H;
-    he = run_gemm(s.dtype, GK_WGRAD, g, st);
+    he = run_gemm(s.dtype, accumulate ? GK_WGRAD_ACC : GK_WGRAD, g, st);
     if (he != hipSuccess) return hip_fail(he, "dB launch");
   }
   // 3. dA (| dA_up) = X^T dZ
@@ -302,7 +303,9 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, cons
     g.epi.ld0 = Ft;
     g.epi.ld1 = Ft;
     g.epi.split = Ft;
-    he = run_gemm(s.dtype, sw ? GK_WGRAD_SPLIT : GK_WGRAD, g, st);
+    const GemmKind k = sw ? (accumulate ? GK_WGRAD_SPLIT_ACC : GK_WGRAD_SPLIT)
+                          : (accumulate ? GK_WGRAD_ACC : GK_WGRAD);
+    he = run_gemm(s.dtype, k, g, st);
     if (he != hipSuccess) return hip_fail(he, "dA launch");
   }
   // 4. dX_partial = dZ A^T  (SwiGLU: [dG|dU] [Ag|Au]^T)
@@ -316,6 +319,24 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, cons
     if (he != hipSuccess) return hip_fail(he, "dX launch");
   }
   return ok();
+}
+}  // namespace
+
+int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void* A_up,
+                     const void* B, const void* Z_save, const void* H_act, const void* dY,
+                     void* dX_partial, float* dA, float* dA_up, float* dB, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  return shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up, dB, workspace,
+                   ws_bytes, stream, false);
+}
+
+int tp_mlp_shard_bwd_accum(const tp_mlp_desc* desc, const void* X, const void* A,
+                           const void* A_up, const void* B, const void* Z_save,
+                           const void* H_act, const void* dY, void* dX_partial, float* dA,
+                           float* dA_up, float* dB, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  return shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up, dB, workspace,
+                   ws_bytes, stream, true);
 }
 
 namespace {
@@ -478,11 +499,11 @@ size_t tp_grouped_expert_bwd_workspace(const tp_expert_desc* desc, const int64_t
   return (size_t)(x.R * x.F) * 2 * 2;
 }
 
-int tp_grouped_expert_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* X_perm,
-                          const void* Wg, const void* Wu, const void* Wd, const void* Z_save,
-                          const void* H_act, const void* dY_perm, void* dX_perm, float* dWg,
-                          float* dWu, float* dWd, void* workspace, size_t ws_bytes,
-                          void* stream) {
+namespace {
+int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* X_perm,
+                const void* Wg, const void* Wu, const void* Wd, const void* Z_save,
+                const void* H_act, const void* dY_perm, void* dX_perm, float* dWg, float* dWu,
+                float* dWd, void* workspace, size_t ws_bytes, void* stream, bool accumulate) {
   Experts x;
   int rc = check_experts(desc, offsets, x);
   if (rc) return rc;
@@ -538,7 +559,7 @@ int tp_grouped_expert_bwd(const tp_expert_desc* desc, const int64_t* offsets, co
     g.epi.out0 = dWd;
     g.epi.ld0 = H;
     g.epi.bstride = HF;
-    he = gemm_bf16(GK_WGRAD, g, st);
+    he = gemm_bf16(accumulate ? GK_WGRAD_ACC : GK_WGRAD, g, st);
     if (he != hipSuccess) return hip_fail(he, "grouped dWd launch");
   }
   {
@@ -552,7 +573,7 @@ int tp_grouped_expert_bwd(const tp_expert_desc* desc, const int64_t* offsets, co
     g.epi.ld1 = F;
     g.epi.split = F;
     g.epi.bstride = HF;
-    he = gemm_bf16(GK_WGRAD_SPLIT, g, st);
+    he = gemm_bf16(accumulate ? GK_WGRAD_SPLIT_ACC : GK_WGRAD_SPLIT, g, st);
     if (he != hipSuccess) return hip_fail(he, "grouped dWg/dWu launch");
   }
   if (x.R > 0) {
@@ -566,6 +587,25 @@ int tp_grouped_expert_bwd(const tp_expert_desc* desc, const int64_t* offsets, co
     if (he != hipSuccess) return hip_fail(he, "grouped dX launch");
   }
   return ok();
+}
+}  // namespace
+
+int tp_grouped_expert_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* X_perm,
+                          const void* Wg, const void* Wu, const void* Wd, const void* Z_save,
+                          const void* H_act, const void* dY_perm, void* dX_perm, float* dWg,
+                          float* dWu, float* dWd, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  return grouped_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm, dX_perm, dWg, dWu,
+                     dWd, workspace, ws_bytes, stream, false);
+}
+
+int tp_grouped_expert_bwd_accum(const tp_expert_desc* desc, const int64_t* offsets,
+                                const void* X_perm, const void* Wg, const void* Wu,
+                                const void* Wd, const void* Z_save, const void* H_act,
+                                const void* dY_perm, void* dX_perm, float* dWg, float* dWu,
+                                float* dWd, void* workspace, size_t ws_bytes, void* stream) {
+  return grouped_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm, dX_perm, dWg, dWu,
+                     dWd, workspace, ws_bytes, stream, true);
 }
 
 }  // extern "C"

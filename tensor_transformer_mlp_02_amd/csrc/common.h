@@ -116,6 +116,8 @@ enum {
   EPI_SWIGLU_BWD = 4,   // g = aux[m,n], u = aux[m,split+n]:
                         // out0[m,n] = c u silu'(g), out0[m,split+n] = c silu(g)
   EPI_STORE_SPLIT = 5,  // n < split: out0[m,n]; else out1[m,n-split]
+  EPI_ACC = 6,          // out0[m,n] += c  (weight-gradient accumulation)
+  EPI_ACC_SPLIT = 7,    // EPI_STORE_SPLIT with += (each element has one writer)
 };
 
 struct OpArgs {
@@ -247,6 +249,18 @@ __device__ __forceinline__ void epilogue4(const EpiArgs& ea, int e, int64_t m,
       Store4<OutT>::store(ea.out0, e * ea.bstride + m * ea.ld0 + n, c);
     else
       Store4<OutT>::store(ea.out1, e * ea.bstride + m * ea.ld1 + (n - ea.split), c);
+  } else if constexpr (EPI == EPI_ACC || EPI == EPI_ACC_SPLIT) {
+    void* o = ea.out0;
+    int64_t off = e * ea.bstride + m * ea.ld0 + n;
+    if (EPI == EPI_ACC_SPLIT && n >= ea.split) {
+      o = ea.out1;
+      off = e * ea.bstride + m * ea.ld1 + (n - ea.split);
+    }
+    float v[4];
+    Store4<OutT>::load(o, off, v);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += c[i];
+    Store4<OutT>::store(o, off, v);
   } else if constexpr (EPI == EPI_GELU_FWD) {
     float h[4];
 #pragma unroll
@@ -341,6 +355,18 @@ __device__ __forceinline__ void epilogue8(const EpiArgs& ea, int e, int64_t m, i
       Vec8<OutT>::store(ea.out0, e * ea.bstride + m * ea.ld0 + n, c);
     else
       Vec8<OutT>::store(ea.out1, e * ea.bstride + m * ea.ld1 + (n - ea.split), c);
+  } else if constexpr (EPI == EPI_ACC || EPI == EPI_ACC_SPLIT) {
+    void* o = ea.out0;
+    int64_t off = e * ea.bstride + m * ea.ld0 + n;
+    if (EPI == EPI_ACC_SPLIT && n >= ea.split) {
+      o = ea.out1;
+      off = e * ea.bstride + m * ea.ld1 + (n - ea.split);
+    }
+    float v[8];
+    Vec8<OutT>::load(o, off, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] += c[i];
+    Vec8<OutT>::store(o, off, v);
   } else if constexpr (EPI == EPI_GELU_FWD) {
     float h[8];
 #pragma unroll

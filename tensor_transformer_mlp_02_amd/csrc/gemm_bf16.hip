@@ -1559,6 +1559,10 @@ hipError_t gemm_bf16(GemmKind kind, GemmArgs& g, hipStream_t stream) {
       return launch_mfma<TP_NW_DEFAULT, true, true, BMODE_PLAIN, EPI_STORE, bf16_t>(g, stream);
     case GK_DX_KSPLIT:
       return launch_mfma<TP_NW_DEFAULT, true, true, BMODE_KSPLIT, EPI_STORE, bf16_t>(g, stream);
+    case GK_WGRAD_ACC:
+      return launch_mfma<TP_NW_DEFAULT, false, false, BMODE_PLAIN, EPI_ACC, float>(g, stream);
+    case GK_WGRAD_SPLIT_ACC:
+      return launch_mfma<TP_NW_DEFAULT, false, false, BMODE_PLAIN, EPI_ACC_SPLIT, float>(g, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -144,6 +144,10 @@ hipError_t gemm_f32(GemmKind kind, GemmArgs& g, hipStream_t stream) {
       return launch_f32<true, true, BMODE_PLAIN, false, EPI_STORE>(g, stream);
     case GK_DX_KSPLIT:
       return launch_f32<true, true, BMODE_KSPLIT, false, EPI_STORE>(g, stream);
+    case GK_WGRAD_ACC:
+      return launch_f32<false, false, BMODE_PLAIN, false, EPI_ACC>(g, stream);
+    case GK_WGRAD_SPLIT_ACC:
+      return launch_f32<false, false, BMODE_PLAIN, false, EPI_ACC_SPLIT>(g, stream);
   }
   return hipErrorInvalidValue;
 }

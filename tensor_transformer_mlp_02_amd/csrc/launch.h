@@ -18,6 +18,8 @@ enum GemmKind {
   GK_WGRAD_SPLIT,  // as GK_WGRAD with the columns split over two outputs
   GK_DX,           // dX_partial = dZ A^T
   GK_DX_KSPLIT,    // dX_partial = [dG|dU] [Ag|Au]^T
+  GK_WGRAD_ACC,        // dW += L^T R  (fp32 accumulation buffer)
+  GK_WGRAD_SPLIT_ACC,  // as GK_WGRAD_SPLIT, adding into both outputs
 };
 
 // bf16 storage, MFMA path.

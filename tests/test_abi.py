@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -53,7 +53,7 @@ def fwd(desc, X=addr(1), A=addr(2), A_up=None, B=addr(3), Z=addr(4), H=addr(5), 
     return 0
 
 
-def bwd(desc, A_up=None, dA_up=None, ws=addr(14), ws_bytes=None, **kw):
+def bwd(desc, A_up=None, dA_up=None, ws=addr(14), ws_bytes=None, accumulate=False, **kw):
     p = dict(X=addr(1), A=addr(2), B=addr(3), Z=addr(4), H=addr(5), dY=addr(7),
              dX=addr(8), dA=addr(9), dB=addr(10))
     p.update(kw)
@@ -61,7 +61,8 @@ def bwd(desc, A_up=None, dA_up=None, ws=addr(14), ws_bytes=None, **kw):
         ws_bytes = tp.tp_mlp_shard_bwd_workspace(desc)
     try:
         tp.tp_mlp_shard_bwd(desc, p["X"], p["A"], A_up, p["B"], p["Z"], p["H"], p["dY"],
-                            p["dX"], p["dA"], dA_up, p["dB"], ws, ws_bytes)
+                            p["dX"], p["dA"], dA_up, p["dB"], ws, ws_bytes,
+                            accumulate=accumulate)
     except tp.TpError as e:
         return e.status
     return 0
@@ -116,6 +117,11 @@ def test_backward_argument_checks():
     assert bwd(d, ws=addr(9)) == E_ALIAS               # workspace over dA
     s = gelu_desc(act=tp.TP_ACT_SWIGLU)
     assert tp.tp_mlp_shard_bwd_workspace(s) == 128 * 2 * 128 * 2
+    # the accumulating variant checks its arguments the same way
+    assert bwd(d, ws=None, accumulate=True) == E_WS
+    assert bwd(d, dB=None, accumulate=True) == E_NULL
+    assert bwd(d, dA=addr(1), accumulate=True) == E_ALIAS   # dA over X
+    assert bwd(s, A_up=addr(11), accumulate=True) == E_NULL  # dA_up missing
     assert tp.tp_mlp_shard_bwd_workspace(gelu_desc(dtype=9)) == 0
 
 

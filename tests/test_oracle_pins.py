@@ -218,6 +218,36 @@ def test_indivisible_width_rejected():
         oracle.shard_weights(A, B, 3)
 
 
+@pytest.mark.parametrize("act", [ACT_GELU_TANH, ACT_SWIGLU])
+def test_weight_grads_add_over_microbatches(act):
+    """Gradient accumulation ([P1] §五 5.2): the weight gradients of a batch
+    split into microbatches (rows), added up, are the whole batch's weight
+    gradients, because each is a sum over rows; dX of each microbatch is the
+    matching rows of the whole batch's dX.  Checked against numpy on the
+    whole batch (an accumulation that overwrote, or summed the wrong rows,
+    fails)."""
+    rng = np.random.default_rng(11)
+    N, H, F = 23, 12, 16
+    X = rng.standard_normal((N, H)); dY = rng.standard_normal((N, H))
+    A = rng.standard_normal((H, F)) * 0.3; B = rng.standard_normal((F, H)) * 0.3
+    Au = rng.standard_normal((H, F)) * 0.3 if act == ACT_SWIGLU else None
+    whole = oracle.mlp_bwd(X, A, B, act, dY, oracle.mlp_fwd(X, A, B, act, Au), Au)
+    acc = {k: np.zeros_like(whole[k]) for k in ("dA", "dB")}
+    if act == ACT_SWIGLU:
+        acc["dA_up"] = np.zeros_like(whole["dA_up"])
+    for lo, hi in ((0, 5), (5, 17), (17, 23)):
+        f = oracle.mlp_fwd(X[lo:hi], A, B, act, Au)
+        g = oracle.mlp_bwd(X[lo:hi], A, B, act, dY[lo:hi], f, Au)
+        for k in acc:
+            acc[k] += g[k]
+        assert rel(g["dX"], whole["dX"][lo:hi]) < 1e-13
+    for k in acc:
+        assert rel(acc[k], whole[k]) < 1e-13
+    # and the whole-batch dB is numpy's H^T dY
+    Hh = oracle.mlp_fwd(X, A, B, act, Au)["H"]
+    assert rel(whole["dB"], Hh.T @ dY) < 1e-13
+
+
 def test_t1_shard_is_full_mlp_bitwise():
     N, H, F = 6, 16, 24
     X = RNG.standard_normal((N, H)); A = RNG.standard_normal((H, F)) * 0.3
