@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c4_bf16_swiglu_fwdbwd")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--moe", type=int, default=1,
+                   help="1: also time the MoE dispatch/combine row moves")
     p.add_argument("--overlap", type=int, default=0,
                    help="1: partial sums on a second stream, overlapping the GEMMs")
     p.add_argument("--sum-workgroups", type=int, default=256,
@@ -98,6 +100,51 @@ def cpu_baseline(w, tokens):
         oracle.mlp_bwd(d["X"], d["A"], d["B"], w.act, d["dY"], f, d["A_up"])
     dt = time.perf_counter() - t0
     return dt, gemm_flops(w, tokens)
+
+
+def moe_dispatch_timing(torch, tp, wl, dev, stream, reps=20):
+    """Token dispatch and combine around the grouped experts on the
+    grouped-expert workload's routing (16384 tokens, top-2 of 64 experts,
+    local experts 0..7, H = 4096): permute, weighted combine and the
+    combine's backward, each in GB/s of algorithmic row traffic."""
+    import numpy as np
+    w5 = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
+    logits = wl.normal(1000 * w5.cid + wl.K_LOGITS, (w5.tokens, w5.n_route), 1.0)
+    ids, off = wl.route_top2_local(logits, w5.experts, w5.topk)
+    rw = wl.route_weights(logits, ids, off)
+    ptr, rows = wl.token_rows(ids, w5.tokens)
+    N, H, R = w5.tokens, w5.H, len(ids)
+    tab = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    ids_d, ptr_d, rows_d, rw_d = tab(ids.astype(np.int32)), tab(ptr), tab(rows), tab(rw)
+    g = torch.Generator(device=dev).manual_seed(1000 * w5.cid + 91)
+    X = torch.randn((N, H), generator=g, device=dev).to(torch.bfloat16)
+    dY = torch.randn((N, H), generator=g, device=dev).to(torch.bfloat16)
+    Yp = torch.randn((R, H), generator=g, device=dev).to(torch.bfloat16)
+    Xp = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    Y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    dYp = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(R, dtype=torch.float32, device=dev)
+    calls = {
+        "permute": (lambda: tp.tp_moe_permute(wl.DT_BF16, N, H, R, ids_d, X, Xp, stream=stream),
+                    2 * R * H * 2),
+        "combine": (lambda: tp.tp_moe_combine(wl.DT_BF16, N, H, R, ptr_d, rows_d, rw_d, Yp, Y,
+                                              stream=stream), (R + N) * H * 2),
+        "combine_bwd": (lambda: tp.tp_moe_combine_bwd(wl.DT_BF16, N, H, R, ids_d, rw_d, dY, Yp,
+                                                      dYp, dw, stream=stream), 3 * R * H * 2),
+    }
+    out = {"tokens": N, "H": H, "rows": R}
+    for name, (fn, nbytes) in calls.items():
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        out[name] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
 
 
 def main():
@@ -250,6 +297,8 @@ def main():
         acc_cmp = {"bwd_ms": round(e0.elapsed_time(e1) / reps, 4),
                    "bwd_accum_ms": round(e1.elapsed_time(e2) / reps, 4)}
 
+    moe = moe_dispatch_timing(torch, tp, wl, dev, stream) if args.moe else None
+
     flops = gemm_flops(w)
     value = flops / (ms * 1e-3) / 1e12
     gemm_ms = fwd_ms + bwd_ms
@@ -318,6 +367,7 @@ def main():
                          "partial_sum_hbm_frac": round(ps_gbs / PEAK_HBM_GBS, 4)},
         "reduce_scatter_rank0": rs,
         "grad_accumulation": acc_cmp,
+        "moe_dispatch_combine": moe,
     }
 
     if not args.no_cpu_baseline:

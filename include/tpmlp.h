@@ -271,6 +271,43 @@ int tp_grouped_expert_bwd_accum(const tp_expert_desc *desc, const int64_t *offse
                                 void *workspace, size_t ws_bytes, void *stream);
 
 /* Message of the last failed call on this thread ("" if none). */
+/*
+ * MoE token dispatch and combine around the grouped local experts
+ * ([P3] §09: router scores -> top-k experts -> tokens sent to their
+ * experts -> expert compute -> results merged by weight -> back in the
+ * original token order).  The router is not part of this library: its
+ * decisions arrive as device tables for the R expert-sorted rows (rows of
+ * expert e are offsets[e] .. offsets[e+1]-1, the grouped calls' layout):
+ *   row_token  [R] int32   the token of row r
+ *   row_weight [R] fp32    the router weight of (row_token[r], expert of r)
+ *   tok_ptr    [N+1] int32, tok_rows [R] int32   the rows of token t are
+ *              tok_rows[tok_ptr[t] .. tok_ptr[t+1]-1] (CSR), in the order
+ *              their contributions are summed
+ * Tables need 4-byte alignment, data buffers 16 bytes.  A table entry out
+ * of range contributes nothing (a permuted row becomes zeros); no entry can
+ * make an access leave its buffer.  dtype is TP_BF16 or TP_F32; H a
+ * multiple of 8 (bf16) or 4 (fp32).  All three are HBM-bound row moves.
+ *
+ * tp_moe_permute: X_perm[r, :] = X[row_token[r], :]   (X [N,H], X_perm [R,H])
+ * tp_moe_combine: Y[t, :] = sum over the rows r of token t of
+ *                 row_weight[r] * Y_perm[r, :], in fp32, rounded once; a
+ *                 token without rows gets zeros.  row_weight = NULL means
+ *                 weight 1: that is also the backward of tp_moe_permute
+ *                 (dX[t] = sum of dX_perm over the rows of t).
+ * tp_moe_combine_bwd: the backward of tp_moe_combine:
+ *                 dY_perm[r, :] = row_weight[r] * dY[row_token[r], :]  [R,H]
+ *                 d_weight[r]   = sum_h dY[row_token[r], h] * Y_perm[r, h]
+ *                 (fp32, a fixed reduction order: deterministic)
+ */
+int tp_moe_permute(int32_t dtype, int64_t N, int64_t H, int64_t R, const int32_t *row_token,
+                   const void *X, void *X_perm, void *stream);
+int tp_moe_combine(int32_t dtype, int64_t N, int64_t H, int64_t R, const int32_t *tok_ptr,
+                   const int32_t *tok_rows, const float *row_weight, const void *Y_perm,
+                   void *Y, void *stream);
+int tp_moe_combine_bwd(int32_t dtype, int64_t N, int64_t H, int64_t R,
+                       const int32_t *row_token, const float *row_weight, const void *dY,
+                       const void *Y_perm, void *dY_perm, float *d_weight, void *stream);
+
 const char *tp_last_error(void);
 
 /* Fixed name of a tp_status value. */

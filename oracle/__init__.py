@@ -195,6 +195,39 @@ def reduce_scatter(parts, S, B, H, rank) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# MoE dispatch and combine around the grouped experts ([P3] §09: router ->
+# top-k experts -> tokens sent to their experts -> expert compute -> results
+# merged by weight -> back in token order)
+# ----------------------------------------------------------------------------
+def moe_permute(X, token_ids) -> np.ndarray:
+    """Row r of the expert-sorted matrix is token token_ids[r]."""
+    return to_f64(X)[np.asarray(token_ids, np.int64)]
+
+
+def moe_combine(Y_perm, token_ids, n_tok, row_weight=None) -> np.ndarray:
+    """Y[t] = sum over the rows r holding token t of w[r] Y_perm[r] (w = 1
+    when None); a token without rows gets zeros."""
+    Yp = to_f64(Y_perm)
+    w = np.ones(len(token_ids)) if row_weight is None else np.asarray(row_weight, np.float64)
+    Y = np.zeros((n_tok, Yp.shape[1]))
+    for r, t in enumerate(np.asarray(token_ids, np.int64)):
+        Y[t] += w[r] * Yp[r]
+    return Y
+
+
+def moe_combine_bwd(dY, Y_perm, token_ids, row_weight):
+    """Backward of moe_combine: dY_perm[r] = w[r] dY[t(r)], and the weight
+    gradient dw[r] = <dY[t(r)], Y_perm[r]>."""
+    dY = to_f64(dY)
+    Yp = to_f64(Y_perm)
+    t = np.asarray(token_ids, np.int64)
+    w = np.asarray(row_weight, np.float64)
+    dYp = w[:, None] * dY[t]
+    dw = np.einsum("rh,rh->r", dY[t], Yp)
+    return dYp, dw
+
+
+# ----------------------------------------------------------------------------
 # all shards of a full weight pair, and the unsharded MLP
 # ----------------------------------------------------------------------------
 def shard_weights(A_full, B_full, T, A_up_full=None):

@@ -18,7 +18,8 @@ __all__ = [
     "tp_mlp_desc", "tp_expert_desc", "lib", "library_path",
     "tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_mlp_shard_bwd_accum", "tp_mlp_shard_bwd_workspace",
     "tp_partial_sum", "tp_partial_sum_capped", "tp_partial_sum_scatter", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
-    "tp_grouped_expert_bwd_workspace", "tp_grouped_expert_bwd_accum", "tp_last_error", "tp_status_string",
+    "tp_grouped_expert_bwd_workspace", "tp_grouped_expert_bwd_accum",
+    "tp_moe_permute", "tp_moe_combine", "tp_moe_combine_bwd", "tp_last_error", "tp_status_string",
 ]
 
 TP_F32, TP_BF16 = 0, 1
@@ -92,6 +93,15 @@ def lib() -> ctypes.CDLL:
     L.tp_grouped_expert_bwd.restype = ctypes.c_int
     L.tp_grouped_expert_bwd_accum.argtypes = [ED, I64P] + [_vp] * 12 + [ctypes.c_size_t, _vp]
     L.tp_grouped_expert_bwd_accum.restype = ctypes.c_int
+    L.tp_moe_permute.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 _vp, _vp, _vp, _vp]
+    L.tp_moe_permute.restype = ctypes.c_int
+    L.tp_moe_combine.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                 _vp, _vp, _vp, _vp, _vp, _vp]
+    L.tp_moe_combine.restype = ctypes.c_int
+    L.tp_moe_combine_bwd.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+    L.tp_moe_combine_bwd.restype = ctypes.c_int
     L.tp_last_error.argtypes = []
     L.tp_last_error.restype = ctypes.c_char_p
     L.tp_status_string.argtypes = [ctypes.c_int]
@@ -231,3 +241,22 @@ def tp_mlp_shard_bwd_accum(*args, **kw) -> int:
 
 def tp_grouped_expert_bwd_accum(*args, **kw) -> int:
     return tp_grouped_expert_bwd(*args, accumulate=True, **kw)
+
+
+def tp_moe_permute(dtype: int, N: int, H: int, R: int, row_token, X, X_perm, stream=None) -> int:
+    return _check(lib().tp_moe_permute(int(dtype), int(N), int(H), int(R), _ptr(row_token),
+                                       _ptr(X), _ptr(X_perm), _stream(stream)))
+
+
+def tp_moe_combine(dtype: int, N: int, H: int, R: int, tok_ptr, tok_rows, row_weight, Y_perm, Y,
+                   stream=None) -> int:
+    return _check(lib().tp_moe_combine(int(dtype), int(N), int(H), int(R), _ptr(tok_ptr),
+                                       _ptr(tok_rows), _ptr(row_weight), _ptr(Y_perm), _ptr(Y),
+                                       _stream(stream)))
+
+
+def tp_moe_combine_bwd(dtype: int, N: int, H: int, R: int, row_token, row_weight, dY, Y_perm,
+                       dY_perm, d_weight, stream=None) -> int:
+    return _check(lib().tp_moe_combine_bwd(int(dtype), int(N), int(H), int(R), _ptr(row_token),
+                                           _ptr(row_weight), _ptr(dY), _ptr(Y_perm),
+                                           _ptr(dY_perm), _ptr(d_weight), _stream(stream)))

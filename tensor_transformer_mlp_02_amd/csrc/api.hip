@@ -152,6 +152,34 @@ size_t dz_bytes(const Shard& s) {
 
 }  // namespace
 
+// buffers that are required only when they hold something
+int check_sized(const Buf* bufs, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (bufs[i].bytes == 0) continue;
+    if (!bufs[i].p) return fail(TP_ERR_NULL, "%s is NULL", bufs[i].name);
+    if (!aligned16(bufs[i].p)) return fail(TP_ERR_ALIGN, "%s is not 16-byte aligned", bufs[i].name);
+  }
+  return TP_OK;
+}
+// index / weight tables (int32 or fp32 elements): 4-byte alignment
+int check_tables(const Buf* bufs, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (bufs[i].bytes == 0) continue;
+    if (!bufs[i].p) return fail(TP_ERR_NULL, "%s is NULL", bufs[i].name);
+    if (reinterpret_cast<uintptr_t>(bufs[i].p) & 3u)
+      return fail(TP_ERR_ALIGN, "%s is not 4-byte aligned", bufs[i].name);
+  }
+  return TP_OK;
+}
+int check_rows(int32_t dtype, int64_t N, int64_t H, int64_t R) {
+  if (dtype != TP_F32 && dtype != TP_BF16) return fail(TP_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (N < 0 || R < 0 || H <= 0) return fail(TP_ERR_SHAPE, "N, R must be >= 0 and H > 0");
+  if (N > kMaxDim || R > kMaxDim || H > kMaxLd) return fail(TP_ERR_SHAPE, "dimension too large");
+  const int vec = dtype == TP_BF16 ? 8 : 4;
+  if (H % vec) return fail(TP_ERR_SHAPE, "H must be a multiple of %d for this dtype", vec);
+  return TP_OK;
+}
+
 extern "C" {
 
 const char* tp_last_error(void) { return g_last_error.c_str(); }
@@ -606,6 +634,75 @@ int tp_grouped_expert_bwd_accum(const tp_expert_desc* desc, const int64_t* offse
                                 float* dWd, void* workspace, size_t ws_bytes, void* stream) {
   return grouped_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm, dX_perm, dWg, dWu,
                      dWd, workspace, ws_bytes, stream, true);
+}
+
+// ---------------------------------------------------------------------------
+// MoE dispatch and combine
+// ---------------------------------------------------------------------------
+int tp_moe_permute(int32_t dtype, int64_t N, int64_t H, int64_t R, const int32_t* row_token,
+                   const void* X, void* X_perm, void* stream) {
+  if (int rc = check_rows(dtype, N, H, R)) return rc;
+  const size_t e = dtype == TP_BF16 ? 2 : 4;
+  Buf tab[] = {{row_token, (size_t)R * 4, "row_token"}};
+  Buf in[] = {{X, R > 0 ? (size_t)(N * H) * e : 0, "X"}};
+  Buf out[] = {{X_perm, (size_t)(R * H) * e, "X_perm"}};
+  if (int rc = check_tables(tab, 1)) return rc;
+  if (int rc = check_sized(in, 1)) return rc;
+  if (int rc = check_sized(out, 1)) return rc;
+  Buf ins[] = {tab[0], in[0]};
+  if (int rc = check_alias(ins, 2, out, 1)) return rc;
+  if (int rc = check_device()) return rc;
+  hipError_t he = moe_permute_launch(dtype, row_token, N, H, R, X, X_perm,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "permute launch");
+  return ok();
+}
+
+int tp_moe_combine(int32_t dtype, int64_t N, int64_t H, int64_t R, const int32_t* tok_ptr,
+                   const int32_t* tok_rows, const float* row_weight, const void* Y_perm,
+                   void* Y, void* stream) {
+  if (int rc = check_rows(dtype, N, H, R)) return rc;
+  const size_t e = dtype == TP_BF16 ? 2 : 4;
+  Buf tab[] = {{tok_ptr, N > 0 ? (size_t)(N + 1) * 4 : 0, "tok_ptr"},
+               {tok_rows, N > 0 ? (size_t)R * 4 : 0, "tok_rows"}};
+  Buf wt = {row_weight, row_weight ? (size_t)R * 4 : 0, "row_weight"};
+  Buf in[] = {{Y_perm, N > 0 ? (size_t)(R * H) * e : 0, "Y_perm"}};
+  Buf out[] = {{Y, (size_t)(N * H) * e, "Y"}};
+  if (int rc = check_tables(tab, 2)) return rc;
+  if (int rc = check_tables(&wt, 1)) return rc;
+  if (int rc = check_sized(in, 1)) return rc;
+  if (int rc = check_sized(out, 1)) return rc;
+  Buf ins[] = {tab[0], tab[1], wt, in[0]};
+  if (int rc = check_alias(ins, 4, out, 1)) return rc;
+  if (int rc = check_device()) return rc;
+  hipError_t he = moe_combine_launch(dtype, tok_ptr, tok_rows, row_weight, N, H, R, Y_perm, Y,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "combine launch");
+  return ok();
+}
+
+int tp_moe_combine_bwd(int32_t dtype, int64_t N, int64_t H, int64_t R, const int32_t* row_token,
+                       const float* row_weight, const void* dY, const void* Y_perm,
+                       void* dY_perm, float* d_weight, void* stream) {
+  if (int rc = check_rows(dtype, N, H, R)) return rc;
+  const size_t e = dtype == TP_BF16 ? 2 : 4;
+  Buf tab[] = {{row_token, (size_t)R * 4, "row_token"},
+               {row_weight, (size_t)R * 4, "row_weight"},
+               {d_weight, (size_t)R * 4, "d_weight"}};
+  Buf in[] = {{dY, R > 0 ? (size_t)(N * H) * e : 0, "dY"},
+              {Y_perm, (size_t)(R * H) * e, "Y_perm"}};
+  Buf out[] = {{dY_perm, (size_t)(R * H) * e, "dY_perm"}};
+  if (int rc = check_tables(tab, 3)) return rc;
+  if (int rc = check_sized(in, 2)) return rc;
+  if (int rc = check_sized(out, 1)) return rc;
+  Buf ins[] = {tab[0], tab[1], in[0], in[1]};
+  Buf outs[] = {out[0], tab[2]};
+  if (int rc = check_alias(ins, 4, outs, 2)) return rc;
+  if (int rc = check_device()) return rc;
+  hipError_t he = moe_combine_bwd_launch(dtype, row_token, row_weight, N, H, R, dY, Y_perm,
+                                         dY_perm, d_weight, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "combine backward launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -31,4 +31,13 @@ hipError_t gemm_f32(GemmKind kind, GemmArgs& g, hipStream_t stream);
 hipError_t partial_sum_launch(int dtype, int T, const void* const* parts, int64_t count,
                               void* out, int max_blocks, hipStream_t stream);
 
+hipError_t moe_permute_launch(int dtype, const int32_t* row_token, int64_t N, int64_t H,
+                              int64_t R, const void* X, void* Xp, hipStream_t stream);
+hipError_t moe_combine_launch(int dtype, const int32_t* tok_ptr, const int32_t* tok_rows,
+                              const float* w, int64_t N, int64_t H, int64_t R, const void* Yp,
+                              void* Y, hipStream_t stream);
+hipError_t moe_combine_bwd_launch(int dtype, const int32_t* row_token, const float* w,
+                                  int64_t N, int64_t H, int64_t R, const void* dY,
+                                  const void* Yp, void* dYp, float* dw, hipStream_t stream);
+
 }  // namespace tpmlp

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 16, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -220,3 +220,34 @@ def test_grouped_argument_checks():
 def test_valid_arguments_without_gpu_report_no_device():
     assert fwd(gelu_desc()) == E_DEV
     assert "device" in tp.tp_last_error()
+
+
+def _status(fn, *a):
+    try:
+        fn(*a)
+    except tp.TpError as e:
+        return e.status
+    return 0
+
+
+def test_moe_argument_checks():
+    bf = tp.TP_BF16
+    # permute(dtype, N, H, R, row_token, X, X_perm)
+    P = lambda *a: _status(tp.tp_moe_permute, *a)
+    assert P(9, 10, 64, 5, addr(1), addr(2), addr(3)) == E_DTYPE
+    assert P(bf, 10, 12, 5, addr(1), addr(2), addr(3)) == E_SHAPE       # H % 8
+    assert P(bf, -1, 64, 5, addr(1), addr(2), addr(3)) == E_SHAPE
+    assert P(bf, 10, 64, 5, None, addr(2), addr(3)) == E_NULL
+    assert P(bf, 10, 64, 5, addr(1, 2), addr(2), addr(3)) == E_ALIGN     # table: 4 bytes
+    assert P(bf, 10, 64, 5, addr(1), addr(2, 8), addr(3)) == E_ALIGN     # data: 16 bytes
+    assert P(bf, 10, 64, 5, addr(1), addr(2), addr(2, 64)) == E_ALIAS   # X_perm inside X
+    # combine(dtype, N, H, R, tok_ptr, tok_rows, row_weight, Y_perm, Y)
+    C = lambda *a: _status(tp.tp_moe_combine, *a)
+    assert C(bf, 10, 64, 5, None, addr(2), None, addr(3), addr(4)) == E_NULL
+    assert C(bf, 10, 64, 5, addr(1), addr(2), addr(5, 1), addr(3), addr(4)) == E_ALIGN
+    assert C(bf, 10, 64, 5, addr(1), addr(2), None, addr(3), addr(3)) == E_ALIAS
+    # combine_bwd(dtype, N, H, R, row_token, row_weight, dY, Y_perm, dY_perm, d_weight)
+    B = lambda *a: _status(tp.tp_moe_combine_bwd, *a)
+    assert B(bf, 10, 64, 5, addr(1), None, addr(3), addr(4), addr(5), addr(6)) == E_NULL
+    assert B(bf, 10, 64, 5, addr(1), addr(2), addr(3), addr(4), addr(5), addr(2)) == E_ALIAS
+    assert B(bf, 10, 64, 5, addr(1), addr(2), addr(3), addr(4), addr(4), addr(6)) == E_ALIAS

@@ -384,3 +384,85 @@ def test_grouped_weight_grad_finite_difference():
     for theta, an in ((Wg, b["dWg"]), (Wu, b["dWu"]), (Wd, b["dWd"]), (X, b["dX"])):
         fd = _fd_grad(fn, theta)
         assert rel(an, fd) < 1e-7
+
+
+# ----------------------------------------------------------------------------
+# MoE dispatch and combine
+# ----------------------------------------------------------------------------
+def _moe_small(n_tok=40, H=16, F=24, seed=31):
+    import workloads
+    w = workloads.WORKLOADS["c5_bf16_grouped_swiglu"]
+    d = workloads.gen_moe_inputs(w, tokens=n_tok, H=H, F=F)
+    return w, d
+
+
+def test_moe_layer_equals_per_token_expert_sum():
+    """permute -> grouped experts -> weighted combine equals, token by token,
+    the router-weighted sum of the dense SwiGLU MLPs of the experts the token
+    picked (computed one token at a time), with zeros for tokens that picked
+    no local expert."""
+    w, d = _moe_small()
+    Xp = oracle.moe_permute(d["X"], d["token_ids"])
+    g = oracle.grouped_fwd(Xp, d["offsets"], d["Wg"], d["Wu"], d["Wd"])
+    Y = oracle.moe_combine(g["Y"], d["token_ids"], d["X"].shape[0], d["row_weight"])
+    X = oracle.to_f64(d["X"])
+    off = d["offsets"]
+    expect = np.zeros_like(Y)
+    for e in range(len(off) - 1):
+        for r in range(int(off[e]), int(off[e + 1])):
+            t = int(d["token_ids"][r])
+            f = oracle.mlp_fwd(X[t:t + 1], oracle.to_f64(d["Wg"][e]), oracle.to_f64(d["Wd"][e]),
+                               ACT_SWIGLU, oracle.to_f64(d["Wu"][e]))
+            expect[t] += float(d["row_weight"][r]) * f["Y"][0]
+    assert rel(Y, expect) < 1e-13
+    routed = np.zeros(X.shape[0], bool); routed[d["token_ids"]] = True
+    assert not np.any(Y[~routed]) and routed.any() and (~routed).any()
+
+
+def test_moe_permute_then_unweighted_combine_restores_tokens():
+    w, d = _moe_small(seed=5)
+    ids = d["token_ids"]
+    # keep each token's first row only: the combine then gives the token back
+    first = np.unique(ids, return_index=True)[1]
+    X = oracle.to_f64(d["X"])
+    Y = oracle.moe_combine(oracle.moe_permute(X, ids[first]), ids[first], X.shape[0])
+    assert np.array_equal(Y[ids[first]], X[ids[first]])
+    # with all rows: each token comes back times the number of its rows
+    Y2 = oracle.moe_combine(oracle.moe_permute(X, ids), ids, X.shape[0])
+    cnt = np.bincount(ids, minlength=X.shape[0]).astype(float)
+    assert np.array_equal(Y2, cnt[:, None] * X)
+
+
+def test_moe_combine_backward_by_finite_differences():
+    """L = <dY, combine(Y_perm, w)> is linear in w and in Y_perm, so central
+    differences are exact up to rounding: dL/dw[r] and dL/dY_perm[r, h] match
+    the backward's d_weight and dY_perm."""
+    rng = np.random.default_rng(2)
+    n_tok, H = 9, 5
+    ids = np.array([0, 3, 3, 7, 8, 1, 0, 7], np.int64)
+    w = rng.random(len(ids))
+    Yp = rng.standard_normal((len(ids), H))
+    dY = rng.standard_normal((n_tok, H))
+    L = lambda Yp_, w_: float(np.sum(dY * oracle.moe_combine(Yp_, ids, n_tok, w_)))
+    dYp, dw = oracle.moe_combine_bwd(dY, Yp, ids, w)
+    h = 1e-3
+    for r in range(len(ids)):
+        e = np.zeros_like(w); e[r] = h
+        assert abs((L(Yp, w + e) - L(Yp, w - e)) / (2 * h) - dw[r]) < 1e-10
+        for c in range(H):
+            E = np.zeros_like(Yp); E[r, c] = h
+            assert abs((L(Yp + E, w) - L(Yp - E, w)) / (2 * h) - dYp[r, c]) < 1e-10
+
+
+def test_token_row_lists():
+    """The per-token row lists invert the row -> token map: every row once,
+    each token's rows ascending, and tok_ptr counts match."""
+    import workloads
+    w, d = _moe_small(n_tok=200)
+    ids, ptr, rows = d["token_ids"], d["tok_ptr"], d["tok_rows"]
+    assert ptr[0] == 0 and ptr[-1] == len(ids)
+    assert np.array_equal(np.sort(rows), np.arange(len(ids)))
+    for t in range(len(ptr) - 1):
+        rs = rows[ptr[t]:ptr[t + 1]]
+        assert np.all(ids[rs] == t) and np.all(np.diff(rs) > 0)
+    assert np.all(d["row_weight"] > 0) and np.all(d["row_weight"] < 1)

@@ -34,6 +34,7 @@ DT_F32 = 0
 DT_BF16 = 1
 
 K_X, K_A, K_AUP, K_B, K_DY, K_LOGITS, K_PARTIAL0 = 1, 2, 3, 4, 5, 6, 7
+K_DY_TOKENS = 80   # token-level dY of the MoE layer (past the partial stand-ins' seeds)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -226,6 +227,58 @@ def gen_grouped_inputs(w: Workload, tokens: Optional[int] = None,
         "logits": logits,
     }
     return out
+
+
+def route_weights(logits: np.ndarray, token_ids: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """Router output for each expert-sorted row: the softmax probability
+    (over all experts' logits of its token, no renormalisation over the
+    chosen ones) of the row's expert, float32.  The router is not part of
+    the path; this is the combine's weight input, drawn from the same
+    seeded logits the routing used."""
+    z = logits.astype(np.float64)
+    z = z - z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    p /= p.sum(axis=1, keepdims=True)
+    E = len(offsets) - 1
+    w = np.empty(len(token_ids), np.float32)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        w[lo:hi] = p[token_ids[lo:hi], e]
+    return w
+
+
+def token_rows(token_ids: np.ndarray, n_tok: int):
+    """Inverse of the row -> token map: for each token, the rows that hold
+    it, in increasing row order (= expert order).  Returns (tok_ptr [N+1],
+    tok_rows [R]) as int32 (CSR)."""
+    order = np.argsort(token_ids, kind="stable")
+    counts = np.bincount(token_ids, minlength=n_tok) if len(token_ids) else np.zeros(n_tok, int)
+    ptr = np.zeros(n_tok + 1, np.int64)
+    ptr[1:] = np.cumsum(counts)
+    return ptr.astype(np.int32), order.astype(np.int32)
+
+
+def gen_moe_inputs(w: Workload, tokens: Optional[int] = None, H: Optional[int] = None,
+                   F: Optional[int] = None) -> dict:
+    """Token-level inputs around the grouped experts: X [N,H] (tokens),
+    dY [N,H], the routing rows (token_ids, offsets), their router weights,
+    the per-token row lists, and the expert weights.  Same seeds as
+    gen_grouped_inputs, so X[token_ids] is its X_perm."""
+    g = gen_grouped_inputs(w, tokens, H, F)
+    n_tok = w.tokens if tokens is None else tokens
+    H = w.H if H is None else H
+    X = _draw(w, K_X, (n_tok, H), w.x_std)
+    ptr, rows = token_rows(g["token_ids"], n_tok)
+    return {
+        "X": X,
+        "dY": _draw(w, K_DY_TOKENS, (n_tok, H), w.dy_std),
+        "token_ids": g["token_ids"].astype(np.int32),
+        "offsets": g["offsets"],
+        "row_weight": route_weights(g["logits"], g["token_ids"], g["offsets"]),
+        "tok_ptr": ptr,
+        "tok_rows": rows,
+        "Wg": g["Wg"], "Wu": g["Wu"], "Wd": g["Wd"],
+    }
 
 
 def gen_partials(w: Workload, T: int, shape, std: float, dtype: Optional[int] = None) -> list:
