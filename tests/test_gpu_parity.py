@@ -156,6 +156,45 @@ def test_empty_batch():
             assert torch.count_nonzero(buf.dA_up).item() == 0
 
 
+def test_rows_past_2_to_the_31_elements():
+    """A shard with 2^22 tokens and H = 1024: X, Y, dY and dX hold 2^32
+    elements each, so every row address past element 2^31 needs 64-bit
+    arithmetic.  Inputs are drawn on the GPU from a seeded generator; the
+    oracle recomputes sampled rows (first, last, either side of the 2^31
+    element boundary, and spread between) from those rows alone."""
+    N, H, Ft = 1 << 22, 1024, 256
+    desc = dict(S=N, B=1, H=H, F_shard=Ft, T=1, act=wl.ACT_SWIGLU, dtype=wl.DT_BF16)
+    g = torch.Generator(device="cuda").manual_seed(4242)
+    X = torch.randn((N, H), generator=g, device="cuda").to(torch.bfloat16)
+    dY = (torch.randn((N, H), generator=g, device="cuda") * 0.01).to(torch.bfloat16)
+    A = (torch.randn((H, Ft), generator=g, device="cuda") * 0.03).to(torch.bfloat16)
+    Au = (torch.randn((H, Ft), generator=g, device="cuda") * 0.03).to(torch.bfloat16)
+    B = (torch.randn((Ft, H), generator=g, device="cuda") * 0.03).to(torch.bfloat16)
+    buf = ShardBuffers(desc)
+    print(f"[gpu] 2^32-element rows {desc}", flush=True)
+    tp.tp_mlp_shard_fwd(desc, X, A, Au, B, buf.Z, buf.H, buf.Y)
+    tp.tp_mlp_shard_bwd(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA, buf.dA_up, buf.dB,
+                        buf.ws, buf.ws_bytes)
+    _sync()
+    edge = (1 << 31) // H                       # first row past element 2^31
+    rows = np.unique(np.concatenate([[0, 1, edge - 1, edge, N - 1],
+                                     np.linspace(0, N - 1, 59).astype(np.int64)]))
+    ri = torch.from_numpy(rows).to("cuda")
+    Xs, dYs = to_host(X[ri]), to_host(dY[ri])
+    Ah, Auh, Bh = to_host(A), to_host(Au), to_host(B)
+    f = oracle.mlp_fwd(Xs, Ah, Bh, wl.ACT_SWIGLU, Auh)
+    b = oracle.mlp_bwd(Xs, Ah, Bh, wl.ACT_SWIGLU, dYs, f, Auh)
+    tol = TOL[wl.DT_BF16]
+    Z = f64(to_host(buf.Z[ri]))
+    assert_close("G rows", Z[:, :Ft], f["Z"], tol)
+    assert_close("U rows", Z[:, Ft:], f["U"], tol)
+    assert_close("H rows", f64(to_host(buf.H[ri])), f["H"], tol)
+    assert_close("Y rows", f64(to_host(buf.Y[ri])), f["Y"], tol)
+    assert_close("dX rows", f64(to_host(buf.dX[ri])), b["dX"], tol)
+    del X, dY, buf
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------
 # partial sum
 # ----------------------------------------------------------------------------
