@@ -70,6 +70,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c4_bf16_swiglu_fwdbwd")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fp8", type=int, default=1,
+                   help="1: also time the FP8 (E4M3) forward at the same shape")
     p.add_argument("--moe", type=int, default=1,
                    help="1: also time the MoE dispatch/combine row moves")
     p.add_argument("--overlap", type=int, default=0,
@@ -145,6 +147,63 @@ def moe_dispatch_timing(torch, tp, wl, dev, stream, reps=20):
         out[name] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                      "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     return out
+
+
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (twice the bf16 rate)
+
+
+def fp8_forward_timing(torch, tp, wl, w, X, A, Au, B, stream, reps=10):
+    """The shard forward on E4M3 operands at the same shape: the two FP8
+    GEMMs alone, and the whole forward including the quantization of X and
+    of the three weights (into their transposes)."""
+    dev = X.device
+    N, Hd, Ft = w.N, w.H, w.Ft
+    sw = Au is not None
+    s = lambda v: torch.tensor([v], dtype=torch.float32, device=dev)
+    sx, sa = s(32.0), s(4096.0)
+    Xq = torch.empty((N, Hd), dtype=torch.uint8, device=dev)
+    Aq = torch.empty((Ft, Hd), dtype=torch.uint8, device=dev)
+    Auq = torch.empty((Ft, Hd), dtype=torch.uint8, device=dev) if sw else None
+    Bq = torch.empty((Hd, Ft), dtype=torch.uint8, device=dev)
+    amax = torch.zeros(4, dtype=torch.float32, device=dev)
+    qs = torch.tensor([1 / 32.0, 1 / 4096.0, 1 / 4096.0, 1 / 4096.0, 32.0],
+                      dtype=torch.float32, device=dev)
+    Z = torch.empty((N, 2 * Ft if sw else Ft), dtype=torch.bfloat16, device=dev)
+    Hh = torch.empty((N, Ft), dtype=torch.bfloat16, device=dev)
+    Hq = torch.empty((N, Ft), dtype=torch.uint8, device=dev)
+    Y = torch.empty((N, Hd), dtype=torch.bfloat16, device=dev)
+    desc = dict(S=w.S, B=w.B, H=Hd, F_shard=Ft, T=w.T, act=w.act, dtype=w.dtype)
+    E4 = tp.TP_FP8_E4M3
+
+    def quant():
+        tp.tp_fp8_quantize(E4, False, N, Hd, X, sx, Xq, amax[0:1], stream=stream)
+        tp.tp_fp8_quantize(E4, True, Hd, Ft, A, sa, Aq, amax[1:2], stream=stream)
+        if sw:
+            tp.tp_fp8_quantize(E4, True, Hd, Ft, Au, sa, Auq, amax[2:3], stream=stream)
+        tp.tp_fp8_quantize(E4, True, Ft, Hd, B, sa, Bq, amax[3:4], stream=stream)
+
+    def fwd():
+        tp.tp_mlp_shard_fwd_fp8(desc, Xq, Aq, Auq, Bq, qs, Z, Hh, Hq, amax[0:1], Y, stream=stream)
+
+    quant(); fwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        quant()
+    ev[1].record(stream)
+    for _ in range(reps):
+        fwd()
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = ev[0].elapsed_time(ev[1]) / reps
+    g_ms = ev[1].elapsed_time(ev[2]) / reps
+    flops = 2.0 * N * Hd * Ft * (3 if sw else 2)
+    tf = flops / (g_ms * 1e-3) / 1e12
+    return {"gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 1),
+            "gemm_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "quantize_ms": round(q_ms, 4),
+            "forward_tflops_with_quantize": round(flops / ((g_ms + q_ms) * 1e-3) / 1e12, 1),
+            "bf16_forward_ms_for_comparison": None}
 
 
 def main():
@@ -298,6 +357,10 @@ def main():
                    "bwd_accum_ms": round(e1.elapsed_time(e2) / reps, 4)}
 
     moe = moe_dispatch_timing(torch, tp, wl, dev, stream) if args.moe else None
+    f8 = None
+    if args.fp8 and w.dtype == wl.DT_BF16 and w.H % 128 == 0 and w.Ft % 128 == 0:
+        f8 = fp8_forward_timing(torch, tp, wl, w, X, A, Au, B, stream)
+        f8["bf16_forward_ms_for_comparison"] = round(fwd_ms, 4)
 
     flops = gemm_flops(w)
     value = flops / (ms * 1e-3) / 1e12
@@ -368,6 +431,7 @@ def main():
         "reduce_scatter_rank0": rs,
         "grad_accumulation": acc_cmp,
         "moe_dispatch_combine": moe,
+        "fp8_forward": f8,
     }
 
     if not args.no_cpu_baseline:

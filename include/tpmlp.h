@@ -308,6 +308,45 @@ int tp_moe_combine_bwd(int32_t dtype, int64_t N, int64_t H, int64_t R,
                        const int32_t *row_token, const float *row_weight, const void *dY,
                        const void *Y_perm, void *dY_perm, float *d_weight, void *stream);
 
+/*
+ * FP8 ([P1] §8.2: E4M3 forward, E5M2 backward, per-tensor scaling from
+ * amax; [P3] §10: quantize by scale/amax -> FP8 kernel -> dequantize).
+ * Codes are the OCP 8-bit formats: E4M3 (largest finite 448) and E5M2
+ * (57344).
+ *
+ * tp_fp8_quantize: q = code(clamp(x * scale, -max, max)), round to nearest
+ *   even, the product taken in fp32; amax (if not NULL) is raised to
+ *   max |x| (an atomic max: the caller sets it, e.g. to 0, beforehand).
+ *   fmt        TP_FP8_E4M3 or TP_FP8_E5M2
+ *   transpose  0: q [rows,cols];  1: q [cols,rows] (= the code of x^T),
+ *              rows a multiple of 16
+ *   x          bf16 [rows,cols], cols a multiple of 8
+ *   scale      device float (1 value)
+ *
+ * tp_mlp_shard_fwd_fp8: one shard's forward on E4M3 operands, fp32
+ * accumulate, bf16 activations (desc->dtype must be TP_BF16; H and F_shard
+ * multiples of 128):
+ *   Xq [N,H]; Aq_t, Auq_t [F_shard,H] and Bq_t [H,F_shard]: the codes of
+ *       A^T, A_up^T, B^T (tp_fp8_quantize with transpose = 1), so every
+ *       GEMM operand is K-contiguous; Auq_t NULL for GeLU
+ *   scales  device float[5]: x_inv, a_inv, au_inv, b_inv (the inverses of
+ *       the scales the codes were made with) and h_scale (the scale H is
+ *       quantized with, e.g. from the amax history)
+ *   FC1 sums are multiplied by fp32(x_inv * a_inv) (up projection:
+ *       x_inv * au_inv); the activation gives H, stored as bf16 in H_act
+ *       (and Z_save as in tp_mlp_shard_fwd) and as the E4M3 codes of
+ *       H * h_scale in H_q [N,F_shard]; *h_amax is set to max |H|
+ *   FC2: Y_partial (bf16) = (H_q B^T codes) * fp32(fp32(1 / h_scale) * b_inv)
+ */
+#define TP_FP8_E4M3 0
+#define TP_FP8_E5M2 1
+int tp_fp8_quantize(int32_t fmt, int32_t transpose, int64_t rows, int64_t cols, const void *x,
+                    const float *scale, void *q, float *amax, void *stream);
+int tp_mlp_shard_fwd_fp8(const tp_mlp_desc *desc, const void *Xq, const void *Aq_t,
+                         const void *Auq_t, const void *Bq_t, const float *scales,
+                         void *Z_save, void *H_act, void *H_q, float *h_amax, void *Y_partial,
+                         void *stream);
+
 const char *tp_last_error(void);
 
 /* Fixed name of a tp_status value. */

@@ -228,6 +228,96 @@ def moe_combine_bwd(dY, Y_perm, token_ids, row_weight):
 
 
 # ----------------------------------------------------------------------------
+# FP8 ([P1] §8.2: E4M3 forward / E5M2 backward, per-tensor scaling from
+# amax; [P3] §10: quantize by scale/amax -> FP8 kernel -> dequantize).
+# Formats as in the OCP 8-bit floating point definition: E4M3 (bias 7, no
+# infinities, largest finite 448) and E5M2 (bias 15, largest finite 57344).
+# ----------------------------------------------------------------------------
+FP8_FORMATS = {"e4m3": (4, 3, 448.0), "e5m2": (5, 2, 57344.0)}
+
+
+def fp8_encode(y, fmt="e4m3") -> np.ndarray:
+    """Round-to-nearest-even code of each value, saturating at the largest
+    finite value (values beyond it take its code).  Input: exact values
+    (float32 or float64 arrays); NaN is not expected."""
+    ebits, mbits, vmax = FP8_FORMATS[fmt]
+    bias = (1 << (ebits - 1)) - 1
+    y = np.asarray(y, dtype=np.float64)
+    sign = np.signbit(y).astype(np.uint8) << 7
+    a = np.minimum(np.abs(y), vmax)
+    out = np.zeros(a.shape, np.uint8)
+    emin = 1 - bias
+    nz = a > 0
+    e = np.zeros(a.shape, np.int64)
+    e[nz] = np.floor(np.log2(a[nz])).astype(np.int64)
+    # guard the log2 rounding at exact powers of two
+    e[nz] -= (np.ldexp(1.0, e[nz]) > a[nz])
+    e[nz] += (np.ldexp(1.0, e[nz] + 1) <= a[nz])
+    sub = nz & (e < emin)
+    nor = nz & ~sub
+
+    def rne(u):
+        f = np.floor(u)
+        r = u - f
+        f = f + ((r > 0.5) | ((r == 0.5) & (np.mod(f, 2) == 1)))
+        return f.astype(np.int64)
+
+    # subnormals: units of 2^(emin - mbits); a result of 2^mbits is the
+    # smallest normal's code, which the formula already produces
+    out[sub] = rne(a[sub] / np.ldexp(1.0, emin - mbits)).astype(np.uint8)
+    m = a[nor] / np.ldexp(1.0, e[nor]) - 1.0
+    q = rne(m * (1 << mbits))
+    en = e[nor] + (q == (1 << mbits))
+    q = np.where(q == (1 << mbits), 0, q)
+    out[nor] = (((en + bias) << mbits) | q).astype(np.uint8)
+    return out | sign
+
+
+def fp8_decode(code, fmt="e4m3") -> np.ndarray:
+    """Value of each finite code (float64)."""
+    ebits, mbits, _ = FP8_FORMATS[fmt]
+    bias = (1 << (ebits - 1)) - 1
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> mbits) & ((1 << ebits) - 1)
+    m = c & ((1 << mbits) - 1)
+    val = np.where(e == 0, np.ldexp(m.astype(np.float64), 1 - bias - mbits),
+                   np.ldexp(1.0 + m / (1 << mbits), e - bias))
+    return s * val
+
+
+def fp8_quantize(x, scale, fmt="e4m3"):
+    """Per-tensor quantization: the code of x * scale, the product taken in
+    float32 (as the device does), and amax = max |x|."""
+    xs = (to_f64(x).astype(np.float32) * np.float32(scale)).astype(np.float32)
+    return fp8_encode(xs, fmt), float(np.max(np.abs(to_f64(x)))) if np.size(x) else 0.0
+
+
+def mlp_fwd_fp8(Xq, Aq_t, Bq_t, act, scales, Auq_t=None) -> dict:
+    """One shard's forward on E4M3 operands (codes).  Xq [N,H]; the weights
+    as quantized transposes: Aq_t, Auq_t [Ft,H], Bq_t [H,Ft].  scales =
+    (x_inv, a_inv, au_inv, b_inv, h_scale), float32.  FC1's sums are scaled
+    by float32(x_inv * a_inv) (the up projection by x_inv * au_inv), the
+    activation gives H, H is quantized with h_scale (its codes are the
+    FC2 operand), and FC2's sums are scaled by float32(float32(1 / h_scale)
+    * b_inv).  The products are the oracle's own loops on the decoded
+    values.  Returns Z (G), U, H, Hq (codes), h_amax, Y (float64)."""
+    x_inv, a_inv, au_inv, b_inv, h_scale = (np.float32(v) for v in scales)
+    X = fp8_decode(Xq)
+    dg = float(np.float32(x_inv * a_inv))
+    Ad = fp8_decode(Aq_t).T * dg
+    Aud = fp8_decode(Auq_t).T * float(np.float32(x_inv * au_inv)) if act == ACT_SWIGLU else None
+    # FC1 and the activation (FC2 of this call is not used: its operand is
+    # the quantized H)
+    f = mlp_fwd(X, Ad, np.zeros((Ad.shape[1], X.shape[1])), act, Aud)
+    Hq = fp8_encode((f["H"].astype(np.float32) * h_scale).astype(np.float32))
+    dy = float(np.float32(np.float32(np.float32(1.0) / h_scale) * b_inv))
+    Y = matmul("nt", fp8_decode(Hq), fp8_decode(Bq_t)) * dy
+    return {"Z": f["Z"], "U": f["U"], "H": f["H"], "Hq": Hq,
+            "h_amax": float(np.max(np.abs(f["H"]))) if f["H"].size else 0.0, "Y": Y}
+
+
+# ----------------------------------------------------------------------------
 # all shards of a full weight pair, and the unsharded MLP
 # ----------------------------------------------------------------------------
 def shard_weights(A_full, B_full, T, A_up_full=None):

@@ -19,10 +19,12 @@ __all__ = [
     "tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_mlp_shard_bwd_accum", "tp_mlp_shard_bwd_workspace",
     "tp_partial_sum", "tp_partial_sum_capped", "tp_partial_sum_scatter", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
     "tp_grouped_expert_bwd_workspace", "tp_grouped_expert_bwd_accum",
-    "tp_moe_permute", "tp_moe_combine", "tp_moe_combine_bwd", "tp_last_error", "tp_status_string",
+    "tp_moe_permute", "tp_moe_combine", "tp_moe_combine_bwd",
+    "tp_fp8_quantize", "tp_mlp_shard_fwd_fp8", "TP_FP8_E4M3", "TP_FP8_E5M2", "tp_last_error", "tp_status_string",
 ]
 
 TP_F32, TP_BF16 = 0, 1
+TP_FP8_E4M3, TP_FP8_E5M2 = 0, 1
 TP_ACT_GELU_TANH, TP_ACT_SWIGLU = 0, 1
 STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_DTYPE",
                 4: "TP_ERR_ALIGN", 5: "TP_ERR_WORKSPACE", 6: "TP_ERR_DEVICE",
@@ -102,6 +104,11 @@ def lib() -> ctypes.CDLL:
     L.tp_moe_combine_bwd.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     L.tp_moe_combine_bwd.restype = ctypes.c_int
+    L.tp_fp8_quantize.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                  _vp, _vp, _vp, _vp, _vp]
+    L.tp_fp8_quantize.restype = ctypes.c_int
+    L.tp_mlp_shard_fwd_fp8.argtypes = [D] + [_vp] * 11
+    L.tp_mlp_shard_fwd_fp8.restype = ctypes.c_int
     L.tp_last_error.argtypes = []
     L.tp_last_error.restype = ctypes.c_char_p
     L.tp_status_string.argtypes = [ctypes.c_int]
@@ -260,3 +267,18 @@ def tp_moe_combine_bwd(dtype: int, N: int, H: int, R: int, row_token, row_weight
     return _check(lib().tp_moe_combine_bwd(int(dtype), int(N), int(H), int(R), _ptr(row_token),
                                            _ptr(row_weight), _ptr(dY), _ptr(Y_perm),
                                            _ptr(dY_perm), _ptr(d_weight), _stream(stream)))
+
+
+def tp_fp8_quantize(fmt: int, transpose: bool, rows: int, cols: int, x, scale, q, amax=None,
+                    stream=None) -> int:
+    return _check(lib().tp_fp8_quantize(int(fmt), int(bool(transpose)), int(rows), int(cols),
+                                        _ptr(x), _ptr(scale), _ptr(q), _ptr(amax),
+                                        _stream(stream)))
+
+
+def tp_mlp_shard_fwd_fp8(desc, Xq, Aq_t, Auq_t, Bq_t, scales, Z_save, H_act, H_q, h_amax,
+                         Y_partial, stream=None) -> int:
+    d = _desc(desc)
+    return _check(lib().tp_mlp_shard_fwd_fp8(
+        ctypes.byref(d), _ptr(Xq), _ptr(Aq_t), _ptr(Auq_t), _ptr(Bq_t), _ptr(scales),
+        _ptr(Z_save), _ptr(H_act), _ptr(H_q), _ptr(h_amax), _ptr(Y_partial), _stream(stream)))

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libtpmlp.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["api.hip", "gemm_bf16.hip", "gemm_f32.hip", "partial_sum.hip", "moe.hip"]
+SOURCES = ["api.hip", "gemm_bf16.hip", "gemm_f32.hip", "partial_sum.hip", "moe.hip", "fp8.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -637,6 +637,96 @@ int tp_grouped_expert_bwd_accum(const tp_expert_desc* desc, const int64_t* offse
 }
 
 // ---------------------------------------------------------------------------
+// FP8
+// ---------------------------------------------------------------------------
+int tp_fp8_quantize(int32_t fmt, int32_t transpose, int64_t rows, int64_t cols, const void* x,
+                    const float* scale, void* q, float* amax, void* stream) {
+  if (fmt != TP_FP8_E4M3 && fmt != TP_FP8_E5M2) return fail(TP_ERR_DTYPE, "unknown fp8 format %d", fmt);
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim || rows * cols > ((int64_t)1 << 40))
+    return fail(TP_ERR_SHAPE, "rows and cols must be >= 0 and within range");
+  if (cols % 8) return fail(TP_ERR_SHAPE, "cols must be a multiple of 8");
+  if (transpose && rows % 16) return fail(TP_ERR_SHAPE, "rows must be a multiple of 16 to transpose");
+  const size_t n = (size_t)(rows * cols);
+  Buf in[] = {{x, n * 2, "x"}};
+  Buf out[] = {{q, n, "q"}};
+  Buf tab[] = {{scale, 4, "scale"}};
+  Buf am = {amax, amax ? (size_t)4 : 0, "amax"};
+  if (int rc = check_sized(in, 1)) return rc;
+  if (int rc = check_sized(out, 1)) return rc;
+  if (int rc = check_tables(tab, 1)) return rc;
+  if (int rc = check_tables(&am, 1)) return rc;
+  Buf ins[] = {in[0], tab[0]};
+  Buf outs[] = {out[0], am};
+  if (int rc = check_alias(ins, 2, outs, 2)) return rc;
+  if (int rc = check_device()) return rc;
+  hipError_t he = fp8_quantize_launch(fmt, transpose != 0, rows, cols, x, scale, q, amax,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "quantize launch");
+  return ok();
+}
+
+int tp_mlp_shard_fwd_fp8(const tp_mlp_desc* desc, const void* Xq, const void* Aq_t,
+                         const void* Auq_t, const void* Bq_t, const float* scales, void* Z_save,
+                         void* H_act, void* H_q, float* h_amax, void* Y_partial, void* stream) {
+  Shard s;
+  int rc = check_desc(desc, s);
+  if (rc) return rc;
+  if (s.dtype != TP_BF16) return fail(TP_ERR_DTYPE, "the FP8 forward stores bf16 activations");
+  if (s.H % 128 || s.Ft % 128)
+    return fail(TP_ERR_SHAPE, "H and F_shard must be multiples of 128 for the FP8 path");
+  const bool sw = s.act == TP_ACT_SWIGLU;
+  Buf req[] = {{Xq, (size_t)(s.N * s.H), "Xq"},
+               {Aq_t, (size_t)(s.H * s.Ft), "Aq_t"},
+               {Bq_t, (size_t)(s.Ft * s.H), "Bq_t"},
+               {H_act, (size_t)(s.N * s.Ft) * 2, "H_act"},
+               {H_q, (size_t)(s.N * s.Ft), "H_q"},
+               {Y_partial, (size_t)(s.N * s.H) * 2, "Y_partial"}};
+  if ((rc = check_ptrs(req, 6, true))) return rc;
+  if (sw && !Auq_t) return fail(TP_ERR_NULL, "Auq_t is required for SwiGLU");
+  if (!sw && Auq_t) return fail(TP_ERR_SHAPE, "Auq_t must be NULL for GeLU");
+  Buf opt[] = {{Auq_t, (size_t)(s.H * s.Ft), "Auq_t"},
+               {Z_save, (size_t)(s.N * s.Ft) * (sw ? 2 : 1) * 2, "Z_save"}};
+  if ((rc = check_ptrs(opt, 2, false))) return rc;
+  Buf tab[] = {{scales, 5 * 4, "scales"}, {h_amax, 4, "h_amax"}};
+  if ((rc = check_tables(tab, 2))) return rc;
+  Buf ins[] = {req[0], req[1], req[2], opt[0], tab[0]};
+  Buf outs[] = {req[3], req[4], req[5], opt[1], tab[1]};
+  if ((rc = check_alias(ins, 5, outs, 5))) return rc;
+  if ((rc = check_device())) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t he = zero_float_launch(h_amax, st);
+  if (he != hipSuccess) return hip_fail(he, "amax reset launch");
+  if (s.N == 0) return ok();
+  const int N = (int)s.N, H = (int)s.H, Ft = (int)s.Ft;
+
+  GemmArgs g1 = dense_args(N, Ft, H);
+  g1.a = {Xq, nullptr, H, 0, 0};
+  g1.b = {Aq_t, Auq_t, H, 0, sw ? Ft : 0};
+  g1.epi.out0 = Z_save;
+  g1.epi.out1 = H_act;
+  g1.epi.ld0 = sw ? 2 * (int64_t)Ft : Ft;
+  g1.epi.ld1 = Ft;
+  g1.epi.split = Ft;
+  g1.epi.out2 = H_q;
+  g1.epi.ld2 = Ft;
+  g1.epi.qs = scales;
+  g1.epi.amax = h_amax;
+  he = gemm_fp8(sw ? GK_FC1_SWIGLU_F8 : GK_FC1_GELU_F8, g1, st);
+  if (he != hipSuccess) return hip_fail(he, "FP8 FC1 launch");
+
+  GemmArgs g2 = dense_args(N, H, Ft);
+  g2.a = {H_q, nullptr, Ft, 0, 0};
+  g2.b = {Bq_t, nullptr, Ft, 0, 0};
+  g2.epi.out0 = Y_partial;
+  g2.epi.ld0 = H;
+  g2.epi.qs = scales;
+  he = gemm_fp8(GK_FC2_F8, g2, st);
+  if (he != hipSuccess) return hip_fail(he, "FP8 FC2 launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 // MoE dispatch and combine
 // ---------------------------------------------------------------------------
 int tp_moe_permute(int32_t dtype, int64_t N, int64_t H, int64_t R, const int32_t* row_token,

@@ -135,6 +135,12 @@ struct EpiArgs {
   int64_t ld0, ld1, ldaux;
   int64_t bstride;  // per-problem element offset of out0/out1 (weight grads)
   int64_t split;
+  // FP8 paths only: quantized H (out2, E4M3 bytes, row pitch ld2), the
+  // per-tensor scales (x_inv, a_inv, au_inv, b_inv, h_scale) and max |H|
+  void* out2;
+  int64_t ld2;
+  const float* qs;
+  float* amax;
 };
 
 struct GemmArgs {
@@ -405,6 +411,84 @@ __device__ __forceinline__ void epilogue_swiglu8(const EpiArgs& ea, int64_t m, i
     Vec8<T>::store(ea.out0, m * ea.ld0 + ea.split + f, u);
   }
   Vec8<T>::store(ea.out1, m * ea.ld1 + f, h);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 codes (OCP E4M3 / E5M2): round-to-nearest-even of clamp(x * s) with
+// gfx950's packed converts; four values per 32-bit word, first in the low
+// byte
+// ---------------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, float s) {
+  constexpr float VMAX = FMT == 0 ? 448.0f : 57344.0f;
+  a = fminf(fmaxf(a * s, -VMAX), VMAX);
+  b = fminf(fmaxf(b * s, -VMAX), VMAX);
+  c = fminf(fmaxf(c * s, -VMAX), VMAX);
+  d = fminf(fmaxf(d * s, -VMAX), VMAX);
+  int w;
+  if constexpr (FMT == 0) {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  }
+  return (uint32_t)w;
+}
+
+// FP8 forward epilogues: as the bf16 ones, and H is also written as the
+// E4M3 codes of H * hs (out2, 8 bytes per 8 columns) with max |H| tracked
+__device__ __forceinline__ void store_h_e4m3(const EpiArgs& ea, int64_t m, int64_t f,
+                                             const float h[8], float hs, float& amax) {
+  uint2 q;
+  q.x = fp8x4<0>(h[0], h[1], h[2], h[3], hs);
+  q.y = fp8x4<0>(h[4], h[5], h[6], h[7], hs);
+  *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(ea.out2) + m * ea.ld2 + f) = q;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
+}
+
+template <typename T>
+__device__ __forceinline__ void epilogue_swiglu8_q(const EpiArgs& ea, int64_t m, int64_t f,
+                                                   const float g[8], const float u[8], float hs,
+                                                   float& amax) {
+  float h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = silu_f(g[i]) * u[i];
+  if (ea.out0) {
+    Vec8<T>::store(ea.out0, m * ea.ld0 + f, g);
+    Vec8<T>::store(ea.out0, m * ea.ld0 + ea.split + f, u);
+  }
+  Vec8<T>::store(ea.out1, m * ea.ld1 + f, h);
+  store_h_e4m3(ea, m, f, h, hs, amax);
+}
+
+template <typename T>
+__device__ __forceinline__ void epilogue_gelu8_q(const EpiArgs& ea, int64_t m, int64_t n,
+                                                 const float z[8], float hs, float& amax) {
+  float h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = gelu_f(z[i]);
+  if (ea.out0) Vec8<T>::store(ea.out0, m * ea.ld0 + n, z);
+  Vec8<T>::store(ea.out1, m * ea.ld1 + n, h);
+  store_h_e4m3(ea, m, n, h, hs, amax);
+}
+
+// max over a workgroup of NT threads, folded into *p by one atomic max on
+// the bits (non-negative floats order like their bit patterns); red holds
+// NT / 64 floats of shared memory; every thread of the workgroup calls it
+template <int NT>
+__device__ __forceinline__ void fold_amax_block(float m, float* p, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) t = fmaxf(t, red[w]);
+    atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(t));
+  }
 }
 
 }  // namespace tpmlp

@@ -253,7 +253,11 @@ constexpr int EQ_ROWS = 64;
 constexpr int EQ_PITCH = BN + 4;  // floats
 constexpr int EQ_BYTES = EQ_ROWS * EQ_PITCH * 4;
 
-template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN, int NT>
+// QM (FP8 forward only): 1 = FC1 (sums scaled by x_inv a_inv, resp.
+// x_inv au_inv for the up projection; H also written as E4M3 codes of
+// H h_scale, max |H| folded into ea.amax), 2 = FC2 (sums scaled by
+// (1 / h_scale) b_inv)
+template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN, int NT, int QM = 0>
 __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
                                                   const EpiArgs& ea, const TileCoord& tc,
                                                   int wm, int wn, int lane, int tid, int Ncols,
@@ -261,6 +265,14 @@ __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
   static_assert(WTM == 128 && FM == 4, "passes of 64 rows take two 32-row fragment rows");
   constexpr bool PAIR = EPI == EPI_SWIGLU_FWD;
   const int r_lane = lane & 31, c_lane = lane >> 5;
+  float s0 = 1.0f, s1 = 1.0f, hs = 1.0f, amax = 0.0f;
+  if constexpr (QM == 1) {
+    s0 = ea.qs[0] * ea.qs[1];
+    s1 = ea.qs[0] * ea.qs[2];
+    hs = ea.qs[4];
+  } else if constexpr (QM == 2) {
+    s0 = (1.0f / ea.qs[4]) * ea.qs[3];
+  }
   static_for<0, 4>([&](auto Qc) {
     constexpr int q = decltype(Qc)::value;
     if (wm == q / 2) {
@@ -296,7 +308,13 @@ __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
           *reinterpret_cast<f32x4_t*>(gv + 4) = *reinterpret_cast<const f32x4_t*>(src + 4);
           *reinterpret_cast<f32x4_t*>(uv) = *reinterpret_cast<const f32x4_t*>(src + BN / 2);
           *reinterpret_cast<f32x4_t*>(uv + 4) = *reinterpret_cast<const f32x4_t*>(src + BN / 2 + 4);
-          epilogue_swiglu8<bf16_t>(ea, m, f, gv, uv);
+          if constexpr (QM == 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { gv[e] *= s0; uv[e] *= s1; }
+            epilogue_swiglu8_q<bf16_t>(ea, m, f, gv, uv, hs, amax);
+          } else {
+            epilogue_swiglu8<bf16_t>(ea, m, f, gv, uv);
+          }
         }
       });
     } else {
@@ -311,13 +329,24 @@ __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
           const float* src = stage + row * EQ_PITCH + cc;
           *reinterpret_cast<f32x4_t*>(cv) = *reinterpret_cast<const f32x4_t*>(src);
           *reinterpret_cast<f32x4_t*>(cv + 4) = *reinterpret_cast<const f32x4_t*>(src + 4);
-          epilogue8<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
+          if constexpr (QM != 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cv[e] *= s0;
+          }
+          if constexpr (QM == 1 && EPI == EPI_GELU_FWD)
+            epilogue_gelu8_q<bf16_t>(ea, m, n, cv, hs, amax);
+          else
+            epilogue8<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
         }
       });
     }
     // the next pass rewrites the staging rows
     __syncthreads();
   });
+  if constexpr (QM == 1) {
+    // the staging rows are free after the last pass's barrier
+    if (ea.amax) fold_amax_block<NT>(amax, ea.amax, stage);
+  }
 }
 
 // ---- kernel ----------------------------------------------------------------
@@ -1381,6 +1410,197 @@ __global__ __launch_bounds__(W16_NT, 1) void gemm_w16(GemmArgs g) {
       acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
+
+// ---- FP8 kernel: E4M3 x E4M3 -> fp32 sums, 256 x 256 tiles --------------------
+//
+// Both operands K-contiguous (the weights arrive as quantized transposes).
+// A k tile is 128 codes: the same 128-byte rows, swizzle and direct loads
+// as gemm_lean's 64-wide bf16 tiles.  Four wavefronts of 128 x 128; each k
+// tile is two steps of v_mfma_scale_f32_32x32x64_f8f6f4 with unit block
+// scales (E8M0 127): lane l gives row l % 32, codes 32 (l / 32) .. + 31 of
+// the step's 64 (checked on the GPU against an exact product), i.e. two
+// 16-byte chunks.  Reads run one step ahead; one barrier per tile.  The
+// per-tensor scales are applied in the staged epilogue (QM).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+struct Frag8 {
+  i32x4_t lo, hi;
+  __device__ __forceinline__ void fence() { asm volatile("" : "+v"(lo), "+v"(hi)); }
+  __device__ __forceinline__ i32x8_t op() const {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+template <int OFF>
+__device__ __forceinline__ void ds_read_b128_i(i32x4_t& v, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+}
+__device__ __forceinline__ void mfma_f8_ordered(f32x16_t& acc, const i32x8_t& a,
+                                                const i32x8_t& b, int unit_scale) {
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+               : "+a"(acc)
+               : "v"(a), "v"(b), "v"(unit_scale)
+               : "memory");
+}
+
+template <int BMODE, int EPI, int QM>
+__global__ __launch_bounds__(LEAN_NT, 1) void gemm_f8(GemmArgs g) {
+  constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
+  constexpr int BKB = 128;  // k codes (bytes) per tile
+  constexpr bool PAIR = BMODE == BMODE_PAIR32;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[4 * BM * BK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r_lane = lane & 31, c_lane = lane >> 5;
+
+  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BM);
+  const uint8_t* a0 = reinterpret_cast<const uint8_t*>(g.a.p0);
+  const uint8_t* b0 = reinterpret_cast<const uint8_t*>(g.b.p0);
+  const uint8_t* b1 = reinterpret_cast<const uint8_t*>(g.b.p1);
+  const int64_t lda = g.a.ld, ldb = g.b.ld, bsplit = g.b.split;
+  const int Ncols = g.N;
+  const EpiArgs ea = g.epi;
+  const int n_base = tc.tn * BN;
+  const int m_rows = tc.m_end - tc.m_begin;
+  const int nk = (tc.k_end > tc.k_begin) ? (tc.k_end - tc.k_begin + BKB - 1) / BKB : 0;
+  // B rows of this tile: paired tiles take 128 gate rows from b0 and 128 up
+  // rows from b1 (the same 128 logical columns)
+  const int half = wave >> 1;
+  const int64_t b_row0 = PAIR ? (int64_t)tc.tn * 128 : n_base;
+  const int b_rows = PAIR ? (int)min<int64_t>(128, bsplit - b_row0) : Ncols - n_base;
+
+  const uint32_t lds0 = lds_u32(lds);
+  const uint32_t ldsA = lds0, ldsB = lds0 + 2 * TILE_BYTES;
+
+  uint32_t voffA[8], voffB[8];
+  uint32_t dstA[8], dstB[8];
+  static_for<0, 8>([&](auto Ic) {
+    constexpr int i = decltype(Ic)::value;
+    const int blk = wave * 8 + i;
+    const int r = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    voffA[i] = r < m_rows ? (uint32_t)((int64_t)r * lda + c * 16) : OOB_OFF;
+    dstA[i] = blk * 1024;
+    // paired: rows 0..127 of the tile (waves 0, 1) are gate rows, 128..255 up
+    const int rb = PAIR ? r - 128 * half : r;
+    voffB[i] = rb < b_rows ? (uint32_t)((int64_t)rb * ldb + c * 16) : OOB_OFF;
+    dstB[i] = blk * 1024;
+  });
+  rsrc_t rsA, rsB;
+  int soA = 0, soB = 0;
+  auto set_tile = [&](int k0, bool valid) {
+    rsA = make_rsrc_n(a0 + (int64_t)tc.m_begin * lda, valid ? 0x7fffffffu : 0u);
+    soA = k0;
+    const uint8_t* bp = (PAIR && half) ? b1 : b0;
+    rsB = make_rsrc_n(bp + b_row0 * ldb, valid ? 0x7fffffffu : 0u);
+    soB = k0;
+  };
+  auto load_op = [&](auto Lc, uint32_t buf_off) {
+    constexpr int l = decltype(Lc)::value;
+    if constexpr (l < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsA, (lds_void_t*)(lds + (ldsA - lds0 + buf_off + dstA[l]) / 2), 16, voffA[l], soA, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsB, (lds_void_t*)(lds + (ldsB - lds0 + buf_off + dstB[l - 8]) / 2), 16, voffB[l - 8],
+          soB, 0, 0);
+  };
+
+  // read addresses: step s, half h -> chunk 4 s + 2 c_lane + h of the row
+  uint32_t rdA[4], rdB[4];
+  const int sw = swz(r_lane);
+  static_for<0, 4>([&](auto Xc) {
+    constexpr int x = decltype(Xc)::value;  // 2 s + h
+    const int chunk = 4 * (x >> 1) + 2 * c_lane + (x & 1);
+    rdA[x] = ldsA + (wm * 128 + r_lane) * 128 + ((chunk ^ sw) << 4);
+    // paired B: fragment j of wavefront column wn covers gate (j even) or up
+    // (j odd) rows wn * 64 + (j / 2) * 32 of each half, as in gemm_lean
+    rdB[x] = ldsB + ((PAIR ? wn * 64 : wn * 128) + r_lane) * 128 + ((chunk ^ sw) << 4);
+  });
+
+  Frag8 fa[2][FM], fb[2][FN];
+  constexpr int NREAD = 2 * (FM + FN);
+  auto read_op = [&](auto Rc, auto Sc, uint32_t boff) {
+    constexpr int r = decltype(Rc)::value, S = decltype(Sc)::value;
+    constexpr int frag = (r >> 1) % 4, hpart = r & 1;
+    if constexpr (r < 2 * FM) {
+      if constexpr (hpart == 0) ds_read_b128_i<frag * 4096>(fa[S][frag].lo, rdA[2 * S] + boff);
+      else ds_read_b128_i<frag * 4096>(fa[S][frag].hi, rdA[2 * S + 1] + boff);
+    } else {
+      // fragment j's rows: paired, gate (j even) or up (j odd) rows
+      // wn * 64 + (j / 2) * 32 of each 128-row half; else wn * 128 + 32 j
+      constexpr int off = PAIR ? (frag & 1) * 16384 + (frag >> 1) * 4096 : frag * 4096;
+      if constexpr (hpart == 0) ds_read_b128_i<off>(fb[S][frag].lo, rdB[2 * S] + boff);
+      else ds_read_b128_i<off>(fb[S][frag].hi, rdB[2 * S + 1] + boff);
+    }
+  };
+  auto fence_slot = [&](auto SLc) {
+    constexpr int SL = decltype(SLc)::value;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    static_for<0, FM>([&](auto I) { fa[SL][I].fence(); });
+    static_for<0, FN>([&](auto J) { fb[SL][J].fence(); });
+  };
+
+  f32x16_t acc[FM][FN];
+  static_for<0, FM>([&](auto I) {
+    static_for<0, FN>([&](auto J) { acc[I][J] = (f32x16_t)(0.0f); });
+  });
+  int unit_scale = 127;
+  asm volatile("" : "+v"(unit_scale));
+
+  if (nk > 0) {
+    set_tile(tc.k_begin, true);
+    static_for<0, 16>([&](auto L) { load_op(L, 0u); });
+    set_tile(tc.k_begin + BKB, nk > 1);
+    static_for<0, 16>([&](auto L) { load_op(L, (uint32_t)TILE_BYTES); });
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
+  if (nk > 0) {
+    static_for<0, NREAD>([&](auto R) { read_op(R, std::integral_constant<int, 0>{}, 0u); });
+  }
+  asm volatile("s_nop 4");
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint32_t cur = (uint32_t)(kt & 1) * TILE_BYTES;
+    const uint32_t nxt = cur ^ TILE_BYTES;
+    set_tile(tc.k_begin + (kt + 2) * BKB, kt + 2 < nk);
+    static_for<0, 2>([&](auto Sc) {
+      constexpr int S = decltype(Sc)::value;
+      fence_slot(std::integral_constant<int, S>{});
+      if constexpr (S == 1) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+      }
+      constexpr int NLOAD = S == 1 ? 16 : 0;
+      static_for<0, 16>([&](auto Mc) {
+        constexpr int m = decltype(Mc)::value;
+        constexpr int i = m >> 2, j = m & 3;
+        mfma_f8_ordered(acc[i][j], fb[S][j].op(), fa[S][i].op(), unit_scale);
+        constexpr int r0 = m < 8 ? (m * NREAD) / 8 : NREAD;
+        constexpr int r1 = m < 8 ? ((m + 1) * NREAD) / 8 : NREAD;
+        static_for<r0, r1>([&](auto Oc) {
+          read_op(Oc, std::integral_constant<int, S ^ 1>{}, S == 0 ? cur : nxt);
+        });
+        constexpr int l0 = (m * NLOAD) / 16, l1 = ((m + 1) * NLOAD) / 16;
+        static_for<l0, l1>([&](auto Oc) {
+          constexpr int idx = decltype(Oc)::value;
+          load_op(std::integral_constant<int, (idx & 1) * 8 + (idx >> 1)>{}, cur);
+        });
+      });
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+
+  static_assert(EQ_BYTES <= (int)sizeof(lds), "staging rows exceed shared memory");
+  __syncthreads();
+  write_tile_staged<EPI, BMODE, bf16_t, FM, FN, WTM, WTN, LEAN_NT, QM>(
+      acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
+}
+
 }  // namespace mfma256
 
 // ---------------------------------------------------------------------------
@@ -1537,6 +1757,35 @@ static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
     hipLaunchKernelGGL((mfma256::gemm_kernel<NW, AK, BK_, BMODE, EPI, OutT, false>),
                        dim3(blocks), dim3(64 * NW), 0, stream, g);
   return hipGetLastError();
+}
+
+template <int BMODE, int EPI, int QM>
+static hipError_t launch_f8(GemmArgs& g, hipStream_t stream) {
+  int n_cols = g.N;
+  if (BMODE == BMODE_PAIR32) {
+    // 128 gate + 128 up columns per tile
+    n_cols = (int)((g.b.split + 127) / 128) * 256;
+    g.N = n_cols;
+  }
+  fill_tiles(g, mfma256::BM, mfma256::BN, n_cols);
+  const int blocks = g.tile_off[g.E];
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((mfma256::gemm_f8<BMODE, EPI, QM>), dim3(blocks), dim3(mfma256::LEAN_NT), 0,
+                     stream, g);
+  return hipGetLastError();
+}
+
+hipError_t gemm_fp8(GemmKind kind, GemmArgs& g, hipStream_t stream) {
+  switch (kind) {
+    case GK_FC1_SWIGLU_F8:
+      return launch_f8<BMODE_PAIR32, EPI_SWIGLU_FWD, 1>(g, stream);
+    case GK_FC1_GELU_F8:
+      return launch_f8<BMODE_PLAIN, EPI_GELU_FWD, 1>(g, stream);
+    case GK_FC2_F8:
+      return launch_f8<BMODE_PLAIN, EPI_STORE, 2>(g, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 hipError_t gemm_bf16(GemmKind kind, GemmArgs& g, hipStream_t stream) {

@@ -20,6 +20,9 @@ enum GemmKind {
   GK_DX_KSPLIT,    // dX_partial = [dG|dU] [Ag|Au]^T
   GK_WGRAD_ACC,        // dW += L^T R  (fp32 accumulation buffer)
   GK_WGRAD_SPLIT_ACC,  // as GK_WGRAD_SPLIT, adding into both outputs
+  GK_FC1_SWIGLU_F8,    // FP8: [G|U] = Xq [Agq|Auq]^T scaled; SwiGLU; H, Hq, amax
+  GK_FC1_GELU_F8,      // FP8: Z = Xq Aq^T scaled; GeLU; H, Hq, amax
+  GK_FC2_F8,           // FP8: Y = Hq Bq^T scaled
 };
 
 // bf16 storage, MFMA path.
@@ -30,6 +33,13 @@ hipError_t gemm_f32(GemmKind kind, GemmArgs& g, hipStream_t stream);
 // max_blocks > 0 caps the grid (the kernel strides over the tensor).
 hipError_t partial_sum_launch(int dtype, int T, const void* const* parts, int64_t count,
                               void* out, int max_blocks, hipStream_t stream);
+
+// E4M3 operands, both K-contiguous (GK_*_F8 kinds only)
+hipError_t gemm_fp8(GemmKind kind, GemmArgs& g, hipStream_t stream);
+hipError_t fp8_quantize_launch(int fmt, bool transpose, int64_t rows, int64_t cols,
+                               const void* x, const float* scale, void* q, float* amax,
+                               hipStream_t stream);
+hipError_t zero_float_launch(float* p, hipStream_t stream);
 
 hipError_t moe_permute_launch(int dtype, const int32_t* row_token, int64_t N, int64_t H,
                               int64_t R, const void* X, void* Xp, hipStream_t stream);

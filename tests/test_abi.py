@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -251,3 +251,28 @@ def test_moe_argument_checks():
     assert B(bf, 10, 64, 5, addr(1), None, addr(3), addr(4), addr(5), addr(6)) == E_NULL
     assert B(bf, 10, 64, 5, addr(1), addr(2), addr(3), addr(4), addr(5), addr(2)) == E_ALIAS
     assert B(bf, 10, 64, 5, addr(1), addr(2), addr(3), addr(4), addr(4), addr(6)) == E_ALIAS
+
+
+def test_fp8_argument_checks():
+    Q = lambda *a: _status(tp.tp_fp8_quantize, *a)
+    # quantize(fmt, transpose, rows, cols, x, scale, q, amax)
+    assert Q(2, 0, 16, 16, addr(1), addr(2), addr(3), None) == E_DTYPE
+    assert Q(tp.TP_FP8_E4M3, 0, 16, 12, addr(1), addr(2), addr(3), None) == E_SHAPE   # cols % 8
+    assert Q(tp.TP_FP8_E4M3, 1, 24, 16, addr(1), addr(2), addr(3), None) == E_SHAPE   # rows % 16
+    assert Q(tp.TP_FP8_E4M3, 0, 16, 16, None, addr(2), addr(3), None) == E_NULL
+    assert Q(tp.TP_FP8_E4M3, 0, 16, 16, addr(1), None, addr(3), None) == E_NULL
+    assert Q(tp.TP_FP8_E4M3, 0, 16, 16, addr(1), addr(2, 2), addr(3), None) == E_ALIGN
+    assert Q(tp.TP_FP8_E4M3, 0, 16, 16, addr(1), addr(2), addr(1, 64), None) == E_ALIAS
+    F = lambda d, **kw: _status(
+        tp.tp_mlp_shard_fwd_fp8, d, kw.get("Xq", addr(1)), kw.get("Aq", addr(2)),
+        kw.get("Auq", None), kw.get("Bq", addr(4)), kw.get("qs", addr(5)), kw.get("Z", None),
+        kw.get("H", addr(7)), kw.get("Hq", addr(8)), kw.get("amax", addr(9)),
+        kw.get("Y", addr(10)))
+    d = dict(S=256, B=1, H=256, F_shard=128, T=1, act=tp.TP_ACT_GELU_TANH, dtype=tp.TP_BF16)
+    assert F(dict(d, dtype=tp.TP_F32)) == E_DTYPE
+    assert F(dict(d, H=264)) == E_SHAPE                 # multiples of 128
+    assert F(dict(d, act=tp.TP_ACT_SWIGLU)) == E_NULL   # Auq_t missing
+    assert F(d, Auq=addr(3)) == E_SHAPE                 # GeLU takes none
+    assert F(d, qs=None) == E_NULL
+    assert F(d, amax=addr(9, 2)) == E_ALIGN
+    assert F(d, Y=addr(1)) == E_ALIAS                   # Y over Xq

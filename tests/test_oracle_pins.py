@@ -466,3 +466,65 @@ def test_token_row_lists():
         rs = rows[ptr[t]:ptr[t + 1]]
         assert np.all(ids[rs] == t) and np.all(np.diff(rs) > 0)
     assert np.all(d["row_weight"] > 0) and np.all(d["row_weight"] < 1)
+
+
+# ----------------------------------------------------------------------------
+# FP8 encoding
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt,tdt", [("e4m3", "float8_e4m3fn"), ("e5m2", "float8_e5m2")])
+def test_fp8_codes_round_trip_and_match_torch(fmt, tdt):
+    """Every finite code decodes to a value that encodes back to the same
+    code; decoding agrees with torch's float8 type on all of them; encoding
+    agrees with torch's (round to nearest even) cast on random in-range
+    values and on every midpoint between neighbouring codes."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ebits = 4 if fmt == "e4m3" else 5
+    mbits = 7 - ebits
+    emask = ((1 << ebits) - 1) << mbits
+    finite = codes[((codes & emask) != emask) | ((fmt == "e4m3") & ((codes & 0x7f) != 0x7f))]
+    vals = oracle.fp8_decode(finite, fmt)
+    assert np.array_equal(oracle.fp8_encode(vals, fmt), finite)
+    tv = torch.from_numpy(finite.copy()).view(getattr(torch, tdt)).to(torch.float64).numpy()
+    assert np.array_equal(vals, tv)
+    vmax = oracle.FP8_FORMATS[fmt][2]
+    pos = np.sort(vals[vals >= 0])
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(4)
+    x = np.concatenate([mids, -mids, rng.uniform(-vmax, vmax, 20000),
+                        rng.standard_normal(20000) * 1e-3]).astype(np.float32)
+    want = torch.from_numpy(x).to(getattr(torch, tdt)).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.fp8_encode(x, fmt), want)
+
+
+def test_fp8_saturation_and_signed_zero():
+    assert oracle.fp8_encode(np.array([448.0, 449.0, 500.0, 1e9]), "e4m3").tolist() == [0x7e] * 4
+    assert oracle.fp8_encode(np.array([-1e9]), "e4m3")[0] == 0xfe
+    assert oracle.fp8_encode(np.array([57344.0, 1e9]), "e5m2").tolist() == [0x7b] * 2
+    assert oracle.fp8_encode(np.array([-0.0, 0.0]), "e4m3").tolist() == [0x80, 0x00]
+    # ties to even: 1 + 1/16 lies halfway between codes 0x38 (1.0) and 0x39
+    assert oracle.fp8_encode(np.array([1.0625, 1.1875]), "e4m3").tolist() == [0x38, 0x3a]
+    # smallest subnormal 2^-9 and half of it (tie to even: 0)
+    assert oracle.fp8_encode(np.array([2.0 ** -9, 2.0 ** -10]), "e4m3").tolist() == [0x01, 0x00]
+
+
+def test_fp8_forward_reduces_to_the_bf16_forward_on_exact_codes():
+    """With unit scales and operands that are exactly representable in E4M3
+    (small integers and halves), the FP8 forward is the plain forward on the
+    decoded values, and H's codes are H's own encoding."""
+    rng = np.random.default_rng(6)
+    N, H, F = 7, 16, 8
+    X = rng.integers(-4, 5, (N, H)) / 2.0
+    A = rng.integers(-2, 3, (H, F)) / 8.0
+    Au = rng.integers(-2, 3, (H, F)) / 8.0
+    B = rng.integers(-2, 3, (F, H)) / 8.0
+    q = lambda m: oracle.fp8_encode(m, "e4m3")
+    for act in (ACT_GELU_TANH, ACT_SWIGLU):
+        f8 = oracle.mlp_fwd_fp8(q(X), q(A.T), q(B.T), act, (1, 1, 1, 1, 1),
+                                q(Au.T) if act == ACT_SWIGLU else None)
+        f = oracle.mlp_fwd(X, A, B, act, Au if act == ACT_SWIGLU else None)
+        assert rel(f8["Z"], f["Z"]) < 1e-15 and rel(f8["H"], f["H"]) < 1e-15
+        Hd = oracle.fp8_decode(f8["Hq"])
+        assert np.array_equal(f8["Hq"], q(f["H"].astype(np.float32)))
+        assert rel(f8["Y"], Hd @ B) < 1e-15
+        assert f8["h_amax"] == np.max(np.abs(f["H"]))
