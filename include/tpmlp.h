@@ -57,8 +57,8 @@ typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
 
 /* GeLU in its tanh form (Hendrycks & Gimpel); SwiGLU = silu(X Ag) * (X Au)
  * (Shazeer, "GLU Variants Improve Transformer").  The pages name GeLU for
- * the MLP (§三 3.3 diagram) and SwiGLU, "three matrices", for Llama-style
- * models (§七 mlp.py) without printing either formula. */
+ * the MLP (§三 3.3 diagram) and, for Llama-style models, a SwiGLU MLP with
+ * three weight matrices (§七 mlp.py), without printing either formula. */
 typedef enum tp_act { TP_ACT_GELU_TANH = 0, TP_ACT_SWIGLU = 1 } tp_act;
 
 typedef enum tp_status {
