@@ -71,7 +71,7 @@ def parse():
     p.add_argument("--workload", default="c4_bf16_swiglu_fwdbwd")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fp8", type=int, default=1,
-                   help="1: also time the FP8 (E4M3) forward at the same shape")
+                   help="1: also time the FP8 forward and backward at the same shape")
     p.add_argument("--moe", type=int, default=1,
                    help="1: also time the MoE dispatch/combine row moves")
     p.add_argument("--overlap", type=int, default=0,
@@ -152,58 +152,99 @@ def moe_dispatch_timing(torch, tp, wl, dev, stream, reps=20):
 PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (twice the bf16 rate)
 
 
-def fp8_forward_timing(torch, tp, wl, w, X, A, Au, B, stream, reps=10):
-    """The shard forward on E4M3 operands at the same shape: the two FP8
-    GEMMs alone, and the whole forward including the quantization of X and
-    of the three weights (into their transposes)."""
+def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, reps=10):
+    """The shard forward and backward on FP8 codes at the same shape
+    (E4M3 weights and activations, E5M2 gradients): the GEMM calls alone,
+    and the quantization each needs (forward: X and the weights' transposes;
+    backward: dY and its transpose, the transposes of X's and H's codes, the
+    weights in their own layout)."""
     dev = X.device
     N, Hd, Ft = w.N, w.H, w.Ft
     sw = Au is not None
+    zw = 2 * Ft if sw else Ft
     s = lambda v: torch.tensor([v], dtype=torch.float32, device=dev)
-    sx, sa = s(32.0), s(4096.0)
-    Xq = torch.empty((N, Hd), dtype=torch.uint8, device=dev)
-    Aq = torch.empty((Ft, Hd), dtype=torch.uint8, device=dev)
-    Auq = torch.empty((Ft, Hd), dtype=torch.uint8, device=dev) if sw else None
-    Bq = torch.empty((Hd, Ft), dtype=torch.uint8, device=dev)
-    amax = torch.zeros(4, dtype=torch.float32, device=dev)
+    sx, sa, sdy = s(32.0), s(4096.0), s(1024.0)
+    u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
+    Xq, Aq_t, Bq_t = u8(N, Hd), u8(Ft, Hd), u8(Hd, Ft)
+    Auq_t = u8(Ft, Hd) if sw else None
+    amax = torch.zeros(8, dtype=torch.float32, device=dev)
     qs = torch.tensor([1 / 32.0, 1 / 4096.0, 1 / 4096.0, 1 / 4096.0, 32.0],
                       dtype=torch.float32, device=dev)
-    Z = torch.empty((N, 2 * Ft if sw else Ft), dtype=torch.bfloat16, device=dev)
+    Z = torch.empty((N, zw), dtype=torch.bfloat16, device=dev)
     Hh = torch.empty((N, Ft), dtype=torch.bfloat16, device=dev)
-    Hq = torch.empty((N, Ft), dtype=torch.uint8, device=dev)
+    Hq = u8(N, Ft)
     Y = torch.empty((N, Hd), dtype=torch.bfloat16, device=dev)
     desc = dict(S=w.S, B=w.B, H=Hd, F_shard=Ft, T=w.T, act=w.act, dtype=w.dtype)
-    E4 = tp.TP_FP8_E4M3
+    E4, E5 = tp.TP_FP8_E4M3, tp.TP_FP8_E5M2
+    # backward operands and outputs
+    dYq, dYq_t, Xq_t, Hq_t = u8(N, Hd), u8(Hd, N), u8(Hd, N), u8(Ft, N)
+    Aq, Bq = u8(Hd, Ft), u8(Ft, Hd)
+    Auq = u8(Hd, Ft) if sw else None
+    qb = torch.tensor([1 / 1024.0, 1 / 4096.0, 1 / 32.0, 1 / 32.0, 1 / 4096.0, 4096.0,
+                       1 / 4096.0], dtype=torch.float32, device=dev)
+    dX = torch.empty((N, Hd), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((Hd, Ft), dtype=torch.float32, device=dev)
+    dAu = torch.empty((Hd, Ft), dtype=torch.float32, device=dev) if sw else None
+    dB = torch.empty((Ft, Hd), dtype=torch.float32, device=dev)
+    dZq, dZq_t = u8(N, zw), u8(zw, N)
 
-    def quant():
+    def quant_fwd():
         tp.tp_fp8_quantize(E4, False, N, Hd, X, sx, Xq, amax[0:1], stream=stream)
-        tp.tp_fp8_quantize(E4, True, Hd, Ft, A, sa, Aq, amax[1:2], stream=stream)
+        tp.tp_fp8_quantize(E4, True, Hd, Ft, A, sa, Aq_t, amax[1:2], stream=stream)
         if sw:
-            tp.tp_fp8_quantize(E4, True, Hd, Ft, Au, sa, Auq, amax[2:3], stream=stream)
-        tp.tp_fp8_quantize(E4, True, Ft, Hd, B, sa, Bq, amax[3:4], stream=stream)
+            tp.tp_fp8_quantize(E4, True, Hd, Ft, Au, sa, Auq_t, amax[2:3], stream=stream)
+        tp.tp_fp8_quantize(E4, True, Ft, Hd, B, sa, Bq_t, amax[3:4], stream=stream)
 
     def fwd():
-        tp.tp_mlp_shard_fwd_fp8(desc, Xq, Aq, Auq, Bq, qs, Z, Hh, Hq, amax[0:1], Y, stream=stream)
+        tp.tp_mlp_shard_fwd_fp8(desc, Xq, Aq_t, Auq_t, Bq_t, qs, Z, Hh, Hq, amax[0:1], Y,
+                                stream=stream)
 
-    quant(); fwd()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    def quant_bwd():
+        tp.tp_fp8_quantize(E5, False, N, Hd, dY, sdy, dYq, amax[4:5], stream=stream)
+        tp.tp_fp8_transpose(N, Hd, dYq, dYq_t, stream=stream)
+        tp.tp_fp8_transpose(N, Hd, Xq, Xq_t, stream=stream)
+        tp.tp_fp8_transpose(N, Ft, Hq, Hq_t, stream=stream)
+        tp.tp_fp8_transpose(Ft, Hd, Aq_t, Aq, stream=stream)
+        if sw:
+            tp.tp_fp8_transpose(Ft, Hd, Auq_t, Auq, stream=stream)
+        tp.tp_fp8_transpose(Hd, Ft, Bq_t, Bq, stream=stream)
+
+    def bwd():
+        tp.tp_mlp_shard_bwd_fp8(desc, dYq, dYq_t, Xq_t, Hq_t, Aq, Auq, Bq, Z, qb, dX, dA, dAu,
+                                dB, dZq, dZq_t, amax[5:6], stream=stream)
+
+    quant_fwd(); fwd(); quant_bwd(); bwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     ev[0].record(stream)
     for _ in range(reps):
-        quant()
+        quant_fwd()
     ev[1].record(stream)
     for _ in range(reps):
         fwd()
     ev[2].record(stream)
+    for _ in range(reps):
+        quant_bwd()
+    ev[3].record(stream)
+    for _ in range(reps):
+        bwd()
+    ev[4].record(stream)
     torch.cuda.synchronize()
-    q_ms = ev[0].elapsed_time(ev[1]) / reps
-    g_ms = ev[1].elapsed_time(ev[2]) / reps
-    flops = 2.0 * N * Hd * Ft * (3 if sw else 2)
-    tf = flops / (g_ms * 1e-3) / 1e12
-    return {"gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 1),
-            "gemm_frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
-            "quantize_ms": round(q_ms, 4),
-            "forward_tflops_with_quantize": round(flops / ((g_ms + q_ms) * 1e-3) / 1e12, 1),
-            "bf16_forward_ms_for_comparison": None}
+    ms = [ev[i].elapsed_time(ev[i + 1]) / reps for i in range(4)]
+    f_fl = 2.0 * N * Hd * Ft * (3 if sw else 2)
+    b_fl = 2 * f_fl
+    tf = lambda fl, t: round(fl / (t * 1e-3) / 1e12, 1)
+    fwd_d = {"gemm_ms": round(ms[1], 4), "gemm_tflops": tf(f_fl, ms[1]),
+             "gemm_frac_of_fp8_peak": round(f_fl / (ms[1] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+             "quantize_ms": round(ms[0], 4),
+             "forward_tflops_with_quantize": tf(f_fl, ms[0] + ms[1]),
+             "bf16_forward_ms_for_comparison": None}
+    bwd_d = {"ms": round(ms[3], 4), "tflops": tf(b_fl, ms[3]),
+             "frac_of_fp8_peak": round(b_fl / (ms[3] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+             "quantize_transpose_ms": round(ms[2], 4),
+             "backward_tflops_with_quantize": tf(b_fl, ms[2] + ms[3]),
+             "step_tflops_with_quantize": tf(f_fl + b_fl, sum(ms)),
+             "bf16_backward_ms_for_comparison": None}
+    return fwd_d, bwd_d
 
 
 def main():
@@ -357,10 +398,12 @@ def main():
                    "bwd_accum_ms": round(e1.elapsed_time(e2) / reps, 4)}
 
     moe = moe_dispatch_timing(torch, tp, wl, dev, stream) if args.moe else None
-    f8 = None
-    if args.fp8 and w.dtype == wl.DT_BF16 and w.H % 128 == 0 and w.Ft % 128 == 0:
-        f8 = fp8_forward_timing(torch, tp, wl, w, X, A, Au, B, stream)
+    f8 = f8b = None
+    if (args.fp8 and w.dtype == wl.DT_BF16 and w.H % 128 == 0 and w.Ft % 128 == 0
+            and w.N % 128 == 0 and w.backward):
+        f8, f8b = fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream)
         f8["bf16_forward_ms_for_comparison"] = round(fwd_ms, 4)
+        f8b["bf16_backward_ms_for_comparison"] = round(bwd_ms, 4)
 
     flops = gemm_flops(w)
     value = flops / (ms * 1e-3) / 1e12
@@ -432,6 +475,7 @@ def main():
         "grad_accumulation": acc_cmp,
         "moe_dispatch_combine": moe,
         "fp8_forward": f8,
+        "fp8_backward": f8b,
     }
 
     if not args.no_cpu_baseline:

@@ -347,6 +347,38 @@ int tp_mlp_shard_fwd_fp8(const tp_mlp_desc *desc, const void *Xq, const void *Aq
                          void *Z_save, void *H_act, void *H_q, float *h_amax, void *Y_partial,
                          void *stream);
 
+/*
+ * tp_fp8_transpose: q_t [cols,rows] = q [rows,cols] for 1-byte codes (rows
+ * and cols multiples of 16): the K-contiguous copies the weight-gradient
+ * GEMMs of the FP8 backward need (codes of H and dY).
+ *
+ * tp_mlp_shard_bwd_fp8: one shard's backward on FP8 codes: gradients E5M2,
+ * weights and activations E4M3 ([P1] §8.2), fp32 accumulate.  N, H and
+ * F_shard multiples of 128; desc->dtype TP_BF16.  Codes (1 byte each):
+ *   dYq [N,H], dYq_t [H,N]   dY's E5M2 codes and their transpose
+ *   Xq_t [H,N], Hq_t [F_shard,N]   transposed E4M3 codes of X and H (the
+ *                            forward's H_q, transposed)
+ *   Aq, Auq [H,F_shard], Bq [F_shard,H]   the weights' E4M3 codes in their
+ *                            own layout (Auq NULL for GeLU)
+ *   Z_save    the forward's bf16 Z (SwiGLU: G|U)
+ *   scales    device float[7]: dy_inv, b_inv, h_inv, x_inv, a_inv (one
+ *             scale for the fused [A | A_up] weight), dz_scale, dz_inv
+ *             (= 1 / dz_scale)
+ * Outputs: dX_partial (bf16), dA, dA_up, dB (fp32); workspace dZq [N,zw]
+ * and dZq_t [zw,N] (zw = F_shard, SwiGLU 2 F_shard) receive the E5M2 codes
+ * of dZ * dz_scale; *dz_amax is set to max |dZ|.
+ *   dZ  = act'(Z) * (dYq Bq^T codes) * fp32(dy_inv b_inv)
+ *   dB  = (Hq_t dYq_t^T codes) * fp32(h_inv dy_inv)
+ *   dA  = (Xq_t dZq_t^T codes) * fp32(x_inv dz_inv)   (| dA_up)
+ *   dX  = (dZq [Aq|Auq]^T codes) * fp32(dz_inv a_inv)
+ */
+int tp_fp8_transpose(int64_t rows, int64_t cols, const void *q, void *q_t, void *stream);
+int tp_mlp_shard_bwd_fp8(const tp_mlp_desc *desc, const void *dYq, const void *dYq_t,
+                         const void *Xq_t, const void *Hq_t, const void *Aq, const void *Auq,
+                         const void *Bq, const void *Z_save, const float *scales,
+                         void *dX_partial, float *dA, float *dA_up, float *dB, void *dZq,
+                         void *dZq_t, float *dz_amax, void *stream);
+
 const char *tp_last_error(void);
 
 /* Fixed name of a tp_status value. */

@@ -6,7 +6,8 @@ loop nests live in ``tp_mlp_oracle.c`` (built by ``oracle/build.py`` with
 gcc), and this wrapper only converts storage arrays to float64, allocates
 outputs and loops over shards / experts.
 
-What each function computes, and the passage it follows:
+What each function computes, and the passage it follows ([P1] is the page
+"Megatron-LM 源码精读——大模型并行训练全景", [P3] "Megatron Core 带读"):
 
 * ``mlp_fwd`` / ``mlp_bwd`` -- one shard of the paired column -> act -> row
   MLP and its backward (Megatron-LM 源码精读——大模型并行训练全景, §三
@@ -18,6 +19,13 @@ What each function computes, and the passage it follows:
 * ``grouped_fwd`` / ``grouped_bwd`` -- each local expert runs the SwiGLU MLP
   on its own routed rows (Megatron Core 带读 §09; Megatron-LM 源码精读
   docs index, "MoE 层与 Expert Parallelism": grouped-GEMM expert compute).
+* ``reduce_scatter`` -- the sequence-parallel split of the summed partials.
+* ``moe_permute`` / ``moe_combine`` / ``moe_combine_bwd`` -- token dispatch
+  to the local experts and the weighted merge back (Megatron Core 带读 §09).
+* ``fp8_encode`` / ``fp8_decode`` / ``fp8_quantize`` / ``mlp_fwd_fp8`` /
+  ``mlp_bwd_fp8`` -- per-tensor E4M3 / E5M2 quantization and the shard's
+  forward and backward on codes (Megatron-LM 源码精读 §8.2; Megatron Core
+  带读 §10).
 """
 from __future__ import annotations
 
@@ -315,6 +323,44 @@ def mlp_fwd_fp8(Xq, Aq_t, Bq_t, act, scales, Auq_t=None) -> dict:
     Y = matmul("nt", fp8_decode(Hq), fp8_decode(Bq_t)) * dy
     return {"Z": f["Z"], "U": f["U"], "H": f["H"], "Hq": Hq,
             "h_amax": float(np.max(np.abs(f["H"]))) if f["H"].size else 0.0, "Y": Y}
+
+
+def mlp_bwd_fp8(dYq, Xq, Hq, Aq, Bq, Z, act, scales, U=None, Auq=None) -> dict:
+    """One shard's backward on FP8 codes ([P1] §8.2: gradients in E5M2,
+    weights and activations in E4M3).  Codes in their logical layouts: dYq
+    [N,H] (E5M2), Xq [N,H], Hq [N,Ft] (E4M3), Aq, Auq [H,Ft], Bq [Ft,H]
+    (E4M3); Z (the gate G for SwiGLU) and U are the forward's saved values.
+    scales = (dy_inv, b_inv, h_inv, x_inv, a_inv, dz_scale, dz_inv); the
+    gate and up weights share a_inv.  Steps, each product's code sums
+    scaled by the float32 product of the two inverse scales:
+      dH = dY B^T (dy_inv b_inv), dZ (and dU) from dH and the activation's
+        derivative at the saved Z (U), as in the plain backward;
+      dZq = E5M2 codes of float32(dZ) * dz_scale (the concatenation [dG|dU]
+        for SwiGLU), dz_amax = max |dZ|;
+      dB = H^T dY (h_inv dy_inv); dA (| dA_up) = X^T dZq (x_inv dz_inv);
+      dX = dZq [A | A_up]^T (dz_inv a_inv).
+    Returns float64 dZ (the [dG|dU] values before quantization), dZq,
+    dz_amax, dA, dA_up, dB, dX."""
+    dy_inv, b_inv, h_inv, x_inv, a_inv, dz_scale, dz_inv = (np.float32(v) for v in scales)
+    sw = act == ACT_SWIGLU
+    f32 = lambda a, b: float(np.float32(a * b))
+    dY = fp8_decode(dYq, "e5m2")
+    Xd, Hd, Ad, Bd = fp8_decode(Xq), fp8_decode(Hq), fp8_decode(Aq), fp8_decode(Bq)
+    Aud = fp8_decode(Auq) if sw else None
+    # dH's scale is folded into B; the plain backward then gives the
+    # activation derivative (its own dA, dX, dB are not the FP8 ones)
+    b = mlp_bwd(Xd, Ad, Bd * f32(dy_inv, b_inv), act, dY,
+                {"Z": to_f64(Z), "U": to_f64(U) if sw else None, "H": Hd}, Aud)
+    dZ = np.concatenate([b["dZ"], b["dU"]], axis=1) if sw else b["dZ"]
+    dZq = fp8_encode((dZ.astype(np.float32) * dz_scale).astype(np.float32), "e5m2")
+    dZd = fp8_decode(dZq, "e5m2")
+    Ft = Ad.shape[1]
+    dB = matmul("tn", Hd, dY) * f32(h_inv, dy_inv)
+    dAc = matmul("tn", Xd, dZd) * f32(x_inv, dz_inv)
+    Wc = np.concatenate([Ad, Aud], axis=1) if sw else Ad
+    dX = matmul("nt", dZd, Wc) * f32(dz_inv, a_inv)
+    return {"dZ": dZ, "dZq": dZq, "dz_amax": float(np.max(np.abs(dZ))) if dZ.size else 0.0,
+            "dA": dAc[:, :Ft], "dA_up": dAc[:, Ft:] if sw else None, "dB": dB, "dX": dX}
 
 
 # ----------------------------------------------------------------------------

@@ -20,7 +20,7 @@ __all__ = [
     "tp_partial_sum", "tp_partial_sum_capped", "tp_partial_sum_scatter", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
     "tp_grouped_expert_bwd_workspace", "tp_grouped_expert_bwd_accum",
     "tp_moe_permute", "tp_moe_combine", "tp_moe_combine_bwd",
-    "tp_fp8_quantize", "tp_mlp_shard_fwd_fp8", "TP_FP8_E4M3", "TP_FP8_E5M2", "tp_last_error", "tp_status_string",
+    "tp_fp8_quantize", "tp_mlp_shard_fwd_fp8", "tp_fp8_transpose", "tp_mlp_shard_bwd_fp8", "TP_FP8_E4M3", "TP_FP8_E5M2", "tp_last_error", "tp_status_string",
 ]
 
 TP_F32, TP_BF16 = 0, 1
@@ -109,6 +109,10 @@ def lib() -> ctypes.CDLL:
     L.tp_fp8_quantize.restype = ctypes.c_int
     L.tp_mlp_shard_fwd_fp8.argtypes = [D] + [_vp] * 11
     L.tp_mlp_shard_fwd_fp8.restype = ctypes.c_int
+    L.tp_fp8_transpose.argtypes = [ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
+    L.tp_fp8_transpose.restype = ctypes.c_int
+    L.tp_mlp_shard_bwd_fp8.argtypes = [D] + [_vp] * 17
+    L.tp_mlp_shard_bwd_fp8.restype = ctypes.c_int
     L.tp_last_error.argtypes = []
     L.tp_last_error.restype = ctypes.c_char_p
     L.tp_status_string.argtypes = [ctypes.c_int]
@@ -282,3 +286,17 @@ def tp_mlp_shard_fwd_fp8(desc, Xq, Aq_t, Auq_t, Bq_t, scales, Z_save, H_act, H_q
     return _check(lib().tp_mlp_shard_fwd_fp8(
         ctypes.byref(d), _ptr(Xq), _ptr(Aq_t), _ptr(Auq_t), _ptr(Bq_t), _ptr(scales),
         _ptr(Z_save), _ptr(H_act), _ptr(H_q), _ptr(h_amax), _ptr(Y_partial), _stream(stream)))
+
+
+def tp_fp8_transpose(rows: int, cols: int, q, q_t, stream=None) -> int:
+    return _check(lib().tp_fp8_transpose(int(rows), int(cols), _ptr(q), _ptr(q_t),
+                                         _stream(stream)))
+
+
+def tp_mlp_shard_bwd_fp8(desc, dYq, dYq_t, Xq_t, Hq_t, Aq, Auq, Bq, Z_save, scales, dX_partial,
+                         dA, dA_up, dB, dZq, dZq_t, dz_amax, stream=None) -> int:
+    d = _desc(desc)
+    return _check(lib().tp_mlp_shard_bwd_fp8(
+        ctypes.byref(d), _ptr(dYq), _ptr(dYq_t), _ptr(Xq_t), _ptr(Hq_t), _ptr(Aq), _ptr(Auq),
+        _ptr(Bq), _ptr(Z_save), _ptr(scales), _ptr(dX_partial), _ptr(dA), _ptr(dA_up), _ptr(dB),
+        _ptr(dZq), _ptr(dZq_t), _ptr(dz_amax), _stream(stream)))

@@ -726,6 +726,118 @@ int tp_mlp_shard_fwd_fp8(const tp_mlp_desc* desc, const void* Xq, const void* Aq
   return ok();
 }
 
+int tp_fp8_transpose(int64_t rows, int64_t cols, const void* q, void* q_t, void* stream) {
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim || rows * cols > ((int64_t)1 << 40))
+    return fail(TP_ERR_SHAPE, "rows and cols must be >= 0 and within range");
+  if (rows % 16 || cols % 16) return fail(TP_ERR_SHAPE, "rows and cols must be multiples of 16");
+  const size_t n = (size_t)(rows * cols);
+  Buf in[] = {{q, n, "q"}};
+  Buf out[] = {{q_t, n, "q_t"}};
+  if (int rc = check_sized(in, 1)) return rc;
+  if (int rc = check_sized(out, 1)) return rc;
+  if (int rc = check_alias(in, 1, out, 1)) return rc;
+  if (int rc = check_device()) return rc;
+  hipError_t he = byte_transpose_launch(rows, cols, q, q_t, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "transpose launch");
+  return ok();
+}
+
+int tp_mlp_shard_bwd_fp8(const tp_mlp_desc* desc, const void* dYq, const void* dYq_t,
+                         const void* Xq_t, const void* Hq_t, const void* Aq, const void* Auq,
+                         const void* Bq, const void* Z_save, const float* scales, void* dX_partial,
+                         float* dA, float* dA_up, float* dB, void* dZq, void* dZq_t,
+                         float* dz_amax, void* stream) {
+  Shard s;
+  int rc = check_desc(desc, s);
+  if (rc) return rc;
+  if (s.dtype != TP_BF16) return fail(TP_ERR_DTYPE, "the FP8 backward reads bf16 Z and writes bf16 dX");
+  if (s.H % 128 || s.Ft % 128 || s.N % 128)
+    return fail(TP_ERR_SHAPE, "N, H and F_shard must be multiples of 128 for the FP8 backward");
+  const bool sw = s.act == TP_ACT_SWIGLU;
+  const size_t N = (size_t)s.N, H = (size_t)s.H, Ft = (size_t)s.Ft, zw = sw ? 2 * Ft : Ft;
+  Buf in[] = {{dYq, N * H, "dYq"}, {dYq_t, N * H, "dYq_t"}, {Xq_t, N * H, "Xq_t"},
+              {Hq_t, N * Ft, "Hq_t"}, {Aq, H * Ft, "Aq"}, {Bq, Ft * H, "Bq"},
+              {Z_save, N * zw * 2, "Z_save"}};
+  Buf out[] = {{dX_partial, N * H * 2, "dX_partial"}, {dA, H * Ft * 4, "dA"},
+               {dB, Ft * H * 4, "dB"}, {dZq, N * zw, "dZq"}, {dZq_t, N * zw, "dZq_t"}};
+  if ((rc = check_sized(in, 7))) return rc;
+  if ((rc = check_sized(out, 5))) return rc;
+  if (sw && (!Auq || !dA_up)) return fail(TP_ERR_NULL, "Auq and dA_up are required for SwiGLU");
+  if (!sw && (Auq || dA_up)) return fail(TP_ERR_SHAPE, "Auq and dA_up must be NULL for GeLU");
+  Buf iopt[] = {{Auq, sw ? H * Ft : 0, "Auq"}};
+  Buf oopt[] = {{dA_up, sw ? H * Ft * 4 : 0, "dA_up"}};
+  if ((rc = check_sized(iopt, 1)) || (rc = check_sized(oopt, 1))) return rc;
+  Buf tab[] = {{scales, 7 * 4, "scales"}, {dz_amax, 4, "dz_amax"}};
+  if ((rc = check_tables(tab, 2))) return rc;
+  Buf ins[] = {in[0], in[1], in[2], in[3], in[4], in[5], in[6], iopt[0], tab[0]};
+  Buf outs[] = {out[0], out[1], out[2], out[3], out[4], oopt[0], tab[1]};
+  if ((rc = check_alias(ins, 9, outs, 7))) return rc;
+  if ((rc = check_device())) return rc;
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t he = zero_float_launch(dz_amax, st);
+  if (he != hipSuccess) return hip_fail(he, "amax reset launch");
+  const int n = (int)N, h = (int)H, f = (int)Ft, z = (int)zw;
+  // 1. dZq = code(act'(Z) * (dYq Bq^T) dy_inv b_inv * dz_scale), amax |dZ|
+  {
+    GemmArgs g = dense_args(n, f, h);
+    g.a = {dYq, nullptr, h, 0, 0};
+    g.b = {Bq, nullptr, h, 0, 0};
+    g.epi.aux = Z_save;
+    g.epi.ldaux = z;
+    g.epi.split = f;
+    g.epi.out2 = dZq;
+    g.epi.ld2 = z;
+    g.epi.qs = scales;
+    g.epi.qi = 0; g.epi.qj = 1; g.epi.qk = 5;
+    g.epi.amax = dz_amax;
+    he = gemm_fp8(sw ? GK_DH_SWIGLU_F8 : GK_DH_GELU_F8, g, st);
+    if (he != hipSuccess) return hip_fail(he, "FP8 dH launch");
+  }
+  he = byte_transpose_launch(N, zw, dZq, dZq_t, st);
+  if (he != hipSuccess) return hip_fail(he, "dZ transpose launch");
+  // 2. dB = (Hq^T codes) (dYq codes) h_inv dy_inv
+  {
+    GemmArgs g = dense_args(f, h, n);
+    g.a = {Hq_t, nullptr, n, 0, 0};
+    g.b = {dYq_t, nullptr, n, 0, 0};
+    g.epi.out0 = dB;
+    g.epi.ld0 = h;
+    g.epi.qs = scales;
+    g.epi.qi = 2; g.epi.qj = 0;
+    he = gemm_fp8(GK_WGRAD_F8, g, st);
+    if (he != hipSuccess) return hip_fail(he, "FP8 dB launch");
+  }
+  // 3. dA (| dA_up) = (Xq^T codes) (dZq codes) x_inv dz_inv
+  {
+    GemmArgs g = dense_args(h, z, n);
+    g.a = {Xq_t, nullptr, n, 0, 0};
+    g.b = {dZq_t, nullptr, n, 0, 0};
+    g.epi.out0 = dA;
+    g.epi.out1 = dA_up;
+    g.epi.ld0 = f;
+    g.epi.ld1 = f;
+    g.epi.split = f;
+    g.epi.qs = scales;
+    g.epi.qi = 3; g.epi.qj = 6;
+    he = gemm_fp8(sw ? GK_WGRAD_SPLIT_F8 : GK_WGRAD_F8, g, st);
+    if (he != hipSuccess) return hip_fail(he, "FP8 dA launch");
+  }
+  // 4. dX_partial = (dZq codes) ([Aq | Auq] codes)^T dz_inv a_inv
+  {
+    GemmArgs g = dense_args(n, h, z);
+    g.a = {dZq, nullptr, z, 0, 0};
+    g.b = {Aq, Auq, f, 0, sw ? f : 0};
+    g.epi.out0 = dX_partial;
+    g.epi.ld0 = h;
+    g.epi.qs = scales;
+    g.epi.qi = 6; g.epi.qj = 4;
+    he = gemm_fp8(sw ? GK_DX_KSPLIT_F8 : GK_DX_F8, g, st);
+    if (he != hipSuccess) return hip_fail(he, "FP8 dX launch");
+  }
+  return ok();
+}
+
 // ---------------------------------------------------------------------------
 // MoE dispatch and combine
 // ---------------------------------------------------------------------------

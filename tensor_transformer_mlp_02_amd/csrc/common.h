@@ -141,6 +141,8 @@ struct EpiArgs {
   int64_t ld2;
   const float* qs;
   float* amax;
+  // FP8 backward: dequantize by qs[qi] * qs[qj]; dZ codes use qs[qk]
+  int qi, qj, qk;
 };
 
 struct GemmArgs {
@@ -472,6 +474,46 @@ __device__ __forceinline__ void epilogue_gelu8_q(const EpiArgs& ea, int64_t m, i
   if (ea.out0) Vec8<T>::store(ea.out0, m * ea.ld0 + n, z);
   Vec8<T>::store(ea.out1, m * ea.ld1 + n, h);
   store_h_e4m3(ea, m, n, h, hs, amax);
+}
+
+// FP8 backward: activation derivative from the saved bf16 Z (as
+// EPI_GELU_BWD / EPI_SWIGLU_BWD), written as E5M2 codes of dZ * qscale to
+// out2 (pitch ld2; SwiGLU: dG at n, dU at split + n), max |dZ| tracked
+template <int EPI>
+__device__ __forceinline__ void epilogue_dact8_q(const EpiArgs& ea, int64_t m, int64_t n,
+                                                 const float c[8], float qscale, float& amax) {
+  uint8_t* o = reinterpret_cast<uint8_t*>(ea.out2);
+  if constexpr (EPI == EPI_GELU_BWD) {
+    float z[8], d[8];
+    Vec8<bf16_t>::load(ea.aux, m * ea.ldaux + n, z);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      d[i] = c[i] * gelu_grad_f(z[i]);
+      amax = fmaxf(amax, fabsf(d[i]));
+    }
+    uint2 q;
+    q.x = fp8x4<1>(d[0], d[1], d[2], d[3], qscale);
+    q.y = fp8x4<1>(d[4], d[5], d[6], d[7], qscale);
+    *reinterpret_cast<uint2*>(o + m * ea.ld2 + n) = q;
+  } else {
+    float g[8], u[8], dg[8], du[8];
+    Vec8<bf16_t>::load(ea.aux, m * ea.ldaux + n, g);
+    Vec8<bf16_t>::load(ea.aux, m * ea.ldaux + ea.split + n, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float s = sigmoid_f(g[i]);
+      dg[i] = c[i] * u[i] * (s * (1.0f + g[i] * (1.0f - s)));
+      du[i] = c[i] * (g[i] * s);
+      amax = fmaxf(amax, fmaxf(fabsf(dg[i]), fabsf(du[i])));
+    }
+    uint2 q;
+    q.x = fp8x4<1>(dg[0], dg[1], dg[2], dg[3], qscale);
+    q.y = fp8x4<1>(dg[4], dg[5], dg[6], dg[7], qscale);
+    *reinterpret_cast<uint2*>(o + m * ea.ld2 + n) = q;
+    q.x = fp8x4<1>(du[0], du[1], du[2], du[3], qscale);
+    q.y = fp8x4<1>(du[4], du[5], du[6], du[7], qscale);
+    *reinterpret_cast<uint2*>(o + m * ea.ld2 + ea.split + n) = q;
+  }
 }
 
 // max over a workgroup of NT threads, folded into *p by one atomic max on

@@ -99,6 +99,39 @@ __global__ __launch_bounds__(NT) void quantize_t_kernel(const bf16_t* x, int64_t
 
 __global__ void zero_kernel(float* p) { *p = 0.0f; }
 
+// out[c, r] = in[r, c] for bytes, 64 x 64 tiles through shared memory;
+// rows and cols are multiples of 16
+__global__ __launch_bounds__(NT) void byte_transpose_kernel(const uint8_t* in, int64_t rows,
+                                                            int64_t cols, uint8_t* out) {
+  __shared__ uint8_t tile[64][64 + 4];
+  const int64_t tiles_c = (cols + 63) / 64;
+  const int64_t tiles = ((rows + 63) / 64) * tiles_c;
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t r0 = (t / tiles_c) * 64, c0 = (t % tiles_c) * 64;
+    {
+      const int rr = threadIdx.x / 4, cc = (threadIdx.x % 4) * 16;
+      const int64_t r = r0 + rr, c = c0 + cc;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (r < rows && c < cols) v = *reinterpret_cast<const uint4*>(in + r * cols + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 16; ++k) tile[rr][cc + k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
+    }
+    __syncthreads();
+    {
+      const int oc = threadIdx.x / 4, orr = (threadIdx.x % 4) * 16;
+      const int64_t c = c0 + oc, r = r0 + orr;
+      if (c < cols && r < rows) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 16; ++k) w[k / 4] |= (uint32_t)tile[orr + k][oc] << (8 * (k % 4));
+        *reinterpret_cast<uint4*>(out + c * rows + r) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace f8q
 
 hipError_t fp8_quantize_launch(int fmt, bool transpose, int64_t rows, int64_t cols,
@@ -128,6 +161,17 @@ hipError_t fp8_quantize_launch(int fmt, bool transpose, int64_t rows, int64_t co
       hipLaunchKernelGGL(f8q::quantize_t_kernel<1>, dim3((unsigned)blocks), dim3(f8q::NT), 0,
                          stream, xb, rows, cols, scale, qb, amax);
   }
+  return hipGetLastError();
+}
+
+hipError_t byte_transpose_launch(int64_t rows, int64_t cols, const void* in, void* out,
+                                 hipStream_t stream) {
+  int64_t tiles = ((rows + 63) / 64) * ((cols + 63) / 64);
+  if (tiles == 0) return hipSuccess;
+  if (tiles > 2048) tiles = 2048;
+  hipLaunchKernelGGL(f8q::byte_transpose_kernel, dim3((unsigned)tiles), dim3(f8q::NT), 0, stream,
+                     reinterpret_cast<const uint8_t*>(in), rows, cols,
+                     reinterpret_cast<uint8_t*>(out));
   return hipGetLastError();
 }
 

@@ -253,10 +253,12 @@ constexpr int EQ_ROWS = 64;
 constexpr int EQ_PITCH = BN + 4;  // floats
 constexpr int EQ_BYTES = EQ_ROWS * EQ_PITCH * 4;
 
-// QM (FP8 forward only): 1 = FC1 (sums scaled by x_inv a_inv, resp.
+// QM (FP8 only): 1 = forward FC1 (sums scaled by x_inv a_inv, resp.
 // x_inv au_inv for the up projection; H also written as E4M3 codes of
-// H h_scale, max |H| folded into ea.amax), 2 = FC2 (sums scaled by
-// (1 / h_scale) b_inv)
+// H h_scale, max |H| folded into ea.amax), 2 = forward FC2 (sums scaled by
+// (1 / h_scale) b_inv), 3 = backward, sums scaled by qs[qi] qs[qj], 4 =
+// backward dH: scaled as 3, then the activation derivative written as
+// E5M2 codes of dZ qs[qk] with max |dZ| folded into ea.amax
 template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN, int NT, int QM = 0>
 __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
                                                   const EpiArgs& ea, const TileCoord& tc,
@@ -272,6 +274,9 @@ __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
     hs = ea.qs[4];
   } else if constexpr (QM == 2) {
     s0 = (1.0f / ea.qs[4]) * ea.qs[3];
+  } else if constexpr (QM == 3 || QM == 4) {
+    s0 = ea.qs[ea.qi] * ea.qs[ea.qj];
+    if constexpr (QM == 4) hs = ea.qs[ea.qk];
   }
   static_for<0, 4>([&](auto Qc) {
     constexpr int q = decltype(Qc)::value;
@@ -335,6 +340,8 @@ __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
           }
           if constexpr (QM == 1 && EPI == EPI_GELU_FWD)
             epilogue_gelu8_q<bf16_t>(ea, m, n, cv, hs, amax);
+          else if constexpr (QM == 4)
+            epilogue_dact8_q<EPI>(ea, m, n, cv, hs, amax);
           else
             epilogue8<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
         }
@@ -343,7 +350,7 @@ __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
     // the next pass rewrites the staging rows
     __syncthreads();
   });
-  if constexpr (QM == 1) {
+  if constexpr (QM == 1 || QM == 4) {
     // the staging rows are free after the last pass's barrier
     if (ea.amax) fold_amax_block<NT>(amax, ea.amax, stage);
   }
@@ -1435,15 +1442,26 @@ template <int OFF>
 __device__ __forceinline__ void ds_read_b128_i(i32x4_t& v, uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
 }
+// srcA is the B operand's fragment (format FB: cbsz), srcB the A
+// operand's (format FA: blgp); 0 = E4M3, 1 = E5M2
+template <int FA, int FB>
 __device__ __forceinline__ void mfma_f8_ordered(f32x16_t& acc, const i32x8_t& a,
                                                 const i32x8_t& b, int unit_scale) {
-  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
-               : "+a"(acc)
-               : "v"(a), "v"(b), "v"(unit_scale)
-               : "memory");
+  if constexpr (FA == 0 && FB == 0)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+a"(acc) : "v"(a), "v"(b), "v"(unit_scale) : "memory");
+  else if constexpr (FA == 1 && FB == 0)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] blgp:1"
+                 : "+a"(acc) : "v"(a), "v"(b), "v"(unit_scale) : "memory");
+  else if constexpr (FA == 0 && FB == 1)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:1"
+                 : "+a"(acc) : "v"(a), "v"(b), "v"(unit_scale) : "memory");
+  else
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:1 blgp:1"
+                 : "+a"(acc) : "v"(a), "v"(b), "v"(unit_scale) : "memory");
 }
 
-template <int BMODE, int EPI, int QM>
+template <int BMODE, int EPI, int QM, int FA = 0, int FB = 0, typename OutT = bf16_t>
 __global__ __launch_bounds__(LEAN_NT, 1) void gemm_f8(GemmArgs g) {
   constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
   constexpr int BKB = 128;  // k codes (bytes) per tile
@@ -1494,9 +1512,16 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_f8(GemmArgs g) {
   auto set_tile = [&](int k0, bool valid) {
     rsA = make_rsrc_n(a0 + (int64_t)tc.m_begin * lda, valid ? 0x7fffffffu : 0u);
     soA = k0;
-    const uint8_t* bp = (PAIR && half) ? b1 : b0;
-    rsB = make_rsrc_n(bp + b_row0 * ldb, valid ? 0x7fffffffu : 0u);
-    soB = k0;
+    if constexpr (BMODE == BMODE_KSPLIT) {
+      // k tiles never straddle the split (a multiple of 128)
+      const bool first = k0 < bsplit;
+      rsB = make_rsrc_n((first ? b0 : b1) + b_row0 * ldb, valid ? 0x7fffffffu : 0u);
+      soB = first ? k0 : k0 - (int)bsplit;
+    } else {
+      const uint8_t* bp = (PAIR && half) ? b1 : b0;
+      rsB = make_rsrc_n(bp + b_row0 * ldb, valid ? 0x7fffffffu : 0u);
+      soB = k0;
+    }
   };
   auto load_op = [&](auto Lc, uint32_t buf_off) {
     constexpr int l = decltype(Lc)::value;
@@ -1579,7 +1604,7 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_f8(GemmArgs g) {
       static_for<0, 16>([&](auto Mc) {
         constexpr int m = decltype(Mc)::value;
         constexpr int i = m >> 2, j = m & 3;
-        mfma_f8_ordered(acc[i][j], fb[S][j].op(), fa[S][i].op(), unit_scale);
+        mfma_f8_ordered<FA, FB>(acc[i][j], fb[S][j].op(), fa[S][i].op(), unit_scale);
         constexpr int r0 = m < 8 ? (m * NREAD) / 8 : NREAD;
         constexpr int r1 = m < 8 ? ((m + 1) * NREAD) / 8 : NREAD;
         static_for<r0, r1>([&](auto Oc) {
@@ -1597,7 +1622,7 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_f8(GemmArgs g) {
 
   static_assert(EQ_BYTES <= (int)sizeof(lds), "staging rows exceed shared memory");
   __syncthreads();
-  write_tile_staged<EPI, BMODE, bf16_t, FM, FN, WTM, WTN, LEAN_NT, QM>(
+  write_tile_staged<EPI, BMODE, OutT, FM, FN, WTM, WTN, LEAN_NT, QM>(
       acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
@@ -1759,7 +1784,7 @@ static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int BMODE, int EPI, int QM>
+template <int BMODE, int EPI, int QM, int FA = 0, int FB = 0, typename OutT = bf16_t>
 static hipError_t launch_f8(GemmArgs& g, hipStream_t stream) {
   int n_cols = g.N;
   if (BMODE == BMODE_PAIR32) {
@@ -1770,8 +1795,8 @@ static hipError_t launch_f8(GemmArgs& g, hipStream_t stream) {
   fill_tiles(g, mfma256::BM, mfma256::BN, n_cols);
   const int blocks = g.tile_off[g.E];
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((mfma256::gemm_f8<BMODE, EPI, QM>), dim3(blocks), dim3(mfma256::LEAN_NT), 0,
-                     stream, g);
+  hipLaunchKernelGGL((mfma256::gemm_f8<BMODE, EPI, QM, FA, FB, OutT>), dim3(blocks),
+                     dim3(mfma256::LEAN_NT), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -1783,6 +1808,19 @@ hipError_t gemm_fp8(GemmKind kind, GemmArgs& g, hipStream_t stream) {
       return launch_f8<BMODE_PLAIN, EPI_GELU_FWD, 1>(g, stream);
     case GK_FC2_F8:
       return launch_f8<BMODE_PLAIN, EPI_STORE, 2>(g, stream);
+    // backward: A operand E5M2 (gradients) or E4M3 (activations), B likewise
+    case GK_DH_GELU_F8:
+      return launch_f8<BMODE_PLAIN, EPI_GELU_BWD, 4, 1, 0>(g, stream);
+    case GK_DH_SWIGLU_F8:
+      return launch_f8<BMODE_PLAIN, EPI_SWIGLU_BWD, 4, 1, 0>(g, stream);
+    case GK_WGRAD_F8:
+      return launch_f8<BMODE_PLAIN, EPI_STORE, 3, 0, 1, float>(g, stream);
+    case GK_WGRAD_SPLIT_F8:
+      return launch_f8<BMODE_PLAIN, EPI_STORE_SPLIT, 3, 0, 1, float>(g, stream);
+    case GK_DX_F8:
+      return launch_f8<BMODE_PLAIN, EPI_STORE, 3, 1, 0>(g, stream);
+    case GK_DX_KSPLIT_F8:
+      return launch_f8<BMODE_KSPLIT, EPI_STORE, 3, 1, 0>(g, stream);
     default:
       return hipErrorInvalidValue;
   }

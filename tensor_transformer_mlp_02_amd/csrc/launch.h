@@ -23,6 +23,12 @@ enum GemmKind {
   GK_FC1_SWIGLU_F8,    // FP8: [G|U] = Xq [Agq|Auq]^T scaled; SwiGLU; H, Hq, amax
   GK_FC1_GELU_F8,      // FP8: Z = Xq Aq^T scaled; GeLU; H, Hq, amax
   GK_FC2_F8,           // FP8: Y = Hq Bq^T scaled
+  GK_DH_GELU_F8,       // FP8 bwd: dZq = code(gelu'(Z) * dYq Bq^T scaled), amax
+  GK_DH_SWIGLU_F8,     // FP8 bwd: [dGq|dUq] from dYq Bq^T and the saved G|U, amax
+  GK_WGRAD_F8,         // FP8 bwd: dW = (L^T codes)(R^T codes)^T scaled, fp32 out
+  GK_WGRAD_SPLIT_F8,   // as GK_WGRAD_F8, columns split over two outputs
+  GK_DX_F8,            // FP8 bwd: dX = dZq Aq^T... scaled, bf16 out
+  GK_DX_KSPLIT_F8,     // as GK_DX_F8 with K split over [Aq | Auq]
 };
 
 // bf16 storage, MFMA path.
@@ -40,6 +46,9 @@ hipError_t fp8_quantize_launch(int fmt, bool transpose, int64_t rows, int64_t co
                                const void* x, const float* scale, void* q, float* amax,
                                hipStream_t stream);
 hipError_t zero_float_launch(float* p, hipStream_t stream);
+// bytes [rows, cols] -> [cols, rows]; rows, cols multiples of 16
+hipError_t byte_transpose_launch(int64_t rows, int64_t cols, const void* in, void* out,
+                                 hipStream_t stream);
 
 hipError_t moe_permute_launch(int dtype, const int32_t* row_token, int64_t N, int64_t H,
                               int64_t R, const void* X, void* Xp, hipStream_t stream);

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -276,3 +276,33 @@ def test_fp8_argument_checks():
     assert F(d, qs=None) == E_NULL
     assert F(d, amax=addr(9, 2)) == E_ALIGN
     assert F(d, Y=addr(1)) == E_ALIAS                   # Y over Xq
+
+
+def test_fp8_backward_argument_checks():
+    T = lambda *a: _status(tp.tp_fp8_transpose, *a)
+    assert T(16, 24, addr(1), addr(2)) == E_SHAPE        # cols % 16
+    assert T(-16, 16, addr(1), addr(2)) == E_SHAPE
+    assert T(16, 16, None, addr(2)) == E_NULL
+    assert T(16, 16, addr(1), addr(1, 128)) == E_ALIAS
+    assert T(16, 16, addr(1), addr(2, 8)) == E_ALIGN
+    names = ("dYq", "dYq_t", "Xq_t", "Hq_t", "Aq", "Auq", "Bq", "Z", "qs", "dX", "dA", "dA_up",
+             "dB", "dZq", "dZq_t", "amax")
+    gelu_none = {"Auq", "dA_up"}
+
+    def Bw(d, **kw):
+        sw = d["act"] == tp.TP_ACT_SWIGLU
+        args = [kw[n] if n in kw else (None if (n in gelu_none and not sw) else addr(i + 1))
+                for i, n in enumerate(names)]
+        return _status(tp.tp_mlp_shard_bwd_fp8, d, *args)
+
+    d = dict(S=256, B=1, H=256, F_shard=128, T=1, act=tp.TP_ACT_GELU_TANH, dtype=tp.TP_BF16)
+    assert Bw(dict(d, dtype=tp.TP_F32)) == E_DTYPE
+    assert Bw(dict(d, S=200)) == E_SHAPE                # tokens a multiple of 128
+    assert Bw(dict(d, F_shard=136)) == E_SHAPE
+    assert Bw(d, Auq=addr(6)) == E_SHAPE                # GeLU takes no up weight
+    sw = dict(d, act=tp.TP_ACT_SWIGLU)
+    assert Bw(sw, dA_up=None) == E_NULL
+    assert Bw(d, qs=None) == E_NULL
+    assert Bw(d, amax=addr(16, 2)) == E_ALIGN
+    assert Bw(d, dZq=addr(5, 64)) == E_ALIAS            # workspace over Aq
+    assert Bw(d, dX=addr(8)) == E_ALIAS                 # dX over Z

@@ -25,7 +25,7 @@ import oracle
 import tensor_transformer_mlp_02_amd as tp
 import workloads as wl
 from tensor_transformer_mlp_02_amd.tensors import to_device, to_host
-from parity import TOL, assert_close, f64
+from parity import TOL, assert_close, f64, rel_frob
 
 pytestmark = pytest.mark.gpu
 E4M3, E5M2 = tp.TP_FP8_E4M3, tp.TP_FP8_E5M2
@@ -162,3 +162,235 @@ def test_fp8_forward_swiglu_shard_sampled_rows():
     Hall = torch.abs(dev["H"].float()).max().item()
     # the device's max over fp32 H agrees with the max of its own bf16 H
     assert abs(amax - Hall) <= 2.0 ** -8 * Hall and amax >= f["h_amax"] * (1 - 1e-5)
+
+
+# ---------------------------------------------------------------------------
+# backward: E5M2 gradients against E4M3 weights and activations
+# ---------------------------------------------------------------------------
+def test_byte_transpose_bitwise():
+    for rows, cols in ((16, 16), (272, 144), (1040, 528), (4096, 96)):
+        print(f"[gpu] fp8 transpose {rows}x{cols}", flush=True)
+        x = np.random.default_rng(rows + cols).integers(0, 256, (rows, cols), dtype=np.uint8)
+        q = torch.from_numpy(x).to("cuda")
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+        tp.tp_fp8_transpose(rows, cols, q, qt)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(qt), x.T)
+
+
+# The FP8 backward is held to the bf16 bar: its operands carry 3 (E4M3) and
+# 2 (E5M2) mantissa bits, and the matrix core's FP8 dot products are not an
+# IEEE fp32 sum of the exact products (about 1e-5 relative on the weight
+# gradients, against 1e-7 for fp32 rounding).  The tests print the errors.
+TOL_FP8 = TOL[wl.DT_BF16]
+# dY's, the weights', X's and H's scales, and dZ's (2^12)
+BWD_SCALES = dict(dy=1024.0, x=32.0, a=4096.0, b=4096.0, h=32.0, dz=4096.0)
+
+
+def _bwd_case(N, H, Ft, act, seed, dy_std=0.01):
+    """Seeded bf16 tensors of the backward's inputs (Z, U, H are
+    independent draws: the backward takes them as given), the device's
+    quantization (through the library's quantizer and transpose) and its
+    FP8 backward."""
+    sw = act == wl.ACT_SWIGLU
+    s = BWD_SCALES
+    host = dict(X=wl.normal_bf16(seed + 1, (N, H), 1.0),
+                A=wl.normal_bf16(seed + 2, (H, Ft), 0.015),
+                Au=wl.normal_bf16(seed + 3, (H, Ft), 0.015) if sw else None,
+                B=wl.normal_bf16(seed + 4, (Ft, H), 0.015),
+                dY=wl.normal_bf16(seed + 5, (N, H), dy_std),
+                H=wl.normal_bf16(seed + 6, (N, Ft), 0.5),
+                Z=wl.normal_bf16(seed + 7, (N, 2 * Ft if sw else Ft), 1.0))
+    dYq, _ = _quantize_gpu(host["dY"], s["dy"], E5M2)
+    dYq_t = torch.empty((H, N), dtype=torch.uint8, device="cuda")
+    tp.tp_fp8_transpose(N, H, dYq, dYq_t)
+    Xq_t, _ = _quantize_gpu(host["X"], s["x"], transpose=True)
+    Hq_t, _ = _quantize_gpu(host["H"], s["h"], transpose=True)
+    Aq, _ = _quantize_gpu(host["A"], s["a"])
+    Auq = _quantize_gpu(host["Au"], s["a"])[0] if sw else None
+    Bq, _ = _quantize_gpu(host["B"], s["b"])
+    qs = torch.tensor([1 / s["dy"], 1 / s["b"], 1 / s["h"], 1 / s["x"], 1 / s["a"], s["dz"],
+                       1 / s["dz"]], dtype=torch.float32, device="cuda")
+    zw = 2 * Ft if sw else Ft
+    dev = dict(dX=torch.empty((N, H), dtype=torch.bfloat16, device="cuda"),
+               dA=torch.empty((H, Ft), dtype=torch.float32, device="cuda"),
+               dA_up=torch.empty((H, Ft), dtype=torch.float32, device="cuda") if sw else None,
+               dB=torch.empty((Ft, H), dtype=torch.float32, device="cuda"),
+               dZq=torch.empty((N, zw), dtype=torch.uint8, device="cuda"),
+               dZq_t=torch.empty((zw, N), dtype=torch.uint8, device="cuda"),
+               amax=torch.full((1,), -1.0, dtype=torch.float32, device="cuda"))
+    desc = dict(S=N, B=1, H=H, F_shard=Ft, T=1, act=act, dtype=wl.DT_BF16)
+    print(f"[gpu] fp8 backward {desc}", flush=True)
+    tp.tp_mlp_shard_bwd_fp8(desc, dYq, dYq_t, Xq_t, Hq_t, Aq, Auq, Bq, to_device(host["Z"]), qs,
+                            dev["dX"], dev["dA"], dev["dA_up"], dev["dB"], dev["dZq"],
+                            dev["dZq_t"], dev["amax"])
+    torch.cuda.synchronize()
+    return host, dev
+
+
+def _oracle_bwd(host, act, rows=None, cols=None):
+    """The oracle's own quantization and FP8 backward, on a subset of rows
+    (tokens: exact dZ and dX rows) or of F columns (an F_shard of its own:
+    exact dA, dA_up columns and dB rows)."""
+    sw = act == wl.ACT_SWIGLU
+    s = BWD_SCALES
+    r = slice(None) if rows is None else rows
+    c = slice(None) if cols is None else cols
+    Ft = host["A"].shape[1]
+    q = lambda m, sc: oracle.fp8_quantize(m, sc)[0]
+    Z, U = (host["Z"][:, :Ft], host["Z"][:, Ft:]) if sw else (host["Z"], None)
+    Zb = wl.bf16_bits_to_f32(Z[r][:, c])
+    Ub = wl.bf16_bits_to_f32(U[r][:, c]) if sw else None
+    return oracle.mlp_bwd_fp8(
+        oracle.fp8_quantize(host["dY"][r], s["dy"], "e5m2")[0], q(host["X"][r], s["x"]),
+        q(host["H"][r][:, c], s["h"]), q(host["A"][:, c], s["a"]), q(host["B"][c], s["b"]),
+        Zb, act, (1 / s["dy"], 1 / s["b"], 1 / s["h"], 1 / s["x"], 1 / s["a"], s["dz"],
+                  1 / s["dz"]), Ub, q(host["Au"][:, c], s["a"]) if sw else None)
+
+
+def _dz_bound(host, act, rows=None, cols=None):
+    """Per element, dz_scale times a bound on the error of the device's fp32
+    dZ: dH is an fp32 sum of K exact FP8 products, so its error is at most
+    K 2^-24 sum_k |dY_k B_k| (recursive summation; the matrix core's
+    reductions are no worse); the activation factor multiplies that by at
+    most 1.13 |.| (GeLU'), |U| 1.1 (SwiGLU dG) or |G| (dU); its own fp32
+    evaluation adds 2^-19 |dH| (1 + |G| + |U|), and dZ's rounding 2^-23 |dZ|.
+    Returns the scaled exact dZ y and the bound E (both float64)."""
+    s = BWD_SCALES
+    sw = act == wl.ACT_SWIGLU
+    r = slice(None) if rows is None else rows
+    c = slice(None) if cols is None else cols
+    Ft = host["A"].shape[1]
+    dYd = oracle.fp8_decode(oracle.fp8_quantize(host["dY"][r], s["dy"], "e5m2")[0], "e5m2")
+    Bd = oracle.fp8_decode(oracle.fp8_quantize(host["B"][c], s["b"])[0])
+    sc = float(np.float32(np.float32(1 / s["dy"]) * np.float32(1 / s["b"])))
+    K = dYd.shape[1]
+    dH = oracle.matmul("nt", dYd, Bd) * sc
+    S = oracle.matmul("nt", np.abs(dYd), np.abs(Bd)) * sc
+    acc = K * 2.0 ** -24 * S
+    if sw:
+        G = wl.bf16_bits_to_f32(host["Z"][:, :Ft][r][:, c]).astype(np.float64)
+        U = wl.bf16_bits_to_f32(host["Z"][:, Ft:][r][:, c]).astype(np.float64)
+        ev = 2.0 ** -19 * np.abs(dH) * (1 + np.abs(G) + np.abs(U))
+        E = np.concatenate([acc * 1.1 * np.abs(U) + ev, acc * np.abs(G) + ev], axis=1)
+    else:
+        Z = wl.bf16_bits_to_f32(host["Z"][r][:, c]).astype(np.float64)
+        E = acc * 1.13 + 2.0 ** -19 * np.abs(dH) * (1 + np.abs(Z))
+    return E * s["dz"]
+
+
+def _check_dz_codes(got, b, E):
+    """E5M2 codes of dZ made from the device's fp32 dZ and the oracle's
+    fp64 dZ: equal except where the two straddle a rounding boundary, which
+    is rare; where they differ, the device's code is the rounding of a value
+    within E of the exact scaled dZ (rounding is monotone: its value lies
+    between the codes of y - E and y + E)."""
+    want = b["dZq"]
+    differ = got != want
+    print(f"  dZ codes differing: {differ.sum()} of {differ.size}", flush=True)
+    assert differ.mean() <= 1e-3, differ.mean()
+    if differ.any():
+        y = b["dZ"][differ] * BWD_SCALES["dz"]
+        e = E[differ]
+        lo = oracle.fp8_decode(oracle.fp8_encode(y - e, "e5m2"), "e5m2")
+        hi = oracle.fp8_decode(oracle.fp8_encode(y + e, "e5m2"), "e5m2")
+        v = oracle.fp8_decode(got[differ], "e5m2")
+        bad = (v < lo) | (v > hi)
+        assert not bad.any(), (v[bad][:8], y[bad][:8], e[bad][:8])
+    return int(differ.sum())
+
+
+def _close_given_codes(name, got, ref, slack):
+    """The bf16 bar, with each element's bound widened by `slack`: the
+    largest change that the dZ codes accepted above as differing (by one
+    rounding of an fp32 error) can make in it, sum |operand| |code change|
+    times the scale.  Elsewhere the bound is the usual one."""
+    got = np.asarray(got, np.float64)
+    r = rel_frob(got, ref)
+    print(f"  {name}: relative Frobenius error {r:.3e}", flush=True)
+    assert r <= TOL_FP8, (name, r)
+    rms = np.sqrt(np.mean(ref * ref)) if ref.size else 0.0
+    bad = np.abs(got - ref) > 4 * TOL_FP8 * (np.abs(ref) + rms) + slack
+    assert not bad.any(), (name, np.argwhere(bad)[:4], got[bad][:4], ref[bad][:4])
+
+
+def _code_change(got, b):
+    """decode(device codes) - decode(oracle codes), scaled back to dZ."""
+    d = oracle.fp8_decode(got, "e5m2") - oracle.fp8_decode(b["dZq"], "e5m2")
+    return np.abs(d) / BWD_SCALES["dz"]
+
+
+def _slacks(host, act, dZq_dev, b, rows=None, cols=None):
+    """Per-element slack of dA (| dA_up) and dX from the dZ code changes."""
+    s = BWD_SCALES
+    sw = act == wl.ACT_SWIGLU
+    r = slice(None) if rows is None else rows
+    c = slice(None) if cols is None else cols
+    D = _code_change(dZq_dev, b)
+    Xa = np.abs(oracle.fp8_decode(oracle.fp8_quantize(host["X"][r], s["x"])[0])) / s["x"]
+    Wa = np.abs(oracle.fp8_decode(oracle.fp8_quantize(host["A"][:, c], s["a"])[0])) / s["a"]
+    if sw:
+        Wu = np.abs(oracle.fp8_decode(oracle.fp8_quantize(host["Au"][:, c], s["a"])[0])) / s["a"]
+        Wa = np.concatenate([Wa, Wu], axis=1)
+    sa = oracle.matmul("tn", Xa, D) if D.any() else np.zeros((Xa.shape[1], D.shape[1]))
+    sx = oracle.matmul("nt", D, Wa) if D.any() else np.zeros((D.shape[0], Wa.shape[0]))
+    return sa, sx
+
+
+@pytest.mark.parametrize("act", [wl.ACT_SWIGLU, wl.ACT_GELU_TANH])
+@pytest.mark.parametrize("N", [384, 128])
+def test_fp8_backward_small(act, N):
+    """Several 256-wide tiles with ragged last tiles in every direction
+    (H = 384, F_shard = 640: 1.5 and 2.5 tiles)."""
+    sw = act == wl.ACT_SWIGLU
+    H, Ft = 384, 640
+    host, dev = _bwd_case(N, H, Ft, act, seed=9000 + N + 10 * act)
+    b = _oracle_bwd(host, act)
+    _check_dz_codes(to_host(dev["dZq"]), b, _dz_bound(host, act))
+    assert np.array_equal(to_host(dev["dZq_t"]), to_host(dev["dZq"]).T)
+    amax = float(to_host(dev["amax"])[0])
+    assert abs(amax - b["dz_amax"]) <= 1e-5 * b["dz_amax"]
+    r = assert_close("dB", to_host(dev["dB"]), b["dB"], TOL_FP8)
+    print(f"  dB: relative Frobenius error {r:.3e}", flush=True)
+    sa, sx = _slacks(host, act, to_host(dev["dZq"]), b)
+    _close_given_codes("dA", to_host(dev["dA"]), b["dA"], sa[:, :Ft])
+    if sw:
+        _close_given_codes("dA_up", to_host(dev["dA_up"]), b["dA_up"], sa[:, Ft:])
+    _close_given_codes("dX", f64(to_host(dev["dX"])), b["dX"], sx)
+
+
+def test_fp8_backward_swiglu_shard_sampled():
+    """The SwiGLU shard shape (4096 tokens, H = 8192, F/T = 3584): sampled
+    token rows (dZ codes, dX rows) and sampled F columns, each an F_shard of
+    its own for the oracle (dA, dA_up columns, dB rows, dZ code columns)."""
+    w = wl.WORKLOADS["c4_bf16_swiglu_fwdbwd"]
+    N, H, Ft = w.N, w.H, w.Ft
+    act = wl.ACT_SWIGLU
+    host, dev = _bwd_case(N, H, Ft, act, seed=9500)
+    rows = np.unique(np.linspace(0, N - 1, 24).astype(np.int64))
+    cols = np.unique(np.linspace(0, Ft - 1, 16).astype(np.int64))
+    br = _oracle_bwd(host, act, rows=rows)
+    ri = torch.from_numpy(rows).to("cuda")
+    zr = to_host(dev["dZq"][ri])
+    _check_dz_codes(zr, br, _dz_bound(host, act, rows=rows))
+    _close_given_codes("dX rows", f64(to_host(dev["dX"][ri])), br["dX"],
+                       _slacks(host, act, zr, br, rows=rows)[1])
+    bc = _oracle_bwd(host, act, cols=cols)
+    ci = torch.from_numpy(cols).to("cuda")
+    zc = torch.cat([ci, ci + Ft])
+    zc_h = to_host(dev["dZq"][:, zc])
+    _check_dz_codes(zc_h, bc, _dz_bound(host, act, cols=cols))
+    r = assert_close("dB rows", to_host(dev["dB"][ci]), bc["dB"], TOL_FP8)
+    print(f"  dB rows: relative Frobenius error {r:.3e}", flush=True)
+    sa = _slacks(host, act, zc_h, bc, cols=cols)[0]
+    nc = len(cols)
+    _close_given_codes("dA cols", to_host(dev["dA"][:, ci]), bc["dA"], sa[:, :nc])
+    _close_given_codes("dA_up cols", to_host(dev["dA_up"][:, ci]), bc["dA_up"], sa[:, nc:])
+    amax = float(to_host(dev["amax"])[0])
+    assert amax >= max(br["dz_amax"], bc["dz_amax"]) * (1 - 1e-5)
+    # the largest magnitude among the codes (E5M2 magnitudes order like their
+    # 7 low bits) is amax * dz_scale rounded to E5M2: within 2^-3 of it
+    top = int((dev["dZq"] & 0x7f).max().item())
+    top_v = float(oracle.fp8_decode(np.array([top], np.uint8), "e5m2")[0])
+    want = amax * BWD_SCALES["dz"]
+    assert abs(top_v - want) <= 0.125 * want

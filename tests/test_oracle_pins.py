@@ -528,3 +528,74 @@ def test_fp8_forward_reduces_to_the_bf16_forward_on_exact_codes():
         assert np.array_equal(f8["Hq"], q(f["H"].astype(np.float32)))
         assert rel(f8["Y"], Hd @ B) < 1e-15
         assert f8["h_amax"] == np.max(np.abs(f["H"]))
+
+
+def _exact_bwd_case(act, rng):
+    """Operands exactly representable in E4M3 / E5M2 (small multiples of
+    powers of two), Z and U on a grid that keeps every activation
+    derivative away from zero (so no dZ falls below E5M2's normal range)."""
+    N, H, F = 6, 16, 8
+    X = rng.integers(-4, 5, (N, H)) / 2.0
+    Hh = rng.integers(-4, 5, (N, F)) / 4.0
+    A = rng.integers(-2, 3, (H, F)) / 8.0
+    Au = rng.integers(-2, 3, (H, F)) / 8.0
+    B = rng.integers(-2, 3, (F, H)) / 8.0
+    dY = rng.integers(-3, 4, (N, H)) / 16.0
+    grid = np.array([-2.0, -1.5, -1.0, -0.5, 0.5, 1.0, 1.5, 2.0])
+    Z = rng.choice(grid, (N, F))
+    U = rng.choice(grid, (N, F))
+    return X, Hh, A, Au, B, dY, Z, U
+
+
+@pytest.mark.parametrize("act", [ACT_GELU_TANH, ACT_SWIGLU])
+def test_fp8_backward_reduces_to_the_plain_backward_on_exact_codes(act):
+    """Unit scales and exact codes: dZ is the plain backward's (definition
+    pinned by finite differences above), its codes are its own E5M2
+    encoding, and dB, dA, dX are numpy's products of the decoded codes."""
+    sw = act == ACT_SWIGLU
+    X, Hh, A, Au, B, dY, Z, U = _exact_bwd_case(act, np.random.default_rng(8))
+    q4 = lambda m: oracle.fp8_encode(m, "e4m3")
+    b8 = oracle.mlp_bwd_fp8(oracle.fp8_encode(dY, "e5m2"), q4(X), q4(Hh), q4(A), q4(B), Z, act,
+                            (1, 1, 1, 1, 1, 1, 1), U if sw else None, q4(Au) if sw else None)
+    ref = oracle.mlp_bwd(X, A, B, act, dY, {"Z": Z, "U": U if sw else None, "H": Hh},
+                         Au if sw else None)
+    dZ = np.concatenate([ref["dZ"], ref["dU"]], axis=1) if sw else ref["dZ"]
+    assert rel(b8["dZ"], dZ) < 1e-15
+    assert np.array_equal(b8["dZq"], oracle.fp8_encode(dZ.astype(np.float32), "e5m2"))
+    assert b8["dz_amax"] == np.max(np.abs(dZ))
+    dZd = oracle.fp8_decode(b8["dZq"], "e5m2")
+    # quantization really moved dZ (so the checks below see the codes)
+    assert np.any(dZd != dZ)
+    F = A.shape[1]
+    assert rel(b8["dB"], Hh.T @ dY) < 1e-15
+    assert rel(b8["dA"], X.T @ dZd[:, :F]) < 1e-15
+    if sw:
+        assert rel(b8["dA_up"], X.T @ dZd[:, F:]) < 1e-15
+        assert rel(b8["dX"], dZd @ np.concatenate([A, Au], axis=1).T) < 1e-15
+    else:
+        assert b8["dA_up"] is None
+        assert rel(b8["dX"], dZd @ A.T) < 1e-15
+
+
+@pytest.mark.parametrize("act", [ACT_GELU_TANH, ACT_SWIGLU])
+def test_fp8_backward_power_of_two_scales_cancel(act):
+    """Each tensor quantized with its own power-of-two scale and passed its
+    inverse: the decoded products, dZ and its codes are unchanged from the
+    unit-scale run apart from dZq's exponent (scaled by dz_scale), so a
+    scale applied to the wrong product shows up as a power of two."""
+    sw = act == ACT_SWIGLU
+    X, Hh, A, Au, B, dY, Z, U = _exact_bwd_case(act, np.random.default_rng(9))
+    sdy, sb, sh, sx, sa, sdz = 4.0, 16.0, 2.0, 8.0, 32.0, 64.0
+    q4 = lambda m, s: oracle.fp8_quantize(m, s)[0]
+    unit = oracle.mlp_bwd_fp8(oracle.fp8_encode(dY, "e5m2"), q4(X, 1), q4(Hh, 1), q4(A, 1),
+                              q4(B, 1), Z, act, (1,) * 7, U if sw else None,
+                              q4(Au, 1) if sw else None)
+    sc = oracle.mlp_bwd_fp8(oracle.fp8_quantize(dY, sdy, "e5m2")[0], q4(X, sx), q4(Hh, sh),
+                            q4(A, sa), q4(B, sb), Z, act,
+                            (1 / sdy, 1 / sb, 1 / sh, 1 / sx, 1 / sa, sdz, 1 / sdz),
+                            U if sw else None, q4(Au, sa) if sw else None)
+    for k in ("dZ", "dB", "dA", "dX") + (("dA_up",) if sw else ()):
+        assert np.array_equal(sc[k], unit[k]), k
+    assert np.array_equal(oracle.fp8_decode(sc["dZq"], "e5m2"),
+                          oracle.fp8_decode(unit["dZq"], "e5m2") * sdz)
+    assert sc["dz_amax"] == unit["dz_amax"]
