@@ -78,6 +78,9 @@ def parse():
                    help="1: partial sums on a second stream, overlapping the GEMMs")
     p.add_argument("--sum-workgroups", type=int, default=256,
                    help="workgroup cap of the overlapped partial sums")
+    p.add_argument("--side", type=int, default=1,
+                   help="0: time the step only (no reduce-scatter, accumulation, MoE or FP8 "
+                        "side measurements), as for the profiler's per-kernel summaries")
     p.add_argument("--cpu-tokens", type=int, default=0,
                    help="tokens of the oracle sample (0: sized to ~15 s)")
     return p.parse_args()
@@ -361,7 +364,7 @@ def main():
     # sequence-parallel form of the same exchange (outside the timed step):
     # rank 0's [S/T,B,H] slice of the sum, the reduce-scatter arithmetic
     rs = None
-    if w.S % w.T == 0:
+    if args.side and w.S % w.T == 0:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         slice_out = torch.empty((w.S // w.T) * w.B * w.H, dtype=Ysum.dtype, device=dev)
         for _ in range(3):
@@ -381,7 +384,7 @@ def main():
     # gradient-accumulation form of the backward (weight gradients added
     # into the fp32 buffers), timed beside the plain backward
     acc_cmp = None
-    if w.backward:
+    if args.side and w.backward:
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         reps = 5
         e0.record(stream)
@@ -397,9 +400,9 @@ def main():
         acc_cmp = {"bwd_ms": round(e0.elapsed_time(e1) / reps, 4),
                    "bwd_accum_ms": round(e1.elapsed_time(e2) / reps, 4)}
 
-    moe = moe_dispatch_timing(torch, tp, wl, dev, stream) if args.moe else None
+    moe = moe_dispatch_timing(torch, tp, wl, dev, stream) if (args.side and args.moe) else None
     f8 = f8b = None
-    if (args.fp8 and w.dtype == wl.DT_BF16 and w.H % 128 == 0 and w.Ft % 128 == 0
+    if (args.side and args.fp8 and w.dtype == wl.DT_BF16 and w.H % 128 == 0 and w.Ft % 128 == 0
             and w.N % 128 == 0 and w.backward):
         f8, f8b = fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream)
         f8["bf16_forward_ms_for_comparison"] = round(fwd_ms, 4)
