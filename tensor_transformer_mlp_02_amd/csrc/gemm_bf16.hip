@@ -1691,7 +1691,11 @@ static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols) {
 // FLOP than 32 x 32 x 16 (measured on an MFMA-only loop and on the GEMM
 // k loop), so its cost is scaled by that.
 // Returns 0 (256 x 256), 1 (256 x 224) or 2 (224 x 256).
-constexpr double W16_CYCLE_FACTOR = 1.09;
+#ifndef TP_W16_FACTOR
+#define TP_W16_FACTOR 1.09
+#endif
+constexpr double W16_CYCLE_FACTOR = TP_W16_FACTOR;
+constexpr double W16_PAIR_EXTRA = 1.1;
 static int pick_shape(const GemmArgs& g, int bmode, bool w16_ok) {
   if (!TP_USE_W16 || !w16_ok) return 0;
   const int cus = device_cus();
@@ -1700,9 +1704,12 @@ static int pick_shape(const GemmArgs& g, int bmode, bool w16_ok) {
     return f * (double)((tiles + cus - 1) / cus) * BMT * BNT;
   };
   if (bmode == BMODE_PAIR32) {
+    // the paired 224-wide tiles also pay a heavier epilogue: measured in the
+    // whole step (SwiGLU FC1, 4096 tokens, H = 8192, F/T = 3584), 448
+    // 256-wide tiles in two waves beat 512 224-wide ones by 3 %
     const int split = (int)g.b.split;
     const double c0 = cost(256, 256, count_tiles(g, 256, 128, split));
-    const double c1 = cost(256, 224, count_tiles(g, 256, 112, split));
+    const double c1 = W16_PAIR_EXTRA * cost(256, 224, count_tiles(g, 256, 112, split));
     return c1 < c0 ? 1 : 0;
   }
   const double c0 = cost(256, 256, count_tiles(g, 256, 256, g.N));
