@@ -93,6 +93,16 @@ def gemm_flops(w, N=None):
     return per * n_fwd * (3 if w.backward else 1)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, tokens):
     """The fp64 oracle, as it stands, on a token sample of the workload."""
     import numpy as np
@@ -105,6 +115,49 @@ def cpu_baseline(w, tokens):
         oracle.mlp_bwd(d["X"], d["A"], d["B"], w.act, d["dY"], f, d["A_up"])
     dt = time.perf_counter() - t0
     return dt, gemm_flops(w, tokens)
+
+
+def grouped_expert_timing(torch, tp, wl, stream, reps=20):
+    """The grouped local experts on the grouped-expert workload (16384 tokens
+    routed top-2 over 64 experts, local experts 0..7, H = 4096, F = 1408,
+    SwiGLU): forward and backward launches over the ragged rows, in
+    algorithmic TFLOP/s (18 H F per row for forward + backward)."""
+    from tensor_transformer_mlp_02_amd.tensors import to_device, ExpertBuffers
+    w5 = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
+    g = wl.gen_grouped_inputs(w5)
+    off = g["offsets"]
+    R, E, H, F = int(off[-1]), len(off) - 1, w5.H, w5.F
+    d = {k: to_device(g[k]) for k in ("X_perm", "Wg", "Wu", "Wd", "dY_perm")}
+    desc = dict(H=H, F=F, E=E, dtype=wl.DT_BF16)
+    buf = ExpertBuffers(desc, off)
+
+    def fwd():
+        tp.tp_grouped_expert_fwd(desc, off, d["X_perm"], d["Wg"], d["Wu"], d["Wd"], buf.Z,
+                                 buf.H, buf.Y, stream=stream)
+
+    def bwd():
+        tp.tp_grouped_expert_bwd(desc, off, d["X_perm"], d["Wg"], d["Wu"], d["Wd"], buf.Z,
+                                 buf.H, d["dY_perm"], buf.dX, buf.dWg, buf.dWu, buf.dWd,
+                                 buf.ws, buf.ws_bytes, stream=stream)
+    fwd(); bwd()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        fwd()
+    ev[1].record(stream)
+    for _ in range(reps):
+        bwd()
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    f_ms = ev[0].elapsed_time(ev[1]) / reps
+    b_ms = ev[1].elapsed_time(ev[2]) / reps
+    f_fl, b_fl = 6.0 * H * F * R, 12.0 * H * F * R
+    tf = (f_fl + b_fl) / ((f_ms + b_ms) * 1e-3) / 1e12
+    return {"rows": R, "experts": E, "rows_per_expert": [int(x) for x in off[1:] - off[:-1]],
+            "H": H, "F": F, "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "fwd_tflops": round(f_fl / (f_ms * 1e-3) / 1e12, 1),
+            "bwd_tflops": round(b_fl / (b_ms * 1e-3) / 1e12, 1),
+            "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def moe_dispatch_timing(torch, tp, wl, dev, stream, reps=20):
@@ -401,6 +454,7 @@ def main():
                    "bwd_accum_ms": round(e1.elapsed_time(e2) / reps, 4)}
 
     moe = moe_dispatch_timing(torch, tp, wl, dev, stream) if (args.side and args.moe) else None
+    grouped = grouped_expert_timing(torch, tp, wl, stream) if (args.side and args.moe) else None
     f8 = f8b = None
     if (args.side and args.fp8 and w.dtype == wl.DT_BF16 and w.H % 128 == 0 and w.Ft % 128 == 0
             and w.N % 128 == 0 and w.backward):
@@ -453,7 +507,10 @@ def main():
                            "seeded stand-ins",
                    "partial_sums": ("second stream, overlapping the GEMMs, at most %d "
                                     "workgroups" % args.sum_workgroups) if args.overlap
-                                   else "in order on the compute stream"},
+                                   else "in order on the compute stream",
+                   "act_derivative": "epilogue of the dY B^T GEMM (dZ written once)",
+                   "caches": "each step's two partial sums move 1.1 GB through HBM, more than "
+                             "the 256 MB Infinity Cache, so every step's GEMMs start cold"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "kernel": "bf16 MFMA GEMM with fused epilogues (%d launches per step)" % n_gemm,
@@ -477,6 +534,7 @@ def main():
         "reduce_scatter_rank0": rs,
         "grad_accumulation": acc_cmp,
         "moe_dispatch_combine": moe,
+        "grouped_experts": grouped,
         "fp8_forward": f8,
         "fp8_backward": f8b,
     }
@@ -496,6 +554,7 @@ def main():
             "kind": "oracle",
             "sample": f"fp64 oracle, forward+backward of the same shard on {tokens} of "
                       f"{w.N} tokens ({fl / 1e9:.1f} GFLOP in {dt:.1f} s)",
+            "cpu": cpu_model(),
         }
     print(json.dumps(line), flush=True)
 
