@@ -354,7 +354,8 @@ int tp_mlp_shard_fwd_fp8(const tp_mlp_desc *desc, const void *Xq, const void *Aq
  *
  * tp_mlp_shard_bwd_fp8: one shard's backward on FP8 codes: gradients E5M2,
  * weights and activations E4M3 ([P1] §8.2), fp32 accumulate.  N, H and
- * F_shard multiples of 128; desc->dtype TP_BF16.  Codes (1 byte each):
+ * F_shard multiples of 128, N at most 2^22; desc->dtype TP_BF16.  Codes
+ * (1 byte each):
  *   dYq [N,H], dYq_t [H,N]   dY's E5M2 codes and their transpose
  *   Xq_t [H,N], Hq_t [F_shard,N]   transposed E4M3 codes of X and H (the
  *                            forward's H_q, transposed)

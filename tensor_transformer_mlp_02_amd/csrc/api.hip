@@ -97,6 +97,9 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// tokens of the FP8 backward: its weight-gradient GEMMs contract over the
+// tokens of K-contiguous code rows, 256 rows x N bytes per 32-bit tile offset
+constexpr int64_t kMaxFp8Tokens = (int64_t)1 << 22;
 // Largest leading dimension (H, and the Z_save width 2 F_shard): the bf16
 // kernels address one 256-row tile through 32-bit buffer offsets, so
 // 256 rows x ld x 2 bytes must stay below 2^31.
@@ -753,6 +756,9 @@ int tp_mlp_shard_bwd_fp8(const tp_mlp_desc* desc, const void* dYq, const void* d
   if (s.dtype != TP_BF16) return fail(TP_ERR_DTYPE, "the FP8 backward reads bf16 Z and writes bf16 dX");
   if (s.H % 128 || s.Ft % 128 || s.N % 128)
     return fail(TP_ERR_SHAPE, "N, H and F_shard must be multiples of 128 for the FP8 backward");
+  // the weight-gradient GEMMs read 256 rows of N codes through 32-bit offsets
+  if (s.N > kMaxFp8Tokens)
+    return fail(TP_ERR_SHAPE, "the FP8 backward takes at most %lld tokens", (long long)kMaxFp8Tokens);
   const bool sw = s.act == TP_ACT_SWIGLU;
   const size_t N = (size_t)s.N, H = (size_t)s.H, Ft = (size_t)s.Ft, zw = sw ? 2 * Ft : Ft;
   Buf in[] = {{dYq, N * H, "dYq"}, {dYq_t, N * H, "dYq_t"}, {Xq_t, N * H, "Xq_t"},

@@ -299,6 +299,7 @@ def test_fp8_backward_argument_checks():
     assert Bw(dict(d, dtype=tp.TP_F32)) == E_DTYPE
     assert Bw(dict(d, S=200)) == E_SHAPE                # tokens a multiple of 128
     assert Bw(dict(d, F_shard=136)) == E_SHAPE
+    assert Bw(dict(d, S=(1 << 22) + 128)) == E_SHAPE    # token limit of the code rows
     assert Bw(d, Auq=addr(6)) == E_SHAPE                # GeLU takes no up weight
     sw = dict(d, act=tp.TP_ACT_SWIGLU)
     assert Bw(sw, dA_up=None) == E_NULL

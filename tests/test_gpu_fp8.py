@@ -394,3 +394,30 @@ def test_fp8_backward_swiglu_shard_sampled():
     top_v = float(oracle.fp8_decode(np.array([top], np.uint8), "e5m2")[0])
     want = amax * BWD_SCALES["dz"]
     assert abs(top_v - want) <= 0.125 * want
+
+
+def test_fp8_backward_empty_batch():
+    """N = 0: no rows to differentiate; the weight gradients are empty sums
+    (zero) and max |dZ| is 0."""
+    H, Ft = 256, 128
+    for act in (wl.ACT_SWIGLU, wl.ACT_GELU_TANH):
+        sw = act == wl.ACT_SWIGLU
+        e = torch.empty(64 * 16, dtype=torch.uint8, device="cuda")
+        ptr = [e.data_ptr() + 16 * k for k in range(8)]
+        Aq = torch.full((H, Ft), 0x38, dtype=torch.uint8, device="cuda")
+        Auq = torch.full((H, Ft), 0x38, dtype=torch.uint8, device="cuda") if sw else None
+        Bq = torch.full((Ft, H), 0x38, dtype=torch.uint8, device="cuda")
+        qs = torch.ones(7, dtype=torch.float32, device="cuda")
+        dA = torch.full((H, Ft), 7.0, device="cuda")
+        dAu = torch.full((H, Ft), 7.0, device="cuda") if sw else None
+        dB = torch.full((Ft, H), 7.0, device="cuda")
+        amax = torch.full((1,), -1.0, device="cuda")
+        desc = dict(S=0, B=1, H=H, F_shard=Ft, T=1, act=act, dtype=wl.DT_BF16)
+        print(f"[gpu] fp8 backward empty batch {desc}", flush=True)
+        tp.tp_mlp_shard_bwd_fp8(desc, ptr[0], ptr[1], ptr[2], ptr[3], Aq, Auq, Bq, ptr[4], qs,
+                                ptr[5], dA, dAu, dB, ptr[6], ptr[7], amax)
+        torch.cuda.synchronize()
+        for t in (dA, dAu, dB):
+            if t is not None:
+                assert not torch.any(t)
+        assert float(amax[0]) == 0.0
