@@ -185,8 +185,9 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& g, int block, i
   while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
   const int local = tile - g.tile_off[e];
   const int lo = g.row_off[e], hi = g.row_off[e + 1];
-  const int rows = (g.ragged == RAGGED_M) ? hi - lo : g.M;
-  const int tiles_m = (rows + BM - 1) / BM;
+  // tile rows of this problem as the launcher counted them (a ragged
+  // problem's last few rows may be left to the thin-tile launch)
+  const int tiles_m = (g.tile_off[e + 1] - g.tile_off[e]) / g.tiles_n;
   const int group = local / (RASTER_G * g.tiles_n);
   const int first_m = group * RASTER_G;
   const int gm = min(RASTER_G, tiles_m - first_m);

@@ -1626,6 +1626,202 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_f8(GemmArgs g) {
       acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
+// ---- thin kernel: the last few rows of a ragged problem --------------------
+//
+// A grouped launch whose problems have row counts just above a multiple of
+// 256 (e.g. 518..530 rows per expert) would spend a whole 256-row tile on
+// each problem's last few rows, and those tiles make a second wave.  The
+// launcher gives such a remainder (at most THIN_MAX rows) to this kernel
+// instead: tiles of 32 rows x 256 columns, 4 wavefronts of 32 x 64 (two
+// 32 x 32 x 16 MFMA blocks each), a ring of THIN_STAGES shared-memory
+// stages of [A 32 x 64 | B 256 x 64] filled by direct loads.  A k tile is
+// only 8 MFMAs per wavefront, far less than a load's latency, so the loads
+// run THIN_STAGES - 1 tiles ahead.  Each output element
+// gets the same chain of 32 x 32 x 16 MFMAs over the same 16-wide k steps
+// as in the 256 x 256 kernels, so its value is the one those compute.
+// Requirements (checked by the launcher): opA K-contiguous, a k split a
+// multiple of 64.
+constexpr int THIN_M = 32;
+constexpr int THIN_MAX = 64;
+constexpr int THIN_NT = 256;
+constexpr int THIN_STAGES = 4;
+// direct loads per wavefront and k tile: one for A, eight for B
+constexpr int THIN_LOADS = 9;
+
+template <bool B_KMAJOR, int BMODE, int EPI, typename OutT>
+__global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
+  constexpr int A_ELEMS = THIN_M * BK;
+  constexpr int BUF_ELEMS = A_ELEMS + BN * BK;
+  constexpr int NS = THIN_STAGES;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[NS * BUF_ELEMS];
+  constexpr bool PAIR = EPI == EPI_SWIGLU_FWD;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r_lane = lane & 31, c_lane = lane >> 5;
+
+  // problem e's thin tiles cover its rows from the last multiple of 256 on
+  const int tile = xcd_logical_block(blockIdx.x, gridDim.x);
+  int e = 0;
+  while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
+  const int local = tile - g.tile_off[e];
+  const int lo = g.row_off[e], hi = g.row_off[e + 1];
+  const int tiles_m = (g.tile_off[e + 1] - g.tile_off[e]) / g.tiles_n;
+  TileCoord tc;
+  tc.e = e;
+  tc.tm = local % tiles_m;
+  tc.tn = local / tiles_m;
+  tc.m_begin = lo + ((hi - lo) / BM) * BM + tc.tm * THIN_M;
+  tc.m_end = hi;
+  tc.k_begin = 0;
+  tc.k_end = g.K;
+
+  const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
+  const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
+  const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
+  const int64_t lda = g.a.ld, ldb = g.b.ld, bsplit = g.b.split;
+  const int Ncols = g.N, Ktot = g.K;
+  const EpiArgs ea = g.epi;
+  const int n_base = tc.tn * BN;
+  const int m_rows = tc.m_end - tc.m_begin;
+  const int nk = (Ktot + BK - 1) / BK;
+  const int half_w = wave >> 1;
+
+  // k tile from k0 into buffer `buf` (k0 >= K masks every load)
+  auto issue = [&](int k0, bf16_t* buf) {
+    {
+      // A: 32 rows x 64 k, one 1 KiB direct load per wavefront
+      const int r = wave * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const int k = k0 + c * 8;
+      const uint32_t off = (r < m_rows && k < Ktot)
+                               ? (uint32_t)(((int64_t)r * lda + k) * 2) : OOB_OFF;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a0 + (int64_t)tc.m_begin * lda),
+                                               (lds_void_t*)(buf + wave * 512), 16, off, 0, 0,
+                                               0);
+    }
+    bf16_t* tb = buf + A_ELEMS;
+    if constexpr (B_KMAJOR) {
+      if constexpr (BMODE == BMODE_KSPLIT) {
+        const bool first = k0 < bsplit;
+        const bf16_t* bp = first ? b0 : b1;
+        const int kl = first ? k0 : k0 - (int)bsplit;
+        const int lim = first ? (int)bsplit : Ktot - (int)bsplit;
+        direct_kmajor<4, 0, 8>(make_rsrc(bp + (int64_t)n_base * ldb), ldb, Ncols - n_base, kl,
+                               k0 < Ktot ? lim : 0, tb, wave, lane);
+      } else {
+        direct_kmajor<4, 0, 8>(make_rsrc(b0 + (int64_t)n_base * ldb), ldb, Ncols - n_base, k0,
+                               Ktot, tb, wave, lane);
+      }
+    } else if constexpr (BMODE == BMODE_PAIR32) {
+      // half 0: gate columns, half 1: up columns, both f = 128 tn ..
+      const bf16_t* bp = half_w ? b1 : b0;
+      direct_mn<4, 0, 8>(make_rsrc(bp + (int64_t)k0 * ldb), ldb, tc.tn * 128, (int)bsplit,
+                         Ktot - k0, tb, wave, lane);
+    } else {
+      direct_mn<4, 0, 8>(make_rsrc(b0 + (int64_t)k0 * ldb), ldb, n_base + half_w * 128, Ncols,
+                         Ktot - k0, tb, wave, lane);
+    }
+  };
+  // tile column of this wavefront's opB block j
+  auto b_col = [&](int j) { return PAIR ? j * (BN / 2) + wave * 32 : wave * 64 + j * 32; };
+
+  f32x16_t acc[2];
+  acc[0] = (f32x16_t)(0.0f);
+  acc[1] = (f32x16_t)(0.0f);
+
+  // prologue: tiles 0 .. NS-2 in flight, wait for tile 0
+  if (nk > 0) {
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t) issue(t * BK, lds + t * BUF_ELEMS);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * THIN_LOADS) : "memory");
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bf16_t* cur = lds + (kt % NS) * BUF_ELEMS;
+    // tile kt + NS - 1 refills the stage of tile kt - 1, which every
+    // wavefront finished reading before the last barrier (past the end:
+    // masked loads, zeros, never read)
+    issue((kt + NS - 1) * BK, lds + ((kt + NS - 1) % NS) * BUF_ELEMS);
+    const bf16_t* tb = cur + A_ELEMS;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int c = 2 * s + c_lane;
+      const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(cur + lds_off(r_lane, c));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8_t fb;
+        if constexpr (B_KMAJOR)
+          fb = *reinterpret_cast<const bf16x8_t*>(tb + lds_off(b_col(j) + r_lane, c));
+        else
+          fb = frag_mn(tb, b_col(j), 16 * s, lane);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc[j], 0, 0, 0);
+      }
+    }
+    // tile kt + 1 has landed for every wavefront (tiles kt + 2 .. kt + NS - 1
+    // stay in flight), and `cur` is free
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * THIN_LOADS) : "memory");
+    __syncthreads();
+  }
+  // the masked loads of the stages past the end land before the stage
+  // area is reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // stage the 32 x 256 fp32 sums row-major (paired SwiGLU: gate sums in
+  // columns 0..127, up sums in 128..255), then each thread takes 8
+  // consecutive columns of a row
+  float* stage = reinterpret_cast<float*>(lds);
+  static_assert(THIN_M * EQ_PITCH * 4 <= (int)sizeof(lds), "staging rows exceed shared memory");
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col0 = b_col(j);
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const f32x4_t v = {acc[j][4 * gq], acc[j][4 * gq + 1], acc[j][4 * gq + 2],
+                         acc[j][4 * gq + 3]};
+      *reinterpret_cast<f32x4_t*>(stage + r_lane * EQ_PITCH + col0 + 8 * gq + 4 * c_lane) = v;
+    }
+  }
+  __syncthreads();
+  if constexpr (PAIR) {
+    constexpr int CH = THIN_M * (BN / 2) / 8;
+#pragma unroll
+    for (int kk = 0; kk < CH / THIN_NT; ++kk) {
+      const int k = kk * THIN_NT + tid;
+      const int row = k >> 4, cc = (k & 15) * 8;
+      const int64_t m = tc.m_begin + row;
+      const int64_t f = (int64_t)tc.tn * (BN / 2) + cc;
+      if (m < tc.m_end && f < ea.split) {
+        float gv[8], uv[8];
+        const float* src = stage + row * EQ_PITCH + cc;
+        *reinterpret_cast<f32x4_t*>(gv) = *reinterpret_cast<const f32x4_t*>(src);
+        *reinterpret_cast<f32x4_t*>(gv + 4) = *reinterpret_cast<const f32x4_t*>(src + 4);
+        *reinterpret_cast<f32x4_t*>(uv) = *reinterpret_cast<const f32x4_t*>(src + BN / 2);
+        *reinterpret_cast<f32x4_t*>(uv + 4) = *reinterpret_cast<const f32x4_t*>(src + BN / 2 + 4);
+        epilogue_swiglu8<bf16_t>(ea, m, f, gv, uv);
+      }
+    }
+  } else {
+    constexpr int CH = THIN_M * BN / 8;
+#pragma unroll
+    for (int kk = 0; kk < CH / THIN_NT; ++kk) {
+      const int k = kk * THIN_NT + tid;
+      const int row = k >> 5, cc = (k & 31) * 8;
+      const int64_t m = tc.m_begin + row;
+      const int64_t n = (int64_t)n_base + cc;
+      if (m < tc.m_end && n < Ncols) {
+        float cv[8];
+        const float* src = stage + row * EQ_PITCH + cc;
+        *reinterpret_cast<f32x4_t*>(cv) = *reinterpret_cast<const f32x4_t*>(src);
+        *reinterpret_cast<f32x4_t*>(cv + 4) = *reinterpret_cast<const f32x4_t*>(src + 4);
+        epilogue8<EPI, bf16_t, OutT>(ea, tc.e, m, n, cv);
+      }
+    }
+  }
+}
+
 }  // namespace mfma256
 
 // ---------------------------------------------------------------------------
@@ -1645,18 +1841,81 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_f8(GemmArgs g) {
 #define TP_USE_W16 1
 #endif
 
-static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols) {
+#ifndef TP_USE_THIN
+#define TP_USE_THIN 1
+#endif
+
+// Tile rows of a problem with `rows` rows.  With thin_max > 0 a remainder of
+// at most thin_max rows past the last whole BM-row tile is left to the thin
+// kernel (which then covers it; see fill_thin).
+static int row_tiles(int rows, int BM, int thin_max) {
+  if (thin_max > 0) {
+    const int rem = rows % BM;
+    return rows / BM + (rem > thin_max ? 1 : 0);
+  }
+  return (rows + BM - 1) / BM;
+}
+
+static int problem_rows(const GemmArgs& g, int e) {
+  return g.ragged == RAGGED_M ? g.row_off[e + 1] - g.row_off[e] : g.M;
+}
+
+static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols, int thin_max = 0) {
   g.tiles_n = (n_cols + BN - 1) / BN;
   g.tile_off[0] = 0;
+  for (int e = 0; e < g.E; ++e)
+    g.tile_off[e + 1] = g.tile_off[e] + row_tiles(problem_rows(g, e), BM, thin_max) * g.tiles_n;
+}
+
+// Thin tiles (32 rows) of the remainders the 256-row tiles leave out.
+static void fill_thin(GemmArgs& g, int tiles_n) {
+  using namespace mfma256;
+  g.tiles_n = tiles_n;
+  g.tile_off[0] = 0;
   for (int e = 0; e < g.E; ++e) {
-    int rows;
-    if (g.ragged == RAGGED_M)
-      rows = g.row_off[e + 1] - g.row_off[e];
-    else
-      rows = g.M;
-    int tm = (rows + BM - 1) / BM;
-    g.tile_off[e + 1] = g.tile_off[e] + tm * g.tiles_n;
+    const int rem = problem_rows(g, e) % BM;
+    const int tm = (rem > 0 && rem <= THIN_MAX) ? (rem + THIN_M - 1) / THIN_M : 0;
+    g.tile_off[e + 1] = g.tile_off[e] + tm * tiles_n;
   }
+}
+
+// Whether a launch leaves remainders to the thin kernel: ragged rows (the
+// grouped experts), a K-contiguous opA, a k split on a 64 boundary, and at
+// least one problem whose rows end a few rows past a multiple of 256.
+static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols, int thin_max = 0);
+static int device_cus();
+
+// The thin launch is issued only when it takes the 256-row launch down by
+// at least one wave of tiles over the compute units; otherwise its tiles
+// would only add time after a launch that already fits.
+template <bool AK, bool BK_, int BMODE>
+static int thin_rows_max(const GemmArgs& g) {
+  using namespace mfma256;
+  if (!TP_USE_THIN || !AK || (BMODE == BMODE_PAIR32 && BK_) || g.ragged != RAGGED_M) return 0;
+  if (BMODE == BMODE_KSPLIT && g.b.split % BK != 0) return 0;
+  bool any = false;
+  for (int e = 0; e < g.E; ++e) {
+    const int rem = problem_rows(g, e) % BM;
+    any = any || (rem > 0 && rem <= THIN_MAX);
+  }
+  if (!any) return 0;
+  const bool pair = BMODE == BMODE_PAIR32;
+  const int n_cols = pair ? (int)g.b.split : g.N, bn = pair ? BN / 2 : BN;
+  const int cus = device_cus();
+  const int w_plain = (count_tiles(g, BM, bn, n_cols, 0) + cus - 1) / cus;
+  const int w_thin = (count_tiles(g, BM, bn, n_cols, THIN_MAX) + cus - 1) / cus;
+  return w_thin < w_plain ? THIN_MAX : 0;
+}
+
+template <bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_thin(GemmArgs& g, hipStream_t stream) {
+  using namespace mfma256;
+  fill_thin(g, BMODE == BMODE_PAIR32 ? (int)((g.b.split + 127) / 128) : (g.N + BN - 1) / BN);
+  const int blocks = g.tile_off[g.E];
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_thin<BK_, BMODE, EPI, OutT>), dim3(blocks), dim3(THIN_NT), 0, stream,
+                     g);
+  return hipGetLastError();
 }
 
 // compute units of the current device (cached per device)
@@ -1675,13 +1934,10 @@ static int device_cus() {
 }
 
 // tiles of a BMT x BNT grid (n_cols: columns as tiled)
-static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols) {
+static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols, int thin_max) {
   const int tn = (n_cols + BNT - 1) / BNT;
   int t = 0;
-  for (int e = 0; e < g.E; ++e) {
-    const int rows = g.ragged == RAGGED_M ? g.row_off[e + 1] - g.row_off[e] : g.M;
-    t += ((rows + BMT - 1) / BMT) * tn;
-  }
+  for (int e = 0; e < g.E; ++e) t += row_tiles(problem_rows(g, e), BMT, thin_max) * tn;
   return t;
 }
 
@@ -1696,7 +1952,9 @@ static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols) {
 #endif
 constexpr double W16_CYCLE_FACTOR = TP_W16_FACTOR;
 constexpr double W16_PAIR_EXTRA = 1.1;
-static int pick_shape(const GemmArgs& g, int bmode, bool w16_ok) {
+// thin_max: remainders left to the thin kernel by 256-row tiles (the
+// 224-row shape covers every row itself).
+static int pick_shape(const GemmArgs& g, int bmode, bool w16_ok, int thin_max) {
   if (!TP_USE_W16 || !w16_ok) return 0;
   const int cus = device_cus();
   auto cost = [&](int BMT, int BNT, int tiles) {
@@ -1708,20 +1966,21 @@ static int pick_shape(const GemmArgs& g, int bmode, bool w16_ok) {
     // whole step (SwiGLU FC1, 4096 tokens, H = 8192, F/T = 3584), 448
     // 256-wide tiles in two waves beat 512 224-wide ones by 3 %
     const int split = (int)g.b.split;
-    const double c0 = cost(256, 256, count_tiles(g, 256, 128, split));
-    const double c1 = W16_PAIR_EXTRA * cost(256, 224, count_tiles(g, 256, 112, split));
+    const double c0 = cost(256, 256, count_tiles(g, 256, 128, split, thin_max));
+    const double c1 =
+        W16_PAIR_EXTRA * cost(256, 224, count_tiles(g, 256, 112, split, thin_max));
     return c1 < c0 ? 1 : 0;
   }
-  const double c0 = cost(256, 256, count_tiles(g, 256, 256, g.N));
-  const double c1 = cost(256, 224, count_tiles(g, 256, 224, g.N));
-  const double c2 = cost(224, 256, count_tiles(g, 224, 256, g.N));
+  const double c0 = cost(256, 256, count_tiles(g, 256, 256, g.N, thin_max));
+  const double c1 = cost(256, 224, count_tiles(g, 256, 224, g.N, thin_max));
+  const double c2 = thin_max > 0 ? 1e300 : cost(224, 256, count_tiles(g, 224, 256, g.N));
   if (c1 < c0 && c1 <= c2) return 1;
   if (c2 < c0) return 2;
   return 0;
 }
 
 template <bool AK, bool BK_, int BMODE, int EPI, typename OutT, int BMT, int BNT>
-static hipError_t launch_w16(GemmArgs& g, hipStream_t stream) {
+static hipError_t launch_w16(GemmArgs& g, hipStream_t stream, int thin_max) {
   if constexpr (BMODE == BMODE_KSPLIT || (BMODE == BMODE_PAIR32 && (BK_ || BNT != 224))) {
     return hipErrorInvalidValue;
   } else {
@@ -1730,7 +1989,7 @@ static hipError_t launch_w16(GemmArgs& g, hipStream_t stream) {
       const int tiles_n = (int)((g.b.split + 111) / 112);
       g.N = tiles_n * 224;
     }
-    fill_tiles(g, BMT, BNT, g.N);
+    fill_tiles(g, BMT, BNT, g.N, BMT == 256 ? thin_max : 0);
     const int blocks = g.tile_off[g.E];
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL((mfma256::gemm_w16<AK, BK_, BMODE, EPI, OutT, BMT, BNT>), dim3(blocks),
@@ -1739,16 +1998,37 @@ static hipError_t launch_w16(GemmArgs& g, hipStream_t stream) {
   }
 }
 
+// The 256-row launch, then (for grouped problems ending a few rows past a
+// multiple of 256) the thin launch over those rows.
+template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_rows(GemmArgs& g, hipStream_t stream, int thin_max);
+
 template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
+  const int thin_max = thin_rows_max<AK, BK_, BMODE>(g);
+  if constexpr (AK && !(BMODE == BMODE_PAIR32 && BK_)) {
+    if (thin_max > 0) {
+      GemmArgs gt = g;  // the main launch rewrites its tile table (and N)
+      hipError_t he = launch_rows<NW, AK, BK_, BMODE, EPI, OutT>(g, stream, thin_max);
+      if (he != hipSuccess) return he;
+      return launch_thin<BK_, BMODE, EPI, OutT>(gt, stream);
+    }
+  }
+  return launch_rows<NW, AK, BK_, BMODE, EPI, OutT>(g, stream, 0);
+}
+
+template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_rows(GemmArgs& g, hipStream_t stream, int thin_max) {
   {
     const bool k_whole = (!AK && !BK_) || g.K % mfma256::BK == 0;
     const bool w16_ok = k_whole && BMODE != BMODE_KSPLIT && !(BMODE == BMODE_PAIR32 && BK_);
-    switch (pick_shape(g, BMODE, w16_ok)) {
-      case 1: return launch_w16<AK, BK_, BMODE, EPI, OutT, 256, 224>(g, stream);
+    switch (pick_shape(g, BMODE, w16_ok, thin_max)) {
+      case 1: return launch_w16<AK, BK_, BMODE, EPI, OutT, 256, 224>(g, stream, thin_max);
       case 2:
+        // (never chosen when remainders go to the thin kernel: 224-row
+        // tiles would cover those rows too)
         if constexpr (BMODE != BMODE_PAIR32)
-          return launch_w16<AK, BK_, BMODE, EPI, OutT, 224, 256>(g, stream);
+          if (thin_max == 0) return launch_w16<AK, BK_, BMODE, EPI, OutT, 224, 256>(g, stream, 0);
         break;
       default: break;
     }
@@ -1759,7 +2039,7 @@ static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
     n_cols = ((int)((g.b.split + 31) / 32)) * 64;
     g.N = n_cols;
   }
-  fill_tiles(g, mfma256::BM, mfma256::BN, n_cols);
+  fill_tiles(g, mfma256::BM, mfma256::BN, n_cols, thin_max);
   int blocks = g.tile_off[g.E];
   if (blocks == 0) return hipSuccess;
   // the hand-ordered kernel needs whole 64-wide k tiles of K-contiguous

@@ -439,6 +439,70 @@ def test_grouped_small_ragged_with_empty_expert():
             assert_close(f"{k}[{e}]", g[e], b[k][e], tol)   # expert 1: exact zeros
 
 
+def test_grouped_row_remainders_whole_tensors():
+    """Experts whose rows end 1, 3, 33, 64, 65 or 200 rows past a multiple of
+    256, one expert empty, k extents in whole 64-wide tiles: whole tensors
+    against the oracle.  (Every product here fits the compute units in one
+    wave with 256-row tiles, so no remainder goes to the 32-row tiles.)"""
+    counts = [257, 576, 3, 0, 289, 200, 321]
+    H, F = 512, 192
+    w, d = _grouped_inputs(counts, H, F, seed=82)
+    dev, buf = _run_grouped(d, H, F)
+    f = oracle.grouped_fwd(d["X_perm"], d["offsets"], d["Wg"], d["Wu"], d["Wd"])
+    b = oracle.grouped_bwd(d["X_perm"], d["offsets"], d["Wg"], d["Wu"], d["Wd"],
+                           d["dY_perm"], f)
+    tol = TOL[wl.DT_BF16]
+    Z = f64(to_host(buf.Z))
+    assert_close("G", Z[:, :F], f["G"], tol)
+    assert_close("U", Z[:, F:], f["U"], tol)
+    assert_close("H", f64(to_host(buf.H)), f["H"], tol)
+    assert_close("Y", f64(to_host(buf.Y)), f["Y"], tol)
+    assert_close("dX", f64(to_host(buf.dX)), b["dX"], tol)
+    for k in ("dWg", "dWu", "dWd"):
+        g = to_host(getattr(buf, k))
+        for e in range(len(counts)):
+            assert_close(f"{k}[{e}]", g[e], b[k][e], tol)
+
+
+def test_grouped_thin_tiles_remove_a_wave():
+    """Rows ending 33, 64, 3 and 1 rows past a multiple of 256 (two experts
+    empty), H = F = 4096: the 256-row tiles of every row-ragged product
+    (FC1, FC2, dH, dX) fill whole waves of 256 compute units only if those
+    remainders go to the 32-row tiles, so the thin launches run.  Every
+    remainder row and 16 more rows per expert against the oracle; weight
+    gradients on 32 sampled columns over all rows."""
+    counts = [1024 + 33, 0, 2048 + 64, 3, 1024 + 1, 0]
+    H = F = 4096
+    w, d = _grouped_inputs(counts, H, F, seed=83)
+    dev, buf = _run_grouped(d, H, F)
+    tol = TOL[wl.DT_BF16]
+    off = d["offsets"]
+    rows, sub_off = [], [0]
+    for e in range(len(counts)):
+        lo, hi = int(off[e]), int(off[e + 1])
+        tail = lo + ((hi - lo) // 256) * 256
+        r = np.union1d(np.arange(tail, hi), lo + sample_idx(hi - lo, 16)) if hi > lo else []
+        rows.extend(list(r)); sub_off.append(sub_off[-1] + len(r))
+    rows = np.array(rows, dtype=np.int64)
+    f = oracle.grouped_fwd(d["X_perm"][rows], sub_off, d["Wg"], d["Wu"], d["Wd"])
+    b = oracle.grouped_bwd(d["X_perm"][rows], sub_off, d["Wg"], d["Wu"], d["Wd"],
+                           d["dY_perm"][rows], f)
+    Z = f64(to_host(buf.Z[rows]))
+    assert_close("G rows", Z[:, :F], f["G"], tol)
+    assert_close("U rows", Z[:, F:], f["U"], tol)
+    assert_close("H rows", f64(to_host(buf.H[rows])), f["H"], tol)
+    assert_close("Y rows", f64(to_host(buf.Y[rows])), f["Y"], tol)
+    assert_close("dX rows", f64(to_host(buf.dX[rows])), b["dX"], tol)
+    cols = sample_idx(F, 32)
+    Wg = np.ascontiguousarray(d["Wg"][:, :, cols]); Wu = np.ascontiguousarray(d["Wu"][:, :, cols])
+    Wd = np.ascontiguousarray(d["Wd"][:, cols, :])
+    fn = oracle.grouped_fwd(d["X_perm"], off, Wg, Wu, Wd)
+    bn = oracle.grouped_bwd(d["X_perm"], off, Wg, Wu, Wd, d["dY_perm"], fn)
+    assert_close("dWg cols", to_host(buf.dWg[:, :, cols]), bn["dWg"], tol)
+    assert_close("dWu cols", to_host(buf.dWu[:, :, cols]), bn["dWu"], tol)
+    assert_close("dWd rows", to_host(buf.dWd[:, cols, :]), bn["dWd"], tol)
+
+
 def test_grouped_rows_equal_dense_shard_bitwise():
     """Expert e's rows through the grouped call equal tp_mlp_shard_fwd/bwd
     (SwiGLU, T = 1) on those rows alone, bit for bit: the same tiles run the
