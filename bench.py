@@ -6,7 +6,12 @@ One step = the whole shard path on one batch, inputs resident in HBM:
   backward  dH (+ activation-derivative epilogue), dB, dA, dX tp_mlp_shard_bwd
   sum       dX = dX_0 + 7 stand-in partials                   tp_partial_sum
 The metric counts the GEMM FLOPs only (2 M N K per product: 9 products for
-SwiGLU, 6 for GeLU); the step time includes the two partial sums.
+SwiGLU, 6 for GeLU); the step time includes the two partial sums.  The sums
+stand in for the rank's all-reduces and, like communication, run by default
+on a second stream beside the GEMMs that do not depend on them (sum(Y) beside
+the backward, sum(dX) beside the next forward); --overlap 0 runs the step in
+order on one stream, and the default run also times that form
+("serial_step").
 
 Prints one JSON line.  Only one GPU is used: --gpus above 1 exits.
 """
@@ -74,8 +79,9 @@ def parse():
                    help="1: also time the FP8 forward and backward at the same shape")
     p.add_argument("--moe", type=int, default=1,
                    help="1: also time the MoE dispatch/combine row moves")
-    p.add_argument("--overlap", type=int, default=0,
-                   help="1: partial sums on a second stream, overlapping the GEMMs")
+    p.add_argument("--overlap", type=int, default=1,
+                   help="1: partial sums on a second stream, overlapping the GEMMs; "
+                        "0: everything in order on one stream")
     p.add_argument("--sum-workgroups", type=int, default=256,
                    help="workgroup cap of the overlapped partial sums")
     p.add_argument("--side", type=int, default=1,
@@ -333,48 +339,77 @@ def main():
     count = w.N * w.H
     stream = torch.cuda.current_stream()
 
-    # The partial sums stand in for the all-reduces of a real rank, so they
-    # run on a second stream (default priority) like communication would:
-    # sum(Y) overlaps the backward GEMMs and sum(dX) the next forward, on the
-    # compute units the GEMM grids leave idle.  Events keep every dependency:
-    # a sum starts after the GEMM that wrote its input, and the next write of
-    # Y (forward) or dX (backward) waits for the sum that reads it.
-    side = torch.cuda.Stream(device=dev) if args.overlap else stream
+    # The partial sums stand in for the all-reduces of a real rank, so by
+    # default they run on a second stream (default priority) like
+    # communication would: sum(Y) overlaps the backward GEMMs and sum(dX) the
+    # next forward, each on a capped number of workgroups.  Events keep every
+    # dependency: a sum starts after the GEMM that wrote its input, and the
+    # next write of Y (forward) or dX (backward) waits for the sum that reads
+    # it.  overlap=False runs everything in order on the compute stream.
+    def run_steps(overlap, steps, warmup):
+        side = torch.cuda.Stream(device=dev) if overlap else stream
 
-    def psum(*a, stream):
-        # overlapped: a few workgroups, so the sum takes only the compute
-        # units the GEMM grids leave free
-        if args.overlap:
-            return tp.tp_partial_sum_capped(*a, args.sum_workgroups, stream=stream)
-        return tp.tp_partial_sum(*a, stream=stream)
-    y_ready, dx_ready = torch.cuda.Event(), torch.cuda.Event()
-    y_read, dx_read = torch.cuda.Event(), torch.cuda.Event()
-    y_read.record(side)
-    dx_read.record(side)
-
-    def step(ev=None):
-        if ev: ev[0].record(stream)
-        stream.wait_event(y_read)
-        tp.tp_mlp_shard_fwd(desc, X, A, Au, B, buf.Z, buf.H, buf.Y, stream=stream)
-        if ev: ev[1].record(stream)
-        y_ready.record(stream)
-        side.wait_event(y_ready)
-        if ev: ev[5].record(side)
-        psum(w.dtype, w.T, [buf.Y] + stand, count, Ysum, stream=side)
-        if ev: ev[6].record(side)
+        def psum(*a, stream):
+            if overlap:
+                return tp.tp_partial_sum_capped(*a, args.sum_workgroups, stream=stream)
+            return tp.tp_partial_sum(*a, stream=stream)
+        y_ready, dx_ready = torch.cuda.Event(), torch.cuda.Event()
+        y_read, dx_read = torch.cuda.Event(), torch.cuda.Event()
         y_read.record(side)
+        dx_read.record(side)
+
+        def step(ev=None):
+            if ev: ev[0].record(stream)
+            stream.wait_event(y_read)
+            tp.tp_mlp_shard_fwd(desc, X, A, Au, B, buf.Z, buf.H, buf.Y, stream=stream)
+            if ev: ev[1].record(stream)
+            y_ready.record(stream)
+            side.wait_event(y_ready)
+            if ev: ev[5].record(side)
+            psum(w.dtype, w.T, [buf.Y] + stand, count, Ysum, stream=side)
+            if ev: ev[6].record(side)
+            y_read.record(side)
+            if w.backward:
+                if ev: ev[2].record(stream)
+                stream.wait_event(dx_read)
+                tp.tp_mlp_shard_bwd(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
+                                    buf.dA_up, buf.dB, buf.ws, buf.ws_bytes, stream=stream)
+                if ev: ev[3].record(stream)
+                dx_ready.record(stream)
+                side.wait_event(dx_ready)
+                if ev: ev[7].record(side)
+                psum(w.dtype, w.T, [buf.dX] + stand, count, dXsum, stream=side)
+                if ev: ev[8].record(side)
+                dx_read.record(side)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        # timed region: K whole steps between two events on the compute
+        # stream (the last one after it has waited for the side stream);
+        # per-call events on each stream split the time between the GEMM
+        # calls and the sums
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(steps)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        side.wait_event(t_start)
+        for k in range(steps):
+            step(evs[k])
+        done = torch.cuda.Event()
+        done.record(side)
+        stream.wait_event(done)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms = t_start.elapsed_time(t_end) / steps
+        fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        ps = [e[5].elapsed_time(e[6]) for e in evs]
+        bwd_ms = 0.0
         if w.backward:
-            if ev: ev[2].record(stream)
-            stream.wait_event(dx_read)
-            tp.tp_mlp_shard_bwd(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
-                                buf.dA_up, buf.dB, buf.ws, buf.ws_bytes, stream=stream)
-            if ev: ev[3].record(stream)
-            dx_ready.record(stream)
-            side.wait_event(dx_ready)
-            if ev: ev[7].record(side)
-            psum(w.dtype, w.T, [buf.dX] + stand, count, dXsum, stream=side)
-            if ev: ev[8].record(side)
-            dx_read.record(side)
+            bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+            ps += [e[7].elapsed_time(e[8]) for e in evs]
+        return ms, fwd_ms, bwd_ms, float(np.mean(ps))
 
     # calibration copy (one partial sum of a single buffer = a copy)
     n_calib = CALIB_COPY_BYTES // 2
@@ -384,35 +419,11 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: K whole steps between two events on the compute stream
-    # (the last one after it has waited for the side stream); per-call events
-    # on each stream split the time between the GEMM calls and the sums
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    side.wait_event(t_start)
-    for k in range(args.steps):
-        step(evs[k])
-    done = torch.cuda.Event()
-    done.record(side)
-    stream.wait_event(done)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms = total_ms / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ps_ms = [e[5].elapsed_time(e[6]) for e in evs]
-    bwd_ms = 0.0
-    if w.backward:
-        bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-        ps_ms += [e[7].elapsed_time(e[8]) for e in evs]
-    ps_ms = float(np.mean(ps_ms))
+    ms, fwd_ms, bwd_ms, ps_ms = run_steps(bool(args.overlap), args.steps, args.warmup)
+    # the same steps in order on one stream: the GEMMs and the sums undisturbed
+    serial = None
+    if args.overlap and args.side:
+        serial = run_steps(False, args.steps, args.warmup)
 
     # sequence-parallel form of the same exchange (outside the timed step):
     # rank 0's [S/T,B,H] slice of the sum, the reduce-scatter arithmetic
@@ -531,6 +542,17 @@ def main():
                          "partial_sum_each": round(ps_ms, 4),
                          "partial_sum_GBps": round(ps_gbs, 1),
                          "partial_sum_hbm_frac": round(ps_gbs / PEAK_HBM_GBS, 4)},
+        "serial_step": None if serial is None else {
+            "note": "the same steps in order on one stream (sums not overlapped)",
+            "ms_per_step": round(serial[0], 4),
+            "tflops": round(flops / (serial[0] * 1e-3) / 1e12, 2),
+            "gemm_tflops": round(flops / ((serial[1] + serial[2]) * 1e-3) / 1e12, 2),
+            "gemm_frac_of_bf16_peak": round(
+                flops / ((serial[1] + serial[2]) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "breakdown_ms": {"fwd_gemms": round(serial[1], 4), "bwd_gemms": round(serial[2], 4),
+                             "partial_sum_each": round(serial[3], 4)},
+            "partial_sum_GBps": round(ps_bytes / (serial[3] * 1e-3) / 1e9, 1),
+            "partial_sum_hbm_frac": round(ps_bytes / (serial[3] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "reduce_scatter_rank0": rs,
         "grad_accumulation": acc_cmp,
         "moe_dispatch_combine": moe,
