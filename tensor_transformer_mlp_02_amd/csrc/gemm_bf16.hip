@@ -1879,15 +1879,15 @@ static void fill_thin(GemmArgs& g, int tiles_n) {
   }
 }
 
-// Whether a launch leaves remainders to the thin kernel: ragged rows (the
-// grouped experts), a K-contiguous opA, a k split on a 64 boundary, and at
-// least one problem whose rows end a few rows past a multiple of 256.
 static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols, int thin_max = 0);
 static int device_cus();
 
-// The thin launch is issued only when it takes the 256-row launch down by
-// at least one wave of tiles over the compute units; otherwise its tiles
-// would only add time after a launch that already fits.
+// Whether a launch leaves remainders to the thin kernel: ragged rows (the
+// grouped experts), a K-contiguous opA, a k split on a 64 boundary, at
+// least one problem whose rows end a few rows past a multiple of 256, and
+// the 256-row launch one wave of tiles over the compute units shorter for
+// it (otherwise the thin tiles would only add time after a launch that
+// already fits).
 template <bool AK, bool BK_, int BMODE>
 static int thin_rows_max(const GemmArgs& g) {
   using namespace mfma256;
