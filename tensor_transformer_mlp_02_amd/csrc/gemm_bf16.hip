@@ -1626,33 +1626,43 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_f8(GemmArgs g) {
       acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
-// ---- thin kernel: the last few rows of a ragged problem --------------------
+// ---- short-row kernel: 32 or 128 rows of a ragged problem ----------------
 //
-// A grouped launch whose problems have row counts just above a multiple of
-// 256 (e.g. 518..530 rows per expert) would spend a whole 256-row tile on
-// each problem's last few rows, and those tiles make a second wave.  The
-// launcher gives such a remainder (at most THIN_MAX rows) to this kernel
-// instead: tiles of 32 rows x 256 columns, 4 wavefronts of 32 x 64 (two
-// 32 x 32 x 16 MFMA blocks each), a ring of THIN_STAGES shared-memory
-// stages of [A 32 x 64 | B 256 x 64] filled by direct loads.  A k tile is
-// only 8 MFMAs per wavefront, far less than a load's latency, so the loads
-// run THIN_STAGES - 1 tiles ahead.  Each output element
-// gets the same chain of 32 x 32 x 16 MFMAs over the same 16-wide k steps
-// as in the 256 x 256 kernels, so its value is the one those compute.
+// Tiles of TM rows x 256 columns (TM = 32 or 128), 4 wavefronts side by side,
+// each TM x 64 (TM/32 x 2 blocks of 32 x 32 x 16 MFMAs), a ring of NS
+// shared-memory stages of [A TM x 64 | B 256 x 64] filled by direct loads
+// that run NS - 1 k tiles ahead.  Each output element gets the same chain of
+// 32 x 32 x 16 MFMAs over the same 16-wide k steps as in the 256 x 256
+// kernels, so its value is the one those compute.  Two uses in grouped
+// launches:
+//  - TAIL (TM = 32): problems whose rows end a few rows past a multiple of
+//    256 (e.g. 518..530 rows per expert) would spend a whole 256-row tile on
+//    each problem's last rows, and those tiles make a second wave.  The
+//    launcher gives such a remainder (at most THIN_MAX rows) to these tiles.
+//  - all rows (TM = 128): a launch whose 256-row tiles leave many compute
+//    units idle in its only wave (e.g. 147 tiles on 256 CUs) runs on twice
+//    as many half-height tiles instead.
 // Requirements (checked by the launcher): opA K-contiguous, a k split a
 // multiple of 64.
 constexpr int THIN_M = 32;
 constexpr int THIN_MAX = 64;
 constexpr int THIN_NT = 256;
-constexpr int THIN_STAGES = 4;
-// direct loads per wavefront and k tile: one for A, eight for B
-constexpr int THIN_LOADS = 9;
+constexpr int ROWS_M = 128;
 
-template <bool B_KMAJOR, int BMODE, int EPI, typename OutT>
-__global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
-  constexpr int A_ELEMS = THIN_M * BK;
+template <int TM>
+struct RowsCfg {
+  static constexpr int FM = TM / 32;          // fragment rows per wavefront
+  static constexpr int NS = TM == 32 ? 4 : 3;  // stages (144 KiB either way)
+  static constexpr int A_LOADS = TM / 32;     // 1 KiB A loads per wavefront
+  static constexpr int LOADS = A_LOADS + 8;   // direct loads per wavefront, k tile
+};
+
+template <int TM, bool TAIL, bool B_KMAJOR, int BMODE, int EPI, typename OutT>
+__global__ __launch_bounds__(THIN_NT, 1) void gemm_rows(GemmArgs g) {
+  using C = RowsCfg<TM>;
+  constexpr int FM = C::FM, NS = C::NS;
+  constexpr int A_ELEMS = TM * BK;
   constexpr int BUF_ELEMS = A_ELEMS + BN * BK;
-  constexpr int NS = THIN_STAGES;
   __shared__ __attribute__((aligned(1024))) bf16_t lds[NS * BUF_ELEMS];
   constexpr bool PAIR = EPI == EPI_SWIGLU_FWD;
 
@@ -1661,7 +1671,8 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r_lane = lane & 31, c_lane = lane >> 5;
 
-  // problem e's thin tiles cover its rows from the last multiple of 256 on
+  // TAIL: problem e's tiles cover its rows from the last multiple of 256 on;
+  // otherwise all of its rows
   const int tile = xcd_logical_block(blockIdx.x, gridDim.x);
   int e = 0;
   while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
@@ -1672,7 +1683,7 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
   tc.e = e;
   tc.tm = local % tiles_m;
   tc.tn = local / tiles_m;
-  tc.m_begin = lo + ((hi - lo) / BM) * BM + tc.tm * THIN_M;
+  tc.m_begin = lo + (TAIL ? ((hi - lo) / BM) * BM : 0) + tc.tm * TM;
   tc.m_end = hi;
   tc.k_begin = 0;
   tc.k_end = g.K;
@@ -1690,15 +1701,17 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
 
   // k tile from k0 into buffer `buf` (k0 >= K masks every load)
   auto issue = [&](int k0, bf16_t* buf) {
-    {
-      // A: 32 rows x 64 k, one 1 KiB direct load per wavefront
-      const int r = wave * 8 + (lane >> 3);
+    // A: TM rows x 64 k, TM / 32 direct loads of 1 KiB (8 rows) per wavefront
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      const int blk = wave * C::A_LOADS + i;
+      const int r = blk * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz(r);
       const int k = k0 + c * 8;
       const uint32_t off = (r < m_rows && k < Ktot)
                                ? (uint32_t)(((int64_t)r * lda + k) * 2) : OOB_OFF;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(a0 + (int64_t)tc.m_begin * lda),
-                                               (lds_void_t*)(buf + wave * 512), 16, off, 0, 0,
+                                               (lds_void_t*)(buf + blk * 512), 16, off, 0, 0,
                                                0);
     }
     bf16_t* tb = buf + A_ELEMS;
@@ -1727,15 +1740,18 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
   // tile column of this wavefront's opB block j
   auto b_col = [&](int j) { return PAIR ? j * (BN / 2) + wave * 32 : wave * 64 + j * 32; };
 
-  f32x16_t acc[2];
-  acc[0] = (f32x16_t)(0.0f);
-  acc[1] = (f32x16_t)(0.0f);
+  f32x16_t acc[FM][2];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    acc[i][0] = (f32x16_t)(0.0f);
+    acc[i][1] = (f32x16_t)(0.0f);
+  }
 
   // prologue: tiles 0 .. NS-2 in flight, wait for tile 0
   if (nk > 0) {
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t) issue(t * BK, lds + t * BUF_ELEMS);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * THIN_LOADS) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * C::LOADS) : "memory");
   }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
@@ -1748,7 +1764,10 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       const int c = 2 * s + c_lane;
-      const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(cur + lds_off(r_lane, c));
+      bf16x8_t fa[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(cur + lds_off(i * 32 + r_lane, c));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8_t fb;
@@ -1756,12 +1775,14 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
           fb = *reinterpret_cast<const bf16x8_t*>(tb + lds_off(b_col(j) + r_lane, c));
         else
           fb = frag_mn(tb, b_col(j), 16 * s, lane);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa, acc[j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa[i], acc[i][j], 0, 0, 0);
       }
     }
     // tile kt + 1 has landed for every wavefront (tiles kt + 2 .. kt + NS - 1
     // stay in flight), and `cur` is free
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * THIN_LOADS) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * C::LOADS) : "memory");
     __syncthreads();
   }
   // the masked loads of the stages past the end land before the stage
@@ -1769,24 +1790,28 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // stage the 32 x 256 fp32 sums row-major (paired SwiGLU: gate sums in
+  // stage the TM x 256 fp32 sums row-major (paired SwiGLU: gate sums in
   // columns 0..127, up sums in 128..255), then each thread takes 8
   // consecutive columns of a row
   float* stage = reinterpret_cast<float*>(lds);
-  static_assert(THIN_M * EQ_PITCH * 4 <= (int)sizeof(lds), "staging rows exceed shared memory");
+  static_assert(TM * EQ_PITCH * 4 <= (int)sizeof(lds), "staging rows exceed shared memory");
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col0 = b_col(j);
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const f32x4_t v = {acc[j][4 * gq], acc[j][4 * gq + 1], acc[j][4 * gq + 2],
-                         acc[j][4 * gq + 3]};
-      *reinterpret_cast<f32x4_t*>(stage + r_lane * EQ_PITCH + col0 + 8 * gq + 4 * c_lane) = v;
+    for (int j = 0; j < 2; ++j) {
+      const int col0 = b_col(j);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4_t v = {acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                           acc[i][j][4 * gq + 3]};
+        *reinterpret_cast<f32x4_t*>(stage + (i * 32 + r_lane) * EQ_PITCH + col0 + 8 * gq +
+                                    4 * c_lane) = v;
+      }
     }
   }
   __syncthreads();
   if constexpr (PAIR) {
-    constexpr int CH = THIN_M * (BN / 2) / 8;
+    constexpr int CH = TM * (BN / 2) / 8;
 #pragma unroll
     for (int kk = 0; kk < CH / THIN_NT; ++kk) {
       const int k = kk * THIN_NT + tid;
@@ -1804,7 +1829,7 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_thin(GemmArgs g) {
       }
     }
   } else {
-    constexpr int CH = THIN_M * BN / 8;
+    constexpr int CH = TM * BN / 8;
 #pragma unroll
     for (int kk = 0; kk < CH / THIN_NT; ++kk) {
       const int k = kk * THIN_NT + tid;
@@ -1867,20 +1892,34 @@ static void fill_tiles(GemmArgs& g, int BM, int BN, int n_cols, int thin_max = 0
     g.tile_off[e + 1] = g.tile_off[e] + row_tiles(problem_rows(g, e), BM, thin_max) * g.tiles_n;
 }
 
-// Thin tiles (32 rows) of the remainders the 256-row tiles leave out.
-static void fill_thin(GemmArgs& g, int tiles_n) {
+// Short-row tiles (TM rows): with `tail`, of the remainders the 256-row
+// tiles leave out (at most THIN_MAX rows past a multiple of 256); without,
+// of every row.
+static int short_row_tiles(int rows, int TM, bool tail) {
   using namespace mfma256;
+  if (!tail) return (rows + TM - 1) / TM;
+  const int rem = rows % BM;
+  return (rem > 0 && rem <= THIN_MAX) ? (rem + TM - 1) / TM : 0;
+}
+
+static void fill_short(GemmArgs& g, int TM, bool tail, int tiles_n) {
   g.tiles_n = tiles_n;
   g.tile_off[0] = 0;
-  for (int e = 0; e < g.E; ++e) {
-    const int rem = problem_rows(g, e) % BM;
-    const int tm = (rem > 0 && rem <= THIN_MAX) ? (rem + THIN_M - 1) / THIN_M : 0;
-    g.tile_off[e + 1] = g.tile_off[e] + tm * tiles_n;
-  }
+  for (int e = 0; e < g.E; ++e)
+    g.tile_off[e + 1] = g.tile_off[e] + short_row_tiles(problem_rows(g, e), TM, tail) * tiles_n;
 }
 
 static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols, int thin_max = 0);
 static int device_cus();
+
+// The short-row kernel's requirements: ragged rows (the grouped experts), a
+// K-contiguous opA, a k split on a 64 boundary.
+template <bool AK, bool BK_, int BMODE>
+static bool short_rows_ok(const GemmArgs& g) {
+  using namespace mfma256;
+  if (!TP_USE_THIN || !AK || (BMODE == BMODE_PAIR32 && BK_) || g.ragged != RAGGED_M) return false;
+  return BMODE != BMODE_KSPLIT || g.b.split % BK == 0;
+}
 
 // Whether a launch leaves remainders to the thin kernel: ragged rows (the
 // grouped experts), a K-contiguous opA, a k split on a 64 boundary, at
@@ -1891,8 +1930,7 @@ static int device_cus();
 template <bool AK, bool BK_, int BMODE>
 static int thin_rows_max(const GemmArgs& g) {
   using namespace mfma256;
-  if (!TP_USE_THIN || !AK || (BMODE == BMODE_PAIR32 && BK_) || g.ragged != RAGGED_M) return 0;
-  if (BMODE == BMODE_KSPLIT && g.b.split % BK != 0) return 0;
+  if (!short_rows_ok<AK, BK_, BMODE>(g)) return 0;
   bool any = false;
   for (int e = 0; e < g.E; ++e) {
     const int rem = problem_rows(g, e) % BM;
@@ -1907,14 +1945,36 @@ static int thin_rows_max(const GemmArgs& g) {
   return w_thin < w_plain ? THIN_MAX : 0;
 }
 
-template <bool BK_, int BMODE, int EPI, typename OutT>
-static hipError_t launch_thin(GemmArgs& g, hipStream_t stream) {
+// Whether the whole launch runs on 128-row tiles instead: when its 256-row
+// tiles (with any thin remainder tiles) take whole waves over the compute
+// units that half-height tiles take fewer of, by tile area.  The half-height
+// kernel reads more shared memory per MFMA, so its area counts 1.5 times.
+constexpr double ROWS128_FACTOR = 1.5;
+template <bool AK, bool BK_, int BMODE>
+static bool rows128_pays(const GemmArgs& g, int thin_max) {
   using namespace mfma256;
-  fill_thin(g, BMODE == BMODE_PAIR32 ? (int)((g.b.split + 127) / 128) : (g.N + BN - 1) / BN);
+  if (!short_rows_ok<AK, BK_, BMODE>(g)) return false;
+  const bool pair = BMODE == BMODE_PAIR32;
+  const int n_cols = pair ? (int)g.b.split : g.N, bn = pair ? BN / 2 : BN;
+  const int tn = (n_cols + bn - 1) / bn;
+  const int cus = device_cus();
+  int t128 = 0;
+  for (int e = 0; e < g.E; ++e) t128 += short_row_tiles(problem_rows(g, e), ROWS_M, false) * tn;
+  const double c256 = (double)((count_tiles(g, BM, bn, n_cols, thin_max) + cus - 1) / cus) *
+                      BM * BN;
+  const double c128 = ROWS128_FACTOR * (double)((t128 + cus - 1) / cus) * ROWS_M * BN;
+  return c128 < c256;
+}
+
+template <int TM, bool TAIL, bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_short(GemmArgs& g, hipStream_t stream) {
+  using namespace mfma256;
+  fill_short(g, TM, TAIL,
+             BMODE == BMODE_PAIR32 ? (int)((g.b.split + 127) / 128) : (g.N + BN - 1) / BN);
   const int blocks = g.tile_off[g.E];
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_thin<BK_, BMODE, EPI, OutT>), dim3(blocks), dim3(THIN_NT), 0, stream,
-                     g);
+  hipLaunchKernelGGL((gemm_rows<TM, TAIL, BK_, BMODE, EPI, OutT>), dim3(blocks), dim3(THIN_NT),
+                     0, stream, g);
   return hipGetLastError();
 }
 
@@ -2007,11 +2067,13 @@ template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   const int thin_max = thin_rows_max<AK, BK_, BMODE>(g);
   if constexpr (AK && !(BMODE == BMODE_PAIR32 && BK_)) {
+    if (rows128_pays<AK, BK_, BMODE>(g, thin_max))
+      return launch_short<mfma256::ROWS_M, false, BK_, BMODE, EPI, OutT>(g, stream);
     if (thin_max > 0) {
       GemmArgs gt = g;  // the main launch rewrites its tile table (and N)
       hipError_t he = launch_rows<NW, AK, BK_, BMODE, EPI, OutT>(g, stream, thin_max);
       if (he != hipSuccess) return he;
-      return launch_thin<BK_, BMODE, EPI, OutT>(gt, stream);
+      return launch_short<mfma256::THIN_M, true, BK_, BMODE, EPI, OutT>(gt, stream);
     }
   }
   return launch_rows<NW, AK, BK_, BMODE, EPI, OutT>(g, stream, 0);
