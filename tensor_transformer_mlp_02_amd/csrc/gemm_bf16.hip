@@ -1753,7 +1753,10 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_rows(GemmArgs g) {
     for (int t = 0; t < NS - 1; ++t) issue(t * BK, lds + t * BUF_ELEMS);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * C::LOADS) : "memory");
   }
-  __syncthreads();
+  // a plain s_barrier: __syncthreads() would also drain the loads of the
+  // tiles behind tile 0; the empty asm keeps every shared-memory read below it
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   for (int kt = 0; kt < nk; ++kt) {
     const bf16_t* cur = lds + (kt % NS) * BUF_ELEMS;
     // tile kt + NS - 1 refills the stage of tile kt - 1, which every
@@ -1761,29 +1764,39 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_rows(GemmArgs g) {
     // masked loads, zeros, never read)
     issue((kt + NS - 1) * BK, lds + ((kt + NS - 1) % NS) * BUF_ELEMS);
     const bf16_t* tb = cur + A_ELEMS;
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
+    // fragments of k step s go to slot s % 2: the next step's reads are in
+    // flight while this step's MFMAs run
+    bf16x8_t fa[2][FM], fb[2][2];
+    auto read_step = [&](int s, int slot) {
       const int c = 2 * s + c_lane;
-      bf16x8_t fa[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(cur + lds_off(i * 32 + r_lane, c));
+        fa[slot][i] = *reinterpret_cast<const bf16x8_t*>(cur + lds_off(i * 32 + r_lane, c));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bf16x8_t fb;
         if constexpr (B_KMAJOR)
-          fb = *reinterpret_cast<const bf16x8_t*>(tb + lds_off(b_col(j) + r_lane, c));
+          fb[slot][j] = *reinterpret_cast<const bf16x8_t*>(tb + lds_off(b_col(j) + r_lane, c));
         else
-          fb = frag_mn(tb, b_col(j), 16 * s, lane);
+          fb[slot][j] = frag_mn(tb, b_col(j), 16 * s, lane);
+      }
+    };
+    read_step(0, 0);
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      if (s + 1 < BK / 16) read_step(s + 1, (s + 1) & 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb, fa[i], acc[i][j], 0, 0, 0);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][j], fa[s & 1][i],
+                                                              acc[i][j], 0, 0, 0);
     }
-    // tile kt + 1 has landed for every wavefront (tiles kt + 2 .. kt + NS - 1
-    // stay in flight), and `cur` is free
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NS - 2) * C::LOADS) : "memory");
-    __syncthreads();
+    // after the barrier, tile kt + 1 has landed for every wavefront (tiles
+    // kt + 2 .. kt + NS - 1 stay in flight) and every read of `cur` has
+    // completed (lgkmcnt), so the next trip may refill it
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((NS - 2) * C::LOADS) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   }
   // the masked loads of the stages past the end land before the stage
   // area is reused
