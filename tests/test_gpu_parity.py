@@ -322,6 +322,33 @@ def test_run_to_run_bitwise_determinism():
         assert torch.equal(getattr(b1, k), getattr(b2, k)), k
 
 
+def test_grouped_run_to_run_bitwise_determinism():
+    """The grouped launches at the grouped workload's shape (4079 rows over
+    8 experts, H = 4096, F = 1408: 256-row tiles, 32-row remainder tiles for
+    FC2 and dX, 128-row tiles for dH), twice on the same inputs: every
+    output bit for bit."""
+    counts = [506, 528, 522, 530, 467, 525, 483, 518]
+    H, F, E = 4096, 1408, len(counts)
+    off = np.zeros(E + 1, np.int64); off[1:] = np.cumsum(counts)
+    R = int(off[-1])
+    g = torch.Generator(device="cuda"); g.manual_seed(5)
+    def rn(shape, std):
+        return (torch.randn(shape, device="cuda", generator=g) * std).to(torch.bfloat16)
+    X, dY = rn((R, H), 1.0), rn((R, H), 1e-2)
+    Wg, Wu, Wd = rn((E, H, F), 0.02), rn((E, H, F), 0.02), rn((E, F, H), 0.02)
+    desc = dict(H=H, F=F, E=E, dtype=wl.DT_BF16)
+    outs = []
+    for _ in range(2):
+        b = ExpertBuffers(desc, off)
+        tp.tp_grouped_expert_fwd(desc, off, X, Wg, Wu, Wd, b.Z, b.H, b.Y)
+        tp.tp_grouped_expert_bwd(desc, off, X, Wg, Wu, Wd, b.Z, b.H, dY, b.dX, b.dWg, b.dWu,
+                                 b.dWd, b.ws, b.ws_bytes)
+        outs.append(b)
+    _sync()
+    for k in ("Z", "H", "Y", "dX", "dWg", "dWu", "dWd"):
+        assert torch.equal(getattr(outs[0], k), getattr(outs[1], k)), k
+
+
 # ----------------------------------------------------------------------------
 # full workloads on sampled outputs
 # ----------------------------------------------------------------------------
