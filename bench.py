@@ -520,8 +520,10 @@ def main():
                                     "workgroups" % args.sum_workgroups) if args.overlap
                                    else "in order on the compute stream",
                    "act_derivative": "epilogue of the dY B^T GEMM (dZ written once)",
-                   "caches": "each step's two partial sums move 1.1 GB through HBM, more than "
-                             "the 256 MB Infinity Cache, so every step's GEMMs start cold"},
+                   "caches": "nothing is warmed on purpose: each step's two partial sums "
+                             "stream 1.1 GB through HBM (non-temporal), and each GEMM finds "
+                             "in the 256 MB Infinity Cache only what the launches before it "
+                             "left there"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
             "kernel": "bf16 MFMA GEMM with fused epilogues (%d launches per step)" % n_gemm,
