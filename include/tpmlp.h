@@ -17,6 +17,16 @@
  * mappings).  Shapes follow "Megatron Core 带读" §02: hidden [S,B,H],
  * column output [S,B,O/p], row input [S,B,I/p], row partial [S,B,O].
  *
+ * Citations below use these keys for the pages they come from:
+ *   [P1] "Megatron-LM 源码精读——大模型并行训练全景" (sections §三 3.1-3.5
+ *        tensor parallelism, §五 5.2 gradient-accumulation fusion, §七
+ *        the model's MLP, §八 8.2 FP8); a bare "§" with no key is [P1]
+ *   [P2] "Megatron-LM and 3D Parallelism" (context only)
+ *   [P3] "Megatron Core 带读" (§02 tensor shapes, §06 sequence
+ *        parallelism, §09 MoE dispatch / combine, §10 FP8)
+ *   [P4] "Megatron-LM 源码精读" docs index ("MoE 层与 Expert Parallelism":
+ *        grouped-GEMM expert compute)
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * Layout:    every matrix is row-major and contiguous.  [S,B,H] hidden
@@ -270,7 +280,6 @@ int tp_grouped_expert_bwd_accum(const tp_expert_desc *desc, const int64_t *offse
                                 void *dX_perm, float *dWg, float *dWu, float *dWd,
                                 void *workspace, size_t ws_bytes, void *stream);
 
-/* Message of the last failed call on this thread ("" if none). */
 /*
  * MoE token dispatch and combine around the grouped local experts
  * ([P3] §09: router scores -> top-k experts -> tokens sent to their
@@ -380,6 +389,9 @@ int tp_mlp_shard_bwd_fp8(const tp_mlp_desc *desc, const void *dYq, const void *d
                          void *dX_partial, float *dA, float *dA_up, float *dB, void *dZq,
                          void *dZq_t, float *dz_amax, void *stream);
 
+/* Message of the last failed call on this thread ("" if none; a
+ * successful call clears it).  The pointer stays valid until this thread's
+ * next call into the library. */
 const char *tp_last_error(void);
 
 /* Fixed name of a tp_status value. */

@@ -121,15 +121,32 @@ def lib() -> ctypes.CDLL:
     return L
 
 
-def _ptr(t) -> Optional[int]:
-    """Device address of a tensor (must be contiguous), an int, or None."""
+def _ptr(t, nbytes: Optional[int] = None, name: str = "tensor") -> Optional[int]:
+    """Device address of a tensor, an int (a raw device address, passed as
+    given), or None.  A tensor must be contiguous, live on the current GPU
+    (a host tensor's address would reach a kernel as a device address) and,
+    when nbytes is given, hold at least that many bytes."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+    import torch
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
-        raise ValueError("tensors passed to the library must be contiguous")
+        raise ValueError(f"{name} must be contiguous")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, "
+                         f"{nbytes} needed")
     return t.data_ptr()
+
+
+def _sized(pairs):
+    """_ptr of each (tensor, bytes, name) triple."""
+    return [_ptr(t, n, name) for (t, n, name) in pairs]
 
 
 def _stream(stream) -> Optional[int]:
@@ -167,16 +184,50 @@ def _edesc(desc) -> tp_expert_desc:
     return tp_expert_desc(**desc)
 
 
-def _offsets(offsets: Sequence[int]):
+def _offsets(offsets: Sequence[int], E: int):
+    """Host array of the E+1 row offsets (the library reads exactly E+1)."""
     vals = [int(v) for v in offsets]
+    if len(vals) != E + 1:
+        raise ValueError(f"offsets has {len(vals)} entries, E + 1 = {E + 1} needed")
     return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def _partials(partials, T: int, nbytes: Optional[int]):
+    """Host array of the T partial pointers (the library reads exactly T)."""
+    if partials is None:
+        return None
+    if len(partials) != T:
+        raise ValueError(f"{len(partials)} partials given, T = {T}")
+    return (_vp * T)(*[_ptr(p, nbytes, f"partials[{i}]") for i, p in enumerate(partials)])
+
+
+def _elt(dtype: int) -> int:
+    return 2 if dtype == TP_BF16 else 4
+
+
+def _shard_sizes(d: tp_mlp_desc):
+    """Bytes of each shard tensor the descriptor implies (0 for an invalid
+    descriptor: the library's own checks then report it)."""
+    N, H, Ft = max(d.S, 0) * max(d.B, 0), max(d.H, 0), max(d.F_shard, 0)
+    e = _elt(d.dtype)
+    zw = 2 * Ft if d.act == TP_ACT_SWIGLU else Ft
+    return dict(X=N * H * e, A=H * Ft * e, B=Ft * H * e, Z=N * zw * e, H=N * Ft * e,
+                Y=N * H * e, dA=H * Ft * 4, dB=Ft * H * 4)
+
+
+def _expert_sizes(d: tp_expert_desc, R: int):
+    E, H, F = max(d.E, 0), max(d.H, 0), max(d.F, 0)
+    return dict(X=R * H * 2, W=E * H * F * 2, Z=R * 2 * F * 2, H=R * F * 2, Y=R * H * 2,
+                dW=E * H * F * 4)
 
 
 def tp_mlp_shard_fwd(desc, X, A, A_up, B, Z_save, H_act, Y_partial, stream=None) -> int:
     d = _desc(desc)
-    return _check(lib().tp_mlp_shard_fwd(
-        ctypes.byref(d), _ptr(X), _ptr(A), _ptr(A_up), _ptr(B), _ptr(Z_save),
-        _ptr(H_act), _ptr(Y_partial), _stream(stream)))
+    n = _shard_sizes(d)
+    p = _sized([(X, n["X"], "X"), (A, n["A"], "A"), (A_up, n["A"], "A_up"), (B, n["B"], "B"),
+                (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"),
+                (Y_partial, n["Y"], "Y_partial")])
+    return _check(lib().tp_mlp_shard_fwd(ctypes.byref(d), *p, _stream(stream)))
 
 
 def tp_mlp_shard_bwd_workspace(desc) -> int:
@@ -188,50 +239,55 @@ def tp_mlp_shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_
                      workspace, ws_bytes: int, stream=None, accumulate: bool = False) -> int:
     """accumulate=True calls tp_mlp_shard_bwd_accum (dA, dA_up, dB += ...)."""
     d = _desc(desc)
+    n = _shard_sizes(d)
     fn = lib().tp_mlp_shard_bwd_accum if accumulate else lib().tp_mlp_shard_bwd
-    return _check(fn(
-        ctypes.byref(d), _ptr(X), _ptr(A), _ptr(A_up), _ptr(B), _ptr(Z_save), _ptr(H_act),
-        _ptr(dY), _ptr(dX_partial), _ptr(dA), _ptr(dA_up), _ptr(dB), _ptr(workspace),
-        int(ws_bytes), _stream(stream)))
+    p = _sized([(X, n["X"], "X"), (A, n["A"], "A"), (A_up, n["A"], "A_up"), (B, n["B"], "B"),
+                (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"), (dY, n["Y"], "dY"),
+                (dX_partial, n["X"], "dX_partial"), (dA, n["dA"], "dA"),
+                (dA_up, n["dA"], "dA_up"), (dB, n["dB"], "dB"),
+                (workspace, int(ws_bytes), "workspace")])
+    return _check(fn(ctypes.byref(d), *p, int(ws_bytes), _stream(stream)))
 
 
 def tp_partial_sum(dtype: int, T: int, partials, count: int, out, stream=None) -> int:
-    arr = None
-    if partials is not None:
-        arr = (_vp * max(1, len(partials)))(*[_ptr(p) for p in partials])
-    return _check(lib().tp_partial_sum(int(dtype), int(T), arr, int(count), _ptr(out),
-                                       _stream(stream)))
+    nb = max(int(count), 0) * _elt(dtype)
+    arr = _partials(partials, int(T), nb)
+    return _check(lib().tp_partial_sum(int(dtype), int(T), arr, int(count),
+                                       _ptr(out, nb, "out"), _stream(stream)))
 
 
 def tp_partial_sum_capped(dtype: int, T: int, partials, count: int, out, max_workgroups: int,
                           stream=None) -> int:
-    arr = None
-    if partials is not None:
-        arr = (_vp * max(1, len(partials)))(*[_ptr(p) for p in partials])
-    return _check(lib().tp_partial_sum_capped(int(dtype), int(T), arr, int(count), _ptr(out),
-                                              int(max_workgroups), _stream(stream)))
+    nb = max(int(count), 0) * _elt(dtype)
+    arr = _partials(partials, int(T), nb)
+    return _check(lib().tp_partial_sum_capped(int(dtype), int(T), arr, int(count),
+                                              _ptr(out, nb, "out"), int(max_workgroups),
+                                              _stream(stream)))
 
 
 def tp_partial_sum_scatter(dtype: int, T: int, partials, S: int, B: int, H: int, rank: int,
                            out, stream=None) -> int:
-    arr = None
-    if partials is not None:
-        arr = (_vp * max(1, len(partials)))(*[_ptr(p) for p in partials])
+    full = max(int(S), 0) * max(int(B), 0) * max(int(H), 0) * _elt(dtype)
+    arr = _partials(partials, int(T), full)
+    sl = full // int(T) if int(T) > 0 and int(S) % int(T) == 0 else None
     return _check(lib().tp_partial_sum_scatter(int(dtype), int(T), arr, int(S), int(B), int(H),
-                                               int(rank), _ptr(out), _stream(stream)))
+                                               int(rank), _ptr(out, sl, "out"), _stream(stream)))
 
 
 def tp_grouped_expert_fwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, Y_perm,
                           stream=None) -> int:
     d = _edesc(desc)
-    return _check(lib().tp_grouped_expert_fwd(
-        ctypes.byref(d), _offsets(offsets), _ptr(X_perm), _ptr(Wg), _ptr(Wu), _ptr(Wd),
-        _ptr(Z_save), _ptr(H_act), _ptr(Y_perm), _stream(stream)))
+    off = _offsets(offsets, d.E)
+    n = _expert_sizes(d, int(off[d.E]))
+    p = _sized([(X_perm, n["X"], "X_perm"), (Wg, n["W"], "Wg"), (Wu, n["W"], "Wu"),
+                (Wd, n["W"], "Wd"), (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"),
+                (Y_perm, n["Y"], "Y_perm")])
+    return _check(lib().tp_grouped_expert_fwd(ctypes.byref(d), off, *p, _stream(stream)))
 
 
 def tp_grouped_expert_bwd_workspace(desc, offsets) -> int:
     d = _edesc(desc)
-    return int(lib().tp_grouped_expert_bwd_workspace(ctypes.byref(d), _offsets(offsets)))
+    return int(lib().tp_grouped_expert_bwd_workspace(ctypes.byref(d), _offsets(offsets, d.E)))
 
 
 def tp_grouped_expert_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm,
@@ -239,11 +295,15 @@ def tp_grouped_expert_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_p
                           stream=None, accumulate: bool = False) -> int:
     """accumulate=True calls tp_grouped_expert_bwd_accum (dW* += ...)."""
     d = _edesc(desc)
+    off = _offsets(offsets, d.E)
+    n = _expert_sizes(d, int(off[d.E]))
     fn = lib().tp_grouped_expert_bwd_accum if accumulate else lib().tp_grouped_expert_bwd
-    return _check(fn(
-        ctypes.byref(d), _offsets(offsets), _ptr(X_perm), _ptr(Wg), _ptr(Wu), _ptr(Wd),
-        _ptr(Z_save), _ptr(H_act), _ptr(dY_perm), _ptr(dX_perm), _ptr(dWg), _ptr(dWu),
-        _ptr(dWd), _ptr(workspace), int(ws_bytes), _stream(stream)))
+    p = _sized([(X_perm, n["X"], "X_perm"), (Wg, n["W"], "Wg"), (Wu, n["W"], "Wu"),
+                (Wd, n["W"], "Wd"), (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"),
+                (dY_perm, n["Y"], "dY_perm"), (dX_perm, n["X"], "dX_perm"),
+                (dWg, n["dW"], "dWg"), (dWu, n["dW"], "dWu"), (dWd, n["dW"], "dWd"),
+                (workspace, int(ws_bytes), "workspace")])
+    return _check(fn(ctypes.byref(d), off, *p, int(ws_bytes), _stream(stream)))
 
 
 def tp_mlp_shard_bwd_accum(*args, **kw) -> int:
@@ -255,48 +315,67 @@ def tp_grouped_expert_bwd_accum(*args, **kw) -> int:
 
 
 def tp_moe_permute(dtype: int, N: int, H: int, R: int, row_token, X, X_perm, stream=None) -> int:
-    return _check(lib().tp_moe_permute(int(dtype), int(N), int(H), int(R), _ptr(row_token),
-                                       _ptr(X), _ptr(X_perm), _stream(stream)))
+    e, n, h, r = _elt(dtype), max(int(N), 0), max(int(H), 0), max(int(R), 0)
+    p = _sized([(row_token, r * 4, "row_token"), (X, n * h * e, "X"),
+                (X_perm, r * h * e, "X_perm")])
+    return _check(lib().tp_moe_permute(int(dtype), int(N), int(H), int(R), *p, _stream(stream)))
 
 
 def tp_moe_combine(dtype: int, N: int, H: int, R: int, tok_ptr, tok_rows, row_weight, Y_perm, Y,
                    stream=None) -> int:
-    return _check(lib().tp_moe_combine(int(dtype), int(N), int(H), int(R), _ptr(tok_ptr),
-                                       _ptr(tok_rows), _ptr(row_weight), _ptr(Y_perm), _ptr(Y),
-                                       _stream(stream)))
+    e, n, h, r = _elt(dtype), max(int(N), 0), max(int(H), 0), max(int(R), 0)
+    p = _sized([(tok_ptr, (n + 1) * 4, "tok_ptr"), (tok_rows, r * 4, "tok_rows"),
+                (row_weight, r * 4, "row_weight"), (Y_perm, r * h * e, "Y_perm"),
+                (Y, n * h * e, "Y")])
+    return _check(lib().tp_moe_combine(int(dtype), int(N), int(H), int(R), *p, _stream(stream)))
 
 
 def tp_moe_combine_bwd(dtype: int, N: int, H: int, R: int, row_token, row_weight, dY, Y_perm,
                        dY_perm, d_weight, stream=None) -> int:
-    return _check(lib().tp_moe_combine_bwd(int(dtype), int(N), int(H), int(R), _ptr(row_token),
-                                           _ptr(row_weight), _ptr(dY), _ptr(Y_perm),
-                                           _ptr(dY_perm), _ptr(d_weight), _stream(stream)))
+    e, n, h, r = _elt(dtype), max(int(N), 0), max(int(H), 0), max(int(R), 0)
+    p = _sized([(row_token, r * 4, "row_token"), (row_weight, r * 4, "row_weight"),
+                (dY, n * h * e, "dY"), (Y_perm, r * h * e, "Y_perm"),
+                (dY_perm, r * h * e, "dY_perm"), (d_weight, r * 4, "d_weight")])
+    return _check(lib().tp_moe_combine_bwd(int(dtype), int(N), int(H), int(R), *p,
+                                           _stream(stream)))
 
 
 def tp_fp8_quantize(fmt: int, transpose: bool, rows: int, cols: int, x, scale, q, amax=None,
                     stream=None) -> int:
+    n = max(int(rows), 0) * max(int(cols), 0)
+    p = _sized([(x, n * 2, "x"), (scale, 4, "scale"), (q, n, "q"), (amax, 4, "amax")])
     return _check(lib().tp_fp8_quantize(int(fmt), int(bool(transpose)), int(rows), int(cols),
-                                        _ptr(x), _ptr(scale), _ptr(q), _ptr(amax),
-                                        _stream(stream)))
+                                        *p, _stream(stream)))
 
 
 def tp_mlp_shard_fwd_fp8(desc, Xq, Aq_t, Auq_t, Bq_t, scales, Z_save, H_act, H_q, h_amax,
                          Y_partial, stream=None) -> int:
     d = _desc(desc)
-    return _check(lib().tp_mlp_shard_fwd_fp8(
-        ctypes.byref(d), _ptr(Xq), _ptr(Aq_t), _ptr(Auq_t), _ptr(Bq_t), _ptr(scales),
-        _ptr(Z_save), _ptr(H_act), _ptr(H_q), _ptr(h_amax), _ptr(Y_partial), _stream(stream)))
+    n = _shard_sizes(d)
+    p = _sized([(Xq, n["X"] // 2, "Xq"), (Aq_t, n["A"] // 2, "Aq_t"),
+                (Auq_t, n["A"] // 2, "Auq_t"), (Bq_t, n["B"] // 2, "Bq_t"),
+                (scales, 5 * 4, "scales"), (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"),
+                (H_q, n["H"] // 2, "H_q"), (h_amax, 4, "h_amax"),
+                (Y_partial, n["Y"], "Y_partial")])
+    return _check(lib().tp_mlp_shard_fwd_fp8(ctypes.byref(d), *p, _stream(stream)))
 
 
 def tp_fp8_transpose(rows: int, cols: int, q, q_t, stream=None) -> int:
-    return _check(lib().tp_fp8_transpose(int(rows), int(cols), _ptr(q), _ptr(q_t),
-                                         _stream(stream)))
+    n = max(int(rows), 0) * max(int(cols), 0)
+    return _check(lib().tp_fp8_transpose(int(rows), int(cols), _ptr(q, n, "q"),
+                                         _ptr(q_t, n, "q_t"), _stream(stream)))
 
 
 def tp_mlp_shard_bwd_fp8(desc, dYq, dYq_t, Xq_t, Hq_t, Aq, Auq, Bq, Z_save, scales, dX_partial,
                          dA, dA_up, dB, dZq, dZq_t, dz_amax, stream=None) -> int:
     d = _desc(desc)
-    return _check(lib().tp_mlp_shard_bwd_fp8(
-        ctypes.byref(d), _ptr(dYq), _ptr(dYq_t), _ptr(Xq_t), _ptr(Hq_t), _ptr(Aq), _ptr(Auq),
-        _ptr(Bq), _ptr(Z_save), _ptr(scales), _ptr(dX_partial), _ptr(dA), _ptr(dA_up), _ptr(dB),
-        _ptr(dZq), _ptr(dZq_t), _ptr(dz_amax), _stream(stream)))
+    n = _shard_sizes(d)
+    zq = n["Z"] // 2
+    p = _sized([(dYq, n["Y"] // 2, "dYq"), (dYq_t, n["Y"] // 2, "dYq_t"),
+                (Xq_t, n["X"] // 2, "Xq_t"), (Hq_t, n["H"] // 2, "Hq_t"),
+                (Aq, n["A"] // 2, "Aq"), (Auq, n["A"] // 2, "Auq"), (Bq, n["B"] // 2, "Bq"),
+                (Z_save, n["Z"], "Z_save"), (scales, 7 * 4, "scales"),
+                (dX_partial, n["X"], "dX_partial"), (dA, n["dA"], "dA"),
+                (dA_up, n["dA"], "dA_up"), (dB, n["dB"], "dB"), (dZq, zq, "dZq"),
+                (dZq_t, zq, "dZq_t"), (dz_amax, 4, "dz_amax")])
+    return _check(lib().tp_mlp_shard_bwd_fp8(ctypes.byref(d), *p, _stream(stream)))

@@ -307,3 +307,32 @@ def test_fp8_backward_argument_checks():
     assert Bw(d, amax=addr(16, 2)) == E_ALIGN
     assert Bw(d, dZq=addr(5, 64)) == E_ALIAS            # workspace over Aq
     assert Bw(d, dX=addr(8)) == E_ALIAS                 # dX over Z
+
+
+def test_binding_rejects_host_tensors_and_wrong_table_lengths():
+    """The Python binding refuses what the library cannot check: a host
+    tensor (its address would reach a kernel as a device address), a
+    partials list whose length differs from T, and an offsets list that is
+    not E + 1 long (the library reads exactly T pointers and E + 1 offsets).
+    All raise ValueError before any library call."""
+    import torch
+    d = gelu_desc()
+    x_host = torch.zeros(128 * 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tp.tp_mlp_shard_fwd(d, x_host, addr(2), None, addr(3), addr(4), addr(5), addr(6))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tp.tp_partial_sum(tp.TP_BF16, 1, [x_host], 16, addr(1))
+    with pytest.raises(ValueError, match="partials given"):
+        tp.tp_partial_sum(tp.TP_BF16, 4, [addr(1), addr(2)], 1024, addr(3))
+    with pytest.raises(ValueError, match="partials given"):
+        tp.tp_partial_sum_capped(tp.TP_BF16, 1, [addr(1), addr(2)], 1024, addr(3), 8)
+    with pytest.raises(ValueError, match="partials given"):
+        tp.tp_partial_sum_scatter(tp.TP_BF16, 8, [addr(1)] * 7, 64, 2, 256, 0, addr(3))
+    ed = dict(H=256, F=128, E=4, dtype=tp.TP_BF16)
+    with pytest.raises(ValueError, match="offsets has"):
+        tp.tp_grouped_expert_fwd(ed, [0, 5, 9], addr(1), addr(2), addr(3), addr(4), addr(5),
+                                 addr(6), addr(7))
+    with pytest.raises(ValueError, match="offsets has"):
+        tp.tp_grouped_expert_bwd_workspace(ed, [0, 1, 2, 3, 4, 5])
+    # the right lengths reach the library (which reports the missing GPU)
+    assert tp.tp_grouped_expert_bwd_workspace(ed, [0, 1, 2, 3, 4]) > 0

@@ -145,6 +145,21 @@ def test_fp8_forward_small(act, N):
                f64(to_host(dev["Y"])), act, Ft, float(to_host(dev["amax"])[0]))
 
 
+@pytest.mark.parametrize("act", [wl.ACT_SWIGLU, wl.ACT_GELU_TANH])
+def test_fp8_forward_rounding_scales(act):
+    """Scales that are not powers of two, a different one per tensor (the
+    gate and up weights too): the fused fp32 dequantization factors round,
+    and a scale applied to the wrong product would be off by a non-power-of-
+    two factor.  Against the oracle's forward, whose scale handling is
+    pinned on the CPU at power-of-two and at rounding scales."""
+    N, H, Ft = 300, 256, 384
+    scales = (37.0, 3000.0, 2500.0, 5000.0, 123.0)
+    host, dev = _fwd_case(N, H, Ft, act, scales, seed=5600 + 10 * act)
+    f = _oracle_fwd(host, act, scales)
+    _check_fwd(f, f64(to_host(dev["Z"])), f64(to_host(dev["H"])), to_host(dev["Hq"]),
+               f64(to_host(dev["Y"])), act, Ft, float(to_host(dev["amax"])[0]), hs=scales[4])
+
+
 def test_fp8_forward_swiglu_shard_sampled_rows():
     """The SwiGLU shard shape (4096 tokens, H = 8192, F/T = 3584): sampled
     rows against the oracle (per-row outputs only need their own row of X

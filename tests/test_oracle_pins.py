@@ -599,3 +599,86 @@ def test_fp8_backward_power_of_two_scales_cancel(act):
     assert np.array_equal(oracle.fp8_decode(sc["dZq"], "e5m2"),
                           oracle.fp8_decode(unit["dZq"], "e5m2") * sdz)
     assert sc["dz_amax"] == unit["dz_amax"]
+
+
+def _exact_fwd_case(act, rng):
+    """Forward operands exact in E4M3 at every power-of-two scale used below,
+    chosen so that H lands in E4M3's normal range at both H scales (no
+    subnormal or saturated code, so scaling H by a power of two scales its
+    codes' values exactly): each column of A (and A_up) picks one entry of X,
+    so Z (G, U) lies on the grid +-{0.5, 1, 1.5, 2}."""
+    N, H, F = 9, 16, 8
+    grid = np.array([-2.0, -1.5, -1.0, -0.5, 0.5, 1.0, 1.5, 2.0])
+    X = rng.choice(grid, (N, H))
+    A = np.zeros((H, F)); Au = np.zeros((H, F))
+    A[rng.integers(0, H, F), np.arange(F)] = 1.0
+    Au[rng.integers(0, H, F), np.arange(F)] = 1.0
+    B = rng.integers(-2, 3, (F, H)) / 8.0
+    return X, A, Au, B
+
+
+@pytest.mark.parametrize("act", [ACT_GELU_TANH, ACT_SWIGLU])
+def test_fp8_forward_power_of_two_scales_cancel(act):
+    """Per-tensor scaling of the forward ("Megatron-LM 源码精读——大模型并行训练全景"
+    §八 8.2: one scale per tensor; "Megatron Core 带读" §10: quantize by the
+    scale, FP8 product, dequantize): every tensor quantized with its own
+    power-of-two scale and dequantized by its inverse gives the unit-scale
+    run's Z, U, H, Y bit for bit, and H's codes carry exactly h_scale.  A
+    scale applied to the wrong product, an inverse swapped between the gate
+    and up weights, or FC2 dequantized by h_scale instead of 1/h_scale each
+    move a result by a power of two and fail here."""
+    sw = act == ACT_SWIGLU
+    X, A, Au, B = _exact_fwd_case(act, np.random.default_rng(12))
+    q = lambda m, s: oracle.fp8_quantize(m, s)[0]
+    unit = oracle.mlp_fwd_fp8(q(X, 1), q(A, 1).T, q(B, 1).T, act, (1, 1, 1, 1, 1),
+                              q(Au, 1).T if sw else None)
+    sx, sa, sau, sb, sh = 8.0, 32.0, 2.0, 64.0, 16.0
+    sc = oracle.mlp_fwd_fp8(q(X, sx), q(A, sa).T, q(B, sb).T, act,
+                            (1 / sx, 1 / sa, 1 / sau, 1 / sb, sh), q(Au, sau).T if sw else None)
+    # the codes really changed (the scales reached the quantizer)
+    assert not np.array_equal(q(X, sx), q(X, 1)) and not np.array_equal(q(B, sb), q(B, 1))
+    for k in ("Z", "H", "Y") + (("U",) if sw else ()):
+        assert np.array_equal(sc[k], unit[k]), k
+    hu = oracle.fp8_decode(unit["Hq"])
+    assert np.min(np.abs(hu)) >= 2.0 ** -6 and np.max(np.abs(hu)) * sh <= 448.0
+    assert np.array_equal(oracle.fp8_decode(sc["Hq"]), hu * sh)
+    assert sc["h_amax"] == unit["h_amax"]
+    # and the scaled run is not the unit one by accident: a wrong FC2 scale
+    # (h_scale * b_inv) would give Y * h_scale^2
+    wrong = oracle.mlp_fwd_fp8(q(X, sx), q(A, sa).T, q(B, sb).T, act,
+                               (1 / sx, 1 / sa, 1 / sau, 1 / sb, 1 / sh),
+                               q(Au, sau).T if sw else None)
+    assert not np.array_equal(wrong["Y"], unit["Y"])
+
+
+@pytest.mark.parametrize("act", [ACT_GELU_TANH, ACT_SWIGLU])
+def test_fp8_forward_rounding_scales_dequantize_the_right_products(act):
+    """Scales that are not powers of two (the fused fp32 factors round): each
+    product of decoded codes, divided by the exact product of its two
+    scales, matches the oracle's dequantized sums to fp32 rounding of the
+    factor (three roundings, < 2e-7 relative), so each inverse multiplies
+    its own product at any scale."""
+    sw = act == ACT_SWIGLU
+    rng = np.random.default_rng(13)
+    N, H, F = 11, 32, 16
+    X = rng.standard_normal((N, H))
+    A = rng.standard_normal((H, F)) * 0.05
+    Au = rng.standard_normal((H, F)) * 0.05
+    B = rng.standard_normal((F, H)) * 0.05
+    sx, sa, sau, sb, sh = 37.0, 3000.0, 2500.0, 5000.0, 123.0
+    q = lambda m, s: oracle.fp8_quantize(m, s)[0]
+    Xq, Aq, Auq, Bq = q(X, sx), q(A, sa), q(Au, sau), q(B, sb)
+    f = oracle.mlp_fwd_fp8(Xq, Aq.T, Bq.T, act, (1 / sx, 1 / sa, 1 / sau, 1 / sb, sh),
+                           Auq.T if sw else None)
+    Xd, Ad, Aud, Bd = (oracle.fp8_decode(c) for c in (Xq, Aq, Auq, Bq))
+    G = Xd @ Ad / (sx * sa)
+    assert np.max(np.abs(f["Z"] - G)) <= 2e-7 * np.max(np.abs(G))
+    if sw:
+        Uv = Xd @ Aud / (sx * sau)
+        assert np.max(np.abs(f["U"] - Uv)) <= 2e-7 * np.max(np.abs(Uv))
+    Hd = oracle.fp8_decode(f["Hq"])
+    Y = Hd @ Bd / (sh * sb)
+    assert np.max(np.abs(f["Y"] - Y)) <= 2e-7 * np.max(np.abs(Y))
+    # H's codes are the encoding of H * h_scale taken in fp32
+    assert np.array_equal(f["Hq"], oracle.fp8_encode(
+        (f["H"].astype(np.float32) * np.float32(sh)).astype(np.float32)))
