@@ -9,16 +9,27 @@ The metric counts the GEMM FLOPs only (2 M N K per product: 9 products for
 SwiGLU, 6 for GeLU); the step time includes the two partial sums.  The sums
 stand in for the rank's all-reduces and, like communication, run by default
 on a second stream beside the GEMMs that do not depend on them (sum(Y) beside
-the backward, sum(dX) beside the next forward); --overlap 0 runs the step in
-order on one stream, and the default run also times that form
-("serial_step").
+the backward, sum(dX) beside the next forward).
+
+Caches: the headline steps rotate several input sets (X, the weights, dY;
+together well over the 256 MB Infinity Cache), so every step reads its
+inputs cold, as a layer of a real model would.  The same steps on one input
+set ("warm") are timed beside them.  `value` is the GEMM FLOPs of a step over
+the median of the timed steps' durations (each step's interval between the
+starts of consecutive steps on the compute stream).
+
+Every GEMM launch inside the timed steps is bracketed by HIP events on its
+own stream (the library's tp_launch_events hook), so each kernel's duration
+comes from the same run; `roofline` is the longest (dominant) one.
 
 Prints one JSON line.  Only one GPU is used: --gpus above 1 exits.
 """
 import argparse
+import ctypes
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -26,13 +37,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (twice the bf16 rate)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # copy of known size run outside the timed region: under a counter profile
 # its FETCH_SIZE / WRITE_SIZE calibrate the GEMM kernels' byte counts
 CALIB_COPY_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic_c4_swiglu.txt")
-CLOCK_FILE = os.path.join(ROOT, "profiles", "gemm_clock_c4_swiglu.txt")
 KERNEL_SOURCES = ["gemm_bf16.hip", "common.h", "api.hip"]
+# 60 % of the bf16 peak, as GEMM time per step (the shard targets)
+TARGET_FRAC = 0.60
 
 
 def kernel_source_hash() -> str:
@@ -46,9 +59,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_field(path, key):
-    """A figure from a committed counter summary, or None when the file is
-    missing or was taken on other kernel sources."""
+def recorded_fields(path):
+    """The key: value lines of a committed counter summary, or None when the
+    file is missing or was taken on other kernel sources."""
     try:
         fields = {}
         with open(path) as f:
@@ -58,14 +71,9 @@ def recorded_field(path, key):
                     fields[k.strip()] = v.strip()
         if fields.get("kernel_source_hash") != kernel_source_hash():
             return None
-        return float(fields[key])
-    except (OSError, KeyError, ValueError):
+        return fields
+    except OSError:
         return None
-
-
-def recorded_traffic():
-    """HBM bytes per GEMM launch (FETCH_SIZE + WRITE_SIZE, calibrated)."""
-    return recorded_field(TRAFFIC_FILE, "hbm_bytes_per_gemm_launch")
 
 
 def parse():
@@ -74,29 +82,178 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c4_bf16_swiglu_fwdbwd")
+    p.add_argument("--sets", type=int, default=3,
+                   help="input sets rotated over the headline steps (cold caches)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--fp8", type=int, default=1,
                    help="1: also time the FP8 forward and backward at the same shape")
     p.add_argument("--moe", type=int, default=1,
-                   help="1: also time the MoE dispatch/combine row moves")
+                   help="1: also time the grouped experts and the MoE dispatch/combine")
     p.add_argument("--overlap", type=int, default=1,
                    help="1: partial sums on a second stream, overlapping the GEMMs; "
                         "0: everything in order on one stream")
     p.add_argument("--sum-workgroups", type=int, default=256,
                    help="workgroup cap of the overlapped partial sums")
     p.add_argument("--side", type=int, default=1,
-                   help="0: time the step only (no reduce-scatter, accumulation, MoE or FP8 "
-                        "side measurements), as for the profiler's per-kernel summaries")
+                   help="0: time the headline steps only (no warm, in-order, other-shape, "
+                        "reduce-scatter, accumulation, MoE or FP8 measurements), as for "
+                        "the profiler's per-kernel summaries")
+    p.add_argument("--clock", type=int, default=1,
+                   help="1: sample the shader clock while the steps run again")
     p.add_argument("--cpu-tokens", type=int, default=0,
-                   help="tokens of the oracle sample (0: sized to ~15 s)")
+                   help="tokens of the oracle sample (0: sized to ~20 s)")
     return p.parse_args()
 
 
-def gemm_flops(w, N=None):
+# ---------------------------------------------------------------------------
+# HIP events through the runtime torch has loaded (the library and torch
+# share it): raw handles for the library's launch-timing hook
+# ---------------------------------------------------------------------------
+class HipEvents:
+    def __init__(self, torch):
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.lib = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        self.made += out
+        return out
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, stream.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(t.value)
+
+    def free(self):
+        for h in self.made:
+            self.lib.hipEventDestroy(h)
+        self.made = []
+
+
+def median(xs):
+    import numpy as np
+    return float(np.median(np.asarray(xs, dtype=np.float64)))
+
+
+def tflops(fl, ms):
+    return fl / (ms * 1e-3) / 1e12
+
+
+# ---------------------------------------------------------------------------
+# shader clock sampled while the GEMMs run (amdsmi gpu metrics)
+# ---------------------------------------------------------------------------
+class ClockSampler:
+    """Samples the GPU's current graphics clocks every few ms in a thread.
+    Reports None when the metrics are not readable on this machine."""
+
+    def __init__(self, torch):
+        self.samples, self.error, self.h = [], None, None
+        try:
+            import amdsmi
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            bus = torch.cuda.get_device_properties(0).pci_bus_id
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if int(bdf.split(":")[1], 16) == bus:
+                    self.h = h
+            if self.h is None:
+                self.error = "no amdsmi handle with the device's PCI bus"
+        except Exception as e:  # metrics are context: never fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        cl = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 10000]
+        if not cl and isinstance(m.get("current_gfxclk"), int):
+            cl = [m["current_gfxclk"]]
+        return sum(cl) / len(cl) if cl else None
+
+    def run(self, fn):
+        """fn() runs GPU work; sample until it returns."""
+        if self.h is None:
+            fn()
+            return
+        stop = threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                try:
+                    v = self._read()
+                    if v:
+                        self.samples.append(v)
+                except Exception as e:
+                    self.error = f"{type(e).__name__}: {e}"
+                    return
+                time.sleep(0.002)
+        t = threading.Thread(target=loop, daemon=True)
+        t.start()
+        try:
+            fn()
+        finally:
+            stop.set()
+            t.join()
+
+    def mean_ghz(self):
+        if len(self.samples) < 5:
+            return None
+        s = sorted(self.samples)
+        return sum(s) / len(s) / 1000.0
+
+
+# ---------------------------------------------------------------------------
+# workload arithmetic
+# ---------------------------------------------------------------------------
+GEMM_ROLES_FWD = ["FC1", "FC2"]
+GEMM_ROLES_BWD = ["dH", "dB", "dA", "dX"]
+
+
+def role_flops(w, N=None):
+    """Algorithmic FLOPs of each GEMM launch of one step."""
     N = w.N if N is None else N
     per = 2.0 * N * w.H * w.Ft
-    n_fwd = 3 if w.act == 1 else 2
-    return per * n_fwd * (3 if w.backward else 1)
+    sw = w.act == 1
+    f = {"FC1": per * (2 if sw else 1), "FC2": per}
+    if w.backward:
+        f.update({"dH": per, "dB": per, "dA": per * (2 if sw else 1),
+                  "dX": per * (2 if sw else 1)})
+    return f
+
+
+def gemm_flops(w, N=None):
+    return sum(role_flops(w, N).values())
+
+
+def role_bytes(w):
+    """Algorithmic HBM bytes of each GEMM launch: operands read once, outputs
+    written once (bf16 activations, fp32 weight gradients)."""
+    N, Hd, Ft = w.N, w.H, w.Ft
+    nz = 2 if w.act == 1 else 1
+    e2, e4 = 2, 4
+    b = {"FC1": (N * Hd + nz * Hd * Ft) * e2 + (nz + 1) * N * Ft * e2,
+         "FC2": (N * Ft + Ft * Hd) * e2 + N * Hd * e2}
+    if w.backward:
+        b.update({"dH": (N * Hd + Ft * Hd + nz * N * Ft) * e2 + nz * N * Ft * e2,
+                  "dB": (N * Ft + N * Hd) * e2 + Ft * Hd * e4,
+                  "dA": (N * Hd + nz * N * Ft) * e2 + nz * Hd * Ft * e4,
+                  "dX": (nz * N * Ft + nz * Hd * Ft) * e2 + N * Hd * e2})
+    return b
 
 
 def cpu_model() -> str:
@@ -111,7 +268,6 @@ def cpu_model() -> str:
 
 def cpu_baseline(w, tokens):
     """The fp64 oracle, as it stands, on a token sample of the workload."""
-    import numpy as np
     import oracle
     import workloads as wl
     d = wl.gen_mlp_inputs(w, n_rows=max(tokens, 1))
@@ -123,54 +279,212 @@ def cpu_baseline(w, tokens):
     return dt, gemm_flops(w, tokens)
 
 
-def grouped_expert_timing(torch, tp, wl, stream, reps=20):
+# ---------------------------------------------------------------------------
+# the shard step
+# ---------------------------------------------------------------------------
+class ShardBench:
+    """Inputs (several sets), outputs and stand-in partials of one dense
+    workload, and its timed steps."""
+
+    def __init__(self, torch, tp, wl, w, n_sets, hev, sum_workgroups):
+        from tensor_transformer_mlp_02_amd.tensors import to_device, ShardBuffers
+        self.torch, self.tp, self.w, self.hev = torch, tp, w, hev
+        self.sum_workgroups = sum_workgroups
+        self.sets = []
+        for s in range(max(1, n_sets)):
+            d = wl.gen_mlp_inputs(w, set_index=s)
+            self.sets.append({k: (to_device(v) if v is not None else None)
+                              for k, v in d.items() if k in ("X", "A", "A_up", "B", "dY")})
+        self.desc = dict(S=w.S, B=w.B, H=w.H, F_shard=w.Ft, T=w.T, act=w.act, dtype=w.dtype)
+        self.buf = ShardBuffers(self.desc, backward=w.backward)
+        self.stand = [to_device(p) for p in wl.gen_partials(w, w.T - 1, (w.N, w.H), 0.05)]
+        self.Ysum = torch.empty_like(self.buf.Y)
+        self.dXsum = torch.empty_like(self.buf.Y)
+        self.count = w.N * w.H
+        self.roles = GEMM_ROLES_FWD + ["sumY"] + (GEMM_ROLES_BWD + ["sumdX"] if w.backward
+                                                  else [])
+
+    def input_bytes(self, n_sets):
+        s = self.sets[0]
+        return n_sets * sum(t.numel() * t.element_size() for t in s.values() if t is not None)
+
+    def run(self, n_sets, overlap, steps, warmup, timed=True):
+        """Warmup + timed steps rotating the first n_sets input sets.  Returns
+        per-step durations (ms) and each launch's durations by role."""
+        torch, tp, w, hev = self.torch, self.tp, self.w, self.hev
+        dev = self.buf.Y.device
+        stream = torch.cuda.current_stream()
+        side = torch.cuda.Stream(device=dev) if overlap else stream
+        buf, stand, count = self.buf, self.stand, self.count
+        desc = self.desc
+
+        def psum(T, parts, out, st):
+            if overlap:
+                return tp.tp_partial_sum_capped(w.dtype, T, parts, count, out,
+                                                self.sum_workgroups, stream=st)
+            return tp.tp_partial_sum(w.dtype, T, parts, count, out, stream=st)
+
+        # events keep every dependency: a sum starts after the GEMM that
+        # wrote its input, and the next write of Y (forward) or dX (backward)
+        # waits for the sum that reads it
+        y_ready, dx_ready = torch.cuda.Event(), torch.cuda.Event()
+        y_read, dx_read = torch.cuda.Event(), torch.cuda.Event()
+        y_read.record(side)
+        dx_read.record(side)
+        n_ev = 2 * len(self.roles)
+
+        def step(k, evs=None):
+            s = self.sets[k % n_sets]
+            if evs is not None:
+                tp.tp_launch_events(evs)
+            stream.wait_event(y_read)
+            tp.tp_mlp_shard_fwd(desc, s["X"], s["A"], s["A_up"], s["B"], buf.Z, buf.H, buf.Y,
+                                stream=stream)
+            y_ready.record(stream)
+            side.wait_event(y_ready)
+            psum(w.T, [buf.Y] + stand, self.Ysum, side)
+            y_read.record(side)
+            if w.backward:
+                stream.wait_event(dx_read)
+                tp.tp_mlp_shard_bwd(desc, s["X"], s["A"], s["A_up"], s["B"], buf.Z, buf.H,
+                                    s["dY"], buf.dX, buf.dA, buf.dA_up, buf.dB, buf.ws,
+                                    buf.ws_bytes, stream=stream)
+                dx_ready.record(stream)
+                side.wait_event(dx_ready)
+                psum(w.T, [buf.dX] + stand, self.dXsum, side)
+                dx_read.record(side)
+            if evs is not None:
+                used = tp.tp_launch_events_used()
+                tp.tp_launch_events(None)
+                if used != n_ev:
+                    raise RuntimeError(f"{used} launch events recorded, {n_ev} expected")
+
+        for k in range(warmup):
+            step(k)
+        torch.cuda.synchronize()
+        if not timed:
+            return None
+        starts = hev.create(steps + 1)
+        launch_evs = [hev.create(n_ev) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k in range(steps):
+            hev.record(starts[k], stream)
+            if k == 0:
+                side.wait_stream(stream)
+            step(warmup + k, launch_evs[k])
+        side_done = torch.cuda.Event()
+        side_done.record(side)
+        stream.wait_event(side_done)
+        hev.record(starts[steps], stream)
+        torch.cuda.synchronize()
+        step_ms = [hev.ms(starts[k], starts[k + 1]) for k in range(steps)]
+        total_ms = hev.ms(starts[0], starts[steps])
+        per_role = {r: [hev.ms(e[2 * i], e[2 * i + 1]) for e in launch_evs]
+                    for i, r in enumerate(self.roles)}
+        hev.free()
+        return {"step_ms": step_ms, "total_ms": total_ms, "roles": per_role}
+
+
+def summarize(w, res, label):
+    """Median step, GEMM time per step and each GEMM launch's figures."""
+    fl = role_flops(w)
+    flops = sum(fl.values())
+    med = median(res["step_ms"])
+    roles = {}
+    for r, f in fl.items():
+        us = median(res["roles"][r]) * 1e3
+        roles[r] = {"us": round(us, 1), "tflops": round(tflops(f, us * 1e-3), 1),
+                    "frac": round(tflops(f, us * 1e-3) / PEAK_BF16_TFLOPS, 4)}
+    gemm_ms = sum(median(res["roles"][r]) for r in fl)
+    out = {"inputs": label,
+           "ms_per_step_median": round(med, 4),
+           "ms_per_step_mean": round(res["total_ms"] / len(res["step_ms"]), 4),
+           "tflops": round(tflops(flops, med), 2),
+           "gemm_ms": round(gemm_ms, 4),
+           "gemm_tflops": round(tflops(flops, gemm_ms), 2),
+           "gemm_frac_of_bf16_peak": round(tflops(flops, gemm_ms) / PEAK_BF16_TFLOPS, 4),
+           "gemm_target_ms_at_60pct": round(flops / (TARGET_FRAC * PEAK_BF16_TFLOPS * 1e12) * 1e3,
+                                            4),
+           "launches": roles}
+    sums = [x for r in ("sumY", "sumdX") if r in res["roles"] for x in res["roles"][r]]
+    if sums:
+        ps_ms = median(sums)
+        ps_bytes = (w.T + 1) * w.N * w.H * 2
+        out["partial_sum_us"] = round(ps_ms * 1e3, 1)
+        out["partial_sum_GBps"] = round(ps_bytes / (ps_ms * 1e-3) / 1e9, 1)
+        out["partial_sum_hbm_frac"] = round(ps_bytes / (ps_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# side measurements
+# ---------------------------------------------------------------------------
+def grouped_expert_timing(torch, tp, wl, hev, n_sets, steps=20, warmup=3):
     """The grouped local experts on the grouped-expert workload (16384 tokens
     routed top-2 over 64 experts, local experts 0..7, H = 4096, F = 1408,
-    SwiGLU): forward and backward launches over the ragged rows, in
-    algorithmic TFLOP/s (18 H F per row for forward + backward)."""
+    SwiGLU): forward and backward over the ragged rows, rotating input sets,
+    each launch timed with events; algorithmic TFLOP/s (6 H F per row
+    forward, 12 H F backward)."""
     from tensor_transformer_mlp_02_amd.tensors import to_device, ExpertBuffers
     w5 = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
-    g = wl.gen_grouped_inputs(w5)
+    sets = []
+    for s in range(n_sets):
+        g = wl.gen_grouped_inputs(w5, set_index=s)
+        sets.append({k: to_device(g[k]) for k in ("X_perm", "Wg", "Wu", "Wd", "dY_perm")})
     off = g["offsets"]
     R, E, H, F = int(off[-1]), len(off) - 1, w5.H, w5.F
-    d = {k: to_device(g[k]) for k in ("X_perm", "Wg", "Wu", "Wd", "dY_perm")}
     desc = dict(H=H, F=F, E=E, dtype=wl.DT_BF16)
     buf = ExpertBuffers(desc, off)
+    stream = torch.cuda.current_stream()
+    roles = ["FC1", "FC2", "dH", "dWd", "dWg|dWu", "dX"]
 
-    def fwd():
+    def step(k, evs=None):
+        d = sets[k % n_sets]
+        if evs is not None:
+            tp.tp_launch_events(evs)
         tp.tp_grouped_expert_fwd(desc, off, d["X_perm"], d["Wg"], d["Wu"], d["Wd"], buf.Z,
                                  buf.H, buf.Y, stream=stream)
-
-    def bwd():
         tp.tp_grouped_expert_bwd(desc, off, d["X_perm"], d["Wg"], d["Wu"], d["Wd"], buf.Z,
                                  buf.H, d["dY_perm"], buf.dX, buf.dWg, buf.dWu, buf.dWd,
                                  buf.ws, buf.ws_bytes, stream=stream)
-    fwd(); bwd()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    ev[0].record(stream)
-    for _ in range(reps):
-        fwd()
-    ev[1].record(stream)
-    for _ in range(reps):
-        bwd()
-    ev[2].record(stream)
+        if evs is not None:
+            tp.tp_launch_events(None)
+    for k in range(warmup):
+        step(k)
     torch.cuda.synchronize()
-    f_ms = ev[0].elapsed_time(ev[1]) / reps
-    b_ms = ev[1].elapsed_time(ev[2]) / reps
-    f_fl, b_fl = 6.0 * H * F * R, 12.0 * H * F * R
-    tf = (f_fl + b_fl) / ((f_ms + b_ms) * 1e-3) / 1e12
+    starts = hev.create(steps + 1)
+    evs = [hev.create(2 * len(roles)) for _ in range(steps)]
+    for k in range(steps):
+        hev.record(starts[k], stream)
+        step(warmup + k, evs[k])
+    hev.record(starts[steps], stream)
+    torch.cuda.synchronize()
+    step_ms = median([hev.ms(starts[k], starts[k + 1]) for k in range(steps)])
+    per = {r: median([hev.ms(e[2 * i], e[2 * i + 1]) for e in evs]) for i, r in enumerate(roles)}
+    hev.free()
+    fl = {"FC1": 4.0 * H * F * R, "FC2": 2.0 * H * F * R, "dH": 2.0 * H * F * R,
+          "dWd": 2.0 * H * F * R, "dWg|dWu": 4.0 * H * F * R, "dX": 4.0 * H * F * R}
+    tot = sum(fl.values())
+    f_ms = per["FC1"] + per["FC2"]
+    b_ms = sum(per[r] for r in roles[2:])
     return {"rows": R, "experts": E, "rows_per_expert": [int(x) for x in off[1:] - off[:-1]],
-            "H": H, "F": F, "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
-            "fwd_tflops": round(f_fl / (f_ms * 1e-3) / 1e12, 1),
-            "bwd_tflops": round(b_fl / (b_ms * 1e-3) / 1e12, 1),
-            "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            "H": H, "F": F, "inputs": f"{n_sets} input sets rotated",
+            "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
+            "step_ms_median": round(step_ms, 4),
+            "tflops": round(tflops(tot, step_ms), 1),
+            "frac_of_bf16_peak": round(tflops(tot, step_ms) / PEAK_BF16_TFLOPS, 4),
+            "launches": {r: {"us": round(per[r] * 1e3, 1),
+                             "tflops": round(tflops(fl[r], per[r]), 1),
+                             "frac": round(tflops(fl[r], per[r]) / PEAK_BF16_TFLOPS, 4)}
+                         for r in roles}}
 
 
-def moe_dispatch_timing(torch, tp, wl, dev, stream, reps=20):
+def moe_dispatch_timing(torch, tp, wl, dev, stream, hev, reps=20):
     """Token dispatch and combine around the grouped experts on the
     grouped-expert workload's routing (16384 tokens, top-2 of 64 experts,
     local experts 0..7, H = 4096): permute, weighted combine and the
-    combine's backward, each in GB/s of algorithmic row traffic."""
+    combine's backward, each in GB/s of algorithmic row traffic (median of
+    event-timed launches)."""
     import numpy as np
     w5 = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
     logits = wl.normal(1000 * w5.cid + wl.K_LOGITS, (w5.tokens, w5.n_route), 1.0)
@@ -199,27 +513,25 @@ def moe_dispatch_timing(torch, tp, wl, dev, stream, reps=20):
     out = {"tokens": N, "H": H, "rows": R}
     for name, (fn, nbytes) in calls.items():
         fn()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+        evs = hev.create(2 * reps)
+        for k in range(reps):
+            tp.tp_launch_events(evs[2 * k:2 * k + 2])
             fn()
-        e1.record(stream)
+        tp.tp_launch_events(None)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / reps * 1e3
+        us = median([hev.ms(evs[2 * k], evs[2 * k + 1]) for k in range(reps)]) * 1e3
         out[name] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                      "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    hev.free()
     return out
 
 
-PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA (twice the bf16 rate)
-
-
-def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, reps=10):
+def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, hev, reps=10):
     """The shard forward and backward on FP8 codes at the same shape
     (E4M3 weights and activations, E5M2 gradients): the GEMM calls alone,
     and the quantization each needs (forward: X and the weights' transposes;
     backward: dY and its transpose, the transposes of X's and H's codes, the
-    weights in their own layout)."""
+    weights in their own layout).  Medians of event-timed repetitions."""
     dev = X.device
     N, Hd, Ft = w.N, w.H, w.Ft
     sw = Au is not None
@@ -238,7 +550,6 @@ def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, reps=10):
     Y = torch.empty((N, Hd), dtype=torch.bfloat16, device=dev)
     desc = dict(S=w.S, B=w.B, H=Hd, F_shard=Ft, T=w.T, act=w.act, dtype=w.dtype)
     E4, E5 = tp.TP_FP8_E4M3, tp.TP_FP8_E5M2
-    # backward operands and outputs
     dYq, dYq_t, Xq_t, Hq_t = u8(N, Hd), u8(Hd, N), u8(Hd, N), u8(Ft, N)
     Aq, Bq = u8(Hd, Ft), u8(Ft, Hd)
     Auq = u8(Hd, Ft) if sw else None
@@ -276,37 +587,71 @@ def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, reps=10):
                                 dB, dZq, dZq_t, amax[5:6], stream=stream)
 
     quant_fwd(); fwd(); quant_bwd(); bwd()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    ev[0].record(stream)
-    for _ in range(reps):
-        quant_fwd()
-    ev[1].record(stream)
-    for _ in range(reps):
-        fwd()
-    ev[2].record(stream)
-    for _ in range(reps):
-        quant_bwd()
-    ev[3].record(stream)
-    for _ in range(reps):
-        bwd()
-    ev[4].record(stream)
     torch.cuda.synchronize()
-    ms = [ev[i].elapsed_time(ev[i + 1]) / reps for i in range(4)]
+    parts = [quant_fwd, fwd, quant_bwd, bwd]
+    evs = hev.create(reps * 5)
+    for k in range(reps):
+        for i, fn in enumerate(parts):
+            hev.record(evs[5 * k + i], stream)
+            fn()
+        hev.record(evs[5 * k + 4], stream)
+    torch.cuda.synchronize()
+    ms = [median([hev.ms(evs[5 * k + i], evs[5 * k + i + 1]) for k in range(reps)])
+          for i in range(4)]
+    hev.free()
     f_fl = 2.0 * N * Hd * Ft * (3 if sw else 2)
     b_fl = 2 * f_fl
-    tf = lambda fl, t: round(fl / (t * 1e-3) / 1e12, 1)
+    tf = lambda fl, t: round(tflops(fl, t), 1)
     fwd_d = {"gemm_ms": round(ms[1], 4), "gemm_tflops": tf(f_fl, ms[1]),
-             "gemm_frac_of_fp8_peak": round(f_fl / (ms[1] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+             "gemm_frac_of_fp8_peak": round(tflops(f_fl, ms[1]) / PEAK_FP8_TFLOPS, 4),
              "quantize_ms": round(ms[0], 4),
-             "forward_tflops_with_quantize": tf(f_fl, ms[0] + ms[1]),
-             "bf16_forward_ms_for_comparison": None}
+             "forward_tflops_with_quantize": tf(f_fl, ms[0] + ms[1])}
     bwd_d = {"ms": round(ms[3], 4), "tflops": tf(b_fl, ms[3]),
-             "frac_of_fp8_peak": round(b_fl / (ms[3] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+             "frac_of_fp8_peak": round(tflops(b_fl, ms[3]) / PEAK_FP8_TFLOPS, 4),
              "quantize_transpose_ms": round(ms[2], 4),
              "backward_tflops_with_quantize": tf(b_fl, ms[2] + ms[3]),
-             "step_tflops_with_quantize": tf(f_fl + b_fl, sum(ms)),
-             "bf16_backward_ms_for_comparison": None}
+             "step_tflops_with_quantize": tf(f_fl + b_fl, sum(ms))}
     return fwd_d, bwd_d
+
+
+def reduce_scatter_timing(torch, tp, w, sb, hev, reps=20):
+    """Sequence-parallel form of the same exchange: rank 0's [S/T,B,H] slice
+    of the sum (the reduce-scatter arithmetic)."""
+    stream = torch.cuda.current_stream()
+    out = torch.empty((w.S // w.T) * w.B * w.H, dtype=sb.Ysum.dtype, device=sb.Ysum.device)
+    parts = [sb.buf.Y] + sb.stand
+    for _ in range(3):
+        tp.tp_partial_sum_scatter(w.dtype, w.T, parts, w.S, w.B, w.H, 0, out)
+    evs = hev.create(2 * reps)
+    for k in range(reps):
+        tp.tp_launch_events(evs[2 * k:2 * k + 2])
+        tp.tp_partial_sum_scatter(w.dtype, w.T, parts, w.S, w.B, w.H, 0, out, stream=stream)
+    tp.tp_launch_events(None)
+    torch.cuda.synchronize()
+    ms = median([hev.ms(evs[2 * k], evs[2 * k + 1]) for k in range(reps)])
+    hev.free()
+    nbytes = (w.T + 1) * out.numel() * 2
+    return {"us": round(ms * 1e3, 2), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": nbytes}
+
+
+def accumulation_timing(torch, tp, sb, hev, reps=5):
+    """The backward with the weight gradients added into the fp32 buffers,
+    beside the plain backward (median of event-timed calls)."""
+    stream = torch.cuda.current_stream()
+    s, b, d = sb.sets[0], sb.buf, sb.desc
+    out = {}
+    for name, fn in (("bwd_ms", tp.tp_mlp_shard_bwd), ("bwd_accum_ms", tp.tp_mlp_shard_bwd_accum)):
+        evs = hev.create(2 * reps)
+        for k in range(reps):
+            hev.record(evs[2 * k], stream)
+            fn(d, s["X"], s["A"], s["A_up"], s["B"], b.Z, b.H, s["dY"], b.dX, b.dA, b.dA_up,
+               b.dB, b.ws, b.ws_bytes, stream=stream)
+            hev.record(evs[2 * k + 1], stream)
+        torch.cuda.synchronize()
+        out[name] = round(median([hev.ms(evs[2 * k], evs[2 * k + 1]) for k in range(reps)]), 4)
+    hev.free()
+    return out
 
 
 def main():
@@ -316,100 +661,17 @@ def main():
               "(collectives across GPUs) are not part of this library", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import tensor_transformer_mlp_02_amd as tp
-    from tensor_transformer_mlp_02_amd.tensors import to_device, ShardBuffers
     import workloads as wl
 
     w = wl.WORKLOADS[args.workload]
     assert w.dtype == wl.DT_BF16
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    d = wl.gen_mlp_inputs(w)
-    X, A, B = to_device(d["X"]), to_device(d["A"]), to_device(d["B"])
-    Au = to_device(d["A_up"]) if d["A_up"] is not None else None
-    dY = to_device(d["dY"]) if w.backward else None
-    desc = dict(S=w.S, B=w.B, H=w.H, F_shard=w.Ft, T=w.T, act=w.act, dtype=w.dtype)
-    buf = ShardBuffers(desc, backward=w.backward)
-    # the other T-1 ranks' partial outputs: seeded stand-ins of the same shape
-    stand = [to_device(p) for p in wl.gen_partials(w, w.T - 1, (w.N, w.H), 0.05)]
-    Ysum = torch.empty_like(buf.Y)
-    dXsum = torch.empty_like(buf.Y)
-    count = w.N * w.H
-    stream = torch.cuda.current_stream()
-
-    # The partial sums stand in for the all-reduces of a real rank, so by
-    # default they run on a second stream (default priority) like
-    # communication would: sum(Y) overlaps the backward GEMMs and sum(dX) the
-    # next forward, each on a capped number of workgroups.  Events keep every
-    # dependency: a sum starts after the GEMM that wrote its input, and the
-    # next write of Y (forward) or dX (backward) waits for the sum that reads
-    # it.  overlap=False runs everything in order on the compute stream.
-    def run_steps(overlap, steps, warmup):
-        side = torch.cuda.Stream(device=dev) if overlap else stream
-
-        def psum(*a, stream):
-            if overlap:
-                return tp.tp_partial_sum_capped(*a, args.sum_workgroups, stream=stream)
-            return tp.tp_partial_sum(*a, stream=stream)
-        y_ready, dx_ready = torch.cuda.Event(), torch.cuda.Event()
-        y_read, dx_read = torch.cuda.Event(), torch.cuda.Event()
-        y_read.record(side)
-        dx_read.record(side)
-
-        def step(ev=None):
-            if ev: ev[0].record(stream)
-            stream.wait_event(y_read)
-            tp.tp_mlp_shard_fwd(desc, X, A, Au, B, buf.Z, buf.H, buf.Y, stream=stream)
-            if ev: ev[1].record(stream)
-            y_ready.record(stream)
-            side.wait_event(y_ready)
-            if ev: ev[5].record(side)
-            psum(w.dtype, w.T, [buf.Y] + stand, count, Ysum, stream=side)
-            if ev: ev[6].record(side)
-            y_read.record(side)
-            if w.backward:
-                if ev: ev[2].record(stream)
-                stream.wait_event(dx_read)
-                tp.tp_mlp_shard_bwd(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
-                                    buf.dA_up, buf.dB, buf.ws, buf.ws_bytes, stream=stream)
-                if ev: ev[3].record(stream)
-                dx_ready.record(stream)
-                side.wait_event(dx_ready)
-                if ev: ev[7].record(side)
-                psum(w.dtype, w.T, [buf.dX] + stand, count, dXsum, stream=side)
-                if ev: ev[8].record(side)
-                dx_read.record(side)
-
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        # timed region: K whole steps between two events on the compute
-        # stream (the last one after it has waited for the side stream);
-        # per-call events on each stream split the time between the GEMM
-        # calls and the sums
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(steps)]
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_start.record(stream)
-        side.wait_event(t_start)
-        for k in range(steps):
-            step(evs[k])
-        done = torch.cuda.Event()
-        done.record(side)
-        stream.wait_event(done)
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        ms = t_start.elapsed_time(t_end) / steps
-        fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-        ps = [e[5].elapsed_time(e[6]) for e in evs]
-        bwd_ms = 0.0
-        if w.backward:
-            bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-            ps += [e[7].elapsed_time(e[8]) for e in evs]
-        return ms, fwd_ms, bwd_ms, float(np.mean(ps))
+    hev = HipEvents(torch)
+    overlap = bool(args.overlap)
+    progress = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     # calibration copy (one partial sum of a single buffer = a copy)
     n_calib = CALIB_COPY_BYTES // 2
@@ -419,85 +681,88 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
-    ms, fwd_ms, bwd_ms, ps_ms = run_steps(bool(args.overlap), args.steps, args.warmup)
-    # the same steps in order on one stream: the GEMMs and the sums undisturbed
-    serial = None
-    if args.overlap and args.side:
-        serial = run_steps(False, args.steps, args.warmup)
+    progress(f"{w.name}: drawing {args.sets} input sets")
+    sb = ShardBench(torch, tp, wl, w, args.sets, hev, args.sum_workgroups)
+    progress("headline steps")
+    cold = sb.run(args.sets, overlap, args.steps, args.warmup)
+    head = summarize(w, cold, f"{args.sets} input sets rotated "
+                              f"({sb.input_bytes(args.sets) / 2**20:.0f} MiB): cold caches")
+    warm = serial = None
+    if args.side:
+        progress("warm and in-order steps")
+        warm = summarize(w, sb.run(1, overlap, args.steps, args.warmup),
+                         "one input set: warm caches")
+        if overlap:
+            serial = summarize(w, sb.run(args.sets, False, args.steps, args.warmup),
+                               f"{args.sets} input sets rotated, in order on one stream")
 
-    # sequence-parallel form of the same exchange (outside the timed step):
-    # rank 0's [S/T,B,H] slice of the sum, the reduce-scatter arithmetic
-    rs = None
+    clock = None
+    if args.clock:
+        progress("clock sampling")
+        cs = ClockSampler(torch)
+        n_clock = max(50, int(400.0 / max(head["ms_per_step_median"], 0.1)))
+        cs.run(lambda: sb.run(args.sets, overlap, 0, n_clock, timed=False))
+        ghz = cs.mean_ghz()
+        gemm_tf = head["gemm_tflops"]
+        clock = {"sclk_ghz": None if ghz is None else round(ghz, 3),
+                 "samples": len(cs.samples),
+                 "source": "amdsmi current graphics clocks, sampled every ~2 ms while "
+                           f"{n_clock} more headline steps ran in this process",
+                 "error": cs.error}
+        if ghz:
+            clock["bf16_peak_at_sclk"] = round(PEAK_BF16_TFLOPS * ghz / 2.4, 1)
+            clock["gemm_frac_at_sclk"] = round(gemm_tf / (PEAK_BF16_TFLOPS * ghz / 2.4), 4)
+
+    rs = acc_cmp = None
     if args.side and w.S % w.T == 0:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        slice_out = torch.empty((w.S // w.T) * w.B * w.H, dtype=Ysum.dtype, device=dev)
-        for _ in range(3):
-            tp.tp_partial_sum_scatter(w.dtype, w.T, [buf.Y] + stand, w.S, w.B, w.H, 0, slice_out)
-        reps = 20
-        e0.record(stream)
-        for _ in range(reps):
-            tp.tp_partial_sum_scatter(w.dtype, w.T, [buf.Y] + stand, w.S, w.B, w.H, 0, slice_out)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rs_ms = e0.elapsed_time(e1) / reps
-        rs_bytes = (w.T + 1) * slice_out.numel() * 2
-        rs = {"us": round(rs_ms * 1e3, 2), "GBps": round(rs_bytes / (rs_ms * 1e-3) / 1e9, 1),
-              "hbm_frac": round(rs_bytes / (rs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-              "bytes": rs_bytes}
-
-    # gradient-accumulation form of the backward (weight gradients added
-    # into the fp32 buffers), timed beside the plain backward
-    acc_cmp = None
+        rs = reduce_scatter_timing(torch, tp, w, sb, hev)
     if args.side and w.backward:
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        reps = 5
-        e0.record(stream)
-        for _ in range(reps):
-            tp.tp_mlp_shard_bwd(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
-                                buf.dA_up, buf.dB, buf.ws, buf.ws_bytes, stream=stream)
-        e1.record(stream)
-        for _ in range(reps):
-            tp.tp_mlp_shard_bwd_accum(desc, X, A, Au, B, buf.Z, buf.H, dY, buf.dX, buf.dA,
-                                      buf.dA_up, buf.dB, buf.ws, buf.ws_bytes, stream=stream)
-        e2.record(stream)
-        torch.cuda.synchronize()
-        acc_cmp = {"bwd_ms": round(e0.elapsed_time(e1) / reps, 4),
-                   "bwd_accum_ms": round(e1.elapsed_time(e2) / reps, 4)}
-
-    moe = moe_dispatch_timing(torch, tp, wl, dev, stream) if (args.side and args.moe) else None
-    grouped = grouped_expert_timing(torch, tp, wl, stream) if (args.side and args.moe) else None
+        acc_cmp = accumulation_timing(torch, tp, sb, hev)
     f8 = f8b = None
-    if (args.side and args.fp8 and w.dtype == wl.DT_BF16 and w.H % 128 == 0 and w.Ft % 128 == 0
-            and w.N % 128 == 0 and w.backward):
-        f8, f8b = fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream)
-        f8["bf16_forward_ms_for_comparison"] = round(fwd_ms, 4)
-        f8b["bf16_backward_ms_for_comparison"] = round(bwd_ms, 4)
+    if (args.side and args.fp8 and w.H % 128 == 0 and w.Ft % 128 == 0 and w.N % 128 == 0
+            and w.backward):
+        progress("fp8")
+        s0 = sb.sets[0]
+        f8, f8b = fp8_timing(torch, tp, wl, w, s0["X"], s0["A"], s0["A_up"], s0["B"], s0["dY"],
+                             torch.cuda.current_stream(), hev)
+    del sb
+    torch.cuda.empty_cache()
+
+    # the other dense shard shapes: GeLU forward only, and with the backward
+    others = {}
+    if args.side:
+        for name in ("c2_bf16_gelu_fwd", "c3_bf16_gelu_fwdbwd"):
+            if name == w.name:
+                continue
+            progress(name)
+            wo = wl.WORKLOADS[name]
+            so = ShardBench(torch, tp, wl, wo, args.sets, hev, args.sum_workgroups)
+            r = summarize(wo, so.run(args.sets, overlap, args.steps, args.warmup),
+                          f"{args.sets} input sets rotated: cold caches")
+            r["gflop_per_step"] = round(gemm_flops(wo) / 1e9, 1)
+            others[name] = r
+            del so
+            torch.cuda.empty_cache()
+
+    moe = grouped = None
+    if args.side and args.moe:
+        progress("grouped experts and MoE row moves")
+        moe = moe_dispatch_timing(torch, tp, wl, dev, torch.cuda.current_stream(), hev)
+        grouped = grouped_expert_timing(torch, tp, wl, hev, args.sets)
 
     flops = gemm_flops(w)
-    value = flops / (ms * 1e-3) / 1e12
-    gemm_ms = fwd_ms + bwd_ms
-    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
-    n_gemm = (2 + (4 if w.backward else 0))
-    ps_bytes = (w.T + 1) * count * 2
-    # algorithmic HBM bytes of the GEMM launches of one step: every operand
-    # read once, every output written once (bf16 activations, fp32 weight
-    # gradients)
-    N, Hd, Ft = w.N, w.H, w.Ft
-    e2, e4 = 2, 4
-    nz = 2 if w.act == 1 else 1          # Z_save columns per Ft (G|U)
-    fwd_bytes = (N * Hd + nz * Hd * Ft) * e2 + (nz + 1) * N * Ft * e2 \
-        + (N * Ft + Ft * Hd) * e2 + N * Hd * e2
-    bwd_bytes = 0
-    if w.backward:
-        bwd_bytes = (N * Hd + Ft * Hd + nz * N * Ft) * e2 + nz * N * Ft * e2 \
-            + (N * Ft + N * Hd) * e2 + Ft * Hd * e4 \
-            + (N * Hd + nz * N * Ft) * e2 + nz * Hd * Ft * e4 \
-            + (nz * N * Ft + nz * Hd * Ft) * e2 + N * Hd * e2
-    algo_bytes = fwd_bytes + bwd_bytes
-    ps_gbs = ps_bytes / (ps_ms * 1e-3) / 1e9
-    # the shader clock the GEMMs ran at under load (counter summary of the
-    # same kernels): the MFMA peak at that clock is what the silicon offered
-    sclk = recorded_field(CLOCK_FILE, "sclk_ghz_gemm_mean")
+    value = tflops(flops, head["ms_per_step_median"])
+    # dominant kernel: the GEMM launch with the longest median duration
+    dom = max(head["launches"], key=lambda r: head["launches"][r]["us"])
+    dl = head["launches"][dom]
+    rb = role_bytes(w)
+    traffic = recorded_fields(TRAFFIC_FILE)
+    dom_traffic = None
+    if traffic is not None:
+        try:
+            dom_traffic = float(traffic[f"hbm_bytes_{dom}"])
+        except (KeyError, ValueError):
+            dom_traffic = None
 
     line = {
         "metric": "TP-shard MLP fwd+bwd TFLOP/s on 1 GPU + % of bf16 MFMA peak",
@@ -506,7 +771,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": head["ms_per_step_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -517,44 +782,30 @@ def main():
                    "rank": "one tensor-parallel rank; the other 7 ranks' partials are "
                            "seeded stand-ins",
                    "partial_sums": ("second stream, overlapping the GEMMs, at most %d "
-                                    "workgroups" % args.sum_workgroups) if args.overlap
+                                    "workgroups" % args.sum_workgroups) if overlap
                                    else "in order on the compute stream",
                    "act_derivative": "epilogue of the dY B^T GEMM (dZ written once)",
-                   "caches": "nothing is warmed on purpose: each step's two partial sums "
-                             "stream 1.1 GB through HBM (non-temporal), and each GEMM finds "
-                             "in the 256 MB Infinity Cache only what the launches before it "
-                             "left there"},
+                   "caches": head["inputs"],
+                   "timing": "median of the timed steps' intervals (HIP events on the "
+                             "compute stream); each GEMM launch bracketed by HIP events"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {
-            "kernel": "bf16 MFMA GEMM with fused epilogues (%d launches per step)" % n_gemm,
+            "kernel": f"{dom} GEMM (the longest launch of the step)",
             "bound": "mfma",
-            "achieved": round(gemm_tflops, 2),
+            "achieved": dl["tflops"],
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": recorded_traffic(),
-            "algorithmic_bytes_per_launch": round(algo_bytes / n_gemm),
+            "frac": dl["frac"],
+            "traffic": dom_traffic,
+            "algorithmic_bytes": rb[dom],
+            "flops_per_launch": role_flops(w)[dom],
+            "launch_us_median": dl["us"],
         },
-        "clock_under_load": None if sclk is None else {
-            "sclk_ghz": sclk,
-            "peak_at_sclk": round(PEAK_BF16_TFLOPS * sclk / 2.4, 1),
-            "frac_at_sclk": round(gemm_tflops / (PEAK_BF16_TFLOPS * sclk / 2.4), 4),
-            "source": "profiles/gemm_clock_c4_swiglu.txt (rocprofv3 SQ_BUSY_CYCLES)"},
-        "breakdown_ms": {"fwd_gemms": round(fwd_ms, 4), "bwd_gemms": round(bwd_ms, 4),
-                         "partial_sum_each": round(ps_ms, 4),
-                         "partial_sum_GBps": round(ps_gbs, 1),
-                         "partial_sum_hbm_frac": round(ps_gbs / PEAK_HBM_GBS, 4)},
-        "serial_step": None if serial is None else {
-            "note": "the same steps in order on one stream (sums not overlapped)",
-            "ms_per_step": round(serial[0], 4),
-            "tflops": round(flops / (serial[0] * 1e-3) / 1e12, 2),
-            "gemm_tflops": round(flops / ((serial[1] + serial[2]) * 1e-3) / 1e12, 2),
-            "gemm_frac_of_bf16_peak": round(
-                flops / ((serial[1] + serial[2]) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "breakdown_ms": {"fwd_gemms": round(serial[1], 4), "bwd_gemms": round(serial[2], 4),
-                             "partial_sum_each": round(serial[3], 4)},
-            "partial_sum_GBps": round(ps_bytes / (serial[3] * 1e-3) / 1e9, 1),
-            "partial_sum_hbm_frac": round(ps_bytes / (serial[3] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "step": head,
+        "warm_step": warm,
+        "serial_step": serial,
+        "clock_under_load": clock,
+        "other_shapes": others or None,
         "reduce_scatter_rank0": rs,
         "grad_accumulation": acc_cmp,
         "moe_dispatch_combine": moe,
@@ -562,9 +813,15 @@ def main():
         "fp8_forward": f8,
         "fp8_backward": f8b,
     }
+    if f8b is not None:
+        f8b["bf16_backward_ms_for_comparison"] = round(
+            sum(head["launches"][r]["us"] for r in GEMM_ROLES_BWD) / 1e3, 4)
+        f8["bf16_forward_ms_for_comparison"] = round(
+            sum(head["launches"][r]["us"] for r in GEMM_ROLES_FWD) / 1e3, 4)
 
     if not args.no_cpu_baseline:
         import oracle
+        progress("cpu baseline")
         tokens = args.cpu_tokens
         if tokens <= 0:
             dt, fl = cpu_baseline(w, 128)           # calibrate on 128 tokens

@@ -397,6 +397,28 @@ const char *tp_last_error(void);
 /* Fixed name of a tp_status value. */
 const char *tp_status_string(int status);
 
+/*
+ * Launch timing (a measurement aid, not a step of the method): the GPU
+ * time of each product the calls enqueue, taken with the caller's HIP
+ * events on the stream each product runs on.
+ * tp_launch_events hands this thread's subsequent calls `count` hipEvent_t
+ * handles (created by the caller with timing enabled; they must stay valid
+ * while set).  The j-th timed unit records events[2j] on its stream just
+ * before its kernels and events[2j+1] just after, so
+ * hipEventElapsedTime(events[2j], events[2j+1]) is that unit's time.  A unit
+ * is one product of the path: one GEMM with its fused epilogue (a GEMM
+ * over ragged rows may be more than one kernel), one partial sum, one
+ * quantization, transpose or MoE row move.  Units past the last pair run
+ * untimed.  A new call replaces the set and restarts the count; count 0
+ * (events may then be NULL) stops the timing.  count must be even and at
+ * most TP_MAX_LAUNCH_EVENTS, every handle non-NULL.  Touches no GPU state.
+ * tp_launch_events_used: events recorded on this thread since the last
+ * tp_launch_events call (twice the number of timed units).
+ */
+#define TP_MAX_LAUNCH_EVENTS 4096
+int tp_launch_events(void *const *events, int32_t count);
+int32_t tp_launch_events_used(void);
+
 #ifdef __cplusplus
 }
 #endif

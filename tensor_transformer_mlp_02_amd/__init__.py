@@ -21,6 +21,7 @@ __all__ = [
     "tp_grouped_expert_bwd_workspace", "tp_grouped_expert_bwd_accum",
     "tp_moe_permute", "tp_moe_combine", "tp_moe_combine_bwd",
     "tp_fp8_quantize", "tp_mlp_shard_fwd_fp8", "tp_fp8_transpose", "tp_mlp_shard_bwd_fp8", "TP_FP8_E4M3", "TP_FP8_E5M2", "tp_last_error", "tp_status_string",
+    "tp_launch_events", "tp_launch_events_used",
 ]
 
 TP_F32, TP_BF16 = 0, 1
@@ -113,6 +114,10 @@ def lib() -> ctypes.CDLL:
     L.tp_fp8_transpose.restype = ctypes.c_int
     L.tp_mlp_shard_bwd_fp8.argtypes = [D] + [_vp] * 17
     L.tp_mlp_shard_bwd_fp8.restype = ctypes.c_int
+    L.tp_launch_events.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32]
+    L.tp_launch_events.restype = ctypes.c_int
+    L.tp_launch_events_used.argtypes = []
+    L.tp_launch_events_used.restype = ctypes.c_int32
     L.tp_last_error.argtypes = []
     L.tp_last_error.restype = ctypes.c_char_p
     L.tp_status_string.argtypes = [ctypes.c_int]
@@ -170,6 +175,18 @@ def tp_last_error() -> str:
 
 def tp_status_string(status: int) -> str:
     return lib().tp_status_string(int(status)).decode()
+
+
+def tp_launch_events(events) -> int:
+    """Time this thread's next calls: ``events`` is a sequence of raw
+    hipEvent_t handles (ints), two per timed unit, or None / [] to stop."""
+    evs = [int(e) for e in (events or [])]
+    arr = (_vp * len(evs))(*evs) if evs else None
+    return _check(lib().tp_launch_events(arr, len(evs)))
+
+
+def tp_launch_events_used() -> int:
+    return int(lib().tp_launch_events_used())
 
 
 def _desc(desc) -> tp_mlp_desc:

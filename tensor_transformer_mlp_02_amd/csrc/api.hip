@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <string>
+#include <vector>
 
 #include "common.h"
 #include "launch.h"
@@ -145,8 +146,66 @@ GemmArgs dense_args(int M, int N, int K) {
   return g;
 }
 
+// Launch timing (tp_launch_events): this thread's caller-owned events and
+// how many of them have been recorded.  One timed unit is one product of
+// the path (a GEMM with its fused epilogue, a partial sum, a quantization,
+// ...), which may be more than one kernel.
+thread_local std::vector<hipEvent_t> g_events;
+thread_local size_t g_events_used = 0;
+
+template <typename F>
+hipError_t timed(hipStream_t st, F&& launch) {
+  if (g_events_used + 2 > g_events.size()) return launch();
+  hipError_t he = hipEventRecord(g_events[g_events_used], st);
+  if (he != hipSuccess) return he;
+  he = launch();
+  if (he != hipSuccess) return he;
+  he = hipEventRecord(g_events[g_events_used + 1], st);
+  if (he == hipSuccess) g_events_used += 2;
+  return he;
+}
+
 hipError_t run_gemm(int dtype, GemmKind kind, GemmArgs& g, hipStream_t st) {
-  return dtype == TP_BF16 ? gemm_bf16(kind, g, st) : gemm_f32(kind, g, st);
+  return timed(st, [&] { return dtype == TP_BF16 ? gemm_bf16(kind, g, st) : gemm_f32(kind, g, st); });
+}
+hipError_t tgemm_bf16(GemmKind kind, GemmArgs& g, hipStream_t st) {
+  return timed(st, [&] { return gemm_bf16(kind, g, st); });
+}
+hipError_t tgemm_fp8(GemmKind kind, GemmArgs& g, hipStream_t st) {
+  return timed(st, [&] { return gemm_fp8(kind, g, st); });
+}
+hipError_t t_partial_sum_launch(int dtype, int T, const void* const* parts, int64_t count,
+                                void* out, int max_blocks, hipStream_t st) {
+  return timed(st, [&] { return partial_sum_launch(dtype, T, parts, count, out, max_blocks, st); });
+}
+hipError_t t_fp8_quantize_launch(int fmt, bool tr, int64_t rows, int64_t cols, const void* x,
+                                 const float* scale, void* q, float* amax, hipStream_t st) {
+  return timed(st, [&] { return fp8_quantize_launch(fmt, tr, rows, cols, x, scale, q, amax, st); });
+}
+hipError_t t_zero_float_launch(float* p, hipStream_t st) {
+  return timed(st, [&] { return zero_float_launch(p, st); });
+}
+hipError_t t_byte_transpose_launch(int64_t rows, int64_t cols, const void* in, void* out,
+                                   hipStream_t st) {
+  return timed(st, [&] { return byte_transpose_launch(rows, cols, in, out, st); });
+}
+hipError_t t_moe_permute_launch(int dtype, const int32_t* row_token, int64_t N, int64_t H,
+                                int64_t R, const void* X, void* Xp, hipStream_t st) {
+  return timed(st, [&] { return moe_permute_launch(dtype, row_token, N, H, R, X, Xp, st); });
+}
+hipError_t t_moe_combine_launch(int dtype, const int32_t* tok_ptr, const int32_t* tok_rows,
+                                const float* w, int64_t N, int64_t H, int64_t R, const void* Yp,
+                                void* Y, hipStream_t st) {
+  return timed(st, [&] {
+    return moe_combine_launch(dtype, tok_ptr, tok_rows, w, N, H, R, Yp, Y, st);
+  });
+}
+hipError_t t_moe_combine_bwd_launch(int dtype, const int32_t* row_token, const float* w,
+                                    int64_t N, int64_t H, int64_t R, const void* dY,
+                                    const void* Yp, void* dYp, float* dw, hipStream_t st) {
+  return timed(st, [&] {
+    return moe_combine_bwd_launch(dtype, row_token, w, N, H, R, dY, Yp, dYp, dw, st);
+  });
 }
 
 size_t dz_bytes(const Shard& s) {
@@ -186,6 +245,20 @@ int check_rows(int32_t dtype, int64_t N, int64_t H, int64_t R) {
 extern "C" {
 
 const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+int tp_launch_events(void* const* events, int32_t count) {
+  if (count < 0 || count > TP_MAX_LAUNCH_EVENTS || (count & 1))
+    return fail(TP_ERR_SHAPE, "count must be even and in 0..%d", TP_MAX_LAUNCH_EVENTS);
+  if (count > 0 && !events) return fail(TP_ERR_NULL, "events is NULL");
+  for (int32_t i = 0; i < count; ++i)
+    if (!events[i]) return fail(TP_ERR_NULL, "events[%d] is NULL", i);
+  g_events.assign(reinterpret_cast<const hipEvent_t*>(events),
+                  reinterpret_cast<const hipEvent_t*>(events) + count);
+  g_events_used = 0;
+  return ok();
+}
+
+int32_t tp_launch_events_used(void) { return (int32_t)g_events_used; }
 
 const char* tp_status_string(int status) {
   switch (status) {
@@ -389,7 +462,7 @@ int partial_sum_common(int32_t dtype, int32_t T, const void* const* partials, in
   }
   if (int rc = check_device()) return rc;
   if (count == 0) return ok();
-  hipError_t he = partial_sum_launch(dtype, T, partials, count, out, max_blocks,
+  hipError_t he = t_partial_sum_launch(dtype, T, partials, count, out, max_blocks,
                                      reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "partial-sum launch");
   return ok();
@@ -427,7 +500,7 @@ int tp_partial_sum_scatter(int32_t dtype, int32_t T, const void* const* partials
   }
   if (int rc = check_device()) return rc;
   if (slice == 0) return ok();
-  hipError_t he = partial_sum_launch(dtype, T, sl, slice, out, 0,
+  hipError_t he = t_partial_sum_launch(dtype, T, sl, slice, out, 0,
                                      reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "partial-sum launch");
   return ok();
@@ -510,7 +583,7 @@ int tp_grouped_expert_fwd(const tp_expert_desc* desc, const int64_t* offsets, co
   g1.epi.ld0 = 2 * (int64_t)F;
   g1.epi.ld1 = F;
   g1.epi.split = F;
-  hipError_t he = gemm_bf16(GK_FC1_SWIGLU, g1, st);
+  hipError_t he = tgemm_bf16(GK_FC1_SWIGLU, g1, st);
   if (he != hipSuccess) return hip_fail(he, "grouped FC1 launch");
 
   GemmArgs g2 = dense_args(0, H, F);
@@ -519,7 +592,7 @@ int tp_grouped_expert_fwd(const tp_expert_desc* desc, const int64_t* offsets, co
   g2.b = {Wd, nullptr, H, (int64_t)F * H, 0};
   g2.epi.out0 = Y_perm;
   g2.epi.ld0 = H;
-  he = gemm_bf16(GK_FC2, g2, st);
+  he = tgemm_bf16(GK_FC2, g2, st);
   if (he != hipSuccess) return hip_fail(he, "grouped FC2 launch");
   return ok();
 }
@@ -579,7 +652,7 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
     g.epi.out0 = workspace;
     g.epi.ld0 = 2 * (int64_t)F;
     g.epi.split = F;
-    he = gemm_bf16(GK_DH_SWIGLU, g, st);
+    he = tgemm_bf16(GK_DH_SWIGLU, g, st);
     if (he != hipSuccess) return hip_fail(he, "grouped dH launch");
   }
   {
@@ -590,7 +663,7 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
     g.epi.out0 = dWd;
     g.epi.ld0 = H;
     g.epi.bstride = HF;
-    he = gemm_bf16(accumulate ? GK_WGRAD_ACC : GK_WGRAD, g, st);
+    he = tgemm_bf16(accumulate ? GK_WGRAD_ACC : GK_WGRAD, g, st);
     if (he != hipSuccess) return hip_fail(he, "grouped dWd launch");
   }
   {
@@ -604,7 +677,7 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
     g.epi.ld1 = F;
     g.epi.split = F;
     g.epi.bstride = HF;
-    he = gemm_bf16(accumulate ? GK_WGRAD_SPLIT_ACC : GK_WGRAD_SPLIT, g, st);
+    he = tgemm_bf16(accumulate ? GK_WGRAD_SPLIT_ACC : GK_WGRAD_SPLIT, g, st);
     if (he != hipSuccess) return hip_fail(he, "grouped dWg/dWu launch");
   }
   if (x.R > 0) {
@@ -614,7 +687,7 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
     g.b = {Wg, Wu, F, HF, F};
     g.epi.out0 = dX_perm;
     g.epi.ld0 = H;
-    he = gemm_bf16(GK_DX_KSPLIT, g, st);
+    he = tgemm_bf16(GK_DX_KSPLIT, g, st);
     if (he != hipSuccess) return hip_fail(he, "grouped dX launch");
   }
   return ok();
@@ -662,7 +735,7 @@ int tp_fp8_quantize(int32_t fmt, int32_t transpose, int64_t rows, int64_t cols, 
   Buf outs[] = {out[0], am};
   if (int rc = check_alias(ins, 2, outs, 2)) return rc;
   if (int rc = check_device()) return rc;
-  hipError_t he = fp8_quantize_launch(fmt, transpose != 0, rows, cols, x, scale, q, amax,
+  hipError_t he = t_fp8_quantize_launch(fmt, transpose != 0, rows, cols, x, scale, q, amax,
                                       reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "quantize launch");
   return ok();
@@ -698,7 +771,7 @@ int tp_mlp_shard_fwd_fp8(const tp_mlp_desc* desc, const void* Xq, const void* Aq
   if ((rc = check_device())) return rc;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t he = zero_float_launch(h_amax, st);
+  hipError_t he = t_zero_float_launch(h_amax, st);
   if (he != hipSuccess) return hip_fail(he, "amax reset launch");
   if (s.N == 0) return ok();
   const int N = (int)s.N, H = (int)s.H, Ft = (int)s.Ft;
@@ -715,7 +788,7 @@ int tp_mlp_shard_fwd_fp8(const tp_mlp_desc* desc, const void* Xq, const void* Aq
   g1.epi.ld2 = Ft;
   g1.epi.qs = scales;
   g1.epi.amax = h_amax;
-  he = gemm_fp8(sw ? GK_FC1_SWIGLU_F8 : GK_FC1_GELU_F8, g1, st);
+  he = tgemm_fp8(sw ? GK_FC1_SWIGLU_F8 : GK_FC1_GELU_F8, g1, st);
   if (he != hipSuccess) return hip_fail(he, "FP8 FC1 launch");
 
   GemmArgs g2 = dense_args(N, H, Ft);
@@ -724,7 +797,7 @@ int tp_mlp_shard_fwd_fp8(const tp_mlp_desc* desc, const void* Xq, const void* Aq
   g2.epi.out0 = Y_partial;
   g2.epi.ld0 = H;
   g2.epi.qs = scales;
-  he = gemm_fp8(GK_FC2_F8, g2, st);
+  he = tgemm_fp8(GK_FC2_F8, g2, st);
   if (he != hipSuccess) return hip_fail(he, "FP8 FC2 launch");
   return ok();
 }
@@ -740,7 +813,7 @@ int tp_fp8_transpose(int64_t rows, int64_t cols, const void* q, void* q_t, void*
   if (int rc = check_sized(out, 1)) return rc;
   if (int rc = check_alias(in, 1, out, 1)) return rc;
   if (int rc = check_device()) return rc;
-  hipError_t he = byte_transpose_launch(rows, cols, q, q_t, reinterpret_cast<hipStream_t>(stream));
+  hipError_t he = t_byte_transpose_launch(rows, cols, q, q_t, reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "transpose launch");
   return ok();
 }
@@ -781,7 +854,7 @@ int tp_mlp_shard_bwd_fp8(const tp_mlp_desc* desc, const void* dYq, const void* d
   if ((rc = check_device())) return rc;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipError_t he = zero_float_launch(dz_amax, st);
+  hipError_t he = t_zero_float_launch(dz_amax, st);
   if (he != hipSuccess) return hip_fail(he, "amax reset launch");
   const int n = (int)N, h = (int)H, f = (int)Ft, z = (int)zw;
   // 1. dZq = code(act'(Z) * (dYq Bq^T) dy_inv b_inv * dz_scale), amax |dZ|
@@ -797,10 +870,10 @@ int tp_mlp_shard_bwd_fp8(const tp_mlp_desc* desc, const void* dYq, const void* d
     g.epi.qs = scales;
     g.epi.qi = 0; g.epi.qj = 1; g.epi.qk = 5;
     g.epi.amax = dz_amax;
-    he = gemm_fp8(sw ? GK_DH_SWIGLU_F8 : GK_DH_GELU_F8, g, st);
+    he = tgemm_fp8(sw ? GK_DH_SWIGLU_F8 : GK_DH_GELU_F8, g, st);
     if (he != hipSuccess) return hip_fail(he, "FP8 dH launch");
   }
-  he = byte_transpose_launch(N, zw, dZq, dZq_t, st);
+  he = t_byte_transpose_launch(N, zw, dZq, dZq_t, st);
   if (he != hipSuccess) return hip_fail(he, "dZ transpose launch");
   // 2. dB = (Hq^T codes) (dYq codes) h_inv dy_inv
   {
@@ -811,7 +884,7 @@ int tp_mlp_shard_bwd_fp8(const tp_mlp_desc* desc, const void* dYq, const void* d
     g.epi.ld0 = h;
     g.epi.qs = scales;
     g.epi.qi = 2; g.epi.qj = 0;
-    he = gemm_fp8(GK_WGRAD_F8, g, st);
+    he = tgemm_fp8(GK_WGRAD_F8, g, st);
     if (he != hipSuccess) return hip_fail(he, "FP8 dB launch");
   }
   // 3. dA (| dA_up) = (Xq^T codes) (dZq codes) x_inv dz_inv
@@ -826,7 +899,7 @@ int tp_mlp_shard_bwd_fp8(const tp_mlp_desc* desc, const void* dYq, const void* d
     g.epi.split = f;
     g.epi.qs = scales;
     g.epi.qi = 3; g.epi.qj = 6;
-    he = gemm_fp8(sw ? GK_WGRAD_SPLIT_F8 : GK_WGRAD_F8, g, st);
+    he = tgemm_fp8(sw ? GK_WGRAD_SPLIT_F8 : GK_WGRAD_F8, g, st);
     if (he != hipSuccess) return hip_fail(he, "FP8 dA launch");
   }
   // 4. dX_partial = (dZq codes) ([Aq | Auq] codes)^T dz_inv a_inv
@@ -838,7 +911,7 @@ int tp_mlp_shard_bwd_fp8(const tp_mlp_desc* desc, const void* dYq, const void* d
     g.epi.ld0 = h;
     g.epi.qs = scales;
     g.epi.qi = 6; g.epi.qj = 4;
-    he = gemm_fp8(sw ? GK_DX_KSPLIT_F8 : GK_DX_F8, g, st);
+    he = tgemm_fp8(sw ? GK_DX_KSPLIT_F8 : GK_DX_F8, g, st);
     if (he != hipSuccess) return hip_fail(he, "FP8 dX launch");
   }
   return ok();
@@ -860,7 +933,7 @@ int tp_moe_permute(int32_t dtype, int64_t N, int64_t H, int64_t R, const int32_t
   Buf ins[] = {tab[0], in[0]};
   if (int rc = check_alias(ins, 2, out, 1)) return rc;
   if (int rc = check_device()) return rc;
-  hipError_t he = moe_permute_launch(dtype, row_token, N, H, R, X, X_perm,
+  hipError_t he = t_moe_permute_launch(dtype, row_token, N, H, R, X, X_perm,
                                      reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "permute launch");
   return ok();
@@ -883,7 +956,7 @@ int tp_moe_combine(int32_t dtype, int64_t N, int64_t H, int64_t R, const int32_t
   Buf ins[] = {tab[0], tab[1], wt, in[0]};
   if (int rc = check_alias(ins, 4, out, 1)) return rc;
   if (int rc = check_device()) return rc;
-  hipError_t he = moe_combine_launch(dtype, tok_ptr, tok_rows, row_weight, N, H, R, Y_perm, Y,
+  hipError_t he = t_moe_combine_launch(dtype, tok_ptr, tok_rows, row_weight, N, H, R, Y_perm, Y,
                                      reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "combine launch");
   return ok();
@@ -907,7 +980,7 @@ int tp_moe_combine_bwd(int32_t dtype, int64_t N, int64_t H, int64_t R, const int
   Buf outs[] = {out[0], tab[2]};
   if (int rc = check_alias(ins, 4, outs, 2)) return rc;
   if (int rc = check_device()) return rc;
-  hipError_t he = moe_combine_bwd_launch(dtype, row_token, row_weight, N, H, R, dY, Y_perm,
+  hipError_t he = t_moe_combine_bwd_launch(dtype, row_token, row_weight, N, H, R, dY, Y_perm,
                                          dY_perm, d_weight, reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "combine backward launch");
   return ok();

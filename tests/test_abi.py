@@ -22,12 +22,12 @@ def addr(k, off=0):
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(tp_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t|const char \*)\s*(tp_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -336,3 +336,23 @@ def test_binding_rejects_host_tensors_and_wrong_table_lengths():
         tp.tp_grouped_expert_bwd_workspace(ed, [0, 1, 2, 3, 4, 5])
     # the right lengths reach the library (which reports the missing GPU)
     assert tp.tp_grouped_expert_bwd_workspace(ed, [0, 1, 2, 3, 4]) > 0
+
+
+def test_launch_events_checks():
+    """The timing hook validates its arguments and touches no GPU state."""
+    L = tp.lib()
+    ev = (ctypes.c_void_p * 4)(addr(1), addr(2), addr(3), addr(4))
+    L.tp_launch_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+    L.tp_launch_events_used.restype = ctypes.c_int32
+    assert L.tp_launch_events(ev, 3) == E_SHAPE           # odd
+    assert L.tp_launch_events(ev, -2) == E_SHAPE
+    assert L.tp_launch_events(ev, 4098) == E_SHAPE        # above TP_MAX_LAUNCH_EVENTS
+    assert L.tp_launch_events(None, 2) == E_NULL
+    bad = (ctypes.c_void_p * 2)(addr(1), None)
+    assert L.tp_launch_events(bad, 2) == E_NULL
+    assert L.tp_launch_events(ev, 4) == 0
+    assert L.tp_launch_events_used() == 0
+    # a call rejected by its checks launches nothing, so records nothing
+    assert fwd(gelu_desc(H=12)) == E_SHAPE
+    assert L.tp_launch_events_used() == 0
+    assert L.tp_launch_events(None, 0) == 0

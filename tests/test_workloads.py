@@ -74,3 +74,18 @@ def test_grouped_workload_counts():
     counts = np.diff(d["offsets"])
     assert counts.sum() == len(d["token_ids"]) == d["X_perm"].shape[0]
     assert abs(counts.sum() - 2048 * 2 * 8 / 64) < 0.25 * 2048 * 2 * 8 / 64
+
+
+def test_extra_input_sets_are_other_draws_of_the_same_shapes():
+    """Input sets used for cache-cold timing: set 0 is the workload's own
+    draw; other sets have the same shapes and distributions but other
+    seeds."""
+    w = wl.Workload(77, "tiny", wl.DT_BF16, wl.ACT_SWIGLU, S=16, B=2, H=64, F=256, T=4,
+                    w_std=0.02)
+    d0 = wl.gen_mlp_inputs(w)
+    assert all(np.array_equal(d0[k], wl.gen_mlp_inputs(w, set_index=0)[k])
+               for k in ("X", "A", "A_up", "B", "dY"))
+    d1 = wl.gen_mlp_inputs(w, set_index=1)
+    for k in ("X", "A", "A_up", "B", "dY"):
+        assert d1[k].shape == d0[k].shape and d1[k].dtype == d0[k].dtype
+        assert not np.array_equal(d1[k], d0[k]), k

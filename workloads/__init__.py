@@ -131,14 +131,20 @@ def normal_bf16(seed: int, shape, std: float) -> np.ndarray:
     return f32_to_bf16_bits(normal(seed, shape, std))
 
 
-def _draw(w: Workload, k: int, shape, std: float) -> np.ndarray:
-    seed = 1000 * w.cid + k
+# extra input sets of a workload (cache-cold timing rotates several) draw
+# with seeds 1000*c + SET_STRIDE*s + k, s >= 1; set 0 is the workload's own
+SET_STRIDE = 200
+
+
+def _draw(w: Workload, k: int, shape, std: float, set_index: int = 0) -> np.ndarray:
+    seed = 1000 * w.cid + SET_STRIDE * set_index + k
     if w.dtype == DT_BF16:
         return normal_bf16(seed, shape, std)
     return normal(seed, shape, std)
 
 
-def gen_mlp_inputs(w: Workload, shard: int = 0, n_rows: Optional[int] = None) -> dict:
+def gen_mlp_inputs(w: Workload, shard: int = 0, n_rows: Optional[int] = None,
+                   set_index: int = 0) -> dict:
     """Inputs of one tensor-parallel shard of a dense workload.
 
     Returns a dict of storage arrays (float32, or uint16 bf16 bits):
@@ -149,10 +155,21 @@ def gen_mlp_inputs(w: Workload, shard: int = 0, n_rows: Optional[int] = None) ->
     workloads draw the shard's weights directly at shard shape.
     ``n_rows`` truncates the token dimension (a prefix of the same draw is
     NOT guaranteed; it is a smaller draw of its own, for small tests).
+    ``set_index`` > 0 draws another input set of the same shapes and
+    distributions (other seeds), for timing with cold caches.
     """
     N = w.N if n_rows is None else n_rows
     H, F, Ft = w.H, w.F, w.Ft
     out = {}
+    if set_index:
+        assert not w.full_weights
+        d = lambda k, shape, std: _draw(w, k, shape, std, set_index)
+        out["X"] = d(K_X, (N, H), w.x_std)
+        out["A"] = d(K_A, (H, Ft), w.w_std)
+        out["A_up"] = d(K_AUP, (H, Ft), w.w_std) if w.act == ACT_SWIGLU else None
+        out["B"] = d(K_B, (Ft, H), w.w_std)
+        out["dY"] = d(K_DY, (N, H), w.dy_std) if w.backward else None
+        return out
     out["X"] = _draw(w, K_X, (N, H), w.x_std)
     if w.full_weights:
         A_full = _draw(w, K_A, (H, F), w.w_std)
@@ -201,12 +218,15 @@ def route_top2_local(logits: np.ndarray, n_local: int, topk: int = 2):
 
 
 def gen_grouped_inputs(w: Workload, tokens: Optional[int] = None,
-                       H: Optional[int] = None, F: Optional[int] = None) -> dict:
+                       H: Optional[int] = None, F: Optional[int] = None,
+                       set_index: int = 0) -> dict:
     """Inputs of the grouped local-expert workload.
 
     X_perm [R,H] (rows of the token matrix gathered in (expert, token)
     order), offsets [E+1], token_ids [R], Wg/Wu [E,H,F], Wd [E,F,H],
     dY_perm [R,H].  ``tokens``/``H``/``F`` shrink the problem for tests.
+    ``set_index`` > 0 redraws the tokens, weights and dY (other seeds) over
+    the same routing, for timing with cold caches.
     """
     n_tok = w.tokens if tokens is None else tokens
     H = w.H if H is None else H
@@ -215,15 +235,15 @@ def gen_grouped_inputs(w: Workload, tokens: Optional[int] = None,
     seed = 1000 * w.cid
     logits = normal(seed + K_LOGITS, (n_tok, w.n_route), 1.0)
     token_ids, offsets = route_top2_local(logits, E, w.topk)
-    X = _draw(w, K_X, (n_tok, H), w.x_std)
+    X = _draw(w, K_X, (n_tok, H), w.x_std, set_index)
     out = {
         "token_ids": token_ids,
         "offsets": offsets,
         "X_perm": np.ascontiguousarray(X[token_ids]),
-        "Wg": _draw(w, K_A, (E, H, F), w.w_std),
-        "Wu": _draw(w, K_AUP, (E, H, F), w.w_std),
-        "Wd": _draw(w, K_B, (E, F, H), w.w_std),
-        "dY_perm": _draw(w, K_DY, (len(token_ids), H), w.dy_std),
+        "Wg": _draw(w, K_A, (E, H, F), w.w_std, set_index),
+        "Wu": _draw(w, K_AUP, (E, H, F), w.w_std, set_index),
+        "Wd": _draw(w, K_B, (E, F, H), w.w_std, set_index),
+        "dY_perm": _draw(w, K_DY, (len(token_ids), H), w.dy_std, set_index),
         "logits": logits,
     }
     return out
