@@ -94,6 +94,9 @@ def parse():
                         "0: everything in order on one stream")
     p.add_argument("--sum-workgroups", type=int, default=256,
                    help="workgroup cap of the overlapped partial sums")
+    p.add_argument("--sum-y-after", default="FC2",
+                   help="launch after which the overlapped sum(Y) starts: FC2 (as soon as Y "
+                        "is written) or a backward GEMM (dH, dB, dA, dX)")
     p.add_argument("--side", type=int, default=1,
                    help="0: time the headline steps only (no warm, in-order, other-shape, "
                         "reduce-scatter, accumulation, MoE or FP8 measurements), as for "
@@ -118,6 +121,7 @@ class HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
         self.made = []
 
     def create(self, n):
@@ -133,6 +137,10 @@ class HipEvents:
     def record(self, ev, stream):
         if self.lib.hipEventRecord(ev, stream.cuda_stream) != 0:
             raise RuntimeError("hipEventRecord failed")
+
+    def wait(self, stream, ev):
+        if self.lib.hipStreamWaitEvent(stream.cuda_stream, ev, 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
 
     def ms(self, a, b):
         t = ctypes.c_float()
@@ -286,9 +294,10 @@ class ShardBench:
     """Inputs (several sets), outputs and stand-in partials of one dense
     workload, and its timed steps."""
 
-    def __init__(self, torch, tp, wl, w, n_sets, hev, sum_workgroups):
+    def __init__(self, torch, tp, wl, w, n_sets, hev, sum_workgroups, streams):
         from tensor_transformer_mlp_02_amd.tensors import to_device, ShardBuffers
         self.torch, self.tp, self.w, self.hev = torch, tp, w, hev
+        self.stream, self.side = streams
         self.sum_workgroups = sum_workgroups
         self.sets = []
         for s in range(max(1, n_sets)):
@@ -301,20 +310,20 @@ class ShardBench:
         self.Ysum = torch.empty_like(self.buf.Y)
         self.dXsum = torch.empty_like(self.buf.Y)
         self.count = w.N * w.H
-        self.roles = GEMM_ROLES_FWD + ["sumY"] + (GEMM_ROLES_BWD + ["sumdX"] if w.backward
-                                                  else [])
 
     def input_bytes(self, n_sets):
         s = self.sets[0]
         return n_sets * sum(t.numel() * t.element_size() for t in s.values() if t is not None)
 
-    def run(self, n_sets, overlap, steps, warmup, timed=True):
+    def run(self, n_sets, overlap, steps, warmup, timed=True, y_after="FC2"):
         """Warmup + timed steps rotating the first n_sets input sets.  Returns
-        per-step durations (ms) and each launch's durations by role."""
+        per-step durations (ms) and each launch's durations by role.
+        y_after: the launch after which sum(Y) may start (FC2: as soon as Y
+        is written; a backward GEMM's name: once that GEMM has finished, so
+        the sum overlaps the later ones)."""
         torch, tp, w, hev = self.torch, self.tp, self.w, self.hev
-        dev = self.buf.Y.device
-        stream = torch.cuda.current_stream()
-        side = torch.cuda.Stream(device=dev) if overlap else stream
+        stream = self.stream
+        side = self.side if overlap else stream
         buf, stand, count = self.buf, self.stand, self.count
         desc = self.desc
 
@@ -331,7 +340,17 @@ class ShardBench:
         y_read, dx_read = torch.cuda.Event(), torch.cuda.Event()
         y_read.record(side)
         dx_read.record(side)
-        n_ev = 2 * len(self.roles)
+        n_ev = 2 * (len(GEMM_ROLES_FWD) + 1 + (len(GEMM_ROLES_BWD) + 1 if w.backward else 0))
+
+        # the launch events double as the dependency that delays sum(Y)
+        # until a backward GEMM has finished (its "after" event)
+        late_y = y_after != "FC2" and w.backward and overlap
+        if late_y and y_after not in GEMM_ROLES_BWD:
+            raise ValueError(f"y_after must be FC2 or one of {GEMM_ROLES_BWD}")
+        # order of the timed units within a step
+        order = GEMM_ROLES_FWD + ([] if late_y else ["sumY"]) + \
+            (GEMM_ROLES_BWD + (["sumY"] if late_y else []) + ["sumdX"] if w.backward else [])
+        unit = {r: i for i, r in enumerate(order)}
 
         def step(k, evs=None):
             s = self.sets[k % n_sets]
@@ -341,15 +360,20 @@ class ShardBench:
             tp.tp_mlp_shard_fwd(desc, s["X"], s["A"], s["A_up"], s["B"], buf.Z, buf.H, buf.Y,
                                 stream=stream)
             y_ready.record(stream)
-            side.wait_event(y_ready)
-            psum(w.T, [buf.Y] + stand, self.Ysum, side)
-            y_read.record(side)
+            if not late_y:
+                side.wait_event(y_ready)
+                psum(w.T, [buf.Y] + stand, self.Ysum, side)
+                y_read.record(side)
             if w.backward:
                 stream.wait_event(dx_read)
                 tp.tp_mlp_shard_bwd(desc, s["X"], s["A"], s["A_up"], s["B"], buf.Z, buf.H,
                                     s["dY"], buf.dX, buf.dA, buf.dA_up, buf.dB, buf.ws,
                                     buf.ws_bytes, stream=stream)
                 dx_ready.record(stream)
+                if late_y:
+                    hev.wait(side, evs[2 * unit[y_after] + 1])
+                    psum(w.T, [buf.Y] + stand, self.Ysum, side)
+                    y_read.record(side)
                 side.wait_event(dx_ready)
                 psum(w.T, [buf.dX] + stand, self.dXsum, side)
                 dx_read.record(side)
@@ -360,9 +384,10 @@ class ShardBench:
                     raise RuntimeError(f"{used} launch events recorded, {n_ev} expected")
 
         for k in range(warmup):
-            step(k)
+            step(k, hev.create(n_ev) if late_y else None)
         torch.cuda.synchronize()
         if not timed:
+            hev.free()
             return None
         starts = hev.create(steps + 1)
         launch_evs = [hev.create(n_ev) for _ in range(steps)]
@@ -380,7 +405,7 @@ class ShardBench:
         step_ms = [hev.ms(starts[k], starts[k + 1]) for k in range(steps)]
         total_ms = hev.ms(starts[0], starts[steps])
         per_role = {r: [hev.ms(e[2 * i], e[2 * i + 1]) for e in launch_evs]
-                    for i, r in enumerate(self.roles)}
+                    for i, r in enumerate(order)}
         hev.free()
         return {"step_ms": step_ms, "total_ms": total_ms, "roles": per_role}
 
@@ -671,6 +696,11 @@ def main():
     dev = torch.device("cuda", 0)
     hev = HipEvents(torch)
     overlap = bool(args.overlap)
+    # the compute and side streams are made once, one after the other: HIP
+    # hands new streams hardware queues in turn, so two consecutive ones
+    # never share a queue (a shared queue would run the sums in order)
+    streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
+    torch.cuda.set_stream(streams[0])
     progress = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     # calibration copy (one partial sum of a single buffer = a copy)
@@ -682,15 +712,16 @@ def main():
     del calib_src, calib_dst
 
     progress(f"{w.name}: drawing {args.sets} input sets")
-    sb = ShardBench(torch, tp, wl, w, args.sets, hev, args.sum_workgroups)
+    sb = ShardBench(torch, tp, wl, w, args.sets, hev, args.sum_workgroups, streams)
     progress("headline steps")
-    cold = sb.run(args.sets, overlap, args.steps, args.warmup)
+    cold = sb.run(args.sets, overlap, args.steps, args.warmup, y_after=args.sum_y_after)
     head = summarize(w, cold, f"{args.sets} input sets rotated "
                               f"({sb.input_bytes(args.sets) / 2**20:.0f} MiB): cold caches")
     warm = serial = None
     if args.side:
         progress("warm and in-order steps")
-        warm = summarize(w, sb.run(1, overlap, args.steps, args.warmup),
+        warm = summarize(w, sb.run(1, overlap, args.steps, args.warmup,
+                                   y_after=args.sum_y_after),
                          "one input set: warm caches")
         if overlap:
             serial = summarize(w, sb.run(args.sets, False, args.steps, args.warmup),
@@ -701,7 +732,8 @@ def main():
         progress("clock sampling")
         cs = ClockSampler(torch)
         n_clock = max(50, int(400.0 / max(head["ms_per_step_median"], 0.1)))
-        cs.run(lambda: sb.run(args.sets, overlap, 0, n_clock, timed=False))
+        cs.run(lambda: sb.run(args.sets, overlap, 0, n_clock, timed=False,
+                              y_after=args.sum_y_after))
         ghz = cs.mean_ghz()
         gemm_tf = head["gemm_tflops"]
         clock = {"sclk_ghz": None if ghz is None else round(ghz, 3),
@@ -736,8 +768,9 @@ def main():
                 continue
             progress(name)
             wo = wl.WORKLOADS[name]
-            so = ShardBench(torch, tp, wl, wo, args.sets, hev, args.sum_workgroups)
-            r = summarize(wo, so.run(args.sets, overlap, args.steps, args.warmup),
+            so = ShardBench(torch, tp, wl, wo, args.sets, hev, args.sum_workgroups, streams)
+            r = summarize(wo, so.run(args.sets, overlap, args.steps, args.warmup,
+                                     y_after=args.sum_y_after),
                           f"{args.sets} input sets rotated: cold caches")
             r["gflop_per_step"] = round(gemm_flops(wo) / 1e9, 1)
             others[name] = r

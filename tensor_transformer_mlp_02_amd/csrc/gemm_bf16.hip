@@ -241,8 +241,8 @@ __device__ __forceinline__ void store_k(bf16_t* tile, int tid, const Stage<NW>& 
 }
 
 // ---- epilogue through shared memory ----------------------------------------
-// The tile is written out in four passes of 64 rows.  In each pass the two
-// wavefronts holding those rows store their fp32 sums row-major in shared
+// The tile is written out in passes of 64 rows (four for 256-row tiles, two
+// for 128-row ones).  In each pass the wavefronts holding those rows store their fp32 sums row-major in shared
 // memory (rows padded by 16 bytes, so a wavefront's 16-byte writes spread
 // over all banks), then every thread takes 8 consecutive columns of a row:
 // saved activations are loaded and outputs stored as 16-byte pieces of
@@ -259,7 +259,8 @@ constexpr int EQ_BYTES = EQ_ROWS * EQ_PITCH * 4;
 // (1 / h_scale) b_inv), 3 = backward, sums scaled by qs[qi] qs[qj], 4 =
 // backward dH: scaled as 3, then the activation derivative written as
 // E5M2 codes of dZ qs[qk] with max |dZ| folded into ea.amax
-template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN, int NT, int QM = 0>
+template <int EPI, int BMODE, typename OutT, int FM, int FN, int WTM, int WTN, int NT, int QM = 0,
+          int NPASS = 4>
 __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
                                                   const EpiArgs& ea, const TileCoord& tc,
                                                   int wm, int wn, int lane, int tid, int Ncols,
@@ -278,7 +279,7 @@ __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
     s0 = ea.qs[ea.qi] * ea.qs[ea.qj];
     if constexpr (QM == 4) hs = ea.qs[ea.qk];
   }
-  static_for<0, 4>([&](auto Qc) {
+  static_for<0, NPASS>([&](auto Qc) {
     constexpr int q = decltype(Qc)::value;
     if (wm == q / 2) {
       static_for<0, 2>([&](auto Ic) {
@@ -582,18 +583,48 @@ __device__ __forceinline__ uint32_t clamp_records(int64_t bytes) {
 }
 
 
-template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT>
+// Tile rows TMR: 256 (2 x 2 wavefronts of 128 x 128, two shared-memory
+// stages) or 128 (1 x 4 wavefronts of 128 x 64, three stages).  A 128-row
+// tile halves the work per tile for launches whose 256-row tiles would leave
+// compute units idle; each of its k steps has half the MFMAs, so its loads
+// are issued three tiles ahead instead of two, and its fragment reads cost
+// 0.75 KiB of shared memory per MFMA instead of 0.5.  Each stage holds the
+// A tile then the B tile.
+template <int TMR>
+struct LeanCfg {
+  static constexpr int FM = 4, FN = TMR == 256 ? 4 : 2;
+  static constexpr int WTM = 128, WTN = TMR == 256 ? 128 : 64;
+  static constexpr int NBUF = TMR == 256 ? 2 : 3;
+  static constexpr int A_BYTES = TMR * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  // 1 KiB direct loads per wavefront and k tile
+  static constexpr int LA = A_BYTES / 4096, LB = B_BYTES / 4096, NL = LA + LB;
+  // wavefronts per 128-column half of an M/N-contiguous A tile
+  static constexpr int A_WPH = 4 * 128 / TMR;
+};
+
+// direct load `idx` of a k tile's sequence: A and B alternate while both
+// have loads left (A0 B0 A1 B1 ...), then the rest of B
+template <int LA>
+constexpr int lean_load_seq(int idx) {
+  return idx < 2 * LA ? ((idx & 1) ? LA + (idx >> 1) : (idx >> 1)) : idx;
+}
+
+template <int TMR, bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT>
 __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
-  constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[4 * BM * BK];
+  using C = LeanCfg<TMR>;
+  constexpr int FM = C::FM, FN = C::FN, WTM = C::WTM, WTN = C::WTN, NBUF = C::NBUF;
+  constexpr int LA = C::LA, LB = C::LB, NL = C::NL;
+  constexpr uint32_t A_BYTES = C::A_BYTES, STAGE = C::STAGE;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[NBUF * STAGE / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = TMR == 256 ? wave >> 1 : 0, wn = TMR == 256 ? wave & 1 : wave;
   const int r_lane = lane & 31, c_lane = lane >> 5;
 
-  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BM);
+  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, TMR);
   const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
   const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
   const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
@@ -605,35 +636,42 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   const int nk = (tc.k_end > tc.k_begin) ? (tc.k_end - tc.k_begin + BK - 1) / BK : 0;
 
   const uint32_t lds0 = lds_u32(lds);
-  const uint32_t ldsA = lds0, ldsB = lds0 + 2 * TILE_BYTES;
 
   // ---- loop-invariant direct-load offsets (bytes) and LDS destinations
+  // (relative to the stage)
+  // (sized for the largest case: arrays of a template-dependent size
+  // captured by a generic lambda stop the host compiler from emitting the
+  // kernel's launch stub)
   uint32_t voffA[8], voffB[8];
-  uint32_t dstA[8], dstB[8];  // relative to the buffer (0 or TILE_BYTES)
-  static_for<0, 8>([&](auto Ic) {
+  uint32_t dstA[8], dstB[8];
+  static_assert(LA <= 8 && LB <= 8, "direct loads per wavefront");
+  static_for<0, LA>([&](auto Ic) {
     constexpr int i = decltype(Ic)::value;
     if constexpr (A_KMAJOR) {
-      const int blk = wave * 8 + i;
+      const int blk = wave * LA + i;
       const int r = blk * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz(r);
       voffA[i] = r < m_rows ? (uint32_t)(((int64_t)r * lda + c * 8) * 2) : OOB_OFF;
       dstA[i] = blk * 1024;
     } else {
-      const int half = wave >> 1, b = (wave & 1) * 8 + i;
+      const int half = wave / C::A_WPH, b = (wave % C::A_WPH) * LA + i;
       const int k = 4 * b + (lane >> 4);
       const int q = (lane & 15) ^ ((k & 3) << 2);
       const int col = tc.m_begin + half * 128 + 8 * q;
       voffA[i] = col < tc.m_end ? (uint32_t)(((int64_t)k * lda + col) * 2) : OOB_OFF;
-      dstA[i] = half * (TILE_BYTES / 2) + b * 1024;
+      dstA[i] = half * (BK * 128 * 2) + b * 1024;
     }
+  });
+  static_for<0, LB>([&](auto Ic) {
+    constexpr int i = decltype(Ic)::value;
     if constexpr (B_KMAJOR) {
-      const int blk = wave * 8 + i;
+      const int blk = wave * LB + i;
       const int r = blk * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz(r);
       voffB[i] = r < Ncols - n_base ? (uint32_t)(((int64_t)r * ldb + c * 8) * 2) : OOB_OFF;
-      dstB[i] = blk * 1024;
+      dstB[i] = A_BYTES + blk * 1024;
     } else {
-      const int half = wave >> 1, b = (wave & 1) * 8 + i;
+      const int half = wave >> 1, b = (wave & 1) * LB + i;
       const int k = 4 * b + (lane >> 4);
       const int q = (lane & 15) ^ ((k & 3) << 2);
       int col, lim;
@@ -645,7 +683,7 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
         lim = Ncols;
       }
       voffB[i] = col < lim ? (uint32_t)(((int64_t)k * ldb + col) * 2) : OOB_OFF;
-      dstB[i] = half * (TILE_BYTES / 2) + b * 1024;
+      dstB[i] = A_BYTES + half * (BK * 128 * 2) + b * 1024;
     }
   });
   // buffer resources of the k tile starting at k0 (a past-the-end tile gets
@@ -673,20 +711,20 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
                         valid ? clamp_records(rem) : 0u);
     }
   };
-  auto load_op = [&](auto Lc, uint32_t buf_off) {
+  auto load_op = [&](auto Lc, uint32_t stage_off) {
     constexpr int l = decltype(Lc)::value;
-    if constexpr (l < 8)
+    if constexpr (l < LA)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsA, (lds_void_t*)(lds + (ldsA - lds0 + buf_off + dstA[l]) / 2), 16, voffA[l], soA, 0, 0);
+          rsA, (lds_void_t*)(lds + (stage_off + dstA[l]) / 2), 16, voffA[l], soA, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsB, (lds_void_t*)(lds + (ldsB - lds0 + buf_off + dstB[l - 8]) / 2), 16, voffB[l - 8],
-          soB, 0, 0);
+          rsB, (lds_void_t*)(lds + (stage_off + dstB[l - LA]) / 2), 16, voffB[l - LA], soB,
+          0, 0);
   };
 
-  // ---- loop-invariant LDS read addresses (bytes)
+  // ---- loop-invariant LDS read addresses (bytes, stage 0)
   // K-contiguous: one per k step s (the chunk XOR is not affine in s);
-  // blocks add 4 KiB each, buffer parity adds TILE_BYTES.
+  // blocks add 4 KiB each, the stage adds its offset.
   // M/N-contiguous: one per block (the granule XOR is not affine in the
   // block); k steps add 4 KiB, the second transposing read 1 KiB.
   uint32_t rdA[4], rdB[4];
@@ -694,19 +732,19 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   static_for<0, 4>([&](auto Xc) {
     constexpr int x = decltype(Xc)::value;
     if constexpr (A_KMAJOR)
-      rdA[x] = ldsA + (wm * 128 + r_lane) * 128 + (((2 * x + c_lane) ^ sw) << 4);
+      rdA[x] = lds0 + (wm * 128 + r_lane) * 128 + (((2 * x + c_lane) ^ sw) << 4);
     else {
       uint32_t lo, hi;
       frag_mn_addr(lds, wm * 128 + x * 32, 0, lane, lo, hi);
       rdA[x] = lo;
     }
     if constexpr (B_KMAJOR)
-      rdB[x] = ldsB + (wn * 128 + r_lane) * 128 + (((2 * x + c_lane) ^ sw) << 4);
-    else {
-      const int c0 = (BMODE == BMODE_PAIR32) ? (x & 1) * 128 + wn * 64 + (x >> 1) * 32
-                                             : wn * 128 + x * 32;
+      rdB[x] = lds0 + A_BYTES + (wn * WTN + r_lane) * 128 + (((2 * x + c_lane) ^ sw) << 4);
+    else if constexpr (x < FN) {
+      const int c0 = (BMODE == BMODE_PAIR32) ? (x & 1) * 128 + wn * (WTN / 2) + (x >> 1) * 32
+                                             : wn * WTN + x * 32;
       uint32_t lo, hi;
-      frag_mn_addr(lds + 2 * BM * BK, c0, 0, lane, lo, hi);
+      frag_mn_addr(lds + A_BYTES / 2, c0, 0, lane, lo, hi);
       rdB[x] = lo;
     }
   });
@@ -716,12 +754,12 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   // one fragment slot per k step: reads run two steps ahead of the MFMAs
   FA fa[4][FM];
   FB fb[4][FN];
-  constexpr int RA = A_KMAJOR ? 4 : 8, RB = B_KMAJOR ? 4 : 8;
+  constexpr int RA = A_KMAJOR ? FM : 2 * FM, RB = B_KMAJOR ? FN : 2 * FN;
   constexpr int NREAD = RA + RB;
   // LDS reads complete in order, so waiting until at most this many are
   // outstanding lets the most recent step's reads stay in flight
   constexpr int KEEP = NREAD < 15 ? NREAD : 15;
-  // read op r of k step S from the buffer at byte offset `boff`, into slot S
+  // read op r of k step S from the stage at byte offset `boff`, into slot S
   auto read_op = [&](auto Rc, auto Sc, uint32_t boff) {
     constexpr int r = decltype(Rc)::value, S = decltype(Sc)::value;
     if constexpr (r < RA) {
@@ -762,48 +800,56 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
     static_for<0, FN>([&](auto J) { acc[I][J] = (f32x16_t)(0.0f); });
   });
 
-  // prologue: tiles 0 and 1 in flight, wait for tile 0 only
+  // prologue: tiles 0 .. NBUF-1 in flight, wait for tile 0 only (a plain
+  // barrier: __syncthreads would also drain the tiles behind it)
   if (nk > 0) {
-    set_tile(tc.k_begin, true);
-    static_for<0, 16>([&](auto L) { load_op(L, 0u); });
-    set_tile(tc.k_begin + BK, nk > 1);
-    static_for<0, 16>([&](auto L) { load_op(L, (uint32_t)TILE_BYTES); });
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    for (int t = 0; t < NBUF; ++t) {
+      set_tile(tc.k_begin + t * BK, t == 0 || t < nk);
+      const uint32_t stage_off = (uint32_t)t * STAGE;
+      static_for<0, NL>([&](auto L) { load_op(L, stage_off); });
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 1) * NL) : "memory");
   }
-  __syncthreads();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   if (nk > 0) {
     static_for<0, NREAD>([&](auto R) { read_op(R, std::integral_constant<int, 0>{}, 0u); });
     static_for<0, NREAD>([&](auto R) { read_op(R, std::integral_constant<int, 1>{}, 0u); });
   }
   asm volatile("s_nop 4");
 
+  constexpr int NM = FM * FN;            // MFMAs per k step
+  constexpr int RSPAN = NM < 8 ? NM : 8;  // MFMAs that carry the next reads
+  int cs = 0;                             // stage of tile kt
   for (int kt = 0; kt < nk; ++kt) {
-    // byte offsets of the buffer being consumed and of the other one
-    const uint32_t cur = (uint32_t)(kt & 1) * TILE_BYTES;
-    const uint32_t nxt = cur ^ TILE_BYTES;
-    // tile kt + 2 goes into this buffer once everyone has finished with it
-    set_tile(tc.k_begin + (kt + 2) * BK, kt + 2 < nk);
+    // byte offsets of the stage being consumed and of tile kt + 1's
+    const uint32_t cur = (uint32_t)cs * STAGE;
+    const int ns = cs + 1 == NBUF ? 0 : cs + 1;
+    const uint32_t nxt = (uint32_t)ns * STAGE;
+    // tile kt + NBUF goes into this stage once everyone has finished with it
+    set_tile(tc.k_begin + (kt + NBUF) * BK, kt + NBUF < nk);
     static_for<0, 4>([&](auto Sc) {
       constexpr int S = decltype(Sc)::value;
       // step 2 drains every read: with the barrier this makes the whole
-      // buffer free and (after vmcnt) the next tile readable
+      // stage free and (after vmcnt) tile kt + 1 readable
       fence_slot(std::integral_constant<int, S>{}, std::integral_constant<bool, S == 2>{});
       if constexpr (S == 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NBUF - 2) * NL) : "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
       // side operations: reads for the step two ahead (steps 2, 3 read the
-      // next tile's steps 0, 1), within the first 8 MFMAs; at step 2 the
-      // direct loads of tile kt + 2, one per MFMA
-      constexpr int NLOAD = (S >= 2) ? 8 : 0;
-      constexpr int LOFF = (S == 3) ? 8 : 0;  // first direct load of this step
-      static_for<0, 16>([&](auto Mc) {
+      // next tile's steps 0, 1), within the first RSPAN MFMAs; at steps 2
+      // and 3 the direct loads of tile kt + NBUF, spread over the MFMAs
+      constexpr int NLOAD = (S >= 2) ? NL / 2 : 0;
+      constexpr int LOFF = (S == 3) ? NL / 2 : 0;  // first direct load of this step
+      static_for<0, NM>([&](auto Mc) {
         constexpr int m = decltype(Mc)::value;
-        constexpr int i = m >> 2, j = m & 3;
+        constexpr int i = m / FN, j = m % FN;
         mfma_ordered(acc[i][j], fb[S][j].op(), fa[S][i].op());
-        constexpr int r0 = m < 8 ? (m * NREAD) / 8 : NREAD;
-        constexpr int r1 = m < 8 ? ((m + 1) * NREAD) / 8 : NREAD;
-        constexpr int l0 = NREAD + (m * NLOAD) / 16, l1 = NREAD + ((m + 1) * NLOAD) / 16;
+        constexpr int r0 = m < RSPAN ? (m * NREAD) / RSPAN : NREAD;
+        constexpr int r1 = m < RSPAN ? ((m + 1) * NREAD) / RSPAN : NREAD;
+        constexpr int l0 = NREAD + (m * NLOAD) / NM, l1 = NREAD + ((m + 1) * NLOAD) / NM;
         auto side = [&](auto Oc) {
           constexpr int o = decltype(Oc)::value;
           if constexpr (o < NREAD) {
@@ -811,15 +857,15 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
             read_op(std::integral_constant<int, o>{}, std::integral_constant<int, T>{},
                     S < 2 ? cur : nxt);
           } else {
-            // interleave A and B: A0 B0 A1 B1 ...
             constexpr int idx = o - NREAD + LOFF;
-            load_op(std::integral_constant<int, (idx & 1) * 8 + (idx >> 1)>{}, cur);
+            load_op(std::integral_constant<int, lean_load_seq<LA>(idx)>{}, cur);
           }
         };
         static_for<r0, r1>(side);
         static_for<l0, l1>(side);
       });
     });
+    cs = ns;
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 
@@ -827,7 +873,7 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   // tile is staged through shared memory
   static_assert(EQ_BYTES <= (int)sizeof(lds), "staging rows exceed shared memory");
   __syncthreads();
-  write_tile_staged<EPI, BMODE, OutT, FM, FN, WTM, WTN, LEAN_NT>(
+  write_tile_staged<EPI, BMODE, OutT, FM, FN, WTM, WTN, LEAN_NT, 0, TMR / 64>(
       acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
 }
 
@@ -2027,29 +2073,79 @@ constexpr double W16_CYCLE_FACTOR = TP_W16_FACTOR;
 constexpr double W16_PAIR_EXTRA = 1.1;
 // thin_max: remainders left to the thin kernel by 256-row tiles (the
 // 224-row shape covers every row itself).
-static int pick_shape(const GemmArgs& g, int bmode, bool w16_ok, int thin_max) {
-  if (!TP_USE_W16 || !w16_ok) return 0;
+struct ShapeCost {
+  int shape;
+  double cost;
+};
+static ShapeCost pick_shape_cost(const GemmArgs& g, int bmode, bool w16_ok, int thin_max) {
   const int cus = device_cus();
   auto cost = [&](int BMT, int BNT, int tiles) {
     const double f = (BMT == 256 && BNT == 256) ? 1.0 : W16_CYCLE_FACTOR;
     return f * (double)((tiles + cus - 1) / cus) * BMT * BNT;
   };
+  const bool w16 = TP_USE_W16 && w16_ok;
   if (bmode == BMODE_PAIR32) {
     // the paired 224-wide tiles also pay a heavier epilogue: measured in the
     // whole step (SwiGLU FC1, 4096 tokens, H = 8192, F/T = 3584), 448
     // 256-wide tiles in two waves beat 512 224-wide ones by 3 %
     const int split = (int)g.b.split;
     const double c0 = cost(256, 256, count_tiles(g, 256, 128, split, thin_max));
+    if (!w16) return {0, c0};
     const double c1 =
         W16_PAIR_EXTRA * cost(256, 224, count_tiles(g, 256, 112, split, thin_max));
-    return c1 < c0 ? 1 : 0;
+    return c1 < c0 ? ShapeCost{1, c1} : ShapeCost{0, c0};
   }
   const double c0 = cost(256, 256, count_tiles(g, 256, 256, g.N, thin_max));
+  if (!w16) return {0, c0};
   const double c1 = cost(256, 224, count_tiles(g, 256, 224, g.N, thin_max));
   const double c2 = thin_max > 0 ? 1e300 : cost(224, 256, count_tiles(g, 224, 256, g.N));
-  if (c1 < c0 && c1 <= c2) return 1;
-  if (c2 < c0) return 2;
-  return 0;
+  if (c1 < c0 && c1 <= c2) return {1, c1};
+  if (c2 < c0) return {2, c2};
+  return {0, c0};
+}
+static int pick_shape(const GemmArgs& g, int bmode, bool w16_ok, int thin_max) {
+  return pick_shape_cost(g, bmode, w16_ok, thin_max).shape;
+}
+
+// 128-row tiles of the hand-ordered kernel: taken when they fill the compute
+// units in fewer tile-area waves than the 256-row launch would (a launch
+// with few tiles per compute unit, e.g. a weight gradient of 128 tiles on
+// 256 compute units).  Their fragment reads cost 1.5 times the shared
+// memory per MFMA, so their area counts TP_LEAN128_FACTOR times.
+#ifndef TP_LEAN128_FACTOR
+#define TP_LEAN128_FACTOR 1.2
+#endif
+template <bool AK, bool BK_, int BMODE>
+static bool lean_ok(const GemmArgs& g) {
+  const bool k_whole = (!AK && !BK_) || g.K % mfma256::BK == 0;
+  const bool split_ok = BMODE != BMODE_KSPLIT || g.b.split % mfma256::BK == 0;
+  return TP_USE_LEAN && k_whole && split_ok && !(BMODE == BMODE_PAIR32 && BK_);
+}
+template <bool AK, bool BK_, int BMODE>
+static bool lean128_pays(const GemmArgs& g, int thin_max) {
+  if (!lean_ok<AK, BK_, BMODE>(g)) return false;
+  const bool pair = BMODE == BMODE_PAIR32;
+  const int n_cols = pair ? (int)g.b.split : g.N, bn = pair ? 128 : 256;
+  const int cus = device_cus();
+  const int t128 = count_tiles(g, 128, bn, n_cols, 0);
+  const double c128 = TP_LEAN128_FACTOR * (double)((t128 + cus - 1) / cus) * 128 * 256;
+  const bool k_whole = (!AK && !BK_) || g.K % mfma256::BK == 0;
+  const bool w16_ok = k_whole && BMODE != BMODE_KSPLIT && !(BMODE == BMODE_PAIR32 && BK_);
+  return c128 < pick_shape_cost(g, BMODE, w16_ok, thin_max).cost;
+}
+template <bool AK, bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_lean128(GemmArgs& g, hipStream_t stream) {
+  int n_cols = g.N;
+  if (BMODE == BMODE_PAIR32) {
+    n_cols = ((int)((g.b.split + 31) / 32)) * 64;
+    g.N = n_cols;
+  }
+  fill_tiles(g, 128, mfma256::BN, n_cols, 0);
+  const int blocks = g.tile_off[g.E];
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((mfma256::gemm_lean<128, AK, BK_, BMODE, EPI, OutT>), dim3(blocks),
+                     dim3(mfma256::LEAN_NT), 0, stream, g);
+  return hipGetLastError();
 }
 
 template <bool AK, bool BK_, int BMODE, int EPI, typename OutT, int BMT, int BNT>
@@ -2079,8 +2175,12 @@ static hipError_t launch_rows(GemmArgs& g, hipStream_t stream, int thin_max);
 template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
   const int thin_max = thin_rows_max<AK, BK_, BMODE>(g);
+  if (lean128_pays<AK, BK_, BMODE>(g, thin_max))
+    return launch_lean128<AK, BK_, BMODE, EPI, OutT>(g, stream);
   if constexpr (AK && !(BMODE == BMODE_PAIR32 && BK_)) {
-    if (rows128_pays<AK, BK_, BMODE>(g, thin_max))
+    // (the compiler-scheduled 128-row kernel serves launches the hand-ordered
+    // one cannot take: k extents that are not whole 64-wide tiles)
+    if (!lean_ok<AK, BK_, BMODE>(g) && rows128_pays<AK, BK_, BMODE>(g, thin_max))
       return launch_short<mfma256::ROWS_M, false, BK_, BMODE, EPI, OutT>(g, stream);
     if (thin_max > 0) {
       GemmArgs gt = g;  // the main launch rewrites its tile table (and N)
@@ -2125,7 +2225,7 @@ static hipError_t launch_rows(GemmArgs& g, hipStream_t stream, int thin_max) {
   const bool ring_ok = ((!AK && !BK_) || g.K % mfma256::RBK == 0) &&
                        (BMODE != BMODE_KSPLIT || g.b.split % mfma256::RBK == 0);
   if (TP_USE_LEAN && k_whole && split_ok) {
-    hipLaunchKernelGGL((mfma256::gemm_lean<AK, BK_, BMODE, EPI, OutT>), dim3(blocks),
+    hipLaunchKernelGGL((mfma256::gemm_lean<256, AK, BK_, BMODE, EPI, OutT>), dim3(blocks),
                        dim3(mfma256::LEAN_NT), 0, stream, g);
     return hipGetLastError();
   }

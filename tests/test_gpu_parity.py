@@ -116,6 +116,12 @@ SMALL = [
     (wl.DT_F32, wl.ACT_GELU_TANH, 300, 132, 100),
     (wl.DT_F32, wl.ACT_SWIGLU, 70, 68, 36),
     (wl.DT_F32, wl.ACT_SWIGLU, 1, 4, 4),
+    # 256-row tiles with ragged edges in both dimensions (FC1 and dH: 16 x 16
+    # tiles, one wave), the weight gradients and dX on 128-row tiles over a
+    # ragged k extent of 4000 tokens
+    (wl.DT_BF16, wl.ACT_GELU_TANH, 4000, 1024, 4000),
+    # paired SwiGLU forward on 128-row tiles with a ragged gate/up width
+    (wl.DT_BF16, wl.ACT_SWIGLU, 2100, 1024, 1400),
 ]
 
 
@@ -126,6 +132,24 @@ def test_small_shapes_full_tensors(dtype, act, N, H, Ft):
     d = wl.gen_mlp_inputs(w)
     dev, buf = _run_shard(w, d)
     _check_full(w, d, buf)
+
+
+def test_row_tiles_of_128_and_256_agree_bitwise():
+    """Each output element takes the same chain of 32x32x16 MFMAs over the
+    same 16-wide k steps in a 128-row tile as in a 256-row one, so the same
+    rows give the same bits: the forward of 4000 tokens (256-row tiles) and
+    of its first 256 tokens (128-row tiles, few tiles per compute unit)."""
+    H, Ft = 1024, 4000
+    outs = []
+    for N in (4000, 256):
+        w = wl.Workload(71, "rows", wl.DT_BF16, wl.ACT_GELU_TANH, S=N, B=1, H=H, F=Ft, T=1,
+                        w_std=0.05, backward=False)
+        d = wl.gen_mlp_inputs(w, n_rows=4000)
+        d["X"] = d["X"][:N]
+        _, buf = _run_shard(w, d, backward=False)
+        outs.append({k: to_host(getattr(buf, k))[:256] for k in ("Z", "H")})
+    for k in ("Z", "H"):
+        assert np.array_equal(outs[0][k], outs[1][k]), k
 
 
 def test_empty_batch():
