@@ -154,6 +154,26 @@ int tp_mlp_shard_bwd(const tp_mlp_desc *desc, const void *X, const void *A,
                      size_t ws_bytes, void *stream);
 
 /*
+ * tp_mlp_shard_bwd_noalloc -- tp_mlp_shard_bwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and the same results bit for bit.  The
+ * activation-side gradient dZ goes to a scratch array inside the library
+ * (TP_NOALLOC_SCRATCH_BYTES bytes, held by each GPU the library runs on
+ * until the process ends); the call allocates nothing.  It fails with
+ * TP_ERR_WORKSPACE when dZ needs more (N * F_shard * element size, SwiGLU
+ * twice that: up to 2^25 bf16 elements, e.g. 4096 tokens at F_shard = 4096
+ * for SwiGLU or 8192 tokens at F_shard = 4096 for GeLU).  Every call on one
+ * GPU uses that GPU's one array: calls that overlap on one GPU (on streams
+ * that run concurrently) race and must not be made.
+ */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int tp_mlp_shard_bwd_noalloc(const tp_mlp_desc *desc, const void *X, const void *A,
+                             const void *A_up, const void *B, const void *Z_save,
+                             const void *H_act, const void *dY, void *dX_partial, float *dA,
+                             float *dA_up, float *dB, void *stream);
+
+/*
  * tp_partial_sum -- out = sum_{i=0}^{T-1} partials[i], elementwise: the
  * arithmetic the all-reduce performs over the T shards' partial outputs
  * (§三 3.2/3.3: forward sum of Y_i; backward sum of dX_i), here over

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -330,10 +331,44 @@ size_t tp_mlp_shard_bwd_workspace(const tp_mlp_desc* desc) {
 }
 
 namespace {
+// Device-resident scratch for tp_mlp_shard_bwd_noalloc: the activation-side
+// gradient dZ of one call.  Each GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses this name as an address:
+// the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[TP_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+// this device's address of `scratch` (looked up once per device, with that
+// device current); NULL and the error message on failure
+void* scratch_address(int* err) {
+  int dev = -1;
+  hipError_t he = hipGetDevice(&dev);
+  if (he != hipSuccess || dev < 0 || dev >= 64) {
+    *err = fail(TP_ERR_DEVICE, "no current HIP device for the scratch buffer");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    he = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (he != hipSuccess || !p) {
+      *err = hip_fail(he != hipSuccess ? he : hipErrorInvalidSymbol,
+                      "hipGetSymbolAddress of the scratch buffer");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// use_scratch: the workspace is the device's scratch array (resolved after
+// the device check; its size is checked against the array's)
 int shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void* A_up,
               const void* B, const void* Z_save, const void* H_act, const void* dY,
               void* dX_partial, float* dA, float* dA_up, float* dB, void* workspace,
-              size_t ws_bytes, void* stream, bool accumulate) {
+              size_t ws_bytes, void* stream, bool accumulate, bool use_scratch = false) {
   Shard s;
   int rc = check_desc(desc, s);
   if (rc) return rc;
@@ -357,17 +392,29 @@ int shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void*
   if ((rc = check_ptrs(in_opt, 1, false))) return rc;
   if ((rc = check_ptrs(out_opt, 1, false))) return rc;
   const size_t need = dz_bytes(s);
-  if (need > 0) {
+  if (use_scratch) {
+    if (need > (size_t)TP_NOALLOC_SCRATCH_BYTES)
+      return fail(TP_ERR_WORKSPACE,
+                  "dZ needs %zu bytes, more than the %zu-byte scratch buffer of the "
+                  "allocation-free call (N * F_shard%s * element size)",
+                  need, (size_t)TP_NOALLOC_SCRATCH_BYTES, sw ? " * 2" : "");
+  } else if (need > 0) {
     if (!workspace) return fail(TP_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (!aligned16(workspace)) return fail(TP_ERR_ALIGN, "workspace is not 16-byte aligned");
     if (ws_bytes < need)
       return fail(TP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
   }
-  Buf ws = {workspace, need, "workspace"};
+  Buf ws = {use_scratch ? nullptr : workspace, need, "workspace"};
   Buf ins[] = {in_req[0], in_req[1], in_req[2], in_req[3], in_req[4], in_req[5], in_opt[0]};
   Buf outs[] = {out_req[0], out_req[1], out_req[2], out_opt[0], ws};
   if ((rc = check_alias(ins, 7, outs, 5))) return rc;
   if ((rc = check_device())) return rc;
+  if (use_scratch) {
+    int err = TP_OK;
+    workspace = scratch_address(&err);
+    if (!workspace) return err;
+    ws_bytes = TP_NOALLOC_SCRATCH_BYTES;
+  }
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int N = (int)s.N, H = (int)s.H, Ft = (int)s.Ft;
@@ -432,6 +479,14 @@ int tp_mlp_shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, cons
                      size_t ws_bytes, void* stream) {
   return shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up, dB, workspace,
                    ws_bytes, stream, false);
+}
+
+int tp_mlp_shard_bwd_noalloc(const tp_mlp_desc* desc, const void* X, const void* A,
+                             const void* A_up, const void* B, const void* Z_save,
+                             const void* H_act, const void* dY, void* dX_partial, float* dA,
+                             float* dA_up, float* dB, void* stream) {
+  return shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up, dB, nullptr, 0,
+                   stream, false, true);
 }
 
 int tp_mlp_shard_bwd_accum(const tp_mlp_desc* desc, const void* X, const void* A,

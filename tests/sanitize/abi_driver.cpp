@@ -159,9 +159,15 @@ int main() {
         const size_t ws = tp_mlp_shard_bwd_workspace(pd);
         const size_t wsb = rnd() % 2 ? ws : (size_t)(rnd() % 4096);
         auto fn = rnd() % 2 ? tp_mlp_shard_bwd : tp_mlp_shard_bwd_accum;
-        check(fn(pd, ptr_any(1), ptr_any(2), ptr_any(3), ptr_any(4), ptr_any(5), ptr_any(6),
-                 ptr_any(7), ptr_any(8), (float*)ptr_any(9), (float*)ptr_any(10),
-                 (float*)ptr_any(11), ptr_any(12), wsb, nullptr), "fuzz bwd");
+        if (rnd() % 3 == 0)
+          check(tp_mlp_shard_bwd_noalloc(pd, ptr_any(1), ptr_any(2), ptr_any(3), ptr_any(4),
+                                         ptr_any(5), ptr_any(6), ptr_any(7), ptr_any(8),
+                                         (float*)ptr_any(9), (float*)ptr_any(10),
+                                         (float*)ptr_any(11), nullptr), "fuzz bwd noalloc");
+        else
+          check(fn(pd, ptr_any(1), ptr_any(2), ptr_any(3), ptr_any(4), ptr_any(5), ptr_any(6),
+                   ptr_any(7), ptr_any(8), (float*)ptr_any(9), (float*)ptr_any(10),
+                   (float*)ptr_any(11), ptr_any(12), wsb, nullptr), "fuzz bwd");
         break;
       }
       case 2: {

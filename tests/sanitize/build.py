@@ -3,8 +3,8 @@
 * the oracle's C loop nests (oracle/tp_mlp_oracle.c) with gcc and
   AddressSanitizer + UndefinedBehaviorSanitizer, linked into
   oracle_driver.c;
-* the C ABI's argument-check layer (the library's api.hip) compiled for
-  the host only (no device code), with both sanitizers on the host pass,
+* the C ABI's argument-check layer (the library's api.hip), with both
+  sanitizers on the host pass,
   linked into abi_driver.cpp, whose stub launchers abort if a call ever
   gets past the checks.
 
@@ -42,13 +42,16 @@ def build_abi_driver(out_dir: str) -> str:
     host_san = []
     for s in SAN:
         host_san += ["-Xarch_host", f"-fsanitize={s}"]
-    common = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "--cuda-host-only",
+    common = ["-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
               "--offload-arch=gfx950", "-Xarch_host", "-fno-sanitize-recover=all", *host_san,
               "-I", CSRC]
     objs = []
-    for src in (os.path.join(CSRC, "api.hip"), os.path.join(HERE, "abi_driver.cpp")):
+    # api.hip keeps its device side (the allocation-free call's scratch
+    # array lives there); the driver is host code only
+    for src, extra in ((os.path.join(CSRC, "api.hip"), []),
+                       (os.path.join(HERE, "abi_driver.cpp"), ["--cuda-host-only"])):
         obj = os.path.join(out_dir, os.path.basename(src) + ".o")
-        _run([hipcc, *common, "-x", "hip", "-c", src, "-o", obj])
+        _run([hipcc, *common, *extra, "-x", "hip", "-c", src, "-o", obj])
         objs.append(obj)
     clang = os.path.join(ROCM, "llvm", "bin", "clang++")
     _run([clang, *[f"-fsanitize={s}" for s in SAN], "-o", exe, *objs,

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -356,3 +356,26 @@ def test_launch_events_checks():
     assert fwd(gelu_desc(H=12)) == E_SHAPE
     assert L.tp_launch_events_used() == 0
     assert L.tp_launch_events(None, 0) == 0
+
+
+def test_noalloc_backward_rejects_more_than_its_scratch():
+    """The allocation-free backward checks dZ's size against its scratch
+    array (64 MiB: 2^25 bf16 elements) before touching the GPU."""
+    L = tp.lib()
+    def st(desc, A_up=None, dA_up=None):
+        try:
+            tp.tp_mlp_shard_bwd_noalloc(desc, addr(1), addr(2), A_up, addr(3), addr(4), addr(5),
+                                        addr(7), addr(8), addr(9), dA_up, addr(10))
+        except tp.TpError as e:
+            return e.status
+        return 0
+    sw = dict(act=tp.TP_ACT_SWIGLU)
+    # SwiGLU at 4096 tokens and F_shard = 4096: exactly 2^25 elements fit
+    ok = gelu_desc(S=4096, B=1, H=512, F_shard=4096, **sw)
+    assert st(ok, A_up=addr(11), dA_up=addr(12)) == E_DEV
+    big = gelu_desc(S=4097, B=1, H=512, F_shard=4096, **sw)
+    assert st(big, A_up=addr(11), dA_up=addr(12)) == E_WS
+    assert "scratch" in tp.tp_last_error()
+    assert st(gelu_desc(S=8192, B=1, H=512, F_shard=4096)) == E_DEV
+    assert st(gelu_desc(S=8192, B=1, H=512, F_shard=4104)) == E_WS
+    assert st(gelu_desc(H=12)) == E_SHAPE

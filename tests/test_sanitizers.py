@@ -2,7 +2,7 @@
 
 * The fp64 oracle's loop nests and partial-sum table walk, on small and
   degenerate shapes (N = 0, 1, ragged widths, T = 1 and 64).
-* The C ABI's argument-check layer, built for the host only, against the
+* The C ABI's argument-check layer, sanitized on its host side, against the
   documented rejections and 20000 seeded fuzzed calls (descriptors,
   offsets tables, shard pointer arrays, NULL / misaligned / overlapping
   pointers): every call must end in an error status with a message, and
