@@ -171,7 +171,7 @@ class ClockSampler:
     Reports None when the metrics are not readable on this machine."""
 
     def __init__(self, torch):
-        self.samples, self.error, self.h = [], None, None
+        self.samples, self.avg_samples, self.error, self.h, self.raw = [], [], None, None, None
         try:
             import amdsmi
             self.amdsmi = amdsmi
@@ -187,11 +187,17 @@ class ClockSampler:
             self.error = f"{type(e).__name__}: {e}"
 
     def _read(self):
+        """(mean of the per-XCD current clocks, the average clock) in MHz."""
         m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
+        if self.raw is None:
+            self.raw = {k: m.get(k) for k in ("current_gfxclks", "current_gfxclk",
+                                              "average_gfxclk_frequency")}
         cl = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 10000]
         if not cl and isinstance(m.get("current_gfxclk"), int):
             cl = [m["current_gfxclk"]]
-        return sum(cl) / len(cl) if cl else None
+        avg = m.get("average_gfxclk_frequency")
+        avg = avg if isinstance(avg, int) and 0 < avg < 10000 else None
+        return (sum(cl) / len(cl) if cl else None), avg
 
     def run(self, fn):
         """fn() runs GPU work; sample until it returns."""
@@ -203,9 +209,11 @@ class ClockSampler:
         def loop():
             while not stop.is_set():
                 try:
-                    v = self._read()
+                    v, a = self._read()
                     if v:
                         self.samples.append(v)
+                    if a:
+                        self.avg_samples.append(a)
                 except Exception as e:
                     self.error = f"{type(e).__name__}: {e}"
                     return
@@ -218,11 +226,20 @@ class ClockSampler:
             stop.set()
             t.join()
 
-    def mean_ghz(self):
-        if len(self.samples) < 5:
+    @staticmethod
+    def _median_ghz(xs):
+        """Median of the samples in GHz, or None when too few or implausible
+        for a loaded MI355X (outside 0.5..3 GHz: an idle or stale reading)."""
+        if len(xs) < 5:
             return None
-        s = sorted(self.samples)
-        return sum(s) / len(s) / 1000.0
+        v = median(xs) / 1000.0
+        return v if 0.5 <= v <= 3.0 else None
+
+    def ghz(self):
+        return self._median_ghz(self.samples)
+
+    def avg_ghz(self):
+        return self._median_ghz(self.avg_samples)
 
 
 # ---------------------------------------------------------------------------
@@ -734,12 +751,16 @@ def main():
         n_clock = max(50, int(400.0 / max(head["ms_per_step_median"], 0.1)))
         cs.run(lambda: sb.run(args.sets, overlap, 0, n_clock, timed=False,
                               y_after=args.sum_y_after))
-        ghz = cs.mean_ghz()
+        ghz = cs.ghz()
+        avg = cs.avg_ghz()
         gemm_tf = head["gemm_tflops"]
         clock = {"sclk_ghz": None if ghz is None else round(ghz, 3),
+                 "avg_gfxclk_ghz": None if avg is None else round(avg, 3),
                  "samples": len(cs.samples),
-                 "source": "amdsmi current graphics clocks, sampled every ~2 ms while "
-                           f"{n_clock} more headline steps ran in this process",
+                 "source": "amdsmi gpu metrics (median of the per-XCD current graphics "
+                           "clocks; the firmware's average clock beside it), sampled every "
+                           f"~2 ms while {n_clock} more headline steps ran in this process",
+                 "first_sample": cs.raw,
                  "error": cs.error}
         if ghz:
             clock["bf16_peak_at_sclk"] = round(PEAK_BF16_TFLOPS * ghz / 2.4, 1)
