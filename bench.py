@@ -92,7 +92,7 @@ def parse():
     p.add_argument("--overlap", type=int, default=1,
                    help="1: partial sums on a second stream, overlapping the GEMMs; "
                         "0: everything in order on one stream")
-    p.add_argument("--sum-workgroups", type=int, default=256,
+    p.add_argument("--sum-workgroups", type=int, default=192,
                    help="workgroup cap of the overlapped partial sums")
     p.add_argument("--sum-y-after", default="FC2",
                    help="launch after which the overlapped sum(Y) starts: FC2 (as soon as Y "
@@ -101,6 +101,9 @@ def parse():
                    help="0: time the headline steps only (no warm, in-order, other-shape, "
                         "reduce-scatter, accumulation, MoE or FP8 measurements), as for "
                         "the profiler's per-kernel summaries")
+    p.add_argument("--only", default="", choices=["", "grouped", "fp8"],
+                   help="time only the grouped experts or only the FP8 shard (for the "
+                        "profiler's per-kernel summaries); prints their JSON")
     p.add_argument("--clock", type=int, default=1,
                    help="1: sample the shader clock while the steps run again")
     p.add_argument("--cpu-tokens", type=int, default=0,
@@ -641,9 +644,30 @@ def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, hev, reps=10):
     ms = [median([hev.ms(evs[5 * k + i], evs[5 * k + i + 1]) for k in range(reps)])
           for i in range(4)]
     hev.free()
+    # each launch of the two calls, timed on its own (launch-timing hook)
+    f_units = ["zero h_amax", "FC1", "FC2"]
+    b_units = ["zero dz_amax", "dH", "dZ code transpose", "dB", "dA", "dX"]
+    per = {u: [] for u in f_units + b_units}
+    for k in range(reps):
+        for fn, units in ((fwd, f_units), (bwd, b_units)):
+            ev = hev.create(2 * len(units))
+            tp.tp_launch_events(ev)
+            fn()
+            tp.tp_launch_events(None)
+            torch.cuda.synchronize()
+            for i, u in enumerate(units):
+                per[u].append(hev.ms(ev[2 * i], ev[2 * i + 1]))
+    hev.free()
+    per = {u: median(v) for u, v in per.items()}
     f_fl = 2.0 * N * Hd * Ft * (3 if sw else 2)
     b_fl = 2 * f_fl
     tf = lambda fl, t: round(tflops(fl, t), 1)
+    per_fl = {"FC1": 2.0 * N * Hd * Ft * (2 if sw else 1), "FC2": 2.0 * N * Hd * Ft,
+              "dH": 2.0 * N * Hd * Ft, "dB": 2.0 * N * Hd * Ft,
+              "dA": 2.0 * N * Hd * Ft * (2 if sw else 1), "dX": 2.0 * N * Hd * Ft * (2 if sw else 1)}
+    launches = {u: {"us": round(per[u] * 1e3, 1)} for u in per}
+    for u, fl in per_fl.items():
+        launches[u]["frac_of_fp8_peak"] = round(tflops(fl, per[u]) / PEAK_FP8_TFLOPS, 4)
     fwd_d = {"gemm_ms": round(ms[1], 4), "gemm_tflops": tf(f_fl, ms[1]),
              "gemm_frac_of_fp8_peak": round(tflops(f_fl, ms[1]) / PEAK_FP8_TFLOPS, 4),
              "quantize_ms": round(ms[0], 4),
@@ -652,7 +676,8 @@ def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, hev, reps=10):
              "frac_of_fp8_peak": round(tflops(b_fl, ms[3]) / PEAK_FP8_TFLOPS, 4),
              "quantize_transpose_ms": round(ms[2], 4),
              "backward_tflops_with_quantize": tf(b_fl, ms[2] + ms[3]),
-             "step_tflops_with_quantize": tf(f_fl + b_fl, sum(ms))}
+             "step_tflops_with_quantize": tf(f_fl + b_fl, sum(ms)),
+             "launches": launches}
     return fwd_d, bwd_d
 
 
@@ -728,6 +753,19 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    if args.only == "grouped":
+        print(json.dumps({"grouped_experts": grouped_expert_timing(torch, tp, wl, hev,
+                                                                   args.sets)}), flush=True)
+        return
+    if args.only == "fp8":
+        d0 = wl.gen_mlp_inputs(w)
+        from tensor_transformer_mlp_02_amd.tensors import to_device
+        t = {k: (to_device(v) if v is not None else None) for k, v in d0.items()
+             if k in ("X", "A", "A_up", "B", "dY")}
+        f8, f8b = fp8_timing(torch, tp, wl, w, t["X"], t["A"], t["A_up"], t["B"], t["dY"],
+                             torch.cuda.current_stream(), hev)
+        print(json.dumps({"fp8_forward": f8, "fp8_backward": f8b}), flush=True)
+        return
     progress(f"{w.name}: drawing {args.sets} input sets")
     sb = ShardBench(torch, tp, wl, w, args.sets, hev, args.sum_workgroups, streams)
     progress("headline steps")

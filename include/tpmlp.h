@@ -212,11 +212,12 @@ int tp_partial_sum_scatter(int32_t dtype, int32_t T, const void *const *partials
 
 /*
  * tp_partial_sum_capped -- tp_partial_sum on at most `max_workgroups`
- * workgroups of 256 threads (which stride over the whole tensor), so the
- * sum occupies only a few compute units and can run on a second stream
- * beside the shard's GEMMs, the way the all-reduce it stands in for
- * overlaps computation (§三 3.4 places the reduce between the shard's
- * forward and the next layer, and its backward twin after dX_i).
+ * workgroups of 256 threads (which stride over the whole tensor), for a
+ * second stream beside the shard's GEMMs, the way the all-reduce it stands
+ * in for overlaps computation (§三 3.4 places the reduce between the
+ * shard's forward and the next layer, and its backward twin after dX_i).
+ * Its kernel keeps few registers per lane, so its wavefronts can share
+ * SIMDs with a running GEMM's instead of holding compute units.
  *   max_workgroups  >= 1; other arguments as in tp_partial_sum
  * The result is bitwise identical to tp_partial_sum's (same order).
  */

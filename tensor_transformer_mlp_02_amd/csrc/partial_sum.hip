@@ -2,16 +2,16 @@
 // out = sum_{i<T} P_i, summed in fp32 in the fixed order i = 0..T-1 and
 // rounded once.  Bandwidth-bound: every byte is read or written once.
 //
-// A workgroup owns PS_U x 256 consecutive chunks of 8 elements (16 bytes of
-// bf16, 32 bytes of fp32) per pass, a thread PS_U of them, 256 chunks
-// apart: a wavefront's loads cover 1 KiB contiguous per instruction and a
-// workgroup reads one contiguous 8 KiB (bf16) range of each partial, which
-// the memory system serves faster than ranges spread a grid-width apart
-// (5.9 against 5.2 TB/s for 8 bf16 partials of 64 MiB on MI355X).  The
-// partials are taken in groups of PS_G:
-// all PS_G x PS_U loads of a group are issued before the first add, which
-// keeps 256 bytes (bf16) per lane in flight; the adds then run in partial
-// order.  The grid strides over the chunks, so any workgroup count covers
+// A workgroup owns U x 256 consecutive chunks of 8 elements (16 bytes of
+// bf16, 32 bytes of fp32) per pass, a thread U of them, 256 chunks apart
+// (U = 4 for bf16, 2 for fp32: 64 bytes of each partial per thread either
+// way): a wavefront's loads cover 1 KiB contiguous per instruction and a
+// workgroup reads one contiguous 16 KiB range of each partial, which the
+// memory system serves faster than ranges spread a grid-width apart (8
+// bf16 partials of 64 MiB on MI355X: 5.96 TB/s, against 5.76 for 8 KiB
+// ranges and 5.2 spread apart).  The partials are taken in groups of PS_G:
+// all PS_G x U loads of a group are issued before the first add, which
+// keeps 512 bytes per lane in flight; the adds then run in partial order.  The grid strides over the chunks, so any workgroup count covers
 // the whole tensor (the capped variant runs on a few compute units beside
 // other kernels).  The T partial pointers travel by value.
 #include "common.h"
@@ -25,7 +25,8 @@ struct PartialPtrs {
 
 constexpr int PS_NT = 256;
 constexpr int PS_G = 8;  // partials whose loads are in flight together
-constexpr int PS_U = 2;  // chunks per thread per pass
+// chunks per thread per pass
+template <typename T> struct PsU { static constexpr int value = sizeof(T) == 2 ? 4 : 2; };
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -77,10 +78,11 @@ __device__ __forceinline__ float load1(const float* p, int64_t i) { return p[i];
 __device__ __forceinline__ void store1(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 __device__ __forceinline__ void store1(float* p, int64_t i, float v) { p[i] = v; }
 
-template <typename T>
-__global__ __launch_bounds__(PS_NT) void partial_sum_kernel(PartialPtrs ptrs, int nparts,
-                                                            int64_t nchunks, int64_t count,
-                                                            void* out_) {
+// The sum over the chunks a grid of workgroups covers (U chunks per thread
+// per pass; see the file comment).
+template <typename T, int PS_U>
+__device__ __forceinline__ void partial_sum_body(const PartialPtrs& ptrs, int nparts,
+                                                 int64_t nchunks, int64_t count, void* out_) {
   T* out = reinterpret_cast<T*>(out_);
   constexpr int64_t stride = PS_NT;  // between a thread's chunks
   const int64_t pass = (int64_t)gridDim.x * PS_NT * PS_U;
@@ -134,22 +136,56 @@ __global__ __launch_bounds__(PS_NT) void partial_sum_kernel(PartialPtrs ptrs, in
   }
 }
 
+template <typename T>
+__global__ __launch_bounds__(PS_NT) void partial_sum_kernel(PartialPtrs ptrs, int nparts,
+                                                            int64_t nchunks, int64_t count,
+                                                            void* out) {
+  partial_sum_body<T, PsU<T>::value>(ptrs, nparts, nchunks, count, out);
+}
+
+// The capped sum runs beside GEMMs on another stream.  A GEMM wavefront
+// holds at most 416 of the 512 registers per lane of its SIMD, so a
+// wavefront of this kernel (one chunk per thread per pass, at most 88
+// registers) fits beside it: the sum shares SIMDs with the GEMM's
+// wavefronts instead of holding compute units the GEMM's workgroups wait
+// for.  Same order of additions, same results as partial_sum_kernel.
+constexpr int PS_NARROW_VGPRS = 88;
+template <typename T>
+__global__ __launch_bounds__(PS_NT) __attribute__((amdgpu_num_vgpr(PS_NARROW_VGPRS)))
+void partial_sum_narrow_kernel(PartialPtrs ptrs, int nparts, int64_t nchunks, int64_t count,
+                               void* out) {
+  partial_sum_body<T, 1>(ptrs, nparts, nchunks, count, out);
+}
+
 hipError_t partial_sum_launch(int dtype, int T, const void* const* parts, int64_t count,
                               void* out, int max_blocks, hipStream_t stream) {
   if (count == 0) return hipSuccess;
   PartialPtrs ptrs;
   for (int i = 0; i < TP_MAX_SHARDS; ++i) ptrs.p[i] = i < T ? parts[i] : nullptr;
   const int64_t nchunks = count / 8;
-  int64_t blocks = (nchunks + PS_NT * PS_U - 1) / (PS_NT * PS_U);
+  const bool narrow = max_blocks > 0;
+  const int per_block =
+      PS_NT * (narrow ? 1 : (dtype == TP_BF16 ? PsU<bf16_t>::value : PsU<float>::value));
+  int64_t blocks = (nchunks + per_block - 1) / per_block;
   if (blocks < 1) blocks = 1;
   if (blocks > 8192) blocks = 8192;
-  if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
-  if (dtype == TP_BF16)
-    hipLaunchKernelGGL(partial_sum_kernel<bf16_t>, dim3((unsigned)blocks), dim3(PS_NT), 0,
-                       stream, ptrs, T, nchunks, count, out);
-  else
-    hipLaunchKernelGGL(partial_sum_kernel<float>, dim3((unsigned)blocks), dim3(PS_NT), 0,
-                       stream, ptrs, T, nchunks, count, out);
+  if (narrow && blocks > max_blocks) blocks = max_blocks;
+  const dim3 grid((unsigned)blocks), block(PS_NT);
+  if (dtype == TP_BF16) {
+    if (narrow)
+      hipLaunchKernelGGL(partial_sum_narrow_kernel<bf16_t>, grid, block, 0, stream, ptrs, T,
+                         nchunks, count, out);
+    else
+      hipLaunchKernelGGL(partial_sum_kernel<bf16_t>, grid, block, 0, stream, ptrs, T, nchunks,
+                         count, out);
+  } else {
+    if (narrow)
+      hipLaunchKernelGGL(partial_sum_narrow_kernel<float>, grid, block, 0, stream, ptrs, T,
+                         nchunks, count, out);
+    else
+      hipLaunchKernelGGL(partial_sum_kernel<float>, grid, block, 0, stream, ptrs, T, nchunks,
+                         count, out);
+  }
   return hipGetLastError();
 }
 
