@@ -33,7 +33,8 @@ STATUS_NAMES = {0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_DTYP
                 7: "TP_ERR_HIP", 8: "TP_ERR_ALIAS"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libtpmlp.so")
+# TPMLP_LIBRARY selects another build of the library (a build-option variant)
+library_path = os.environ.get("TPMLP_LIBRARY") or os.path.join(_HERE, "libtpmlp.so")
 
 
 class TpError(RuntimeError):

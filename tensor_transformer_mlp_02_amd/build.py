@@ -3,7 +3,14 @@
 Every HIP source is compiled with packed-fp32 instruction forms disabled
 (the compiler otherwise forms v_pk_* fp32 arithmetic from ordinary float
 code); the library is written for gfx950 only.
+
+`--define NAME=VALUE` builds a variant with a build option set (e.g.
+TP_TILE_ORDER, the GEMM tile placement) into a folder of its own,
+_build_<hash of the options>/libtpmlp.so (or --out); the binding loads such
+a library when TPMLP_LIBRARY names it.
 """
+import argparse
+import hashlib
 import os
 import shutil
 import subprocess
@@ -23,9 +30,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *(f"-D{d}" for d in defines), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,18 +45,32 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, defines=(), out=None) -> str:
+    defines = list(defines)
+    build_dir = BUILD_DIR
+    if defines:
+        tag = hashlib.sha256(" ".join(defines).encode()).hexdigest()[:12]
+        build_dir = f"{BUILD_DIR}_{tag}"
+    if out is None:
+        out = os.path.join(build_dir, "libtpmlp.so") if defines else OUT
+    if defines and os.path.abspath(out) == OUT:
+        raise ValueError("a build with defines may not replace the default library")
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE")
+    ap.add_argument("--out", default=None)
+    a = ap.parse_args()
+    print(build(verbose=True, defines=a.define,
+                out=None if a.out is None else os.path.abspath(a.out)))

@@ -164,7 +164,15 @@ struct GemmArgs {
 // within a problem tiles are rastered in groups of RASTER_G tile rows
 // (column by column inside a group), so the blocks that run together on
 // one XCD share a few operand panels instead of touching all of them.
-constexpr int RASTER_G = 4;
+//
+// TP_TILE_ORDER (a build option, default 0) exists to measure what that
+// saving is worth: 1 places tiles in dispatch order (consecutive tiles on
+// different XCDs), 2 rasters groups of a single tile row.  Every order
+// computes each tile the same way, so results are identical.
+#ifndef TP_TILE_ORDER
+#define TP_TILE_ORDER 0
+#endif
+constexpr int RASTER_G = TP_TILE_ORDER == 2 ? 1 : 4;
 
 struct TileCoord {
   int e, tm, tn;
@@ -172,6 +180,7 @@ struct TileCoord {
 };
 
 __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
+  if constexpr (TP_TILE_ORDER == 1) return b;
   const int xcd = b & 7, slot = b >> 3;
   const int q = nb >> 3, r = nb & 7;
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
