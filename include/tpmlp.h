@@ -142,7 +142,9 @@ size_t tp_mlp_shard_bwd_workspace(const tp_mlp_desc *desc);
  *   dA  [H,F_shard] fp32   gradient of A (the gate projection for SwiGLU)
  *   dA_up [H,F_shard] fp32 SwiGLU only, else NULL
  *   dB  [F_shard,H] fp32
- *   workspace, ws_bytes    at least tp_mlp_shard_bwd_workspace(desc) bytes
+ *   workspace, ws_bytes    at least tp_mlp_shard_bwd_workspace(desc) bytes;
+ *                   on return it holds dZ, row-major [N,F_shard] in the
+ *                   dtype ([N,2*F_shard] = [dG | dU] for SwiGLU)
  * The activation derivative is applied inside the kernel that forms
  * dY B_i^T (in its epilogue); no separate elementwise pass runs.
  * With N = 0 the weight gradients are written as zeros.

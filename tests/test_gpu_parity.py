@@ -45,6 +45,24 @@ def _run_shard(w, d, save=True, backward=True, desc=None):
     return dev, buf
 
 
+def _dz_rows(buf, w, N, Ft, rows=None):
+    """dZ as the backward left it in its workspace: [N, Ft] (GeLU) or
+    [N, 2 Ft] = [dG | dU] (SwiGLU), in the shard's storage type."""
+    zw = 2 * Ft if w.act == wl.ACT_SWIGLU else Ft
+    dt = torch.bfloat16 if w.dtype == wl.DT_BF16 else torch.float32
+    n = N * zw * (2 if dt == torch.bfloat16 else 4)
+    z = buf.ws[:n].view(dt).reshape(N, zw)
+    return f64(to_host(z if rows is None else z[rows]))
+
+
+def _check_dz(w, b, dz, Ft, tol):
+    if w.act == wl.ACT_SWIGLU:
+        assert_close("dG (workspace)", dz[:, :Ft], b["dZ"], tol)
+        assert_close("dU (workspace)", dz[:, Ft:], b["dU"], tol)
+    else:
+        assert_close("dZ (workspace)", dz, b["dZ"], tol)
+
+
 def _check_full(w, d, buf, backward=True, tol=None):
     tol = TOL[w.dtype] if tol is None else tol
     f = oracle.mlp_fwd(d["X"], d["A"], d["B"], w.act, d["A_up"])
@@ -59,6 +77,8 @@ def _check_full(w, d, buf, backward=True, tol=None):
     assert_close("Y", f64(to_host(buf.Y)), f["Y"], tol)
     if backward:
         b = oracle.mlp_bwd(d["X"], d["A"], d["B"], w.act, d["dY"], f, d["A_up"])
+        if d["X"].shape[0] > 0:
+            _check_dz(w, b, _dz_rows(buf, w, d["X"].shape[0], Ft), Ft, tol)
         assert_close("dX", f64(to_host(buf.dX)), b["dX"], tol)
         assert_close("dA", to_host(buf.dA), b["dA"], tol)
         assert_close("dB", to_host(buf.dB), b["dB"], tol)
@@ -397,6 +417,7 @@ def _sampled_full(name, n_rows=128, n_cols=64):
     if not w.backward:
         return
     b = oracle.mlp_bwd(sub["X"], d["A"], d["B"], w.act, sub["dY"], f, d["A_up"])
+    _check_dz(w, b, _dz_rows(buf, w, w.N, Ft, rows), Ft, tol)
     assert_close("dX rows", f64(to_host(buf.dX[rows])), b["dX"], tol)
     # weight gradients: the shard narrowed to sampled columns, all tokens
     cols = sample_idx(Ft, n_cols)
