@@ -47,7 +47,10 @@ def _quantize_gpu(x_bits, scale, fmt=E4M3, transpose=False):
 @pytest.mark.parametrize("transpose", [False, True])
 def test_quantize_codes_bitwise(fmt, transpose):
     name = "e4m3" if fmt == E4M3 else "e5m2"
-    for rows, cols, std, scale in ((272, 136, 1.0, 64.0), (64, 8, 1e-3, 1.0), (1040, 520, 3.0, 300.0)):
+    # (4096 x 2304: more pieces than one pass of the capped grid covers, and
+    # more 64 x 256 blocks than workgroups in the transposed form)
+    for rows, cols, std, scale in ((272, 136, 1.0, 64.0), (64, 8, 1e-3, 1.0), (1040, 520, 3.0, 300.0),
+                                   (4096, 2304, 1.0, 16.0)):
         x = wl.normal_bf16(777 + rows, (rows, cols), std)
         print(f"[gpu] fp8 quantize {name} transpose={transpose} {rows}x{cols} scale={scale}",
               flush=True)
@@ -183,7 +186,8 @@ def test_fp8_forward_swiglu_shard_sampled_rows():
 # backward: E5M2 gradients against E4M3 weights and activations
 # ---------------------------------------------------------------------------
 def test_byte_transpose_bitwise():
-    for rows, cols in ((16, 16), (272, 144), (1040, 528), (4096, 96)):
+    # (8208 x 4096: more 64 x 256 blocks than workgroups)
+    for rows, cols in ((16, 16), (272, 144), (1040, 528), (4096, 96), (8208, 4096)):
         print(f"[gpu] fp8 transpose {rows}x{cols}", flush=True)
         x = np.random.default_rng(rows + cols).integers(0, 256, (rows, cols), dtype=np.uint8)
         q = torch.from_numpy(x).to("cuda")
