@@ -101,8 +101,9 @@ def parse():
                    help="0: time the headline steps only (no warm, in-order, other-shape, "
                         "reduce-scatter, accumulation, MoE or FP8 measurements), as for "
                         "the profiler's per-kernel summaries")
-    p.add_argument("--only", default="", choices=["", "grouped", "fp8"],
-                   help="time only the grouped experts or only the FP8 shard (for the "
+    p.add_argument("--only", default="", choices=["", "grouped", "fp8", "dact"],
+                   help="time only the grouped experts, the FP8 shard, or the two "
+                        "placements of the activation derivative in the backward (for the "
                         "profiler's per-kernel summaries); prints their JSON")
     p.add_argument("--clock", type=int, default=1,
                    help="1: sample the shader clock while the steps run again")
@@ -760,6 +761,48 @@ def accumulation_timing(torch, tp, sb, hev, reps=5):
     return out
 
 
+def dact_placement_timing(torch, tp, w, sb, hev, reps=5):
+    """The backward with the activation derivative in the epilogue of dY B^T
+    (tp_mlp_shard_bwd, the default) beside the backward whose dA and dX
+    GEMMs form dZ from dH and Z as they load it
+    (tp_mlp_shard_bwd_dact_prologue): each call's median duration, and each
+    launch's from the same calls with every launch bracketed by events."""
+    stream = torch.cuda.current_stream()
+    s, b, d = sb.sets[0], sb.buf, sb.desc
+    # the saved Z and H of this input set
+    tp.tp_mlp_shard_fwd(d, s["X"], s["A"], s["A_up"], s["B"], b.Z, b.H, b.Y, stream=stream)
+    fl = role_flops(w)
+    out = {}
+    for name, fn in (("epilogue", tp.tp_mlp_shard_bwd),
+                     ("operand_loads", tp.tp_mlp_shard_bwd_dact_prologue)):
+        calls = hev.create(2 * reps)
+        per = [hev.create(2 * len(GEMM_ROLES_BWD)) for _ in range(reps)]
+        for k in range(2 * reps):
+            timed_launches = k >= reps
+            if timed_launches:
+                tp.tp_launch_events(per[k - reps])
+            else:
+                hev.record(calls[2 * k], stream)
+            fn(d, s["X"], s["A"], s["A_up"], s["B"], b.Z, b.H, s["dY"], b.dX, b.dA, b.dA_up,
+               b.dB, b.ws, b.ws_bytes, stream=stream)
+            if timed_launches:
+                tp.tp_launch_events(None)
+            else:
+                hev.record(calls[2 * k + 1], stream)
+        torch.cuda.synchronize()
+        ms = median([hev.ms(calls[2 * k], calls[2 * k + 1]) for k in range(reps)])
+        launches = {}
+        for i, r in enumerate(GEMM_ROLES_BWD):
+            us = median([hev.ms(e[2 * i], e[2 * i + 1]) for e in per]) * 1e3
+            launches[r] = {"us": round(us, 1), "tflops": round(tflops(fl[r], us * 1e-3), 1)}
+        out[name] = {"bwd_ms": round(ms, 4),
+                     "tflops": round(tflops(sum(fl[r] for r in GEMM_ROLES_BWD), ms), 1),
+                     "launches": launches}
+        hev.free()
+    out["default"] = "epilogue"
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -807,6 +850,10 @@ def main():
         return
     progress(f"{w.name}: drawing {args.sets} input sets")
     sb = ShardBench(torch, tp, wl, w, args.sets, hev, args.sum_workgroups, streams)
+    if args.only == "dact":
+        print(json.dumps({"act_derivative_placement": dact_placement_timing(torch, tp, w, sb,
+                                                                            hev)}), flush=True)
+        return
     progress("headline steps")
     cold = sb.run(args.sets, overlap, args.steps, args.warmup, y_after=args.sum_y_after)
     head = summarize(w, cold, f"{args.sets} input sets rotated "
@@ -843,11 +890,13 @@ def main():
             clock["bf16_peak_at_sclk"] = round(PEAK_BF16_TFLOPS * ghz / 2.4, 1)
             clock["gemm_frac_at_sclk"] = round(gemm_tf / (PEAK_BF16_TFLOPS * ghz / 2.4), 4)
 
-    rs = acc_cmp = None
+    rs = acc_cmp = dact_cmp = None
     if args.side and w.S % w.T == 0:
         rs = reduce_scatter_timing(torch, tp, w, sb, hev)
     if args.side and w.backward:
         acc_cmp = accumulation_timing(torch, tp, sb, hev)
+        progress("activation-derivative placement")
+        dact_cmp = dact_placement_timing(torch, tp, w, sb, hev)
     f8 = f8b = None
     if (args.side and args.fp8 and w.H % 128 == 0 and w.Ft % 128 == 0 and w.N % 128 == 0
             and w.backward):
@@ -942,6 +991,7 @@ def main():
         "other_shapes": others or None,
         "reduce_scatter_rank0": rs,
         "grad_accumulation": acc_cmp,
+        "act_derivative_placement": dact_cmp,
         "moe_dispatch_combine": moe,
         "grouped_experts": grouped,
         "fp8_forward": f8,

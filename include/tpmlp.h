@@ -296,6 +296,31 @@ int tp_mlp_shard_bwd_accum(const tp_mlp_desc *desc, const void *X, const void *A
                            const void *H_act, const void *dY, void *dX_partial,
                            float *dA, float *dA_up, float *dB, void *workspace,
                            size_t ws_bytes, void *stream);
+
+/*
+ * tp_mlp_shard_bwd_dact_prologue -- the same backward ([P1] §三 3.4; the
+ * SwiGLU MLP of §七) with the activation derivative at the other place a
+ * backward GEMM can hold it: dH = dY B_i^T is written plainly, and the
+ * GEMMs that consume dZ (dA = X^T dZ and dX_partial = dZ A_i^T) form each
+ * piece of dZ (GeLU: dH * gelu'(Z); SwiGLU: [dH * U * silu'(G) | dH *
+ * silu(G)]) from dH and Z_save while they load it, before the MFMAs use
+ * it.  Every tile that reads a piece forms it again: each element's
+ * derivative is computed H / 256 times in each of the two GEMMs (bf16
+ * tiles; H / 64 for fp32) instead of once.  It exists to be measured against
+ * tp_mlp_shard_bwd, whose placement (in the epilogue of dY B_i^T) is the
+ * default.
+ *   Arguments, layouts, ownership and errors as tp_mlp_shard_bwd, except:
+ *   workspace, ws_bytes    at least N*F_shard elements of the dtype
+ *                   (tp_mlp_shard_bwd_workspace(desc) bytes are enough);
+ *                   on return it holds dH = dY B_i^T, row-major [N,F_shard]
+ * Results agree with tp_mlp_shard_bwd's up to rounding (dZ is formed from
+ * the stored dH here, from dH's fp32 sums there), not bit for bit.
+ */
+int tp_mlp_shard_bwd_dact_prologue(const tp_mlp_desc *desc, const void *X, const void *A,
+                                   const void *A_up, const void *B, const void *Z_save,
+                                   const void *H_act, const void *dY, void *dX_partial,
+                                   float *dA, float *dA_up, float *dB, void *workspace,
+                                   size_t ws_bytes, void *stream);
 int tp_grouped_expert_bwd_accum(const tp_expert_desc *desc, const int64_t *offsets,
                                 const void *X_perm, const void *Wg, const void *Wu,
                                 const void *Wd, const void *Z_save,

@@ -17,7 +17,7 @@ __all__ = [
     "TP_F32", "TP_BF16", "TP_ACT_GELU_TANH", "TP_ACT_SWIGLU", "TpError",
     "tp_mlp_desc", "tp_expert_desc", "lib", "library_path",
     "tp_mlp_shard_fwd", "tp_mlp_shard_bwd", "tp_mlp_shard_bwd_accum", "tp_mlp_shard_bwd_workspace",
-    "tp_mlp_shard_bwd_noalloc",
+    "tp_mlp_shard_bwd_noalloc", "tp_mlp_shard_bwd_dact_prologue",
     "tp_partial_sum", "tp_partial_sum_capped", "tp_partial_sum_scatter", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
     "tp_grouped_expert_bwd_workspace", "tp_grouped_expert_bwd_accum",
     "tp_moe_permute", "tp_moe_combine", "tp_moe_combine_bwd",
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.tp_mlp_shard_bwd_noalloc.restype = ctypes.c_int
     L.tp_mlp_shard_bwd_accum.argtypes = [D] + [_vp] * 12 + [ctypes.c_size_t, _vp]
     L.tp_mlp_shard_bwd_accum.restype = ctypes.c_int
+    L.tp_mlp_shard_bwd_dact_prologue.argtypes = [D] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+    L.tp_mlp_shard_bwd_dact_prologue.restype = ctypes.c_int
     L.tp_partial_sum.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_vp),
                                  ctypes.c_int64, _vp, _vp]
     L.tp_partial_sum.restype = ctypes.c_int
@@ -268,6 +270,22 @@ def tp_mlp_shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_
                 (dA_up, n["dA"], "dA_up"), (dB, n["dB"], "dB"),
                 (workspace, int(ws_bytes), "workspace")])
     return _check(fn(ctypes.byref(d), *p, int(ws_bytes), _stream(stream)))
+
+
+def tp_mlp_shard_bwd_dact_prologue(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA,
+                                   dA_up, dB, workspace, ws_bytes: int, stream=None) -> int:
+    """The backward with the activation derivative formed by the dA and dX
+    GEMMs as they load dZ; the workspace (N * F_shard elements) ends up
+    holding dH."""
+    d = _desc(desc)
+    n = _shard_sizes(d)
+    p = _sized([(X, n["X"], "X"), (A, n["A"], "A"), (A_up, n["A"], "A_up"), (B, n["B"], "B"),
+                (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"), (dY, n["Y"], "dY"),
+                (dX_partial, n["X"], "dX_partial"), (dA, n["dA"], "dA"),
+                (dA_up, n["dA"], "dA_up"), (dB, n["dB"], "dB"),
+                (workspace, int(ws_bytes), "workspace")])
+    return _check(lib().tp_mlp_shard_bwd_dact_prologue(ctypes.byref(d), *p, int(ws_bytes),
+                                                       _stream(stream)))
 
 
 def tp_mlp_shard_bwd_noalloc(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up,

@@ -365,10 +365,13 @@ void* scratch_address(int* err) {
 
 // use_scratch: the workspace is the device's scratch array (resolved after
 // the device check; its size is checked against the array's)
+// dact_in_loads: dH is written plainly and the dA / dX GEMMs form dZ from
+// it and Z_save as they load it (the workspace then holds dH)
 int shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void* A_up,
               const void* B, const void* Z_save, const void* H_act, const void* dY,
               void* dX_partial, float* dA, float* dA_up, float* dB, void* workspace,
-              size_t ws_bytes, void* stream, bool accumulate, bool use_scratch = false) {
+              size_t ws_bytes, void* stream, bool accumulate, bool use_scratch = false,
+              bool dact_in_loads = false) {
   Shard s;
   int rc = check_desc(desc, s);
   if (rc) return rc;
@@ -391,7 +394,7 @@ int shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void*
   Buf out_opt[] = {{dA_up, (size_t)(s.H * s.Ft) * 4, "dA_up"}};
   if ((rc = check_ptrs(in_opt, 1, false))) return rc;
   if ((rc = check_ptrs(out_opt, 1, false))) return rc;
-  const size_t need = dz_bytes(s);
+  const size_t need = dact_in_loads ? (size_t)(s.N * s.Ft) * e : dz_bytes(s);
   if (use_scratch) {
     if (need > (size_t)TP_NOALLOC_SCRATCH_BYTES)
       return fail(TP_ERR_WORKSPACE,
@@ -422,7 +425,17 @@ int shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void*
   hipError_t he;
 
   // 1. dZ = (dY B^T) * act'(Z): the activation derivative in the epilogue
-  if (N > 0) {
+  //    (or dH = dY B^T alone, when the consumers form dZ)
+  if (N > 0 && dact_in_loads) {
+    GemmArgs g = dense_args(N, Ft, H);
+    g.a = {dY, nullptr, H, 0, 0};
+    g.b = {B, nullptr, H, 0, 0};
+    g.epi.out0 = workspace;
+    g.epi.ld0 = Ft;
+    // (the plain both-K-contiguous product kind)
+    he = run_gemm(s.dtype, GK_DX, g, st);
+    if (he != hipSuccess) return hip_fail(he, "dH launch");
+  } else if (N > 0) {
     GemmArgs g = dense_args(N, Ft, H);
     g.a = {dY, nullptr, H, 0, 0};
     g.b = {B, nullptr, H, 0, 0};
@@ -454,8 +467,12 @@ int shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void*
     g.epi.ld0 = Ft;
     g.epi.ld1 = Ft;
     g.epi.split = Ft;
-    const GemmKind k = sw ? (accumulate ? GK_WGRAD_SPLIT_ACC : GK_WGRAD_SPLIT)
-                          : (accumulate ? GK_WGRAD_ACC : GK_WGRAD);
+    GemmKind k = sw ? (accumulate ? GK_WGRAD_SPLIT_ACC : GK_WGRAD_SPLIT)
+                    : (accumulate ? GK_WGRAD_ACC : GK_WGRAD);
+    if (dact_in_loads) {
+      g.b = {workspace, Z_save, Ft, 0, Ft};
+      k = sw ? GK_WGRAD_SPLIT_DACT_SWIGLU : GK_WGRAD_DACT_GELU;
+    }
     he = run_gemm(s.dtype, k, g, st);
     if (he != hipSuccess) return hip_fail(he, "dA launch");
   }
@@ -466,7 +483,12 @@ int shard_bwd(const tp_mlp_desc* desc, const void* X, const void* A, const void*
     g.b = {A, A_up, Ft, 0, Ft};
     g.epi.out0 = dX_partial;
     g.epi.ld0 = H;
-    he = run_gemm(s.dtype, sw ? GK_DX_KSPLIT : GK_DX, g, st);
+    GemmKind k = sw ? GK_DX_KSPLIT : GK_DX;
+    if (dact_in_loads) {
+      g.a = {workspace, Z_save, Ft, 0, Ft};
+      k = sw ? GK_DX_KSPLIT_DACT_SWIGLU : GK_DX_DACT_GELU;
+    }
+    he = run_gemm(s.dtype, k, g, st);
     if (he != hipSuccess) return hip_fail(he, "dX launch");
   }
   return ok();
@@ -487,6 +509,15 @@ int tp_mlp_shard_bwd_noalloc(const tp_mlp_desc* desc, const void* X, const void*
                              float* dA_up, float* dB, void* stream) {
   return shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up, dB, nullptr, 0,
                    stream, false, true);
+}
+
+int tp_mlp_shard_bwd_dact_prologue(const tp_mlp_desc* desc, const void* X, const void* A,
+                                   const void* A_up, const void* B, const void* Z_save,
+                                   const void* H_act, const void* dY, void* dX_partial,
+                                   float* dA, float* dA_up, float* dB, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  return shard_bwd(desc, X, A, A_up, B, Z_save, H_act, dY, dX_partial, dA, dA_up, dB, workspace,
+                   ws_bytes, stream, false, false, true);
 }
 
 int tp_mlp_shard_bwd_accum(const tp_mlp_desc* desc, const void* X, const void* A,

@@ -83,6 +83,32 @@ __device__ __forceinline__ float silu_grad_f(float g) {
   return s * (1.0f + g * (1.0f - s));
 }
 
+// The activation derivative applied to dH while a backward GEMM loads its
+// dZ operand (instead of in the epilogue of dY B^T): one element of dZ =
+// dh gelu'(z) (GeLU), or of [dG | dU] (SwiGLU: second = false gives dG = dh
+// u silu'(g), second = true gives dU = dh silu(g)).  This runs once per
+// element for every tile that reads it, on the vector ALUs, so the sigmoid
+// takes the hardware reciprocal (v_rcp_f32, 1 ulp) instead of a divide.
+enum { DACT_NONE = 0, DACT_GELU = 1, DACT_SWIGLU = 2 };
+
+__device__ __forceinline__ float sigmoid_rcp_f(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+template <int PRO>
+__device__ __forceinline__ float dact_elem(float dh, float z0, float z1, bool second) {
+  if constexpr (PRO == DACT_GELU) {
+    const float z2 = z0 * z0;
+    const float s = sigmoid_rcp_f(2.0f * TP_GELU_C * (z0 + TP_GELU_K * z2 * z0));
+    return dh * (s + z0 * 2.0f * s * (1.0f - s) * TP_GELU_C * (1.0f + 3.0f * TP_GELU_K * z2));
+  } else {
+    // dU = dh s g and dG = dh s u (1 + g (1 - s)): one select, no branch
+    const float s = sigmoid_rcp_f(z0);
+    const float t = second ? z0 : z1 * (1.0f + z0 * (1.0f - s));
+    return dh * s * t;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // GEMM arguments
 //

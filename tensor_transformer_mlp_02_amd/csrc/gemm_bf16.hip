@@ -253,6 +253,98 @@ __device__ __forceinline__ void store_k(bf16_t* tile, int tid, const Stage<NW>& 
   }
 }
 
+// ---- dZ operand formed from dH and the saved activations -----------------
+// The operand tile is taken in STAGE_N pieces per thread of 8 elements
+// each: dH and the saved Z (GeLU) or G and U (SwiGLU) at the same place are
+// loaded into registers, and the 8 dZ values are formed from them on their
+// way into shared memory (as bf16, where the direct loads would have put
+// them).  Operand column f of [dG | dU] reads dH and G at f mod split and,
+// for dG, U.  Masked pieces read as zeros, which give dZ = 0.  `split` is a
+// multiple of 8, so no piece straddles it.  Two register slots take the
+// pieces in turn (piece i in slot i % 2), which keeps 128 accumulators and
+// the staging within the register file of two wavefronts per SIMD.
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+template <int PRO>
+struct DactStage {
+  u32x4v_t dh[2], z0[2], z1[PRO == DACT_SWIGLU ? 2 : 1];
+};
+
+// Piece loads are buffer loads with 32-bit offsets from per-tile bases
+// (rd: dH, rz: the saved activations), `row` counted from the base; a
+// masked piece takes an out-of-range offset and reads zeros.
+template <int PRO>
+__device__ __forceinline__ void dact_load(rsrc_t rd, rsrc_t rz, int64_t ld, int64_t split,
+                                          int row, int64_t f, bool ok, bool second, int slot,
+                                          DactStage<PRO>& s) {
+  const int64_t zld = PRO == DACT_SWIGLU ? 2 * split : split;
+  const uint32_t od = ok ? (uint32_t)((row * ld + f) * 2) : OOB_OFF;
+  const uint32_t oz = ok ? (uint32_t)((row * zld + f) * 2) : OOB_OFF;
+  s.dh[slot] = __builtin_amdgcn_raw_buffer_load_b128(rd, od, 0, 0);
+  s.z0[slot] = __builtin_amdgcn_raw_buffer_load_b128(rz, oz, 0, 0);
+  if constexpr (PRO == DACT_SWIGLU)
+    s.z1[slot] = __builtin_amdgcn_raw_buffer_load_b128(rz, second ? OOB_OFF : oz,
+                                                       (int)(split * 2), 0);
+}
+
+template <int PRO>
+__device__ __forceinline__ uint4 dact_form(const DactStage<PRO>& s, int slot, bool second) {
+  uint32_t o[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t wd = s.dh[slot][p], wz = s.z0[slot][p];
+    const uint32_t wu = PRO == DACT_SWIGLU ? s.z1[slot][p] : 0u;
+    const float lo = dact_elem<PRO>(__uint_as_float(wd << 16), __uint_as_float(wz << 16),
+                                    __uint_as_float(wu << 16), second);
+    const float hi = dact_elem<PRO>(__uint_as_float(wd & 0xffff0000u),
+                                    __uint_as_float(wz & 0xffff0000u),
+                                    __uint_as_float(wu & 0xffff0000u), second);
+    o[p] = pack_bf16x2(lo, hi);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// K-contiguous dZ tile (256 rows x 64 k; bases at the tile's first row):
+// piece c = tid + NT i covers row c / 8, k chunk c % 8
+template <int NW, int PRO>
+__device__ __forceinline__ void dact_load_k(rsrc_t rd, rsrc_t rz, int64_t ld, int64_t split,
+                                            int rows_valid, int k0, int k_lim, int tid, int i,
+                                            DactStage<PRO>& s) {
+  const int c = tid + Cfg<NW>::NT * i;
+  const int r = c >> 3, k = k0 + (c & 7) * 8;
+  const bool second = PRO == DACT_SWIGLU && k >= split;
+  dact_load<PRO>(rd, rz, ld, split, r, second ? k - split : k, r < rows_valid && k < k_lim,
+                 second, i & 1, s);
+}
+template <int NW, int PRO>
+__device__ __forceinline__ void dact_store_k(bf16_t* tile, int tid, int k0, int64_t split, int i,
+                                             const DactStage<PRO>& s) {
+  const int c = tid + Cfg<NW>::NT * i;
+  const int r = c >> 3, kc = c & 7;
+  const bool second = PRO == DACT_SWIGLU && k0 + kc * 8 >= split;
+  *reinterpret_cast<uint4*>(tile + lds_off(r, kc)) = dact_form<PRO>(s, i & 1, second);
+}
+
+// M/N-contiguous dZ tile (64 k rows x 256 columns; bases at the tile's
+// first k row): piece c covers k row c / 32, columns 8 (c % 32) ..
+template <int NW, int PRO>
+__device__ __forceinline__ void dact_load_mn(rsrc_t rd, rsrc_t rz, int64_t ld, int64_t split,
+                                             int n_base, int n_lim, int k_valid, int tid, int i,
+                                             DactStage<PRO>& s) {
+  const int c = tid + Cfg<NW>::NT * i;
+  const int kr = c >> 5, n = n_base + (c & 31) * 8;
+  const bool second = PRO == DACT_SWIGLU && n >= split;
+  dact_load<PRO>(rd, rz, ld, split, kr, second ? n - split : n, kr < k_valid && n < n_lim,
+                 second, i & 1, s);
+}
+template <int NW, int PRO>
+__device__ __forceinline__ void dact_store_mn(bf16_t* tile, int tid, int n_base, int64_t split,
+                                              int i, const DactStage<PRO>& s) {
+  const int c = tid + Cfg<NW>::NT * i;
+  const int kr = c >> 5, col = (c & 31) * 8;
+  const bool second = PRO == DACT_SWIGLU && n_base + col >= split;
+  *reinterpret_cast<uint4*>(tile + mn_off(kr, col)) = dact_form<PRO>(s, i & 1, second);
+}
+
 // ---- epilogue through shared memory ----------------------------------------
 // The tile is written out in passes of 64 rows (four for 256-row tiles, two
 // for 128-row ones).  In each pass the wavefronts holding those rows store their fp32 sums row-major in shared
@@ -371,12 +463,24 @@ __device__ __forceinline__ void write_tile_staged(const f32x16_t (&acc)[FM][FN],
 }
 
 // ---- kernel ----------------------------------------------------------------
-// A_KMAJOR: opA K-contiguous (loaded straight into shared memory) or M-
-// contiguous (through registers, transposed).  B likewise; B_DIRECT selects
-// the direct path for a K-contiguous opB (a k split must then be a multiple
-// of 64 so each k tile comes from one matrix).
-template <int NW, bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT, bool B_DIRECT>
+// A_KMAJOR: opA K-contiguous or M-contiguous, loaded straight into shared
+// memory.  B likewise; B_DIRECT selects the direct path for a K-contiguous
+// opB (a k split must then be a multiple of 64 so each k tile comes from
+// one matrix; otherwise opB goes through registers).
+// PA / PB (DACT_*): opA (K-contiguous) or opB (M/N-contiguous) is a dZ
+// formed from dH and the saved activations as it is loaded, through
+// registers, in 4 pieces per thread and k tile.  While the MFMAs consume
+// one tile: pieces 0 and 1 of the next are loaded with the other operand's
+// direct loads at k step 0, piece i is formed into shared memory at step
+// i + 1 (pieces 2 and 3 at the last step, before the barrier), and piece
+// i + 2 is loaded into the register slot piece i has left.  The vector work
+// is spread over the k steps, beside the other wavefront's MFMAs on the
+// same SIMD.
+template <int NW, bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT, bool B_DIRECT,
+          int PA = DACT_NONE, int PB = DACT_NONE>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
+  static_assert(PA == DACT_NONE || (A_KMAJOR && PB == DACT_NONE), "dZ as K-contiguous opA");
+  static_assert(PB == DACT_NONE || (!B_KMAJOR && BMODE == BMODE_PLAIN), "dZ as M/N-contiguous opB");
   gemm_wave_prio();
   using C = Cfg<NW>;
   constexpr int NWAVES = C::NWAVES, WAVES_N = C::WAVES_N, WTM = C::WTM, WTN = C::WTN;
@@ -400,6 +504,30 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
   const EpiArgs ea = g.epi;
   const int n_base = tc.tn * BN;
   const int m_rows = tc.m_end - tc.m_begin;
+  // the dZ operand's dH, saved activations and split (dense problems only)
+  constexpr int PRO = PA != DACT_NONE ? PA : PB;
+  const bf16_t* d_dh = PA != DACT_NONE ? a0 : b0;
+  const bf16_t* d_zs = reinterpret_cast<const bf16_t*>(PA != DACT_NONE ? g.a.p1 : g.b.p1);
+  const int64_t d_ld = PA != DACT_NONE ? lda : ldb;
+  const int64_t d_split = PA != DACT_NONE ? g.a.split : bsplit;
+  static_assert(PRO == DACT_NONE || C::STAGE_N == BK / 16, "one dZ piece per k step");
+  DactStage<PRO == DACT_NONE ? DACT_GELU : PRO> ds;
+  // load / form dZ piece i of the k tile starting at k0
+  const int64_t d_zld = PRO == DACT_SWIGLU ? 2 * d_split : d_split;
+  auto dload = [&](int i, int k0) {
+    if constexpr (PA != DACT_NONE)
+      dact_load_k<NW, PA>(make_rsrc(d_dh + (int64_t)tc.m_begin * d_ld),
+                          make_rsrc(d_zs + (int64_t)tc.m_begin * d_zld), d_ld, d_split, m_rows,
+                          k0, tc.k_end, tid, i, ds);
+    if constexpr (PB != DACT_NONE)
+      dact_load_mn<NW, PB>(make_rsrc(d_dh + (int64_t)k0 * d_ld),
+                           make_rsrc(d_zs + (int64_t)k0 * d_zld), d_ld, d_split, n_base, Ncols,
+                           tc.k_end - k0, tid, i, ds);
+  };
+  auto dform = [&](int i, int k0, bf16_t* buf) {
+    if constexpr (PA != DACT_NONE) dact_store_k<NW, PA>(buf, tid, k0, d_split, i, ds);
+    if constexpr (PB != DACT_NONE) dact_store_mn<NW, PB>(buf + BM * BK, tid, n_base, d_split, i, ds);
+  };
 
   f32x16_t acc[FM][FN];
   static_for<0, FM>([&](auto I) {
@@ -414,7 +542,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
   // load (the tile past the last one reads as zeros and is never used).
   auto issue = [&](auto I0c, auto I1c, int k0, bf16_t* buf) {
     constexpr int I0 = decltype(I0c)::value, I1 = decltype(I1c)::value;
-    if constexpr (A_KMAJOR) {
+    if constexpr (PA != DACT_NONE) {
+      if constexpr (I0 == 0) {
+        dload(0, k0);
+        dload(1, k0);
+      }
+    } else if constexpr (A_KMAJOR) {
       direct_kmajor<NW, I0, I1>(make_rsrc(a0 + (int64_t)tc.m_begin * lda), lda, m_rows, k0,
                             tc.k_end, buf, wave, lane);
     } else {
@@ -439,6 +572,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
     } else if constexpr (B_KMAJOR) {
       if constexpr (I0 == 0)
         load_k<NW, BMODE>(b0, b1, ldb, bsplit, n_base, Ncols, k0, tc.k_end, tid, sb);
+    } else if constexpr (PB != DACT_NONE) {
+      if constexpr (I0 == 0) {
+        dload(0, k0);
+        dload(1, k0);
+      }
     } else if constexpr (BMODE == BMODE_PAIR32) {
       // half 0: gate columns, half 1: up columns, both f = 128 tn ..
       const bf16_t* bp = half_w ? b1 : b0;
@@ -449,8 +587,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
                         Ncols, tc.k_end - k0, tb, wave, lane);
     }
   };
-  auto commit = [&](bf16_t* buf) {
+  constexpr int NSTEP = BK / 16;
+  // at the last k step (before the loop, `first`: every piece in turn) the
+  // register-staged operand goes to shared memory
+  auto commit = [&](bf16_t* buf, int k0, bool first) {
     if constexpr (B_KMAJOR && !B_DIRECT) store_k(buf + BM * BK, tid, sb);
+    if constexpr (PRO != DACT_NONE) {
+      if (first) {
+        static_for<0, NSTEP - 2>([&](auto Ic) {
+          constexpr int i = decltype(Ic)::value;
+          dform(i, k0, buf);
+          dload(i + 2, k0);
+        });
+      }
+      dform(NSTEP - 2, k0, buf);
+      dform(NSTEP - 1, k0, buf);
+    }
   };
 
   const int r_lane = lane & 31;
@@ -493,11 +645,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
     static_for<0, FM>([&](auto I) { fa[slot][I].fence(); });
     static_for<0, FN>([&](auto J) { fb[slot][J].fence(); });
   };
-  constexpr int NSTEP = BK / 16;
 
   if (nk > 0) {
     issue(std::integral_constant<int, 0>{}, std::integral_constant<int, LDW>{}, tc.k_begin, lds);
-    commit(lds);
+    commit(lds, tc.k_begin, true);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
@@ -519,11 +670,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
       }
       if constexpr (s + 1 < NSTEP) {
         read_frags(cur, s + 1, slot ^ 1);
+        // `nxt` is free since the last barrier: form dZ piece s - 1 into it
+        // and load piece s + 1 into the registers that piece held
+        if constexpr (PRO != DACT_NONE && s >= 1) {
+          dform(s - 1, kn, nxt);
+          dload(s + 1, kn);
+        }
       } else {
         // every wavefront is done reading `cur` and its loads into `nxt`
         // have landed: after the barrier, read the next tile's first step
         // while this step's MFMAs run
-        commit(nxt);
+        commit(nxt, kn, false);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         read_frags(nxt, 0, slot ^ 1);
@@ -2265,6 +2422,29 @@ static hipError_t launch_rows(GemmArgs& g, hipStream_t stream, int thin_max) {
   return hipGetLastError();
 }
 
+// GEMMs whose dZ operand is formed from dH and the saved activations as it
+// is loaded: the general kernel's 8-wavefront layout, whose register file
+// has room for the staged pieces beside 128 accumulators per wavefront.
+// Dense problems only.
+template <int PA, int PB, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_dact(GemmArgs& g, hipStream_t stream) {
+  using namespace mfma256;
+  if (g.E != 1 || g.ragged != RAGGED_NONE || g.a.bstride || g.b.bstride) return hipErrorInvalidValue;
+  fill_tiles(g, BM, BN, g.N);
+  const int blocks = g.tile_off[g.E];
+  if (blocks == 0) return hipSuccess;
+  if constexpr (BK_) {
+    if (BMODE != BMODE_KSPLIT || g.b.split % BK == 0) {
+      hipLaunchKernelGGL((gemm_kernel<8, AK, BK_, BMODE, EPI, OutT, true, PA, PB>), dim3(blocks),
+                         dim3(64 * 8), 0, stream, g);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<8, AK, BK_, BMODE, EPI, OutT, false, PA, PB>), dim3(blocks),
+                     dim3(64 * 8), 0, stream, g);
+  return hipGetLastError();
+}
+
 template <int BMODE, int EPI, int QM, int FA = 0, int FB = 0, typename OutT = bf16_t>
 static hipError_t launch_f8(GemmArgs& g, hipStream_t stream) {
   int n_cols = g.N;
@@ -2331,6 +2511,18 @@ hipError_t gemm_bf16(GemmKind kind, GemmArgs& g, hipStream_t stream) {
       return launch_mfma<TP_NW_DEFAULT, false, false, BMODE_PLAIN, EPI_ACC, float>(g, stream);
     case GK_WGRAD_SPLIT_ACC:
       return launch_mfma<TP_NW_DEFAULT, false, false, BMODE_PLAIN, EPI_ACC_SPLIT, float>(g, stream);
+    case GK_WGRAD_DACT_GELU:
+      return launch_dact<DACT_NONE, DACT_GELU, false, false, BMODE_PLAIN, EPI_STORE, float>(g, stream);
+    case GK_WGRAD_SPLIT_DACT_SWIGLU:
+      return launch_dact<DACT_NONE, DACT_SWIGLU, false, false, BMODE_PLAIN, EPI_STORE_SPLIT, float>(
+          g, stream);
+    case GK_DX_DACT_GELU:
+      return launch_dact<DACT_GELU, DACT_NONE, true, true, BMODE_PLAIN, EPI_STORE, bf16_t>(g, stream);
+    case GK_DX_KSPLIT_DACT_SWIGLU:
+      return launch_dact<DACT_SWIGLU, DACT_NONE, true, true, BMODE_KSPLIT, EPI_STORE, bf16_t>(g,
+                                                                                            stream);
+    default:
+      break;
   }
   return hipErrorInvalidValue;
 }

@@ -12,8 +12,27 @@ namespace f32tile {
 
 constexpr int BM = 64, BN = 64, BK = 16, NT = 256;
 
-template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, bool DUAL, int EPI>
+// One element (row, col) of a dZ operand formed from dH (pitch ld) and the
+// saved activations (Z, pitch split; or G|U, pitch 2 split): column col of
+// [dG | dU] reads dH and G at col mod split.
+template <int PRO>
+__device__ __forceinline__ float dact_f32(const float* dh, const float* zs, int64_t ld,
+                                          int64_t split, int64_t row, int64_t col) {
+  const bool second = PRO == DACT_SWIGLU && col >= split;
+  const int64_t f = second ? col - split : col;
+  const int64_t zld = PRO == DACT_SWIGLU ? 2 * split : split;
+  const float u = (PRO == DACT_SWIGLU && !second) ? zs[row * zld + split + f] : 0.0f;
+  return dact_elem<PRO>(dh[row * ld + f], zs[row * zld + f], u, second);
+}
+
+// PA / PB (DACT_*): opA (K-contiguous) or opB (M/N-contiguous) is a dZ
+// formed from dH and the saved activations (p0, p1, split of its operand
+// arguments) as it is loaded.
+template <bool A_KMAJOR, bool B_KMAJOR, int BMODE, bool DUAL, int EPI, int PA = DACT_NONE,
+          int PB = DACT_NONE>
 __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
+  static_assert(PA == DACT_NONE || A_KMAJOR, "dZ as K-contiguous opA");
+  static_assert(PB == DACT_NONE || !B_KMAJOR, "dZ as M/N-contiguous opB");
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
   __shared__ float Bu[DUAL ? BK : 1][DUAL ? BN + 4 : 1];
@@ -41,8 +60,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
       if (A_KMAJOR) { m = idx >> 4; k = idx & 15; } else { k = idx >> 6; m = idx & 63; }
       int gm = tc.m_begin + m, gk = k0 + k;
       float v = 0.0f;
-      if (gm < tc.m_end && gk < tc.k_end)
-        v = A_KMAJOR ? a0[(int64_t)gm * g.a.ld + gk] : a0[(int64_t)gk * g.a.ld + gm];
+      if (gm < tc.m_end && gk < tc.k_end) {
+        if constexpr (PA != DACT_NONE)
+          v = dact_f32<PA>(a0, reinterpret_cast<const float*>(g.a.p1), g.a.ld, g.a.split, gm, gk);
+        else
+          v = A_KMAJOR ? a0[(int64_t)gm * g.a.ld + gk] : a0[(int64_t)gk * g.a.ld + gm];
+      }
       As[k][m] = v;
     }
 #pragma unroll
@@ -58,6 +81,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
             v = b1[(int64_t)gn * g.b.ld + (gk - g.b.split)];
           else
             v = b0[(int64_t)gn * g.b.ld + gk];
+        } else if constexpr (PB != DACT_NONE) {
+          v = dact_f32<PB>(b0, b1, g.b.ld, g.b.split, gk, gn);
         } else {
           v = b0[(int64_t)gk * g.b.ld + gn];
           if (DUAL) u = b1[(int64_t)gk * g.b.ld + gn];
@@ -114,12 +139,16 @@ static void fill_tiles_f32(GemmArgs& g, int n_cols) {
   }
 }
 
-template <bool AK, bool BK_, int BMODE, bool DUAL, int EPI>
+template <bool AK, bool BK_, int BMODE, bool DUAL, int EPI, int PA = DACT_NONE,
+          int PB = DACT_NONE>
 static hipError_t launch_f32(GemmArgs& g, hipStream_t stream) {
+  if ((PA != DACT_NONE || PB != DACT_NONE) &&
+      (g.E != 1 || g.ragged != RAGGED_NONE || g.a.bstride || g.b.bstride))
+    return hipErrorInvalidValue;  // the formed operand: dense problems only
   fill_tiles_f32(g, DUAL ? (int)g.b.split : g.N);
   int blocks = g.tile_off[g.E];
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((f32tile::gemm_kernel<AK, BK_, BMODE, DUAL, EPI>),
+  hipLaunchKernelGGL((f32tile::gemm_kernel<AK, BK_, BMODE, DUAL, EPI, PA, PB>),
                      dim3(blocks), dim3(f32tile::NT), 0, stream, g);
   return hipGetLastError();
 }
@@ -148,6 +177,17 @@ hipError_t gemm_f32(GemmKind kind, GemmArgs& g, hipStream_t stream) {
       return launch_f32<false, false, BMODE_PLAIN, false, EPI_ACC>(g, stream);
     case GK_WGRAD_SPLIT_ACC:
       return launch_f32<false, false, BMODE_PLAIN, false, EPI_ACC_SPLIT>(g, stream);
+    case GK_WGRAD_DACT_GELU:
+      return launch_f32<false, false, BMODE_PLAIN, false, EPI_STORE, DACT_NONE, DACT_GELU>(g, stream);
+    case GK_WGRAD_SPLIT_DACT_SWIGLU:
+      return launch_f32<false, false, BMODE_PLAIN, false, EPI_STORE_SPLIT, DACT_NONE, DACT_SWIGLU>(
+          g, stream);
+    case GK_DX_DACT_GELU:
+      return launch_f32<true, true, BMODE_PLAIN, false, EPI_STORE, DACT_GELU>(g, stream);
+    case GK_DX_KSPLIT_DACT_SWIGLU:
+      return launch_f32<true, true, BMODE_KSPLIT, false, EPI_STORE, DACT_SWIGLU>(g, stream);
+    default:
+      break;
   }
   return hipErrorInvalidValue;
 }

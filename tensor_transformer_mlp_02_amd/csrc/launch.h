@@ -20,6 +20,16 @@ enum GemmKind {
   GK_DX_KSPLIT,    // dX_partial = [dG|dU] [Ag|Au]^T
   GK_WGRAD_ACC,        // dW += L^T R  (fp32 accumulation buffer)
   GK_WGRAD_SPLIT_ACC,  // as GK_WGRAD_SPLIT, adding into both outputs
+  // The activation derivative formed as an operand is loaded (the other
+  // placement of the derivative): that operand's p0 is dH [rows, split]
+  // (pitch ld), p1 the forward's saved Z (GeLU, pitch split) or G|U
+  // (SwiGLU, pitch 2 split), split = F_shard; each 8-element piece of dZ
+  // (GeLU) or [dG|dU] (SwiGLU) is computed from them on its way to shared
+  // memory.
+  GK_WGRAD_DACT_GELU,          // dA = X^T (dH * gelu'(Z)), opB formed
+  GK_WGRAD_SPLIT_DACT_SWIGLU,  // dA | dA_up = X^T [dG|dU], opB formed
+  GK_DX_DACT_GELU,             // dX_partial = (dH * gelu'(Z)) A^T, opA formed
+  GK_DX_KSPLIT_DACT_SWIGLU,    // dX_partial = [dG|dU] [Ag|Au]^T, opA formed
   GK_FC1_SWIGLU_F8,    // FP8: [G|U] = Xq [Agq|Auq]^T scaled; SwiGLU; H, Hq, amax
   GK_FC1_GELU_F8,      // FP8: Z = Xq Aq^T scaled; GeLU; H, Hq, amax
   GK_FC2_F8,           // FP8: Y = Hq Bq^T scaled

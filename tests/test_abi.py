@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -123,6 +123,40 @@ def test_backward_argument_checks():
     assert bwd(d, dA=addr(1), accumulate=True) == E_ALIAS   # dA over X
     assert bwd(s, A_up=addr(11), accumulate=True) == E_NULL  # dA_up missing
     assert tp.tp_mlp_shard_bwd_workspace(gelu_desc(dtype=9)) == 0
+
+
+def bwd_dact(desc, A_up=None, dA_up=None, ws=addr(14), ws_bytes=None, **kw):
+    p = dict(X=addr(1), A=addr(2), B=addr(3), Z=addr(4), H=addr(5), dY=addr(7),
+             dX=addr(8), dA=addr(9), dB=addr(10))
+    p.update(kw)
+    if ws_bytes is None:
+        ws_bytes = tp.tp_mlp_shard_bwd_workspace(desc)
+    try:
+        tp.tp_mlp_shard_bwd_dact_prologue(desc, p["X"], p["A"], A_up, p["B"], p["Z"], p["H"],
+                                          p["dY"], p["dX"], p["dA"], dA_up, p["dB"], ws,
+                                          ws_bytes)
+    except tp.TpError as e:
+        return e.status
+    return 0
+
+
+def test_dact_prologue_argument_checks():
+    # the workspace holds dH only: N * F_shard elements, for SwiGLU too
+    s = gelu_desc(act=tp.TP_ACT_SWIGLU)
+    up = dict(A_up=addr(11), dA_up=addr(12))
+    dh_bytes = 128 * 128 * 2
+    assert bwd_dact(s, ws_bytes=dh_bytes, **up) == E_DEV   # checks pass; no GPU here
+    assert bwd_dact(s, ws_bytes=dh_bytes - 1, **up) == E_WS
+    assert bwd(s, ws_bytes=dh_bytes, **up) == E_WS         # the epilogue form needs dG|dU
+    d = gelu_desc()
+    assert bwd_dact(d, ws=None) == E_WS
+    assert bwd_dact(d, ws=addr(14, 4)) == E_ALIGN
+    assert bwd_dact(d, Z=None) == E_NULL
+    assert bwd_dact(d, A_up=addr(11)) == E_SHAPE
+    assert bwd_dact(s, A_up=addr(11)) == E_NULL              # dA_up missing
+    assert bwd_dact(d, dX=addr(7)) == E_ALIAS                # dX over dY
+    assert bwd_dact(d, ws=addr(9)) == E_ALIAS                # workspace over dA
+    assert bwd_dact(gelu_desc(dtype=9)) == E_DTYPE
 
 
 def test_workspace_of_the_llama_shard():
