@@ -1325,14 +1325,22 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_ring(GemmArgs g) {
 // own a (BMT/2) x (BNT/2) block of 16 x 16 accumulators; a 16-wide fragment
 // grid is what lets a wavefront cover 112 columns.  k tiles are 64 wide
 // (two 32-wide MFMA steps) in two shared-memory buffers, laid out as in
-// gemm_lean except that M/N-contiguous tiles also XOR granules with bit 3
-// of k: the four k groups of a 16 x 32 fragment read the same 16 columns,
-// and this keeps two neighbouring groups on different banks.  For the
+// gemm_lean except for the swizzles: M/N-contiguous tiles also XOR
+// granules with bit 3 of k (the four k groups of a 16 x 32 fragment read
+// the same 16 columns, and this keeps two neighbouring groups on different
+// banks), and K-contiguous tiles swizzle by row mod 8 only.  For the
 // paired SwiGLU forward, gate columns fill buffer half 0 and up columns
 // half 1 (one source matrix per direct load); the wavefronts of column 0
 // compute gate sums and those of column 1 up sums for the same 112 logical
 // columns, re-paired by the staged epilogue.
 __device__ __forceinline__ int sw16(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
+// K-contiguous tiles here swizzle chunks by row mod 8 only.  A 16 x 32
+// fragment read takes rows r..r+15 at one chunk; with gemm_lean's swizzle
+// (which also flips on bit 3 of the row) those reads cost ~4 bank-conflict
+// cycles each (counted with SQ_LDS_BANK_CONFLICT on the dH launch and on a
+// probe of the read pattern alone), enough to make shared memory, not the
+// MFMAs, the k loop's bound; with row mod 8 they cost none.
+__device__ __forceinline__ int swzk16(int r) { return r & 7; }
 __device__ __forceinline__ int mn16_off(int k, int c) {
   const int h = c >> 7, q = (c >> 3) & 15, e = c & 7;
   return h * (BK * 128) + k * 128 + ((q ^ sw16(k)) << 3) + e;
@@ -1445,7 +1453,7 @@ __global__ __launch_bounds__(W16_NT, 1) void gemm_w16(GemmArgs g) {
     if constexpr (A_KMAJOR) {
       const int blk = wave * 8 + i;
       const int r = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
+      const int c = (lane & 7) ^ swzk16(r);
       voffA[i] = r < m_rows ? (uint32_t)(((int64_t)r * lda + c * 8) * 2) : OOB_OFF;
       dstA[i] = blk * 1024;
     } else {
@@ -1459,7 +1467,7 @@ __global__ __launch_bounds__(W16_NT, 1) void gemm_w16(GemmArgs g) {
     if constexpr (B_KMAJOR) {
       const int blk = wave * 8 + i;
       const int r = blk * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
+      const int c = (lane & 7) ^ swzk16(r);
       voffB[i] = r < n_cols ? (uint32_t)(((int64_t)r * ldb + c * 8) * 2) : OOB_OFF;
       dstB[i] = blk * 1024;
     } else {
@@ -1516,7 +1524,7 @@ __global__ __launch_bounds__(W16_NT, 1) void gemm_w16(GemmArgs g) {
   // M/N-contiguous: one per fragment (k step s adds 8 KiB, the second
   // transposing read 1 KiB)
   uint32_t rdA[FM], rdB[FN];
-  const int sw = swz(r16);
+  const int sw = swzk16(r16);  // fragment rows are 16-aligned: row mod 8 = r16 mod 8
   static_for<0, FM>([&](auto Xc) {
     constexpr int x = decltype(Xc)::value;
     if constexpr (A_KMAJOR) {
