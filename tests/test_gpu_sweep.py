@@ -78,3 +78,26 @@ def test_random_grouped_shapes(shape):
         g = to_host(getattr(buf, k))
         for e in range(len(counts)):
             assert_close(f"{k}[{e}]", g[e], b[k][e], tol)
+
+
+@settings(max_examples=12, **SETTINGS)
+@given(shard_shapes())
+def test_random_shard_shapes_derivative_in_loads(shape):
+    """The backward that forms dZ in the dA / dX operand loads, on the same
+    kind of shapes (k tiles that straddle the [dG | dU] split included)."""
+    from test_gpu_dact import _run
+    dtype, act, N, H, Ft = shape
+    cid = 900 + (N * 5 + H * 11 + Ft * 3 + act) % 600
+    w = wl.Workload(cid, "sweep", dtype, act, S=N, B=1, H=H, F=Ft, T=1,
+                    w_std=0.5 / np.sqrt(H))
+    d = wl.gen_mlp_inputs(w)
+    print(f"[gpu] sweep dact dtype={dtype} act={act} N={N} H={H} Ft={Ft}", flush=True)
+    _, _, _, pro = _run(w, d)
+    f = oracle.mlp_fwd(d["X"], d["A"], d["B"], act, d["A_up"])
+    b = oracle.mlp_bwd(d["X"], d["A"], d["B"], act, d["dY"], f, d["A_up"])
+    tol = TOL[dtype]
+    assert_close("dX", f64(to_host(pro.dX)), b["dX"], tol)
+    assert_close("dA", to_host(pro.dA), b["dA"], tol)
+    assert_close("dB", to_host(pro.dB), b["dB"], tol)
+    if act == wl.ACT_SWIGLU:
+        assert_close("dA_up", to_host(pro.dA_up), b["dA_up"], tol)
