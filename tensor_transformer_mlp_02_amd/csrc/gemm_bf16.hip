@@ -2254,7 +2254,10 @@ static int count_tiles(const GemmArgs& g, int BMT, int BNT, int n_cols, int thin
 #define TP_W16_FACTOR 1.09
 #endif
 constexpr double W16_CYCLE_FACTOR = TP_W16_FACTOR;
-constexpr double W16_PAIR_EXTRA = 1.1;
+#ifndef TP_W16_PAIR_EXTRA
+#define TP_W16_PAIR_EXTRA 1.1
+#endif
+constexpr double W16_PAIR_EXTRA = TP_W16_PAIR_EXTRA;
 // thin_max: remainders left to the thin kernel by 256-row tiles (the
 // 224-row shape covers every row itself).
 struct ShapeCost {
@@ -2269,9 +2272,10 @@ static ShapeCost pick_shape_cost(const GemmArgs& g, int bmode, bool w16_ok, int 
   };
   const bool w16 = TP_USE_W16 && w16_ok;
   if (bmode == BMODE_PAIR32) {
-    // the paired 224-wide tiles also pay a heavier epilogue: measured in the
-    // whole step (SwiGLU FC1, 4096 tokens, H = 8192, F/T = 3584), 448
-    // 256-wide tiles in two waves beat 512 224-wide ones by 3 %
+    // the paired 224-wide tiles also pay a heavier epilogue: measured on
+    // the SwiGLU FC1 (4096 tokens, H = 8192, F/T = 3584), 448 256-wide
+    // tiles in two waves take 431 us in the overlapped step (406 in order),
+    // 512 224-wide ones 480 (442)
     const int split = (int)g.b.split;
     const double c0 = cost(256, 256, count_tiles(g, 256, 128, split, thin_max));
     if (!w16) return {0, c0};
