@@ -124,6 +124,16 @@ int main() {
     check(tp_mlp_shard_bwd(&d, fake(1), fake(2), nullptr, fake(3), fake(4), fake(5), fake(7),
                            fake(8), f, nullptr, (float*)fake(10), fake(14), ws, nullptr),
           "bwd valid", TP_ERR_DEVICE);
+    // the derivative formed in the operand loads needs dH only: N * F_shard elements
+    const size_t dh = (size_t)(d.S * d.B * d.F_shard) * 2;
+    check(tp_mlp_shard_bwd_dact_prologue(&d, fake(1), fake(2), nullptr, fake(3), fake(4), fake(5),
+                                         fake(7), fake(8), f, nullptr, (float*)fake(10), fake(14),
+                                         dh - 16, nullptr),
+          "bwd dact small workspace", TP_ERR_WORKSPACE);
+    check(tp_mlp_shard_bwd_dact_prologue(&d, fake(1), fake(2), nullptr, fake(3), fake(4), fake(5),
+                                         fake(7), fake(8), f, nullptr, (float*)fake(10), fake(14),
+                                         dh, nullptr),
+          "bwd dact valid", TP_ERR_DEVICE);
   }
   {
     const void* parts[TP_MAX_SHARDS + 1];
@@ -158,7 +168,9 @@ int main() {
       case 1: {
         const size_t ws = tp_mlp_shard_bwd_workspace(pd);
         const size_t wsb = rnd() % 2 ? ws : (size_t)(rnd() % 4096);
-        auto fn = rnd() % 2 ? tp_mlp_shard_bwd : tp_mlp_shard_bwd_accum;
+        const int which = (int)(rnd() % 3);
+        auto fn = which == 0 ? tp_mlp_shard_bwd
+                             : which == 1 ? tp_mlp_shard_bwd_accum : tp_mlp_shard_bwd_dact_prologue;
         if (rnd() % 3 == 0)
           check(tp_mlp_shard_bwd_noalloc(pd, ptr_any(1), ptr_any(2), ptr_any(3), ptr_any(4),
                                          ptr_any(5), ptr_any(6), ptr_any(7), ptr_any(8),
