@@ -296,16 +296,65 @@ def cpu_model() -> str:
 
 
 def cpu_baseline(w, tokens):
-    """The fp64 oracle, as it stands, on a token sample of the workload."""
+    """The fp64 oracle, as it stands, on a token sample of the workload.
+    Returns its time, the sample's GEMM FLOPs, and the sample's inputs and
+    oracle results (for sample_parity)."""
     import oracle
     import workloads as wl
     d = wl.gen_mlp_inputs(w, n_rows=max(tokens, 1))
     t0 = time.perf_counter()
     f = oracle.mlp_fwd(d["X"], d["A"], d["B"], w.act, d["A_up"])
+    b = None
     if w.backward:
-        oracle.mlp_bwd(d["X"], d["A"], d["B"], w.act, d["dY"], f, d["A_up"])
+        b = oracle.mlp_bwd(d["X"], d["A"], d["B"], w.act, d["dY"], f, d["A_up"])
     dt = time.perf_counter() - t0
-    return dt, gemm_flops(w, tokens)
+    return dt, gemm_flops(w, tokens), (d, f, b)
+
+
+def sample_parity(torch, tp, w, d, f, b):
+    """The HIP shard on the CPU baseline's token sample against the oracle's
+    results there: relative Frobenius error ||gpu - oracle|| / ||oracle|| of
+    each output tensor (the same inputs; the bar is 2e-2 for bf16 storage,
+    1e-5 for fp32)."""
+    import numpy as np
+    import oracle
+    from tensor_transformer_mlp_02_amd.tensors import to_device, to_host, ShardBuffers
+    N = d["X"].shape[0]
+    desc = dict(S=N, B=1, H=w.H, F_shard=w.Ft, T=w.T, act=w.act, dtype=w.dtype)
+    dev = {k: (to_device(d[k]) if d.get(k) is not None else None)
+           for k in ("X", "A", "A_up", "B", "dY")}
+    buf = ShardBuffers(desc, backward=w.backward)
+    tp.tp_mlp_shard_fwd(desc, dev["X"], dev["A"], dev["A_up"], dev["B"], buf.Z, buf.H, buf.Y)
+    if w.backward:
+        tp.tp_mlp_shard_bwd(desc, dev["X"], dev["A"], dev["A_up"], dev["B"], buf.Z, buf.H,
+                            dev["dY"], buf.dX, buf.dA, buf.dA_up, buf.dB, buf.ws, buf.ws_bytes)
+    torch.cuda.synchronize()
+
+    def rel(got, ref):
+        got = oracle.to_f64(got)
+        ref = np.asarray(ref, np.float64)
+        nr = np.linalg.norm(ref)
+        return float(np.linalg.norm(got - ref) / nr) if nr else float(np.abs(got).max())
+
+    Z = to_host(buf.Z)
+    Ft = w.Ft
+    errs = {}
+    if w.act == 1:
+        errs["G"] = rel(Z[:, :Ft], f["Z"])
+        errs["U"] = rel(Z[:, Ft:], f["U"])
+    else:
+        errs["Z"] = rel(Z, f["Z"])
+    errs["H"] = rel(to_host(buf.H), f["H"])
+    errs["Y"] = rel(to_host(buf.Y), f["Y"])
+    if b is not None:
+        errs["dX"] = rel(to_host(buf.dX), b["dX"])
+        errs["dA"] = rel(to_host(buf.dA), b["dA"])
+        if w.act == 1:
+            errs["dA_up"] = rel(to_host(buf.dA_up), b["dA_up"])
+        errs["dB"] = rel(to_host(buf.dB), b["dB"])
+    bar = 2e-2 if w.dtype == 1 else 1e-5
+    return {"tokens": int(N), "rel_frob": {k: float(f"{v:.3e}") for k, v in errs.items()},
+            "bar": bar, "within_bar": bool(max(errs.values()) <= bar)}
 
 
 # ---------------------------------------------------------------------------
@@ -1008,10 +1057,10 @@ def main():
         progress("cpu baseline")
         tokens = args.cpu_tokens
         if tokens <= 0:
-            dt, fl = cpu_baseline(w, 128)           # calibrate on 128 tokens
+            dt, fl, _ = cpu_baseline(w, 128)        # calibrate on 128 tokens
             rate = fl / max(dt, 1e-6)
             tokens = int(max(16, min(w.N, 20.0 * rate / gemm_flops(w, 1))))
-        dt, fl = cpu_baseline(w, tokens)
+        dt, fl, (d_s, f_s, b_s) = cpu_baseline(w, tokens)
         line["cpu_baseline"] = {
             "value": round(fl / dt / 1e12, 6),
             "unit": "TFLOP/s",
@@ -1021,6 +1070,8 @@ def main():
                       f"{w.N} tokens ({fl / 1e9:.1f} GFLOP in {dt:.1f} s)",
             "cpu": cpu_model(),
         }
+        progress("parity on the baseline's sample")
+        line["parity"] = sample_parity(torch, tp, w, d_s, f_s, b_s)
     print(json.dumps(line), flush=True)
 
 
