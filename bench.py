@@ -170,28 +170,60 @@ def tflops(fl, ms):
 # ---------------------------------------------------------------------------
 # shader clock sampled while the GEMMs run (amdsmi gpu metrics)
 # ---------------------------------------------------------------------------
+def sysfs_sclk_path(bus):
+    """The kernel driver's shader-clock level file (pp_dpm_sclk) of the card
+    on PCI bus `bus`, or None."""
+    import glob
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            bdf = os.path.basename(os.path.realpath(dev))  # e.g. 0000:75:00.0
+            if int(bdf.split(":")[1], 16) == bus and os.path.exists(dev + "/pp_dpm_sclk"):
+                return dev + "/pp_dpm_sclk"
+        except (ValueError, IndexError, OSError):
+            continue
+    return None
+
+
 class ClockSampler:
-    """Samples the GPU's current graphics clocks every few ms in a thread.
-    Reports None when the metrics are not readable on this machine."""
+    """Samples the GPU's current shader clock every few ms in a thread: the
+    level the kernel driver marks current in the card's pp_dpm_sclk (it
+    follows the load), else amdsmi's gpu metrics (whose current clocks stay
+    at an idle value on some machines).  Reports None when neither gives a
+    plausible reading."""
 
     def __init__(self, torch):
         self.samples, self.avg_samples, self.error, self.h, self.raw = [], [], None, None, None
+        bus = torch.cuda.get_device_properties(0).pci_bus_id
+        self.sysfs = sysfs_sclk_path(bus)
         try:
             import amdsmi
             self.amdsmi = amdsmi
             amdsmi.amdsmi_init()
-            bus = torch.cuda.get_device_properties(0).pci_bus_id
             for h in amdsmi.amdsmi_get_processor_handles():
                 bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
                 if int(bdf.split(":")[1], 16) == bus:
                     self.h = h
-            if self.h is None:
-                self.error = "no amdsmi handle with the device's PCI bus"
+            if self.h is None and self.sysfs is None:
+                self.error = "no clock source for the device's PCI bus"
         except Exception as e:  # metrics are context: never fail the bench
-            self.error = f"{type(e).__name__}: {e}"
+            if self.sysfs is None:
+                self.error = f"{type(e).__name__}: {e}"
+
+    def _read_sysfs(self):
+        """The current level of pp_dpm_sclk in MHz (the line marked '*')."""
+        with open(self.sysfs) as fh:
+            for line in fh:
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":", 1)[1].strip().lower().split("mhz")[0])
+        return None
 
     def _read(self):
-        """(mean of the per-XCD current clocks, the average clock) in MHz."""
+        """(current clock, the firmware's average clock) in MHz."""
+        if self.sysfs is not None:
+            v = self._read_sysfs()
+            if self.raw is None:
+                self.raw = {"pp_dpm_sclk": v}
+            return v, None
         m = self.amdsmi.amdsmi_get_gpu_metrics_info(self.h)
         if self.raw is None:
             self.raw = {k: m.get(k) for k in ("current_gfxclks", "current_gfxclk",
@@ -205,7 +237,7 @@ class ClockSampler:
 
     def run(self, fn):
         """fn() runs GPU work; sample until it returns."""
-        if self.h is None:
+        if self.h is None and self.sysfs is None:
             fn()
             return
         stop = threading.Event()
@@ -930,9 +962,12 @@ def main():
         clock = {"sclk_ghz": None if ghz is None else round(ghz, 3),
                  "avg_gfxclk_ghz": None if avg is None else round(avg, 3),
                  "samples": len(cs.samples),
-                 "source": "amdsmi gpu metrics (median of the per-XCD current graphics "
-                           "clocks; the firmware's average clock beside it), sampled every "
-                           f"~2 ms while {n_clock} more headline steps ran in this process",
+                 "source": ("the driver's current shader-clock level (pp_dpm_sclk)"
+                            if cs.sysfs else
+                            "amdsmi gpu metrics (mean of the per-XCD current graphics clocks; "
+                            "the firmware's average clock beside it)")
+                           + f", median of samples every ~2 ms while {n_clock} more headline "
+                             "steps ran in this process",
                  "first_sample": cs.raw,
                  "error": cs.error}
         if ghz:
