@@ -3,7 +3,8 @@ dX GEMMs form dZ from dH and the saved activations as they load it.
 
 Its weight and input gradients are checked against the fp64 oracle's
 backward of the same shard (whole tensors on small shapes with ragged
-tails, sampled rows and columns at the full SwiGLU and GeLU workloads),
+tails and at the full SwiGLU workload, sampled rows and columns at the full
+SwiGLU and GeLU workloads),
 dH (left in the workspace) against the oracle's dY B^T, and every result
 against the default backward's (the derivative in the epilogue), to the
 same bar: the two differ only in rounding (dZ is formed from the stored
@@ -157,3 +158,19 @@ def test_empty_batch():
         assert torch.count_nonzero(buf.dB).item() == 0 and not torch.isnan(buf.dB).any()
         if buf.dA_up is not None:
             assert torch.count_nonzero(buf.dA_up).item() == 0
+
+
+def test_swiglu_full_size_whole_tensors():
+    """Every element of dX, dA, dA_up, dB and dH at the full SwiGLU shard."""
+    w = wl.WORKLOADS["c4_bf16_swiglu_fwdbwd"]
+    d = wl.gen_mlp_inputs(w)
+    desc, dev, ref, pro = _run(w, d)
+    tol = TOL[w.dtype]
+    f = oracle.mlp_fwd(d["X"], d["A"], d["B"], w.act, d["A_up"])
+    b = oracle.mlp_bwd(d["X"], d["A"], d["B"], w.act, d["dY"], f, d["A_up"])
+    assert_close("dH (workspace)", _dh(pro, w, w.N),
+                 oracle.matmul("nt", f64(d["dY"]), f64(d["B"])), tol)
+    assert_close("dX", f64(to_host(pro.dX)), b["dX"], tol)
+    assert_close("dA", to_host(pro.dA), b["dA"], tol)
+    assert_close("dA_up", to_host(pro.dA_up), b["dA_up"], tol)
+    assert_close("dB", to_host(pro.dB), b["dB"], tol)

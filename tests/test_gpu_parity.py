@@ -3,7 +3,8 @@ oracle on the same seeded inputs.
 
 Small shapes are compared element by element over whole tensors (several
 256-wide tiles plus ragged tails in every dimension).  The full workloads
-are compared on sampled rows (per-token outputs: Z, H, Y, dX) and sampled
+are compared element by element too (the oracle runs the whole shard), and
+again on sampled rows (per-token outputs: Z, H, Y, dX, dZ) and sampled
 weight-gradient columns, which the oracle computes exactly by running the
 same shard narrowed to those columns (a narrower column/row split of the
 same weights, so every sampled entry is the full-length sum).
@@ -631,3 +632,39 @@ def test_c5_grouped_full_size_sampled():
     assert_close("dWg cols", to_host(buf.dWg[:, :, cols]), bn["dWg"], tol)
     assert_close("dWu cols", to_host(buf.dWu[:, :, cols]), bn["dWu"], tol)
     assert_close("dWd rows", to_host(buf.dWd[:, cols, :]), bn["dWd"], tol)
+
+
+# ----------------------------------------------------------------------------
+# full workloads, every element (the fp64 oracle runs the whole shard: ~30 s
+# of host time for the SwiGLU shard on 16 cores)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["c2_bf16_gelu_fwd", "c3_bf16_gelu_fwdbwd",
+                                  "c4_bf16_swiglu_fwdbwd"])
+def test_full_size_whole_tensors(name):
+    w = wl.WORKLOADS[name]
+    d = wl.gen_mlp_inputs(w)
+    dev, buf = _run_shard(w, d, backward=w.backward)
+    _check_full(w, d, buf, backward=w.backward)
+
+
+def test_c5_grouped_full_size_whole_tensors():
+    """Every element of the grouped experts' outputs and weight gradients at
+    the full grouped workload (4079 rows over 8 experts)."""
+    w = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
+    d = wl.gen_grouped_inputs(w)
+    H, F, E = w.H, w.F, w.experts
+    dev, buf = _run_grouped(d, H, F)
+    tol = TOL[wl.DT_BF16]
+    off = d["offsets"]
+    f = oracle.grouped_fwd(d["X_perm"], off, d["Wg"], d["Wu"], d["Wd"])
+    b = oracle.grouped_bwd(d["X_perm"], off, d["Wg"], d["Wu"], d["Wd"], d["dY_perm"], f)
+    Z = f64(to_host(buf.Z))
+    assert_close("G", Z[:, :F], f["G"], tol)
+    assert_close("U", Z[:, F:], f["U"], tol)
+    assert_close("H", f64(to_host(buf.H)), f["H"], tol)
+    assert_close("Y", f64(to_host(buf.Y)), f["Y"], tol)
+    assert_close("dX", f64(to_host(buf.dX)), b["dX"], tol)
+    for k in ("dWg", "dWu", "dWd"):
+        g = to_host(getattr(buf, k))
+        for e in range(E):
+            assert_close(f"{k}[{e}]", g[e], b[k][e], tol)
