@@ -570,24 +570,35 @@ def summarize(w, res, label):
 # ---------------------------------------------------------------------------
 # side measurements
 # ---------------------------------------------------------------------------
-def grouped_expert_timing(torch, tp, wl, hev, n_sets, steps=20, warmup=3):
+def grouped_expert_timing(torch, tp, wl, hev, n_sets, steps=20, warmup=3, capacity=None):
     """The grouped local experts on the grouped-expert workload (16384 tokens
     routed top-2 over 64 experts, local experts 0..7, H = 4096, F = 1408,
     SwiGLU): forward and backward over the ragged rows, rotating input sets,
     each launch timed with events; algorithmic TFLOP/s (6 H F per row
     forward, 12 H F backward).  The step median comes from steps that record
     only their start; the launch durations from as many steps with every
-    launch bracketed."""
+    launch bracketed.  With `capacity` the row offsets stay in GPU memory
+    (the device-offset calls) and the row buffers hold `capacity` rows, of
+    which the routed ones are the first."""
     from tensor_transformer_mlp_02_amd.tensors import to_device, ExpertBuffers
     w5 = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
     sets = []
     for s in range(n_sets):
         g = wl.gen_grouped_inputs(w5, set_index=s)
-        sets.append({k: to_device(g[k]) for k in ("X_perm", "Wg", "Wu", "Wd", "dY_perm")})
+        d = {k: to_device(g[k]) for k in ("X_perm", "Wg", "Wu", "Wd", "dY_perm")}
+        if capacity is not None:
+            for k in ("X_perm", "dY_perm"):
+                full = torch.zeros((capacity, w5.H), dtype=d[k].dtype, device=d[k].device)
+                full[:d[k].shape[0]].copy_(d[k])
+                d[k] = full
+        sets.append(d)
     off = g["offsets"]
     R, E, H, F = int(off[-1]), len(off) - 1, w5.H, w5.F
     desc = dict(H=H, F=F, E=E, dtype=wl.DT_BF16)
-    buf = ExpertBuffers(desc, off)
+    # (buffers sized by the last offset: `capacity` rows in the device case)
+    buf = ExpertBuffers(desc, off if capacity is None else [0] * E + [capacity])
+    off_dev = (torch.tensor(off, dtype=torch.int32, device="cuda")
+               if capacity is not None else None)
     stream = torch.cuda.current_stream()
     roles = ["FC1", "FC2", "dH", "dWd", "dWg|dWu", "dX"]
 
@@ -595,11 +606,19 @@ def grouped_expert_timing(torch, tp, wl, hev, n_sets, steps=20, warmup=3):
         d = sets[k % n_sets]
         if evs is not None:
             tp.tp_launch_events(evs)
-        tp.tp_grouped_expert_fwd(desc, off, d["X_perm"], d["Wg"], d["Wu"], d["Wd"], buf.Z,
-                                 buf.H, buf.Y, stream=stream)
-        tp.tp_grouped_expert_bwd(desc, off, d["X_perm"], d["Wg"], d["Wu"], d["Wd"], buf.Z,
-                                 buf.H, d["dY_perm"], buf.dX, buf.dWg, buf.dWu, buf.dWd,
-                                 buf.ws, buf.ws_bytes, stream=stream)
+        if capacity is None:
+            tp.tp_grouped_expert_fwd(desc, off, d["X_perm"], d["Wg"], d["Wu"], d["Wd"], buf.Z,
+                                     buf.H, buf.Y, stream=stream)
+            tp.tp_grouped_expert_bwd(desc, off, d["X_perm"], d["Wg"], d["Wu"], d["Wd"], buf.Z,
+                                     buf.H, d["dY_perm"], buf.dX, buf.dWg, buf.dWu, buf.dWd,
+                                     buf.ws, buf.ws_bytes, stream=stream)
+        else:
+            tp.tp_grouped_expert_fwd_devoff(desc, capacity, off_dev, d["X_perm"], d["Wg"],
+                                            d["Wu"], d["Wd"], buf.Z, buf.H, buf.Y, stream=stream)
+            tp.tp_grouped_expert_bwd_devoff(desc, capacity, off_dev, d["X_perm"], d["Wg"],
+                                            d["Wu"], d["Wd"], buf.Z, buf.H, d["dY_perm"], buf.dX,
+                                            buf.dWg, buf.dWu, buf.dWd, buf.ws, buf.ws_bytes,
+                                            stream=stream)
         if evs is not None:
             tp.tp_launch_events(None)
     for k in range(warmup):
@@ -634,6 +653,8 @@ def grouped_expert_timing(torch, tp, wl, hev, n_sets, steps=20, warmup=3):
     b_ms = sum(per[r] for r in roles[2:])
     return {"rows": R, "experts": E, "rows_per_expert": [int(x) for x in off[1:] - off[:-1]],
             "H": H, "F": F, "inputs": f"{n_sets} input sets rotated",
+            "offsets": "host" if capacity is None else "device",
+            "buffer_rows": R if capacity is None else capacity,
             "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
             "step_ms_median": round(step_ms, 4),
             "launch_timing_pass_step_ms": round(launch_pass_ms, 4),
@@ -643,6 +664,23 @@ def grouped_expert_timing(torch, tp, wl, hev, n_sets, steps=20, warmup=3):
                              "tflops": round(tflops(fl[r], per[r]), 1),
                              "frac": round(tflops(fl[r], per[r]) / PEAK_BF16_TFLOPS, 4)}
                          for r in roles}}
+
+
+def grouped_timing_all(torch, tp, wl, hev, n_sets):
+    """The grouped experts with host offsets, then with device offsets on
+    buffers of exactly the routed rows and on buffers of every row that
+    could be routed here (tokens x top-k: the size a caller that never
+    reads the counts back must provide)."""
+    res = grouped_expert_timing(torch, tp, wl, hev, n_sets)
+    w5 = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
+    keep = ("buffer_rows", "fwd_ms", "bwd_ms", "step_ms_median", "tflops", "frac_of_bf16_peak")
+    dev = {}
+    for name, cap in (("exact", res["rows"]), ("tokens_x_topk", w5.tokens * w5.topk)):
+        r = grouped_expert_timing(torch, tp, wl, hev, n_sets, capacity=cap)
+        dev[name] = {k: r[k] for k in keep}
+        dev[name]["launch_us"] = {k: v["us"] for k, v in r["launches"].items()}
+    res["device_offsets"] = dev
+    return res
 
 
 def moe_dispatch_timing(torch, tp, wl, dev, stream, hev, reps=20):
@@ -917,8 +955,8 @@ def main():
     del calib_src, calib_dst
 
     if args.only == "grouped":
-        print(json.dumps({"grouped_experts": grouped_expert_timing(torch, tp, wl, hev,
-                                                                   args.sets)}), flush=True)
+        print(json.dumps({"grouped_experts": grouped_timing_all(torch, tp, wl, hev, args.sets)}),
+              flush=True)
         return
     if args.only == "fp8":
         d0 = wl.gen_mlp_inputs(w)
@@ -1012,7 +1050,7 @@ def main():
     if args.side and args.moe:
         progress("grouped experts and MoE row moves")
         moe = moe_dispatch_timing(torch, tp, wl, dev, torch.cuda.current_stream(), hev)
-        grouped = grouped_expert_timing(torch, tp, wl, hev, args.sets)
+        grouped = grouped_timing_all(torch, tp, wl, hev, args.sets)
 
     flops = gemm_flops(w)
     value = tflops(flops, head["ms_per_step_median"])

@@ -329,6 +329,46 @@ int tp_grouped_expert_bwd_accum(const tp_expert_desc *desc, const int64_t *offse
                                 void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Grouped experts with the row offsets in device memory (the expert compute
+ * that follows dispatch in "Megatron Core 带读" §09, taking the per-expert
+ * row offsets where a routing step on the GPU leaves them: no copy to the
+ * host and no wait for it, so routing and expert compute can be queued, or
+ * captured in a graph, in one go).  The same computation as
+ * tp_grouped_expert_fwd / _bwd / _bwd_accum, except:
+ *   R        HOST value: the rows the buffers hold (X_perm, Z_save, H_act,
+ *            Y_perm, dY_perm, dX_perm are [R, ...]); 0 <= R <= 2^30
+ *   offsets  DEVICE array of E+1 int32, 4-byte aligned, read by the kernels
+ *            when they run (stream order: an earlier kernel on `stream` may
+ *            write them).  Valid offsets are as for the host calls with
+ *            offsets[E] <= R.  Any values are safe: the kernels take
+ *            o[0] = clamp(offsets[0], 0, R) and o[e+1] = clamp(offsets[e+1],
+ *            o[e], R), so expert e owns rows [o[e], o[e+1]) and no access
+ *            leaves the buffers; rows outside [o[0], o[E]) of every output
+ *            are left unwritten.
+ *   workspace  tp_grouped_expert_devoff_workspace(desc, R) bytes ([R,2F] bf16)
+ *   accumulate 0: weight gradients written (tp_grouped_expert_bwd);
+ *            1: added to (tp_grouped_expert_bwd_accum)
+ * The host cannot see the rows, so the row-tiled products launch for the
+ * worst split of R rows (about E - 1 more tile rows than the most tiles the
+ * offsets can need); workgroups without a tile exit at once.  Results are
+ * those of the host-offset calls up to summation order (the host calls may
+ * pick other tile shapes), bit-identical run to run.
+ * Errors: as the host-offset calls (the offsets' values are not checked).
+ */
+int tp_grouped_expert_fwd_devoff(const tp_expert_desc *desc, int64_t R,
+                                 const int32_t *offsets, const void *X_perm,
+                                 const void *Wg, const void *Wu, const void *Wd,
+                                 void *Z_save, void *H_act, void *Y_perm, void *stream);
+size_t tp_grouped_expert_devoff_workspace(const tp_expert_desc *desc, int64_t R);
+int tp_grouped_expert_bwd_devoff(const tp_expert_desc *desc, int64_t R,
+                                 const int32_t *offsets, const void *X_perm,
+                                 const void *Wg, const void *Wu, const void *Wd,
+                                 const void *Z_save, const void *H_act,
+                                 const void *dY_perm, void *dX_perm, float *dWg,
+                                 float *dWu, float *dWd, void *workspace,
+                                 size_t ws_bytes, int32_t accumulate, void *stream);
+
+/*
  * MoE token dispatch and combine around the grouped local experts
  * ([P3] §09: router scores -> top-k experts -> tokens sent to their
  * experts -> expert compute -> results merged by weight -> back in the

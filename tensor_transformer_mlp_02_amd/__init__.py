@@ -20,6 +20,8 @@ __all__ = [
     "tp_mlp_shard_bwd_noalloc", "tp_mlp_shard_bwd_dact_prologue",
     "tp_partial_sum", "tp_partial_sum_capped", "tp_partial_sum_scatter", "tp_grouped_expert_fwd", "tp_grouped_expert_bwd",
     "tp_grouped_expert_bwd_workspace", "tp_grouped_expert_bwd_accum",
+    "tp_grouped_expert_fwd_devoff", "tp_grouped_expert_bwd_devoff",
+    "tp_grouped_expert_devoff_workspace",
     "tp_moe_permute", "tp_moe_combine", "tp_moe_combine_bwd",
     "tp_fp8_quantize", "tp_mlp_shard_fwd_fp8", "tp_fp8_transpose", "tp_mlp_shard_bwd_fp8", "TP_FP8_E4M3", "TP_FP8_E5M2", "tp_last_error", "tp_status_string",
     "tp_launch_events", "tp_launch_events_used",
@@ -102,6 +104,13 @@ def lib() -> ctypes.CDLL:
     L.tp_grouped_expert_bwd.restype = ctypes.c_int
     L.tp_grouped_expert_bwd_accum.argtypes = [ED, I64P] + [_vp] * 12 + [ctypes.c_size_t, _vp]
     L.tp_grouped_expert_bwd_accum.restype = ctypes.c_int
+    L.tp_grouped_expert_fwd_devoff.argtypes = [ED, ctypes.c_int64] + [_vp] * 9
+    L.tp_grouped_expert_fwd_devoff.restype = ctypes.c_int
+    L.tp_grouped_expert_devoff_workspace.argtypes = [ED, ctypes.c_int64]
+    L.tp_grouped_expert_devoff_workspace.restype = ctypes.c_size_t
+    L.tp_grouped_expert_bwd_devoff.argtypes = ([ED, ctypes.c_int64] + [_vp] * 13 +
+                                               [ctypes.c_size_t, ctypes.c_int32, _vp])
+    L.tp_grouped_expert_bwd_devoff.restype = ctypes.c_int
     L.tp_moe_permute.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                  _vp, _vp, _vp, _vp]
     L.tp_moe_permute.restype = ctypes.c_int
@@ -356,6 +365,42 @@ def tp_grouped_expert_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_p
                 (dWg, n["dW"], "dWg"), (dWu, n["dW"], "dWu"), (dWd, n["dW"], "dWd"),
                 (workspace, int(ws_bytes), "workspace")])
     return _check(fn(ctypes.byref(d), off, *p, int(ws_bytes), _stream(stream)))
+
+
+def tp_grouped_expert_fwd_devoff(desc, R: int, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act,
+                                 Y_perm, stream=None) -> int:
+    """tp_grouped_expert_fwd with the E+1 row offsets an int32 GPU tensor
+    (read by the kernels, clamped into [0, R]); R is the rows the buffers
+    hold."""
+    d = _edesc(desc)
+    n = _expert_sizes(d, max(int(R), 0))
+    p = _sized([(offsets, 4 * (max(d.E, 0) + 1), "offsets"), (X_perm, n["X"], "X_perm"),
+                (Wg, n["W"], "Wg"), (Wu, n["W"], "Wu"), (Wd, n["W"], "Wd"),
+                (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"), (Y_perm, n["Y"], "Y_perm")])
+    return _check(lib().tp_grouped_expert_fwd_devoff(ctypes.byref(d), int(R), *p,
+                                                      _stream(stream)))
+
+
+def tp_grouped_expert_devoff_workspace(desc, R: int) -> int:
+    d = _edesc(desc)
+    return int(lib().tp_grouped_expert_devoff_workspace(ctypes.byref(d), int(R)))
+
+
+def tp_grouped_expert_bwd_devoff(desc, R: int, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act,
+                                 dY_perm, dX_perm, dWg, dWu, dWd, workspace, ws_bytes: int,
+                                 accumulate: bool = False, stream=None) -> int:
+    """tp_grouped_expert_bwd (accumulate=True: _bwd_accum) with device-resident
+    int32 offsets, as tp_grouped_expert_fwd_devoff."""
+    d = _edesc(desc)
+    n = _expert_sizes(d, max(int(R), 0))
+    p = _sized([(offsets, 4 * (max(d.E, 0) + 1), "offsets"), (X_perm, n["X"], "X_perm"),
+                (Wg, n["W"], "Wg"), (Wu, n["W"], "Wu"), (Wd, n["W"], "Wd"),
+                (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"),
+                (dY_perm, n["Y"], "dY_perm"), (dX_perm, n["X"], "dX_perm"),
+                (dWg, n["dW"], "dWg"), (dWu, n["dW"], "dWu"), (dWd, n["dW"], "dWd"),
+                (workspace, int(ws_bytes), "workspace")])
+    return _check(lib().tp_grouped_expert_bwd_devoff(ctypes.byref(d), int(R), *p, int(ws_bytes),
+                                                      1 if accumulate else 0, _stream(stream)))
 
 
 def tp_mlp_shard_bwd_accum(*args, **kw) -> int:

@@ -608,7 +608,7 @@ struct Experts {
   int E;
 };
 
-int check_experts(const tp_expert_desc* d, const int64_t* offsets, Experts& x) {
+int check_expert_desc(const tp_expert_desc* d, Experts& x) {
   if (!d) return fail(TP_ERR_NULL, "desc is NULL");
   if (d->dtype != TP_BF16) return fail(TP_ERR_DTYPE, "grouped experts support bf16 only");
   if (d->E < 1 || d->E > TP_MAX_EXPERTS)
@@ -616,32 +616,58 @@ int check_experts(const tp_expert_desc* d, const int64_t* offsets, Experts& x) {
   if (d->H <= 0 || d->F <= 0 || d->H % 8 || d->F % 8)
     return fail(TP_ERR_SHAPE, "H and F must be positive multiples of 8");
   if (d->H > kMaxLd || d->F > kMaxLd / 2) return fail(TP_ERR_SHAPE, "dimension too large");
+  x.H = d->H;
+  x.F = d->F;
+  x.E = d->E;
+  return TP_OK;
+}
+
+int check_experts(const tp_expert_desc* d, const int64_t* offsets, Experts& x) {
+  int rc = check_expert_desc(d, x);
+  if (rc) return rc;
   if (!offsets) return fail(TP_ERR_NULL, "offsets is NULL");
   if (offsets[0] != 0) return fail(TP_ERR_SHAPE, "offsets[0] must be 0");
   for (int e = 0; e < d->E; ++e)
     if (offsets[e + 1] < offsets[e]) return fail(TP_ERR_SHAPE, "offsets must be non-decreasing");
   if (offsets[d->E] > kMaxDim) return fail(TP_ERR_SHAPE, "too many rows");
-  x.H = d->H;
-  x.F = d->F;
-  x.E = d->E;
   x.R = offsets[d->E];
   return TP_OK;
 }
 
-void set_rows(GemmArgs& g, const Experts& x, const int64_t* offsets, int ragged) {
-  g.E = x.E;
-  g.ragged = ragged;
-  for (int e = 0; e <= x.E; ++e) g.row_off[e] = (int)offsets[e];
+// device-resident offsets: the host checks only the capacity R and the table
+int check_experts_dev(const tp_expert_desc* d, int64_t R, const int32_t* offsets, Experts& x) {
+  int rc = check_expert_desc(d, x);
+  if (rc) return rc;
+  if (R < 0 || R > kMaxDim) return fail(TP_ERR_SHAPE, "R must be in 0..%lld", (long long)kMaxDim);
+  if (!offsets) return fail(TP_ERR_NULL, "offsets is NULL");
+  if (reinterpret_cast<uintptr_t>(offsets) & 3u)
+    return fail(TP_ERR_ALIGN, "offsets is not 4-byte aligned");
+  x.R = R;
+  return TP_OK;
 }
 
-}  // namespace
+// where a grouped call's row offsets are: E+1 host values, or E+1 int32 in
+// device memory that the kernels read (clamped into [0, R]) when they run
+struct Rows {
+  const int64_t* host;
+  const int32_t* dev;
+};
 
-int tp_grouped_expert_fwd(const tp_expert_desc* desc, const int64_t* offsets, const void* X_perm,
-                          const void* Wg, const void* Wu, const void* Wd, void* Z_save,
-                          void* H_act, void* Y_perm, void* stream) {
-  Experts x;
-  int rc = check_experts(desc, offsets, x);
-  if (rc) return rc;
+void set_rows(GemmArgs& g, const Experts& x, const Rows& rows, int ragged) {
+  g.E = x.E;
+  g.ragged = ragged;
+  if (rows.dev) {
+    g.dev_off = rows.dev;
+    g.dev_rows = (int)x.R;
+  } else {
+    for (int e = 0; e <= x.E; ++e) g.row_off[e] = (int)rows.host[e];
+  }
+}
+
+int grouped_fwd(const Experts& x, const Rows& rows, const void* X_perm, const void* Wg,
+                const void* Wu, const void* Wd, void* Z_save, void* H_act, void* Y_perm,
+                void* stream) {
+  int rc;
   const size_t wbytes = (size_t)(x.E * x.H * x.F) * 2;
   Buf req[] = {{X_perm, (size_t)(x.R * x.H) * 2, "X_perm"},
                {Wg, wbytes, "Wg"},
@@ -652,16 +678,17 @@ int tp_grouped_expert_fwd(const tp_expert_desc* desc, const int64_t* offsets, co
   if ((rc = check_ptrs(req, 6, true))) return rc;
   Buf zs = {Z_save, (size_t)(x.R * x.F) * 4, "Z_save"};
   if ((rc = check_ptrs(&zs, 1, false))) return rc;
-  Buf ins[] = {req[0], req[1], req[2], req[3]};
+  Buf ins[] = {req[0], req[1], req[2], req[3],
+               {rows.dev, rows.dev ? (size_t)(x.E + 1) * 4 : 0, "offsets"}};
   Buf outs[] = {req[4], req[5], zs};
-  if ((rc = check_alias(ins, 4, outs, 3))) return rc;
+  if ((rc = check_alias(ins, 5, outs, 3))) return rc;
   if ((rc = check_device())) return rc;
   if (x.R == 0) return ok();
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int H = (int)x.H, F = (int)x.F;
   GemmArgs g1 = dense_args(0, 2 * F, H);
-  set_rows(g1, x, offsets, RAGGED_M);
+  set_rows(g1, x, rows, RAGGED_M);
   g1.a = {X_perm, nullptr, H, 0, 0};
   g1.b = {Wg, Wu, F, (int64_t)H * F, F};
   g1.epi.out0 = Z_save;
@@ -673,7 +700,7 @@ int tp_grouped_expert_fwd(const tp_expert_desc* desc, const int64_t* offsets, co
   if (he != hipSuccess) return hip_fail(he, "grouped FC1 launch");
 
   GemmArgs g2 = dense_args(0, H, F);
-  set_rows(g2, x, offsets, RAGGED_M);
+  set_rows(g2, x, rows, RAGGED_M);
   g2.a = {H_act, nullptr, F, 0, 0};
   g2.b = {Wd, nullptr, H, (int64_t)F * H, 0};
   g2.epi.out0 = Y_perm;
@@ -683,6 +710,27 @@ int tp_grouped_expert_fwd(const tp_expert_desc* desc, const int64_t* offsets, co
   return ok();
 }
 
+}  // namespace
+
+int tp_grouped_expert_fwd(const tp_expert_desc* desc, const int64_t* offsets, const void* X_perm,
+                          const void* Wg, const void* Wu, const void* Wd, void* Z_save,
+                          void* H_act, void* Y_perm, void* stream) {
+  Experts x;
+  int rc = check_experts(desc, offsets, x);
+  if (rc) return rc;
+  return grouped_fwd(x, Rows{offsets, nullptr}, X_perm, Wg, Wu, Wd, Z_save, H_act, Y_perm, stream);
+}
+
+int tp_grouped_expert_fwd_devoff(const tp_expert_desc* desc, int64_t R, const int32_t* offsets,
+                                 const void* X_perm, const void* Wg, const void* Wu,
+                                 const void* Wd, void* Z_save, void* H_act, void* Y_perm,
+                                 void* stream) {
+  Experts x;
+  int rc = check_experts_dev(desc, R, offsets, x);
+  if (rc) return rc;
+  return grouped_fwd(x, Rows{nullptr, offsets}, X_perm, Wg, Wu, Wd, Z_save, H_act, Y_perm, stream);
+}
+
 size_t tp_grouped_expert_bwd_workspace(const tp_expert_desc* desc, const int64_t* offsets) {
   Experts x;
   if (check_experts(desc, offsets, x)) return 0;
@@ -690,13 +738,11 @@ size_t tp_grouped_expert_bwd_workspace(const tp_expert_desc* desc, const int64_t
 }
 
 namespace {
-int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* X_perm,
-                const void* Wg, const void* Wu, const void* Wd, const void* Z_save,
-                const void* H_act, const void* dY_perm, void* dX_perm, float* dWg, float* dWu,
-                float* dWd, void* workspace, size_t ws_bytes, void* stream, bool accumulate) {
-  Experts x;
-  int rc = check_experts(desc, offsets, x);
-  if (rc) return rc;
+int grouped_bwd(const Experts& x, const Rows& rows, const void* X_perm, const void* Wg,
+                const void* Wu, const void* Wd, const void* Z_save, const void* H_act,
+                const void* dY_perm, void* dX_perm, float* dWg, float* dWu, float* dWd,
+                void* workspace, size_t ws_bytes, void* stream, bool accumulate) {
+  int rc;
   const size_t wbytes = (size_t)(x.E * x.H * x.F) * 2;
   const size_t gbytes = (size_t)(x.E * x.H * x.F) * 4;
   Buf in_req[] = {{X_perm, (size_t)(x.R * x.H) * 2, "X_perm"},
@@ -721,7 +767,9 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
   }
   Buf ws = {workspace, need, "workspace"};
   Buf outs[] = {out_req[0], out_req[1], out_req[2], out_req[3], ws};
-  if ((rc = check_alias(in_req, 7, outs, 5))) return rc;
+  Buf ins[] = {in_req[0], in_req[1], in_req[2], in_req[3], in_req[4], in_req[5], in_req[6],
+               {rows.dev, rows.dev ? (size_t)(x.E + 1) * 4 : 0, "offsets"}};
+  if ((rc = check_alias(ins, 8, outs, 5))) return rc;
   if ((rc = check_device())) return rc;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -730,7 +778,7 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
   hipError_t he;
   if (x.R > 0) {
     GemmArgs g = dense_args(0, F, H);
-    set_rows(g, x, offsets, RAGGED_M);
+    set_rows(g, x, rows, RAGGED_M);
     g.a = {dY_perm, nullptr, H, 0, 0};
     g.b = {Wd, nullptr, H, HF, 0};
     g.epi.aux = Z_save;
@@ -743,7 +791,7 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
   }
   {
     GemmArgs g = dense_args(F, H, 0);
-    set_rows(g, x, offsets, RAGGED_K);
+    set_rows(g, x, rows, RAGGED_K);
     g.a = {H_act, nullptr, F, 0, 0};
     g.b = {dY_perm, nullptr, H, 0, 0};
     g.epi.out0 = dWd;
@@ -754,7 +802,7 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
   }
   {
     GemmArgs g = dense_args(H, 2 * F, 0);
-    set_rows(g, x, offsets, RAGGED_K);
+    set_rows(g, x, rows, RAGGED_K);
     g.a = {X_perm, nullptr, H, 0, 0};
     g.b = {workspace, nullptr, 2 * (int64_t)F, 0, 0};
     g.epi.out0 = dWg;
@@ -768,7 +816,7 @@ int grouped_bwd(const tp_expert_desc* desc, const int64_t* offsets, const void* 
   }
   if (x.R > 0) {
     GemmArgs g = dense_args(0, H, 2 * F);
-    set_rows(g, x, offsets, RAGGED_M);
+    set_rows(g, x, rows, RAGGED_M);
     g.a = {workspace, nullptr, 2 * (int64_t)F, 0, 0};
     g.b = {Wg, Wu, F, HF, F};
     g.epi.out0 = dX_perm;
@@ -785,8 +833,11 @@ int tp_grouped_expert_bwd(const tp_expert_desc* desc, const int64_t* offsets, co
                           const void* H_act, const void* dY_perm, void* dX_perm, float* dWg,
                           float* dWu, float* dWd, void* workspace, size_t ws_bytes,
                           void* stream) {
-  return grouped_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm, dX_perm, dWg, dWu,
-                     dWd, workspace, ws_bytes, stream, false);
+  Experts x;
+  int rc = check_experts(desc, offsets, x);
+  if (rc) return rc;
+  return grouped_bwd(x, Rows{offsets, nullptr}, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm,
+                     dX_perm, dWg, dWu, dWd, workspace, ws_bytes, stream, false);
 }
 
 int tp_grouped_expert_bwd_accum(const tp_expert_desc* desc, const int64_t* offsets,
@@ -794,8 +845,31 @@ int tp_grouped_expert_bwd_accum(const tp_expert_desc* desc, const int64_t* offse
                                 const void* Wd, const void* Z_save, const void* H_act,
                                 const void* dY_perm, void* dX_perm, float* dWg, float* dWu,
                                 float* dWd, void* workspace, size_t ws_bytes, void* stream) {
-  return grouped_bwd(desc, offsets, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm, dX_perm, dWg, dWu,
-                     dWd, workspace, ws_bytes, stream, true);
+  Experts x;
+  int rc = check_experts(desc, offsets, x);
+  if (rc) return rc;
+  return grouped_bwd(x, Rows{offsets, nullptr}, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm,
+                     dX_perm, dWg, dWu, dWd, workspace, ws_bytes, stream, true);
+}
+
+size_t tp_grouped_expert_devoff_workspace(const tp_expert_desc* desc, int64_t R) {
+  Experts x;
+  if (check_expert_desc(desc, x) || R < 0 || R > kMaxDim) return 0;
+  return (size_t)(R * x.F) * 2 * 2;
+}
+
+int tp_grouped_expert_bwd_devoff(const tp_expert_desc* desc, int64_t R, const int32_t* offsets,
+                                 const void* X_perm, const void* Wg, const void* Wu,
+                                 const void* Wd, const void* Z_save, const void* H_act,
+                                 const void* dY_perm, void* dX_perm, float* dWg, float* dWu,
+                                 float* dWd, void* workspace, size_t ws_bytes,
+                                 int32_t accumulate, void* stream) {
+  Experts x;
+  int rc = check_experts_dev(desc, R, offsets, x);
+  if (rc) return rc;
+  if (accumulate != 0 && accumulate != 1) return fail(TP_ERR_SHAPE, "accumulate must be 0 or 1");
+  return grouped_bwd(x, Rows{nullptr, offsets}, X_perm, Wg, Wu, Wd, Z_save, H_act, dY_perm,
+                     dX_perm, dWg, dWu, dWd, workspace, ws_bytes, stream, accumulate == 1);
 }
 
 // ---------------------------------------------------------------------------

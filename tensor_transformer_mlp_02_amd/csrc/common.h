@@ -180,6 +180,22 @@ struct GemmArgs {
   int tiles_n;
   int row_off[TP_MAX_EXPERTS + 1];
   int tile_off[TP_MAX_EXPERTS + 1];
+  // Row offsets in device memory (E+1 int32, e.g. written by the routing
+  // step on the same stream), read by every workgroup in place of row_off.
+  // They are taken clamped: offset 0 into [0, dev_rows], offset e+1 into
+  // [offset e, dev_rows], so no value can send an access past dev_rows
+  // rows.  A RAGGED_M launch then has workgroups for every split of
+  // dev_rows rows into E problems; those past the tiles the offsets need
+  // exit at once (TileCoord::e < 0).  Only the 256-row kernels of the
+  // grouped launches (lean, ring, general) take them.
+  const int* dev_off;
+  int dev_rows;
+  // With dev_off, RAGGED_M: the rows of a problem past its last multiple of
+  // 256, if at most dev_thin of them (0: never), go to a thin-tile launch
+  // when that takes fewer waves of 256-row tiles over dev_cus compute
+  // units; every workgroup of both launches takes that decision from the
+  // offsets (the host takes it the same way from host offsets).
+  int dev_thin, dev_cus;
 };
 
 // Problem lookup shared by the GEMM kernels.
@@ -212,17 +228,89 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+// offset e of the device-resident offsets, clamped into [lo, dev_rows]
+__device__ __forceinline__ int dev_row_off(const GemmArgs& g, int e, int lo) {
+  return min(max(g.dev_off[e], lo), g.dev_rows);
+}
+
+// tile rows of `rows` rows in BM-row tiles, the last few left out when
+// remainders of at most `thin` rows go to the thin launch
+__device__ __forceinline__ int dev_tile_rows(int rows, int BM, int thin) {
+  return thin > 0 ? rows / BM + (rows % BM > thin ? 1 : 0) : (rows + BM - 1) / BM;
+}
+
+// Device-resident offsets: whether the 256-row launch leaves remainders to
+// the thin launch (the same answer in every workgroup of both)
+__device__ __forceinline__ bool dev_use_thin(const GemmArgs& g) {
+  if (g.dev_thin <= 0) return false;
+  int plain = 0, thin = 0;
+  int lo = min(max(g.dev_off[0], 0), g.dev_rows);
+  for (int i = 0; i < g.E; ++i) {
+    const int hi = dev_row_off(g, i + 1, lo);
+    plain += dev_tile_rows(hi - lo, 256, 0);
+    thin += dev_tile_rows(hi - lo, 256, g.dev_thin);
+    lo = hi;
+  }
+  const int c = g.dev_cus;
+  return (thin * g.tiles_n + c - 1) / c < (plain * g.tiles_n + c - 1) / c;
+}
+
 __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& g, int block, int nblocks,
                                                  int BM) {
-  const int tile = xcd_logical_block(block, nblocks);
   TileCoord t;
-  int e = 0;
-  while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
-  const int local = tile - g.tile_off[e];
-  const int lo = g.row_off[e], hi = g.row_off[e + 1];
+  int tile, e = 0, t0, t1, lo, hi;
+  if (g.dev_off && g.ragged == RAGGED_M) {
+    // each problem's tiles follow from its rows: ceil(rows / BM) tile rows
+    // (or whole ones only, see dev_thin).  The first `total` workgroups take
+    // the tiles, in the order a launch of exactly that many would (the
+    // others exit at once): the work spreads over every XCD however far the
+    // grid overshoots it.
+    const int thin = BM == 256 && dev_use_thin(g) ? g.dev_thin : 0;
+    const int lo0 = min(max(g.dev_off[0], 0), g.dev_rows);
+    int total = 0;
+    lo = lo0;
+    for (int i = 0; i < g.E; ++i) {
+      hi = dev_row_off(g, i + 1, lo);
+      total += dev_tile_rows(hi - lo, BM, thin) * g.tiles_n;
+      lo = hi;
+    }
+    if (block >= total) {
+      t.e = -1;  // a spare workgroup of the worst-case grid
+      return t;
+    }
+    tile = xcd_logical_block(block, total);
+    lo = lo0;
+    t0 = 0;
+    for (;;) {
+      hi = dev_row_off(g, e + 1, lo);
+      t1 = t0 + dev_tile_rows(hi - lo, BM, thin) * g.tiles_n;
+      if (tile < t1 || e + 1 == g.E) break;
+      ++e;
+      lo = hi;
+      t0 = t1;
+    }
+  } else {
+    tile = xcd_logical_block(block, nblocks);
+    while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
+    t0 = g.tile_off[e];
+    t1 = g.tile_off[e + 1];
+    if (g.dev_off) {
+      // RAGGED_K: the tiles do not depend on the rows, the k range does
+      lo = min(max(g.dev_off[0], 0), g.dev_rows);
+      hi = dev_row_off(g, 1, lo);
+      for (int i = 1; i <= e; ++i) {
+        lo = hi;
+        hi = dev_row_off(g, i + 1, lo);
+      }
+    } else {
+      lo = g.row_off[e];
+      hi = g.row_off[e + 1];
+    }
+  }
+  const int local = tile - t0;
   // tile rows of this problem as the launcher counted them (a ragged
   // problem's last few rows may be left to the thin-tile launch)
-  const int tiles_m = (g.tile_off[e + 1] - g.tile_off[e]) / g.tiles_n;
+  const int tiles_m = (t1 - t0) / g.tiles_n;
   const int group = local / (RASTER_G * g.tiles_n);
   const int first_m = group * RASTER_G;
   const int gm = min(RASTER_G, tiles_m - first_m);

@@ -495,6 +495,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
   const int half_w = wave / (NWAVES / 2);  // tile half this wavefront loads
 
   const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BM);
+  if (tc.e < 0) return;  // spare tile (device-resident offsets)
   const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
   const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
   const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
@@ -797,6 +798,7 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   const int r_lane = lane & 31, c_lane = lane >> 5;
 
   const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, TMR);
+  if (tc.e < 0) return;  // spare tile (device-resident offsets)
   const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
   const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
   const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
@@ -1087,6 +1089,7 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_ring(GemmArgs g) {
   const int r_lane = lane & 31, c_lane = lane >> 5;
 
   const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, BM);
+  if (tc.e < 0) return;  // spare tile (device-resident offsets)
   const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
   const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
   const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
@@ -1903,12 +1906,46 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_rows(GemmArgs g) {
 
   // TAIL: problem e's tiles cover its rows from the last multiple of 256 on;
   // otherwise all of its rows
-  const int tile = xcd_logical_block(blockIdx.x, gridDim.x);
-  int e = 0;
-  while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
-  const int local = tile - g.tile_off[e];
-  const int lo = g.row_off[e], hi = g.row_off[e + 1];
-  const int tiles_m = (g.tile_off[e + 1] - g.tile_off[e]) / g.tiles_n;
+  int e = 0, lo, hi, local, tiles_m;
+  if (g.dev_off) {
+    // device-resident offsets (remainder tiles only): there are tiles when
+    // the 256-row launch leaves the remainders here, and the first `total`
+    // workgroups take them; the others exit at once
+    if (!TAIL || !dev_use_thin(g)) return;
+    auto thin_rows = [&](int rows) {
+      const int rem = rows % BM;
+      return (rem > 0 && rem <= g.dev_thin) ? (rem + TM - 1) / TM : 0;
+    };
+    const int lo0 = min(max(g.dev_off[0], 0), g.dev_rows);
+    int total = 0;
+    lo = lo0;
+    for (int i = 0; i < g.E; ++i) {
+      hi = dev_row_off(g, i + 1, lo);
+      total += thin_rows(hi - lo) * g.tiles_n;
+      lo = hi;
+    }
+    if ((int)blockIdx.x >= total) return;
+    const int tile = xcd_logical_block(blockIdx.x, total);
+    int t0 = 0, t1;
+    lo = lo0;
+    for (;;) {
+      hi = dev_row_off(g, e + 1, lo);
+      t1 = t0 + thin_rows(hi - lo) * g.tiles_n;
+      if (tile < t1 || e + 1 == g.E) break;
+      ++e;
+      lo = hi;
+      t0 = t1;
+    }
+    local = tile - t0;
+    tiles_m = (t1 - t0) / g.tiles_n;
+  } else {
+    const int tile = xcd_logical_block(blockIdx.x, gridDim.x);
+    while (e + 1 < g.E && tile >= g.tile_off[e + 1]) ++e;
+    local = tile - g.tile_off[e];
+    lo = g.row_off[e];
+    hi = g.row_off[e + 1];
+    tiles_m = (g.tile_off[e + 1] - g.tile_off[e]) / g.tiles_n;
+  }
   TileCoord tc;
   tc.e = e;
   tc.tm = local % tiles_m;
@@ -2361,7 +2398,55 @@ template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_rows(GemmArgs& g, hipStream_t stream, int thin_max);
 
 template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_256(GemmArgs& g, int blocks, hipStream_t stream);
+
+// Grouped launches whose row offsets stay in device memory: the host does
+// not see the rows, so a RAGGED_M launch takes 256 x 256 tiles for every
+// split of dev_rows rows into E problems, at most (dev_rows + E (BM - 1)) /
+// BM tile rows in all (the workgroups of spare tiles exit at once), then,
+// where the short-row kernel can take them, a thin launch for remainders
+// of at most THIN_MAX rows (whose workgroups all exit unless the offsets
+// make it pay); the tiles of a RAGGED_K launch do not depend on the rows.
+template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_devoff(GemmArgs& g, hipStream_t stream) {
+  using namespace mfma256;
+  if (g.ragged == RAGGED_NONE || g.dev_rows < 0) return hipErrorInvalidValue;
+  const int n_given = g.N;  // (the thin kernel takes the columns as given)
+  int n_cols = g.N;
+  if (BMODE == BMODE_PAIR32) {
+    n_cols = ((int)((g.b.split + 31) / 32)) * 64;
+    g.N = n_cols;
+  }
+  int64_t blocks;
+  if (g.ragged == RAGGED_M) {
+    g.tiles_n = (n_cols + BN - 1) / BN;
+    blocks = ((int64_t)g.dev_rows + (int64_t)g.E * (BM - 1)) / BM * g.tiles_n;
+  } else {
+    fill_tiles(g, BM, BN, n_cols);
+    blocks = g.tile_off[g.E];
+  }
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  // remainders of at most THIN_MAX rows may go to the thin kernel (the
+  // kernels decide from the offsets as the host would from host ones):
+  // at most THIN_MAX / THIN_M tile rows per problem
+  const bool thin = g.ragged == RAGGED_M && short_rows_ok<AK, BK_, BMODE>(g);
+  g.dev_thin = thin ? THIN_MAX : 0;
+  g.dev_cus = device_cus();
+  hipError_t he = launch_256<NW, AK, BK_, BMODE, EPI, OutT>(g, (int)blocks, stream);
+  if (he != hipSuccess || !thin || blocks == 0) return he;
+  if constexpr (AK && !(BMODE == BMODE_PAIR32 && BK_)) {
+    g.N = n_given;
+    const int tblocks = g.E * (THIN_MAX / THIN_M) * g.tiles_n;
+    hipLaunchKernelGGL((gemm_rows<THIN_M, true, BK_, BMODE, EPI, OutT>), dim3(tblocks),
+                       dim3(THIN_NT), 0, stream, g);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
+  if (g.dev_off) return launch_devoff<NW, AK, BK_, BMODE, EPI, OutT>(g, stream);
   const int thin_max = thin_rows_max<AK, BK_, BMODE>(g);
   if (lean128_pays<AK, BK_, BMODE>(g, thin_max))
     return launch_lean128<AK, BK_, BMODE, EPI, OutT>(g, stream);
@@ -2403,7 +2488,13 @@ static hipError_t launch_rows(GemmArgs& g, hipStream_t stream, int thin_max) {
     g.N = n_cols;
   }
   fill_tiles(g, mfma256::BM, mfma256::BN, n_cols, thin_max);
-  int blocks = g.tile_off[g.E];
+  return launch_256<NW, AK, BK_, BMODE, EPI, OutT>(g, g.tile_off[g.E], stream);
+}
+
+// `blocks` 256 x 256 tiles on the hand-ordered kernel, else the ring
+// kernel, else the general one (whichever first takes the k extents).
+template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
+static hipError_t launch_256(GemmArgs& g, int blocks, hipStream_t stream) {
   if (blocks == 0) return hipSuccess;
   // the hand-ordered kernel needs whole 64-wide k tiles of K-contiguous
   // operands and a 64-aligned k split

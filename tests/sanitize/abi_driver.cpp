@@ -149,6 +149,23 @@ int main() {
     const int64_t bad[] = {0, 5, 3, 9, 9};   // decreasing
     check(tp_grouped_expert_fwd(&ed, bad, fake(1), fake(2), fake(3), fake(4), fake(5), fake(6),
                                 fake(7), nullptr), "grouped offsets", TP_ERR_SHAPE);
+    const int32_t* dev_off = reinterpret_cast<const int32_t*>(fake(8));
+    check(tp_grouped_expert_fwd_devoff(&ed, -1, dev_off, fake(1), fake(2), fake(3), fake(4),
+                                       fake(5), fake(6), fake(7), nullptr),
+          "devoff R", TP_ERR_SHAPE);
+    check(tp_grouped_expert_fwd_devoff(&ed, 100, nullptr, fake(1), fake(2), fake(3), fake(4),
+                                       fake(5), fake(6), fake(7), nullptr),
+          "devoff NULL", TP_ERR_NULL);
+    check(tp_grouped_expert_bwd_devoff(&ed, 100, dev_off, fake(1), fake(2), fake(3), fake(4),
+                                       fake(5), fake(6), fake(9), fake(10), (float*)fake(11),
+                                       (float*)fake(12), (float*)fake(13), fake(14),
+                                       tp_grouped_expert_devoff_workspace(&ed, 100), 3, nullptr),
+          "devoff accumulate", TP_ERR_SHAPE);
+    check(tp_grouped_expert_bwd_devoff(&ed, 100, dev_off, fake(1), fake(2), fake(3), fake(4),
+                                       fake(5), fake(6), fake(9), fake(10), (float*)fake(11),
+                                       (float*)fake(12), (float*)fake(13), fake(14),
+                                       tp_grouped_expert_devoff_workspace(&ed, 100), 1, nullptr),
+          "devoff valid", TP_ERR_DEVICE);
   }
 
   // --- fuzz ---------------------------------------------------------------------
@@ -212,7 +229,27 @@ int main() {
         }
         tp_expert_desc* pe = rnd() % 50 ? &ed : nullptr;
         const int64_t* po = rnd() % 50 ? offs : nullptr;
-        if (variant == 3) {
+        if (rnd() % 3 == 0) {
+          // device-resident offsets: the host must never read the table
+          // (a fake address here), only check R, its pointer and alignment
+          const int64_t R = rnd() % 8 ? (int64_t)(rnd() % 5000) : pick(dims, ND);
+          const int32_t* pdo = reinterpret_cast<const int32_t*>(ptr_any(13));
+          if (variant == 3) {
+            check(tp_grouped_expert_fwd_devoff(pe, R, pdo, ptr_any(1), ptr_any(2), ptr_any(3),
+                                               ptr_any(4), ptr_any(5), ptr_any(6), ptr_any(7),
+                                               nullptr),
+                  "fuzz grouped fwd devoff");
+          } else {
+            const size_t ws = tp_grouped_expert_devoff_workspace(pe, R);
+            check(tp_grouped_expert_bwd_devoff(pe, R, pdo, ptr_any(1), ptr_any(2), ptr_any(3),
+                                               ptr_any(4), ptr_any(5), ptr_any(6), ptr_any(7),
+                                               ptr_any(8), (float*)ptr_any(9),
+                                               (float*)ptr_any(10), (float*)ptr_any(11),
+                                               ptr_any(12), rnd() % 2 ? ws : 64,
+                                               (int32_t)(rnd() % 4), nullptr),
+                  "fuzz grouped bwd devoff");
+          }
+        } else if (variant == 3) {
           check(tp_grouped_expert_fwd(pe, po, ptr_any(1), ptr_any(2), ptr_any(3), ptr_any(4),
                                       ptr_any(5), ptr_any(6), ptr_any(7), nullptr),
                 "fuzz grouped fwd");

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 27, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -247,6 +247,51 @@ def test_grouped_argument_checks():
     assert gfwd(d, off, Wd=None) == E_NULL
     assert gfwd(d, off, Y=addr(2)) == E_ALIAS
     assert tp.tp_grouped_expert_bwd_workspace(d, off) == 31 * 2 * 128 * 2
+
+
+def gdev(desc, R, off=addr(9), accumulate=0, fwd=True, **kw):
+    """Status of a device-offset grouped call (raw C call: no marshalling)."""
+    p = dict(X=addr(1), Wg=addr(2), Wu=addr(3), Wd=addr(4), Z=addr(5), H=addr(6), Y=addr(7),
+             dY=addr(8), dX=addr(10), dWg=addr(11), dWu=addr(12), dWd=addr(13), ws=addr(14))
+    p.update(kw)
+    d = tp._edesc(desc)
+    L = tp.lib()
+    if fwd:
+        rc = L.tp_grouped_expert_fwd_devoff(ctypes.byref(d), R, off, p["X"], p["Wg"], p["Wu"],
+                                            p["Wd"], p["Z"], p["H"], p["Y"], None)
+    else:
+        ws = L.tp_grouped_expert_devoff_workspace(ctypes.byref(d), max(R, 0))
+        rc = L.tp_grouped_expert_bwd_devoff(ctypes.byref(d), R, off, p["X"], p["Wg"], p["Wu"],
+                                            p["Wd"], p["Z"], p["H"], p["dY"], p["dX"], p["dWg"],
+                                            p["dWu"], p["dWd"], p["ws"], ws, accumulate, None)
+    return rc
+
+
+def test_device_offset_grouped_argument_checks():
+    d = dict(H=256, F=128, E=4, dtype=tp.TP_BF16)
+    for fwd in (True, False):
+        assert gdev(dict(d, dtype=tp.TP_F32), 64, fwd=fwd) == E_DTYPE
+        assert gdev(dict(d, E=0), 64, fwd=fwd) == E_SHAPE
+        assert gdev(dict(d, E=65), 64, fwd=fwd) == E_SHAPE
+        assert gdev(dict(d, F=100), 64, fwd=fwd) == E_SHAPE
+        assert gdev(d, -1, fwd=fwd) == E_SHAPE
+        assert gdev(d, (1 << 30) + 1, fwd=fwd) == E_SHAPE
+        assert gdev(d, 64, off=None, fwd=fwd) == E_NULL
+        assert gdev(d, 64, off=addr(9, 2), fwd=fwd) == E_ALIGN       # int32 table
+        assert gdev(d, 64, Wg=None, fwd=fwd) == E_NULL
+    assert gdev(d, 64, X=addr(7)) == E_ALIAS                          # X_perm is Y_perm
+    assert gdev(d, 64, off=addr(7, 16)) == E_ALIAS                    # offsets inside Y_perm
+    assert gdev(d, 64, fwd=False, accumulate=2) == E_SHAPE
+    assert gdev(d, 64, fwd=False, ws=None) == E_WS
+    assert gdev(d, 64, fwd=False, off=addr(12, 64)) == E_ALIAS        # offsets inside dWu
+    L = tp.lib()
+    assert L.tp_grouped_expert_devoff_workspace(ctypes.byref(tp._edesc(d)), 64) == 64 * 2 * 128 * 2
+    assert L.tp_grouped_expert_devoff_workspace(ctypes.byref(tp._edesc(d)), -1) == 0
+    # the binding passes a GPU tensor's address only
+    import torch
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        tp.tp_grouped_expert_fwd_devoff(d, 8, torch.zeros(5, dtype=torch.int32), addr(1),
+                                        addr(2), addr(3), addr(4), addr(5), addr(6), addr(7))
 
 
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
