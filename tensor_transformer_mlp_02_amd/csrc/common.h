@@ -186,16 +186,19 @@ struct GemmArgs {
   // [offset e, dev_rows], so no value can send an access past dev_rows
   // rows.  A RAGGED_M launch then has workgroups for every split of
   // dev_rows rows into E problems; those past the tiles the offsets need
-  // exit at once (TileCoord::e < 0).  Only the 256-row kernels of the
-  // grouped launches (lean, ring, general) take them.
+  // exit at once (TileCoord::e < 0): only the hand-ordered (256 and 128
+  // rows), ring, general and thin kernels run such launches.  A RAGGED_K
+  // launch takes only its k ranges from them (any kernel).
   const int* dev_off;
   int dev_rows;
-  // With dev_off, RAGGED_M: the rows of a problem past its last multiple of
-  // 256, if at most dev_thin of them (0: never), go to a thin-tile launch
-  // when that takes fewer waves of 256-row tiles over dev_cus compute
-  // units; every workgroup of both launches takes that decision from the
-  // offsets (the host takes it the same way from host offsets).
-  int dev_thin, dev_cus;
+  // With dev_off, RAGGED_M: the launcher queues every tiling the host could
+  // have picked from host offsets (256-row tiles; with dev_thin > 0 the
+  // same with remainders of at most dev_thin rows in a thin launch; with
+  // dev_l128 > 0 128-row tiles, their area weighted by dev_l128 / 1000),
+  // and every workgroup takes the host's choice from the offsets (fewest
+  // weighted tile-area waves over dev_cus compute units): the workgroups
+  // of the launches not chosen exit at once.
+  int dev_thin, dev_l128, dev_cus;
 };
 
 // Problem lookup shared by the GEMM kernels.
@@ -228,9 +231,44 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
-// offset e of the device-resident offsets, clamped into [lo, dev_rows]
-__device__ __forceinline__ int dev_row_off(const GemmArgs& g, int e, int lo) {
-  return min(max(g.dev_off[e], lo), g.dev_rows);
+// ---- device-resident offsets: one problem per lane (E <= 64) -------------
+// Every lane of the wavefront must be active; results that index a problem
+// come back through readlane, so they are wave-uniform (scalar).
+
+// Lane i gets problem i's clamped rows [lo, hi); lanes past E get empty
+// problems at the end.  Clamping each offset into [previous one, rows]
+// (the first into [0, rows]) is the same as clamping the running maximum
+// of the offsets into [0, rows].
+__device__ __forceinline__ void dev_lane_rows(const GemmArgs& g, int& lo, int& hi) {
+  const int lane = threadIdx.x & 63;
+  const int first = g.dev_off[0];
+  int v = lane < g.E ? max(g.dev_off[lane + 1], first) : first;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v = max(v, u);
+  }
+  hi = min(max(v, 0), g.dev_rows);
+  const int prev = __shfl_up(hi, 1, 64);
+  lo = lane == 0 ? min(max(first, 0), g.dev_rows) : prev;
+}
+
+// (the same in every lane: returned as a scalar, so that what is decided
+// from it is a uniform branch)
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(x, d, 64);
+    if (lane >= d) x += u;
+  }
+  return x;
 }
 
 // tile rows of `rows` rows in BM-row tiles, the last few left out when
@@ -239,20 +277,46 @@ __device__ __forceinline__ int dev_tile_rows(int rows, int BM, int thin) {
   return thin > 0 ? rows / BM + (rows % BM > thin ? 1 : 0) : (rows + BM - 1) / BM;
 }
 
-// Device-resident offsets: whether the 256-row launch leaves remainders to
-// the thin launch (the same answer in every workgroup of both)
-__device__ __forceinline__ bool dev_use_thin(const GemmArgs& g) {
-  if (g.dev_thin <= 0) return false;
-  int plain = 0, thin = 0;
-  int lo = min(max(g.dev_off[0], 0), g.dev_rows);
-  for (int i = 0; i < g.E; ++i) {
-    const int hi = dev_row_off(g, i + 1, lo);
-    plain += dev_tile_rows(hi - lo, 256, 0);
-    thin += dev_tile_rows(hi - lo, 256, g.dev_thin);
-    lo = hi;
+// The tiling the offsets call for (the same in every workgroup of every
+// launch): 0 = 256-row tiles, 1 = 256-row tiles with thin remainders,
+// 2 = 128-row tiles.  `rows` is this lane's problem's.
+enum { DEV_T256 = 0, DEV_T256_THIN = 1, DEV_T128 = 2 };
+__device__ __forceinline__ int dev_tiling(const GemmArgs& g, int rows) {
+  const int64_t c = g.dev_cus, tn = g.tiles_n;
+  auto waves = [&](int tile_rows) { return (int)((wave_sum(tile_rows) * tn + c - 1) / c); };
+  int pick = DEV_T256;
+  int w256 = waves(dev_tile_rows(rows, 256, 0));
+  if (g.dev_thin > 0) {
+    const int wt = waves(dev_tile_rows(rows, 256, g.dev_thin));
+    if (wt < w256) {
+      pick = DEV_T256_THIN;
+      w256 = wt;
+    }
   }
-  const int c = g.dev_cus;
-  return (thin * g.tiles_n + c - 1) / c < (plain * g.tiles_n + c - 1) / c;
+  // half-height tiles: half the area per wave, weighted by dev_l128 / 1000
+  if (g.dev_l128 > 0 && (int64_t)g.dev_l128 * waves(dev_tile_rows(rows, 128, 0)) <
+                            (int64_t)2000 * w256)
+    pick = DEV_T128;
+  return pick;
+}
+
+// This launch's tile `block` from the per-lane tile counts `tiles` (tile
+// rows x tiles_n per problem): the first `total` workgroups take the tiles
+// in the order a launch of exactly that many would, so the work spreads
+// over every XCD however far the grid overshoots it.  Returns false for a
+// spare workgroup.
+__device__ __forceinline__ bool dev_find_tile(int tiles, int block, int lo_l, int hi_l, int& e,
+                                              int& t0, int& t1, int& lo, int& hi, int& tile) {
+  const int incl = wave_incl_sum(tiles);
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  if (block >= total) return false;
+  tile = xcd_logical_block(block, total);
+  e = __ffsll((unsigned long long)__ballot(tile < incl)) - 1;
+  t1 = __builtin_amdgcn_readlane(incl, e);
+  t0 = t1 - __builtin_amdgcn_readlane(tiles, e);
+  lo = __builtin_amdgcn_readlane(lo_l, e);
+  hi = __builtin_amdgcn_readlane(hi_l, e);
+  return true;
 }
 
 __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& g, int block, int nblocks,
@@ -260,34 +324,18 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& g, int block, i
   TileCoord t;
   int tile, e = 0, t0, t1, lo, hi;
   if (g.dev_off && g.ragged == RAGGED_M) {
-    // each problem's tiles follow from its rows: ceil(rows / BM) tile rows
-    // (or whole ones only, see dev_thin).  The first `total` workgroups take
-    // the tiles, in the order a launch of exactly that many would (the
-    // others exit at once): the work spreads over every XCD however far the
-    // grid overshoots it.
-    const int thin = BM == 256 && dev_use_thin(g) ? g.dev_thin : 0;
-    const int lo0 = min(max(g.dev_off[0], 0), g.dev_rows);
-    int total = 0;
-    lo = lo0;
-    for (int i = 0; i < g.E; ++i) {
-      hi = dev_row_off(g, i + 1, lo);
-      total += dev_tile_rows(hi - lo, BM, thin) * g.tiles_n;
-      lo = hi;
-    }
-    if (block >= total) {
-      t.e = -1;  // a spare workgroup of the worst-case grid
+    int lo_l, hi_l;
+    dev_lane_rows(g, lo_l, hi_l);
+    const int pick = dev_tiling(g, hi_l - lo_l);
+    if ((BM == 128) != (pick == DEV_T128)) {
+      t.e = -1;  // the other tiling's launch does the work
       return t;
     }
-    tile = xcd_logical_block(block, total);
-    lo = lo0;
-    t0 = 0;
-    for (;;) {
-      hi = dev_row_off(g, e + 1, lo);
-      t1 = t0 + dev_tile_rows(hi - lo, BM, thin) * g.tiles_n;
-      if (tile < t1 || e + 1 == g.E) break;
-      ++e;
-      lo = hi;
-      t0 = t1;
+    const int thin = pick == DEV_T256_THIN ? g.dev_thin : 0;
+    if (!dev_find_tile(dev_tile_rows(hi_l - lo_l, BM, thin) * g.tiles_n, block, lo_l, hi_l, e,
+                       t0, t1, lo, hi, tile)) {
+      t.e = -1;  // a spare workgroup of the worst-case grid
+      return t;
     }
   } else {
     tile = xcd_logical_block(block, nblocks);
@@ -296,12 +344,10 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& g, int block, i
     t1 = g.tile_off[e + 1];
     if (g.dev_off) {
       // RAGGED_K: the tiles do not depend on the rows, the k range does
-      lo = min(max(g.dev_off[0], 0), g.dev_rows);
-      hi = dev_row_off(g, 1, lo);
-      for (int i = 1; i <= e; ++i) {
-        lo = hi;
-        hi = dev_row_off(g, i + 1, lo);
-      }
+      int lo_l, hi_l;
+      dev_lane_rows(g, lo_l, hi_l);
+      lo = __builtin_amdgcn_readlane(lo_l, e);
+      hi = __builtin_amdgcn_readlane(hi_l, e);
     } else {
       lo = g.row_off[e];
       hi = g.row_off[e + 1];

@@ -1909,33 +1909,14 @@ __global__ __launch_bounds__(THIN_NT, 1) void gemm_rows(GemmArgs g) {
   int e = 0, lo, hi, local, tiles_m;
   if (g.dev_off) {
     // device-resident offsets (remainder tiles only): there are tiles when
-    // the 256-row launch leaves the remainders here, and the first `total`
-    // workgroups take them; the others exit at once
-    if (!TAIL || !dev_use_thin(g)) return;
-    auto thin_rows = [&](int rows) {
-      const int rem = rows % BM;
-      return (rem > 0 && rem <= g.dev_thin) ? (rem + TM - 1) / TM : 0;
-    };
-    const int lo0 = min(max(g.dev_off[0], 0), g.dev_rows);
-    int total = 0;
-    lo = lo0;
-    for (int i = 0; i < g.E; ++i) {
-      hi = dev_row_off(g, i + 1, lo);
-      total += thin_rows(hi - lo) * g.tiles_n;
-      lo = hi;
-    }
-    if ((int)blockIdx.x >= total) return;
-    const int tile = xcd_logical_block(blockIdx.x, total);
-    int t0 = 0, t1;
-    lo = lo0;
-    for (;;) {
-      hi = dev_row_off(g, e + 1, lo);
-      t1 = t0 + thin_rows(hi - lo) * g.tiles_n;
-      if (tile < t1 || e + 1 == g.E) break;
-      ++e;
-      lo = hi;
-      t0 = t1;
-    }
+    // the offsets call for thin remainders; spare workgroups exit at once
+    if (!TAIL) return;
+    int lo_l, hi_l, t0, t1, tile;
+    dev_lane_rows(g, lo_l, hi_l);
+    if (dev_tiling(g, hi_l - lo_l) != DEV_T256_THIN) return;
+    const int rem = (hi_l - lo_l) % BM;
+    const int tr = (rem > 0 && rem <= g.dev_thin) ? (rem + TM - 1) / TM : 0;
+    if (!dev_find_tile(tr * g.tiles_n, blockIdx.x, lo_l, hi_l, e, t0, t1, lo, hi, tile)) return;
     local = tile - t0;
     tiles_m = (t1 - t0) / g.tiles_n;
   } else {
@@ -2400,40 +2381,51 @@ static hipError_t launch_rows(GemmArgs& g, hipStream_t stream, int thin_max);
 template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_256(GemmArgs& g, int blocks, hipStream_t stream);
 
-// Grouped launches whose row offsets stay in device memory: the host does
-// not see the rows, so a RAGGED_M launch takes 256 x 256 tiles for every
-// split of dev_rows rows into E problems, at most (dev_rows + E (BM - 1)) /
-// BM tile rows in all (the workgroups of spare tiles exit at once), then,
-// where the short-row kernel can take them, a thin launch for remainders
-// of at most THIN_MAX rows (whose workgroups all exit unless the offsets
-// make it pay); the tiles of a RAGGED_K launch do not depend on the rows.
+// Row-ragged grouped launches whose row offsets stay in device memory: the
+// host does not see the rows, so the launch takes 256 x 256 tiles for
+// every split of dev_rows rows into E problems, at most (dev_rows + E (BM -
+// 1)) / BM tile rows in all (the workgroups of spare tiles exit at once),
+// and queues the other tilings the host could pick beside it: 128-row
+// tiles, and a thin launch for remainders of at most THIN_MAX rows.  Every
+// workgroup takes the host's choice from the offsets; those of the
+// launches not chosen exit at once.  (A k-ragged launch's tiles do not
+// depend on the rows: it takes the host's usual choice, and its kernels
+// read their k ranges from the device offsets.)
 template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_devoff(GemmArgs& g, hipStream_t stream) {
   using namespace mfma256;
-  if (g.ragged == RAGGED_NONE || g.dev_rows < 0) return hipErrorInvalidValue;
+  if (g.ragged != RAGGED_M || g.dev_rows < 0) return hipErrorInvalidValue;
   const int n_given = g.N;  // (the thin kernel takes the columns as given)
   int n_cols = g.N;
   if (BMODE == BMODE_PAIR32) {
     n_cols = ((int)((g.b.split + 31) / 32)) * 64;
     g.N = n_cols;
   }
-  int64_t blocks;
-  if (g.ragged == RAGGED_M) {
-    g.tiles_n = (n_cols + BN - 1) / BN;
-    blocks = ((int64_t)g.dev_rows + (int64_t)g.E * (BM - 1)) / BM * g.tiles_n;
-  } else {
-    fill_tiles(g, BM, BN, n_cols);
-    blocks = g.tile_off[g.E];
-  }
-  if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  // remainders of at most THIN_MAX rows may go to the thin kernel (the
-  // kernels decide from the offsets as the host would from host ones):
-  // at most THIN_MAX / THIN_M tile rows per problem
-  const bool thin = g.ragged == RAGGED_M && short_rows_ok<AK, BK_, BMODE>(g);
+  g.tiles_n = (n_cols + BN - 1) / BN;
+  const int64_t blocks = ((int64_t)g.dev_rows + (int64_t)g.E * (BM - 1)) / BM * g.tiles_n;
+  // the other tilings the host could pick (the kernels choose from the
+  // offsets as the host would from host ones): remainders of at most
+  // THIN_MAX rows on the thin kernel, at most THIN_MAX / THIN_M tile rows
+  // per problem; 128-row tiles on the hand-ordered kernel when their
+  // worst-case grid fits one wave over the compute units (every workgroup
+  // of a launch not chosen still holds a compute unit for ~2 us to find
+  // that out: on the grouped-expert workload a grid of 429 such workgroups
+  // added 7.5 us to FC1, where 128-row tiles do not pay)
+  const int64_t b128 = ((int64_t)g.dev_rows + (int64_t)g.E * 127) / 128 * g.tiles_n;
+  const bool l128 = lean_ok<AK, BK_, BMODE>(g) && b128 <= (int64_t)device_cus();
+  const bool thin = short_rows_ok<AK, BK_, BMODE>(g);
+  if (blocks > INT32_MAX || (l128 && b128 > INT32_MAX)) return hipErrorInvalidValue;
   g.dev_thin = thin ? THIN_MAX : 0;
+  g.dev_l128 = l128 ? (int)(TP_LEAN128_FACTOR * 1000 + 0.5) : 0;
   g.dev_cus = device_cus();
   hipError_t he = launch_256<NW, AK, BK_, BMODE, EPI, OutT>(g, (int)blocks, stream);
-  if (he != hipSuccess || !thin || blocks == 0) return he;
+  if (he != hipSuccess || blocks == 0) return he;
+  if (l128) {
+    hipLaunchKernelGGL((gemm_lean<128, AK, BK_, BMODE, EPI, OutT>), dim3((int)b128), dim3(LEAN_NT),
+                       0, stream, g);
+    if ((he = hipGetLastError()) != hipSuccess || !thin) return he;
+  }
+  if (!thin) return hipSuccess;
   if constexpr (AK && !(BMODE == BMODE_PAIR32 && BK_)) {
     g.N = n_given;
     const int tblocks = g.E * (THIN_MAX / THIN_M) * g.tiles_n;
@@ -2446,7 +2438,8 @@ static hipError_t launch_devoff(GemmArgs& g, hipStream_t stream) {
 
 template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_mfma(GemmArgs& g, hipStream_t stream) {
-  if (g.dev_off) return launch_devoff<NW, AK, BK_, BMODE, EPI, OutT>(g, stream);
+  if (g.dev_off && g.ragged == RAGGED_M)
+    return launch_devoff<NW, AK, BK_, BMODE, EPI, OutT>(g, stream);
   const int thin_max = thin_rows_max<AK, BK_, BMODE>(g);
   if (lean128_pays<AK, BK_, BMODE>(g, thin_max))
     return launch_lean128<AK, BK_, BMODE, EPI, OutT>(g, stream);

@@ -148,6 +148,29 @@ def test_capacity_far_above_the_routed_rows():
     _check_oracle(d, d["offsets"], o, H, F)
 
 
+def test_half_height_tiles_decided_on_the_device():
+    """Few rows per expert: the 128-row tiles take fewer tile-area waves,
+    which the kernels decide from the device offsets as the host does from
+    host ones, so the same kernels run the same sums: every output equals
+    the host-offset call's bit for bit, and the oracle's to the bar."""
+    counts, H, F = [100, 60, 0, 200, 30], 512, 256
+    d = _inputs(counts, H, F, seed=87)
+    dev, o = _run(d, H, F, _device_offsets(counts))
+    off = d["offsets"]
+    desc = dict(H=H, F=F, E=len(counts), dtype=wl.DT_BF16)
+    ref = ExpertBuffers(desc, off)
+    print("[gpu] host-offset grouped fwd+bwd", flush=True)
+    tp.tp_grouped_expert_fwd(desc, off, dev["X_perm"], dev["Wg"], dev["Wu"], dev["Wd"],
+                             ref.Z, ref.H, ref.Y)
+    tp.tp_grouped_expert_bwd(desc, off, dev["X_perm"], dev["Wg"], dev["Wu"], dev["Wd"],
+                             ref.Z, ref.H, dev["dY_perm"], ref.dX, ref.dWg, ref.dWu, ref.dWd,
+                             ref.ws, ref.ws_bytes)
+    torch.cuda.synchronize()
+    for k in ("Z", "H", "Y", "dX", "dWg", "dWu", "dWd"):
+        assert torch.equal(getattr(o, k), getattr(ref, k)), k
+    _check_oracle(d, off, o, H, F)
+
+
 def test_thin_remainder_tiles_decided_on_the_device():
     """Rows ending 33, 64, 3 and 1 rows past a multiple of 256 at H = F =
     4096: the 256-row tiles fill whole waves only if those remainders go to
