@@ -105,6 +105,9 @@ def parse():
                    help="time only the grouped experts, the FP8 shard, or the two "
                         "placements of the activation derivative in the backward (for the "
                         "profiler's per-kernel summaries); prints their JSON")
+    p.add_argument("--grouped-offsets", default="both", choices=["both", "host", "device"],
+                   help="with the grouped experts: time the calls with host offsets, with "
+                        "device offsets, or both")
     p.add_argument("--clock", type=int, default=1,
                    help="1: sample the shader clock while the steps run again")
     p.add_argument("--cpu-tokens", type=int, default=0,
@@ -666,16 +669,21 @@ def grouped_expert_timing(torch, tp, wl, hev, n_sets, steps=20, warmup=3, capaci
                          for r in roles}}
 
 
-def grouped_timing_all(torch, tp, wl, hev, n_sets):
+def grouped_timing_all(torch, tp, wl, hev, n_sets, offsets="both"):
     """The grouped experts with host offsets, then with device offsets on
     buffers of exactly the routed rows and on buffers of every row that
     could be routed here (tokens x top-k: the size a caller that never
-    reads the counts back must provide)."""
-    res = grouped_expert_timing(torch, tp, wl, hev, n_sets)
+    reads the counts back must provide).  offsets: "both", "host" or
+    "device" (one kind per profiled run keeps its per-kernel figures
+    apart)."""
     w5 = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
+    res = grouped_expert_timing(torch, tp, wl, hev, n_sets) if offsets != "device" else {}
+    if offsets == "host":
+        return res
+    rows = int(wl.gen_grouped_inputs(w5)["offsets"][-1])
     keep = ("buffer_rows", "fwd_ms", "bwd_ms", "step_ms_median", "tflops", "frac_of_bf16_peak")
     dev = {}
-    for name, cap in (("exact", res["rows"]), ("tokens_x_topk", w5.tokens * w5.topk)):
+    for name, cap in (("exact", rows), ("tokens_x_topk", w5.tokens * w5.topk)):
         r = grouped_expert_timing(torch, tp, wl, hev, n_sets, capacity=cap)
         dev[name] = {k: r[k] for k in keep}
         dev[name]["launch_us"] = {k: v["us"] for k, v in r["launches"].items()}
@@ -955,7 +963,8 @@ def main():
     del calib_src, calib_dst
 
     if args.only == "grouped":
-        print(json.dumps({"grouped_experts": grouped_timing_all(torch, tp, wl, hev, args.sets)}),
+        print(json.dumps({"grouped_experts": grouped_timing_all(torch, tp, wl, hev, args.sets,
+                                                                args.grouped_offsets)}),
               flush=True)
         return
     if args.only == "fp8":
@@ -1050,7 +1059,7 @@ def main():
     if args.side and args.moe:
         progress("grouped experts and MoE row moves")
         moe = moe_dispatch_timing(torch, tp, wl, dev, torch.cuda.current_stream(), hev)
-        grouped = grouped_timing_all(torch, tp, wl, hev, args.sets)
+        grouped = grouped_timing_all(torch, tp, wl, hev, args.sets, args.grouped_offsets)
 
     flops = gemm_flops(w)
     value = tflops(flops, head["ms_per_step_median"])
