@@ -228,6 +228,39 @@ def test_out_of_range_offsets_are_taken_clamped(vals):
     _check_oracle(d, _clamped(vals, R), o, H, F)
 
 
+def test_sixty_four_experts():
+    """E = 64 (the most a call takes: every lane of the offset scan holds an
+    expert, the last reading the table's 65th entry), a third of them
+    empty: whole tensors against the oracle."""
+    rng = np.random.default_rng(88)
+    counts = [int(c) if rng.random() > 0.33 else 0 for c in rng.integers(1, 90, 64)]
+    H, F = 64, 64
+    d = _inputs(counts, H, F, seed=88)
+    _, o = _run(d, H, F, _device_offsets(counts))
+    _check_oracle(d, d["offsets"], o, H, F)
+
+
+def test_no_rows():
+    """R = 0: the forward writes nothing, the backward's weight gradients
+    are sums over no rows (zeros; unchanged when accumulating).  The empty
+    row buffers get distinct dummy addresses."""
+    H, F, E = 64, 32, 3
+    desc = dict(H=H, F=F, E=E, dtype=wl.DT_BF16)
+    W = [torch.randn(s, device="cuda").to(torch.bfloat16) for s in ((E, H, F), (E, H, F), (E, F, H))]
+    off_dev = torch.tensor([0, 7, 9, 400], dtype=torch.int32, device="cuda")   # clamped to 0
+    e = torch.empty(16 * 16, dtype=torch.uint8, device="cuda")
+    ptr = [e.data_ptr() + 16 * k for k in range(8)]
+    print("[gpu] devoff R=0", flush=True)
+    tp.tp_grouped_expert_fwd_devoff(desc, 0, off_dev, ptr[0], *W, ptr[1], ptr[2], ptr[3])
+    for accumulate in (False, True):
+        dW = [torch.full(s, 3.0, device="cuda") for s in ((E, H, F), (E, H, F), (E, F, H))]
+        tp.tp_grouped_expert_bwd_devoff(desc, 0, off_dev, ptr[0], *W, ptr[1], ptr[2], ptr[4],
+                                        ptr[5], *dW, None, 0, accumulate=accumulate)
+        torch.cuda.synchronize()
+        for t in dW:
+            assert bool((t == (3.0 if accumulate else 0.0)).all())
+
+
 def test_weight_gradients_accumulate():
     counts, H, F = [90, 0, 400, 13], 192, 128
     d = _inputs(counts, H, F)
