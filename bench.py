@@ -826,6 +826,22 @@ def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, hev, reps=10):
                 per[u].append(hev.ms(ev[2 * i], ev[2 * i + 1]))
     hev.free()
     per = {u: median(v) for u, v in per.items()}
+    # the next step's scales from the amax history (window 16): one call for
+    # the E4M3 tensors (X, A, A_up, B, H), one for the E5M2 ones (dY, dZ),
+    # on buffers of their own (the scales timed above stay as they are)
+    hist = torch.zeros((7, 16), dtype=torch.float32, device=dev)
+    am = amax[:7].clone()
+    sc = torch.ones(7, dtype=torch.float32, device=dev)
+    inv = torch.ones(7, dtype=torch.float32, device=dev)
+    su_ev = hev.create(2 * reps)
+    for k in range(reps):
+        hev.record(su_ev[2 * k], stream)
+        tp.tp_fp8_scale_update(E4, 5, 16, hist[:5], am[:5], sc[:5], inv[:5], stream=stream)
+        tp.tp_fp8_scale_update(E5, 2, 16, hist[5:], am[5:], sc[5:], inv[5:], stream=stream)
+        hev.record(su_ev[2 * k + 1], stream)
+    torch.cuda.synchronize()
+    su_us = median([hev.ms(su_ev[2 * k], su_ev[2 * k + 1]) for k in range(reps)]) * 1e3
+    hev.free()
     f_fl = 2.0 * N * Hd * Ft * (3 if sw else 2)
     b_fl = 2 * f_fl
     tf = lambda fl, t: round(tflops(fl, t), 1)
@@ -844,7 +860,8 @@ def fp8_timing(torch, tp, wl, w, X, A, Au, B, dY, stream, hev, reps=10):
              "quantize_transpose_ms": round(ms[2], 4),
              "backward_tflops_with_quantize": tf(b_fl, ms[2] + ms[3]),
              "step_tflops_with_quantize": tf(f_fl + b_fl, sum(ms)),
-             "launches": launches}
+             "launches": launches,
+             "scale_update": {"tensors": 7, "window": 16, "calls": 2, "us": round(su_us, 1)}}
     return fwd_d, bwd_d
 
 

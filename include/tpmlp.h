@@ -471,6 +471,29 @@ int tp_mlp_shard_fwd_fp8(const tp_mlp_desc *desc, const void *Xq, const void *Aq
  *   dX  = (dZq [Aq|Auq]^T codes) * fp32(dz_inv a_inv)
  */
 int tp_fp8_transpose(int64_t rows, int64_t cols, const void *q, void *q_t, void *stream);
+
+/*
+ * tp_fp8_scale_update -- delayed per-tensor scaling ([P1] §8.2: each
+ * tensor's scale comes from the history of its amax; [P3] §10: scale from
+ * amax, then quantize).  For each of n tensors of one format, in device
+ * memory (fp32, 4-byte aligned, none overlapping another):
+ *   history [n,len]   row t: tensor t's last len amax values, newest first
+ *   amax [n]          this step's amax (as tp_fp8_quantize and the FP8
+ *                     shard calls leave it); in/out
+ *   scale [n]         the scale of the next quantization; in/out
+ *   scale_inv [n]     1 / scale (NULL: not written)
+ * The call shifts each row one place (its oldest value drops out), stores
+ * amax[t] in front and sets amax[t] = 0 for the next step's atomic max.
+ * With m the largest finite positive value of the row (the new amax
+ * included), scale[t] = (fmax / m) * 2^-margin, fmax = 448 (E4M3) or 57344
+ * (E5M2): a tensor whose |x| <= m then quantizes without saturating.  With
+ * no such value (zeros, NaN, inf only) scale[t] is kept.  Each step is one
+ * correctly rounded fp32 operation.  scale_inv[t] = 1 / scale[t].
+ *   fmt TP_FP8_E4M3 or TP_FP8_E5M2; 0 <= n <= 2^24; 1 <= len <= 1024;
+ *   0 <= margin <= 16.  Nothing is allocated; no memset (capturable).
+ */
+int tp_fp8_scale_update(int32_t fmt, int32_t n, int32_t len, float *history, float *amax,
+                        float *scale, float *scale_inv, int32_t margin, void *stream);
 int tp_mlp_shard_bwd_fp8(const tp_mlp_desc *desc, const void *dYq, const void *dYq_t,
                          const void *Xq_t, const void *Hq_t, const void *Aq, const void *Auq,
                          const void *Bq, const void *Z_save, const float *scales,

@@ -26,6 +26,8 @@ What each function computes, and the passage it follows ([P1] is the page
   ``mlp_bwd_fp8`` -- per-tensor E4M3 / E5M2 quantization and the shard's
   forward and backward on codes (Megatron-LM 源码精读 §8.2; Megatron Core
   带读 §10).
+* ``fp8_scale_update`` -- the next per-tensor scales from each tensor's
+  amax history (same passages).
 """
 from __future__ import annotations
 
@@ -299,6 +301,40 @@ def fp8_quantize(x, scale, fmt="e4m3"):
     float32 (as the device does), and amax = max |x|."""
     xs = (to_f64(x).astype(np.float32) * np.float32(scale)).astype(np.float32)
     return fp8_encode(xs, fmt), float(np.max(np.abs(to_f64(x)))) if np.size(x) else 0.0
+
+
+def fp8_scale_update(history, amax, scale, fmt="e4m3", margin=0) -> dict:
+    """Delayed per-tensor scaling ([P1] §8.2: each tensor's scale is derived
+    from the history of its amax; [P3] §10: the scale comes from amax, then
+    the tensor is quantized with it).  One step for n tensors, float32:
+
+    * the window: each row of history [n, len] (newest first) moves one
+      place back, its oldest value dropping out, and this step's amax takes
+      the front; amax is then cleared for the next step;
+    * its maximum m: the largest finite positive value in the row;
+    * the scale: the format's largest finite value over m, times
+      2^-margin, so a tensor no larger than m in magnitude quantizes without
+      saturating; with no such value the previous scale is kept;
+    * its inverse 1 / scale (what dequantization multiplies by).
+
+    Each division and product is one float32 operation (the device's)."""
+    h = np.array(history, dtype=np.float32, copy=True)
+    a = np.array(amax, dtype=np.float32, copy=True)
+    sc = np.array(scale, dtype=np.float32, copy=True)
+    n, length = h.shape
+    window = np.empty_like(h)
+    window[:, 1:] = h[:, :length - 1]
+    window[:, 0] = a
+    fmax = np.float32(FP8_FORMATS[fmt][2])
+    mult = np.float32(2.0 ** -margin)
+    for t in range(n):
+        ok = [v for v in window[t] if np.isfinite(v) and v > 0]
+        if ok:
+            m = np.float32(max(ok))
+            sc[t] = np.float32(np.float32(fmax / m) * mult)
+    with np.errstate(divide="ignore"):
+        inv = (np.float32(1.0) / sc).astype(np.float32)
+    return {"history": window, "amax": np.zeros_like(a), "scale": sc, "scale_inv": inv}
 
 
 def mlp_fwd_fp8(Xq, Aq_t, Bq_t, act, scales, Auq_t=None) -> dict:

@@ -23,7 +23,7 @@ __all__ = [
     "tp_grouped_expert_fwd_devoff", "tp_grouped_expert_bwd_devoff",
     "tp_grouped_expert_devoff_workspace",
     "tp_moe_permute", "tp_moe_combine", "tp_moe_combine_bwd",
-    "tp_fp8_quantize", "tp_mlp_shard_fwd_fp8", "tp_fp8_transpose", "tp_mlp_shard_bwd_fp8", "TP_FP8_E4M3", "TP_FP8_E5M2", "tp_last_error", "tp_status_string",
+    "tp_fp8_quantize", "tp_mlp_shard_fwd_fp8", "tp_fp8_transpose", "tp_fp8_scale_update", "tp_mlp_shard_bwd_fp8", "TP_FP8_E4M3", "TP_FP8_E5M2", "tp_last_error", "tp_status_string",
     "tp_launch_events", "tp_launch_events_used",
 ]
 
@@ -127,6 +127,9 @@ def lib() -> ctypes.CDLL:
     L.tp_mlp_shard_fwd_fp8.restype = ctypes.c_int
     L.tp_fp8_transpose.argtypes = [ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
     L.tp_fp8_transpose.restype = ctypes.c_int
+    L.tp_fp8_scale_update.argtypes = ([ctypes.c_int32] * 3 + [_vp] * 4 +
+                                      [ctypes.c_int32, _vp])
+    L.tp_fp8_scale_update.restype = ctypes.c_int
     L.tp_mlp_shard_bwd_fp8.argtypes = [D] + [_vp] * 17
     L.tp_mlp_shard_bwd_fp8.restype = ctypes.c_int
     L.tp_launch_events.argtypes = [ctypes.POINTER(_vp), ctypes.c_int32]
@@ -461,6 +464,16 @@ def tp_fp8_transpose(rows: int, cols: int, q, q_t, stream=None) -> int:
     n = max(int(rows), 0) * max(int(cols), 0)
     return _check(lib().tp_fp8_transpose(int(rows), int(cols), _ptr(q, n, "q"),
                                          _ptr(q_t, n, "q_t"), _stream(stream)))
+
+
+def tp_fp8_scale_update(fmt: int, n: int, length: int, history, amax, scale, scale_inv=None,
+                        margin: int = 0, stream=None) -> int:
+    nb = max(int(n), 0) * 4
+    return _check(lib().tp_fp8_scale_update(int(fmt), int(n), int(length),
+                                            _ptr(history, nb * max(int(length), 0), "history"),
+                                            _ptr(amax, nb, "amax"), _ptr(scale, nb, "scale"),
+                                            _ptr(scale_inv, nb, "scale_inv"), int(margin),
+                                            _stream(stream)))
 
 
 def tp_mlp_shard_bwd_fp8(desc, dYq, dYq_t, Xq_t, Hq_t, Aq, Auq, Bq, Z_save, scales, dX_partial,

@@ -186,6 +186,13 @@ hipError_t t_fp8_quantize_launch(int fmt, bool tr, int64_t rows, int64_t cols, c
 hipError_t t_zero_float_launch(float* p, hipStream_t st) {
   return timed(st, [&] { return zero_float_launch(p, st); });
 }
+hipError_t t_fp8_scale_update_launch(int fmt, int n, int len, int margin, float* history,
+                                     float* amax, float* scale, float* scale_inv,
+                                     hipStream_t st) {
+  return timed(st, [&] {
+    return fp8_scale_update_launch(fmt, n, len, margin, history, amax, scale, scale_inv, st);
+  });
+}
 hipError_t t_byte_transpose_launch(int64_t rows, int64_t cols, const void* in, void* out,
                                    hipStream_t st) {
   return timed(st, [&] { return byte_transpose_launch(rows, cols, in, out, st); });
@@ -975,6 +982,28 @@ int tp_fp8_transpose(int64_t rows, int64_t cols, const void* q, void* q_t, void*
   if (int rc = check_device()) return rc;
   hipError_t he = t_byte_transpose_launch(rows, cols, q, q_t, reinterpret_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, "transpose launch");
+  return ok();
+}
+
+int tp_fp8_scale_update(int32_t fmt, int32_t n, int32_t len, float* history, float* amax,
+                        float* scale, float* scale_inv, int32_t margin, void* stream) {
+  if (fmt != TP_FP8_E4M3 && fmt != TP_FP8_E5M2) return fail(TP_ERR_DTYPE, "unknown fmt %d", fmt);
+  if (n < 0 || n > (1 << 24)) return fail(TP_ERR_SHAPE, "n must be in 0..2^24");
+  if (len < 1 || len > 1024) return fail(TP_ERR_SHAPE, "len must be in 1..1024");
+  if (margin < 0 || margin > 16) return fail(TP_ERR_SHAPE, "margin must be in 0..16");
+  const size_t nb = (size_t)n * 4;
+  Buf bufs[] = {{history, nb * (size_t)len, "history"},
+                {amax, nb, "amax"},
+                {scale, nb, "scale"},
+                {scale_inv, scale_inv ? nb : 0, "scale_inv"}};
+  if (int rc = check_tables(bufs, 3)) return rc;
+  if (scale_inv && (reinterpret_cast<uintptr_t>(scale_inv) & 3u))
+    return fail(TP_ERR_ALIGN, "scale_inv is not 4-byte aligned");
+  if (int rc = check_alias(nullptr, 0, bufs, 4)) return rc;
+  if (int rc = check_device()) return rc;
+  hipError_t he = t_fp8_scale_update_launch(fmt, n, len, margin, history, amax, scale, scale_inv,
+                                            reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "scale update launch");
   return ok();
 }
 

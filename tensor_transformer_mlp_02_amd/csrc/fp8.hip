@@ -177,7 +177,47 @@ __global__ __launch_bounds__(NT) void byte_transpose_kernel(const uint8_t* in, i
   }
 }
 
+// Delayed scaling: one thread per tensor shifts its amax history row one
+// place (the oldest value drops out), puts this step's amax at the front and
+// clears it for the next step's atomic max, then derives the next scale from
+// the largest finite positive value of the window (kept when there is none).
+// Every operation is one correctly rounded fp32 operation.
+__global__ __launch_bounds__(NT) void scale_update_kernel(int n, int len, float fmax, float mult,
+                                                          float* history, float* amax,
+                                                          float* scale, float* scale_inv) {
+  const int t = blockIdx.x * NT + threadIdx.x;
+  if (t >= n) return;
+  float* h = history + (int64_t)t * len;
+  const float a = amax[t];
+  float m = (__builtin_isfinite(a) && a > 0.0f) ? a : 0.0f;
+  for (int j = len - 1; j > 0; --j) {
+    const float v = h[j - 1];
+    h[j] = v;
+    if (__builtin_isfinite(v) && v > m) m = v;
+  }
+  h[0] = a;
+  amax[t] = 0.0f;
+  float s = scale[t];
+  if (m > 0.0f) {
+    s = (fmax / m) * mult;
+    scale[t] = s;
+  }
+  if (scale_inv) scale_inv[t] = 1.0f / s;
+}
+
 }  // namespace f8q
+
+hipError_t fp8_scale_update_launch(int fmt, int n, int len, int margin, float* history,
+                                   float* amax, float* scale, float* scale_inv,
+                                   hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const float fmax = fmt == 0 ? 448.0f : 57344.0f;
+  const float mult = ldexpf(1.0f, -margin);
+  hipLaunchKernelGGL(f8q::scale_update_kernel, dim3((unsigned)((n + f8q::NT - 1) / f8q::NT)),
+                     dim3(f8q::NT), 0, stream, n, len, fmax, mult, history, amax, scale,
+                     scale_inv);
+  return hipGetLastError();
+}
 
 hipError_t fp8_quantize_launch(int fmt, bool transpose, int64_t rows, int64_t cols,
                                const void* x, const float* scale, void* q, float* amax,

@@ -56,6 +56,10 @@ hipError_t fp8_quantize_launch(int fmt, bool transpose, int64_t rows, int64_t co
                                const void* x, const float* scale, void* q, float* amax,
                                hipStream_t stream);
 hipError_t zero_float_launch(float* p, hipStream_t stream);
+// amax history [n, len] shift, next scale (and its inverse) per tensor
+hipError_t fp8_scale_update_launch(int fmt, int n, int len, int margin, float* history,
+                                   float* amax, float* scale, float* scale_inv,
+                                   hipStream_t stream);
 // bytes [rows, cols] -> [cols, rows]; rows, cols multiples of 16
 hipError_t byte_transpose_launch(int64_t rows, int64_t cols, const void* in, void* out,
                                  hipStream_t stream);

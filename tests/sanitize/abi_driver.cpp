@@ -32,6 +32,10 @@ hipError_t fp8_quantize_launch(int, bool, int64_t, int64_t, const void*, const f
   reached("fp8_quantize_launch");
 }
 hipError_t zero_float_launch(float*, hipStream_t) { reached("zero_float_launch"); }
+hipError_t fp8_scale_update_launch(int, int, int, int, float*, float*, float*, float*,
+                                   hipStream_t) {
+  reached("fp8_scale_update_launch");
+}
 hipError_t byte_transpose_launch(int64_t, int64_t, const void*, void*, hipStream_t) {
   reached("byte_transpose_launch");
 }
@@ -285,8 +289,15 @@ int main() {
                               (float*)ptr_any(4), nullptr), "fuzz quantize");
         break;
       case 7:
-        check(tp_fp8_transpose(pick(dims, ND), pick(dims, ND), ptr_any(1), ptr_any(2), nullptr),
-              "fuzz transpose");
+        if (rnd() % 2)
+          check(tp_fp8_transpose(pick(dims, ND), pick(dims, ND), ptr_any(1), ptr_any(2), nullptr),
+                "fuzz transpose");
+        else
+          check(tp_fp8_scale_update((int32_t)(rnd() % 3), (int32_t)pick(dims, ND),
+                                    (int32_t)(rnd() % 1100), (float*)ptr_any(1),
+                                    (float*)ptr_any(2), (float*)ptr_any(3), (float*)ptr_any(4),
+                                    (int32_t)(rnd() % 20) - 2, nullptr),
+                "fuzz scale update");
         break;
       case 8:
         check(tp_mlp_shard_fwd_fp8(pd, ptr_any(1), ptr_any(2), ptr_any(3), ptr_any(4),

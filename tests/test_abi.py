@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     L = tp.lib()
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
@@ -458,3 +458,25 @@ def test_noalloc_backward_rejects_more_than_its_scratch():
     assert st(gelu_desc(S=8192, B=1, H=512, F_shard=4096)) == E_DEV
     assert st(gelu_desc(S=8192, B=1, H=512, F_shard=4104)) == E_WS
     assert st(gelu_desc(H=12)) == E_SHAPE
+
+
+def test_fp8_scale_update_argument_checks():
+    L = tp.lib()
+
+    def su(fmt=tp.TP_FP8_E4M3, n=8, length=16, h=addr(1), a=addr(2), s=addr(3), inv=addr(4),
+           margin=0):
+        return L.tp_fp8_scale_update(fmt, n, length, h, a, s, inv, margin, None)
+    assert su(fmt=2) == E_DTYPE
+    assert su(n=-1) == E_SHAPE
+    assert su(n=(1 << 24) + 1) == E_SHAPE
+    assert su(length=0) == E_SHAPE
+    assert su(length=1025) == E_SHAPE
+    assert su(margin=-1) == E_SHAPE
+    assert su(margin=17) == E_SHAPE
+    assert su(h=None) == E_NULL
+    assert su(a=None) == E_NULL
+    assert su(s=None) == E_NULL
+    assert su(a=addr(2, 2)) == E_ALIGN                 # 4-byte tables
+    assert su(inv=addr(4, 1)) == E_ALIGN
+    assert su(s=addr(1, 16)) == E_ALIAS                # scale inside the history
+    assert su(inv=addr(2, 4)) == E_ALIAS               # scale_inv overlapping amax

@@ -440,3 +440,71 @@ def test_fp8_backward_empty_batch():
             if t is not None:
                 assert not torch.any(t)
         assert float(amax[0]) == 0.0
+
+
+# ----------------------------------------------------------------------------
+# delayed scaling: the next scales from the amax history
+# ----------------------------------------------------------------------------
+def _bits(a):
+    return np.asarray(a, np.float32).view(np.int32)
+
+
+@pytest.mark.parametrize("fmt,margin,with_inv", [(E4M3, 0, True), (E5M2, 3, True),
+                                                 (E4M3, 1, False)])
+def test_scale_update_bitwise(fmt, margin, with_inv):
+    """Five updates of 37 tensors with a window of 16: the history, the
+    cleared amax, the scales and their inverses equal the oracle's bit for
+    bit, with zeros, NaN, infinities and values over 40 decades mixed in."""
+    rng = np.random.default_rng(11 + fmt + margin)
+    n, length = 37, 16
+    name = "e4m3" if fmt == E4M3 else "e5m2"
+    hist = np.zeros((n, length), np.float32)
+    scale = np.float32(10.0) ** rng.uniform(-3, 3, n).astype(np.float32)
+    d_hist, d_scale = torch.tensor(hist, device="cuda"), torch.tensor(scale, device="cuda")
+    d_inv = torch.full((n,), 7.0, device="cuda") if with_inv else None
+    for step in range(5):
+        amax = np.float32(10.0) ** rng.uniform(-20, 20, n).astype(np.float32)
+        special = rng.integers(0, 8, n)
+        amax[special == 0] = 0.0
+        amax[special == 1] = np.nan
+        amax[special == 2] = np.inf
+        d_amax = torch.tensor(amax, device="cuda")
+        print(f"[gpu] fp8 scale update fmt={fmt} margin={margin} step={step}", flush=True)
+        tp.tp_fp8_scale_update(fmt, n, length, d_hist, d_amax, d_scale, d_inv, margin)
+        torch.cuda.synchronize()
+        r = oracle.fp8_scale_update(hist, amax, scale, name, margin)
+        hist, scale = r["history"], r["scale"]
+        assert np.array_equal(_bits(d_hist.cpu().numpy()), _bits(hist))
+        assert np.array_equal(_bits(d_amax.cpu().numpy()), _bits(r["amax"]))
+        assert np.array_equal(_bits(d_scale.cpu().numpy()), _bits(scale))
+        if with_inv:
+            assert np.array_equal(_bits(d_inv.cpu().numpy()), _bits(r["scale_inv"]))
+
+
+def test_scale_update_after_quantize():
+    """quantize (amax from the device's atomic max) -> scale update: the
+    new scale is 448 over the tensor's max |x|, and the tensor quantized
+    with it reaches the largest E4M3 code without passing it."""
+    x = wl.normal_bf16(12, (512, 256), 3.0)
+    d_x = to_device(x)
+    d_amax = torch.zeros(1, device="cuda")
+    d_scale = torch.ones(1, device="cuda")
+    d_hist = torch.zeros((1, 4), device="cuda")
+    q = torch.empty((512, 256), dtype=torch.uint8, device="cuda")
+    print("[gpu] fp8 quantize -> scale update", flush=True)
+    tp.tp_fp8_quantize(E4M3, 0, 512, 256, d_x, d_scale, q, d_amax)
+    tp.tp_fp8_scale_update(E4M3, 1, 4, d_hist, d_amax, d_scale)
+    tp.tp_fp8_quantize(E4M3, 0, 512, 256, d_x, d_scale, q, d_amax)
+    torch.cuda.synchronize()
+    m = np.float32(np.max(np.abs(f64(x))))
+    assert float(d_hist[0, 0]) == m
+    assert float(d_scale[0]) == float(np.float32(np.float32(448.0) / m))
+    codes = q.cpu().numpy()
+    assert int((codes & 0x7f).max()) == 0x7e            # the largest finite E4M3 code (448)
+    assert float(d_amax[0]) == m
+
+
+def test_scale_update_no_tensors():
+    h = torch.zeros(16, device="cuda")
+    tp.tp_fp8_scale_update(E4M3, 0, 4, h, h[4:], h[8:])
+    torch.cuda.synchronize()

@@ -682,3 +682,62 @@ def test_fp8_forward_rounding_scales_dequantize_the_right_products(act):
     # H's codes are the encoding of H * h_scale taken in fp32
     assert np.array_equal(f["Hq"], oracle.fp8_encode(
         (f["H"].astype(np.float32) * np.float32(sh)).astype(np.float32)))
+
+
+# ----------------------------------------------------------------------------
+# FP8 delayed scaling: the next scale from the amax history ([P1] §8.2)
+# ----------------------------------------------------------------------------
+def _step(hist, amax, scale, fmt="e4m3", margin=0):
+    return oracle.fp8_scale_update(np.asarray(hist, np.float32), np.asarray(amax, np.float32),
+                                   np.asarray(scale, np.float32), fmt, margin)
+
+
+def test_fp8_scale_closed_forms():
+    r = _step(np.zeros((3, 4)), [448.0, 2.0, 0.5], [1.0, 1.0, 1.0])
+    assert r["scale"].tolist() == [1.0, 224.0, 896.0]          # fmax / amax, exactly
+    # (1/224 and 1/896 are not binary fractions: their fp32 roundings)
+    assert r["scale_inv"].tolist() == [1.0, float(np.float32(1 / 224.0)),
+                                       float(np.float32(1 / 896.0))]
+    assert r["amax"].tolist() == [0.0, 0.0, 0.0]
+    assert r["history"][:, 0].tolist() == [448.0, 2.0, 0.5]
+    assert _step(np.zeros((1, 2)), [57344.0], [3.0], "e5m2")["scale"].tolist() == [1.0]
+    assert _step(np.zeros((1, 2)), [2.0], [3.0], "e4m3", margin=2)["scale"].tolist() == [56.0]
+
+
+def test_fp8_scale_follows_the_window_maximum():
+    """A window of 3: the scale follows the largest of the last 3 amax
+    values; 8 drops out after three more steps."""
+    hist, amax, scale = np.zeros((1, 3), np.float32), None, np.ones(1, np.float32)
+    seen = []
+    for a in (8.0, 1.0, 2.0, 1.0, 1.0):
+        r = _step(hist, [a], scale)
+        hist, scale = r["history"], r["scale"]
+        seen.append(float(scale[0]))
+    assert seen == [56.0, 56.0, 56.0, 224.0, 224.0]
+    assert hist[0].tolist() == [1.0, 1.0, 2.0]
+
+
+def test_fp8_scale_kept_without_a_finite_positive_amax():
+    hist = np.array([[0, 0], [0, -5], [np.nan, 0], [np.inf, 0]], np.float32)
+    amax = np.array([0, 0, np.nan, np.inf], np.float32)
+    r = _step(hist, amax, [5.0, 6.0, 7.0, 8.0])
+    assert r["scale"].tolist() == [5.0, 6.0, 7.0, 8.0]
+    assert np.isnan(r["history"][2, 0]) and np.isinf(r["history"][3, 0])
+    assert r["history"][2, 1] != r["history"][2, 1]       # the NaN moved back one place
+    # a finite value elsewhere in the window still sets the scale
+    r = _step([[np.inf, 4.0, 0.0]], [np.nan], [1.0])
+    assert r["scale"].tolist() == [112.0]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_scaled_amax_reaches_the_largest_code(fmt):
+    """Quantizing the window's maximum with the new scale gives the format's
+    largest finite value (never beyond): the scale uses the whole range."""
+    rng = np.random.default_rng(7)
+    m = np.float32(10.0) ** rng.uniform(-20, 20, 200).astype(np.float32)
+    fmax = oracle.FP8_FORMATS[fmt][2]
+    r = _step(np.zeros((m.size, 1)), m, np.ones(m.size), fmt)
+    y = (m * r["scale"]).astype(np.float32)
+    assert np.all(np.abs(y.astype(np.float64) / fmax - 1.0) <= 2.0 ** -23)
+    assert np.all(oracle.fp8_decode(oracle.fp8_encode(y, fmt), fmt) == fmax)
+    assert np.all(np.abs(r["scale"].astype(np.float64) * r["scale_inv"] - 1.0) <= 2.0 ** -23)
