@@ -381,8 +381,9 @@ int tp_grouped_expert_bwd_devoff(const tp_expert_desc *desc, int64_t R,
  *              tok_rows[tok_ptr[t] .. tok_ptr[t+1]-1] (CSR), in the order
  *              their contributions are summed
  * Tables need 4-byte alignment, data buffers 16 bytes.  A table entry out
- * of range contributes nothing (a permuted row becomes zeros); no entry can
- * make an access leave its buffer.  dtype is TP_BF16 or TP_F32; H a
+ * of range contributes nothing (a permuted row becomes zeros; in the
+ * combine backward its dY_perm row and d_weight are zeros, and its Y_perm
+ * row is not read); no entry can make an access leave its buffer.  dtype is TP_BF16 or TP_F32; H a
  * multiple of 8 (bf16) or 4 (fp32).  All three are HBM-bound row moves.
  *
  * tp_moe_permute: X_perm[r, :] = X[row_token[r], :]   (X [N,H], X_perm [R,H])

@@ -109,12 +109,17 @@ __global__ __launch_bounds__(NT) void combine_bwd_kernel(const int32_t* row_toke
     const float s = w[r];
     float dot = 0.f;
     for (int64_t c = threadIdx.x; c < chunks; c += NT) {
-      float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, y[8], o[8];
-      if (ok) Row8<T>::load(dY + (int64_t)t * H + 8 * c, g);
-      Row8<T>::load(Yp + r * H + 8 * c, y);
+      // a row whose token is out of range reads nothing and gets zeros (its
+      // Y_perm row may never have been written)
+      float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, o[8];
+      if (ok) {
+        Row8<T>::load(dY + (int64_t)t * H + 8 * c, g);
+        Row8<T>::load(Yp + r * H + 8 * c, y);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        o[e] = s * g[e];
+        o[e] = ok ? s * g[e] : 0.f;
         dot += g[e] * y[e];
       }
       Row8<T>::store(dYp + r * H + 8 * c, o);

@@ -57,6 +57,34 @@ def test_permute_rows_with_out_of_range_tokens_are_zero():
     assert np.array_equal(got[keep], d["X"][ids[keep]])
 
 
+def test_combine_backward_rows_with_out_of_range_tokens_are_zero():
+    """Rows whose token is outside [0, N) read neither dY nor their Y_perm
+    row (which here holds NaN, as an unwritten buffer may) and get zero
+    dY_perm rows and d_weight, whatever their weight; the other rows match
+    the oracle."""
+    w, d, dev = _inputs(64, 16, 24)
+    N, H = d["X"].shape
+    ids = d["token_ids"].astype(np.int32).copy()
+    R = len(ids)
+    bad = [0, R // 2]
+    ids[bad[0]], ids[bad[1]] = -1, N
+    rw = d["row_weight"].astype(np.float32).copy()
+    rw[bad] = np.nan
+    yp = wl.normal_bf16(5, (R, H), 1.0)
+    yp[bad] = 0x7fc0                                     # bf16 NaN
+    dYp = torch.empty((R, H), dtype=torch.bfloat16, device="cuda")
+    dw = torch.empty(R, dtype=torch.float32, device="cuda")
+    print(f"[gpu] moe combine backward guarded rows R={R}", flush=True)
+    tp.tp_moe_combine_bwd(BF, N, H, R, _tab(ids), _tab(rw), dev["dY"], to_device(yp), dYp, dw)
+    torch.cuda.synchronize()
+    g, gw = to_host(dYp), to_host(dw)
+    assert not np.any(g[bad]) and not np.any(gw[bad])
+    keep = np.ones(R, bool); keep[bad] = False
+    ref, ref_w = oracle.moe_combine_bwd(d["dY"], yp[keep], ids[keep], rw[keep])
+    assert_close("dY_perm", f64(g[keep]), ref, TOL[BF])
+    assert_close("d_weight", gw[keep], ref_w, TOL[BF])
+
+
 @pytest.mark.parametrize("size", ["small", "c5"])
 def test_combine_and_its_backward(size):
     w, d, dev = _inputs(*((300, 264, 136) if size == "small" else (None, None, None)))
@@ -125,3 +153,91 @@ def test_moe_layer_forward_and_backward():
         got = to_host(getattr(buf, k))
         for e in range(E):
             assert_close(f"{k}[{e}]", got[e], gb[k][e], tol)
+
+
+def test_moe_layer_with_tables_built_on_the_device():
+    """The same layer with no routing result on the host: the router's
+    decisions (token, expert, weight; top-2 per token, the non-local ones
+    marked with expert E) arrive on the GPU in token order; the dispatch
+    tables and the expert offsets are built there (torch sorts and scans);
+    every buffer holds tokens x top-k rows (what could be routed here), and
+    the experts read their offsets from device memory.  The tables equal the
+    host-built ones, the results the oracle chain's."""
+    w, d, dev = _inputs(512, 264, 136)
+    N, H = d["X"].shape
+    F = d["Wg"].shape[2]
+    ids, off = d["token_ids"], d["offsets"]
+    E, R, k = len(off) - 1, len(ids), w.topk
+    cap = N * k
+    exp_of_row = np.repeat(np.arange(E), np.diff(off))
+    # the decisions in token order: each token's local rows, then its
+    # remaining choices as non-local ones (expert E, weight 0)
+    t_dec, e_dec, w_dec = [], [], []
+    per_tok = {t: [] for t in range(N)}
+    for r in range(R):
+        per_tok[int(ids[r])].append((int(exp_of_row[r]), float(d["row_weight"][r])))
+    for t in range(N):
+        assert len(per_tok[t]) <= k
+        for e_, wt in per_tok[t] + [(E, 0.0)] * (k - len(per_tok[t])):
+            t_dec.append(t); e_dec.append(e_); w_dec.append(wt)
+    t_dev = _tab(np.array(t_dec, np.int64))
+    e_dev = _tab(np.array(e_dec, np.int64))
+    w_dev = _tab(np.array(w_dec, np.float32))
+
+    # --- on the device: dispatch tables and offsets -------------------------
+    srt = torch.argsort(e_dev * N + t_dev)                        # (expert, token) order
+    local = e_dev[srt] < E
+    row_token = torch.where(local, t_dev[srt], torch.full_like(t_dev, -1)).to(torch.int32)
+    row_weight = torch.where(local, w_dev[srt], torch.zeros_like(w_dev)).contiguous()
+    counts = torch.zeros(E + 1, dtype=torch.int64, device="cuda").scatter_add_(
+        0, e_dev, torch.ones_like(e_dev))
+    offsets = torch.cat([torch.zeros(1, dtype=torch.int64, device="cuda"),
+                         torch.cumsum(counts[:E], 0)]).to(torch.int32)
+    tok_key = torch.where(row_token >= 0, row_token.long(), torch.full_like(t_dev, N))
+    tok_rows = torch.argsort(tok_key * cap + torch.arange(cap, device="cuda")).to(torch.int32)
+    per_token = torch.zeros(N + 1, dtype=torch.int64, device="cuda").scatter_add_(
+        0, tok_key, torch.ones_like(tok_key))
+    tok_ptr = torch.cat([torch.zeros(1, dtype=torch.int64, device="cuda"),
+                         torch.cumsum(per_token[:N], 0)]).to(torch.int32)
+
+    desc = dict(H=H, F=F, E=E, dtype=BF)
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda")
+    Xp, Yp, Z, Hh, Y = bf(cap, H), bf(cap, H), bf(cap, 2 * F), bf(cap, F), bf(N, H)
+    dYp, dXp, dX = bf(cap, H), bf(cap, H), bf(N, H)
+    dW = [torch.empty(s, dtype=torch.float32, device="cuda") for s in ((E, H, F), (E, H, F),
+                                                                        (E, F, H))]
+    dw = torch.empty(cap, dtype=torch.float32, device="cuda")
+    ws_bytes = tp.tp_grouped_expert_devoff_workspace(desc, cap)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    print(f"[gpu] moe layer, device tables: N={N} H={H} F={F} capacity={cap}", flush=True)
+    tp.tp_moe_permute(BF, N, H, cap, row_token, dev["X"], Xp)
+    tp.tp_grouped_expert_fwd_devoff(desc, cap, offsets, Xp, dev["Wg"], dev["Wu"], dev["Wd"],
+                                    Z, Hh, Yp)
+    tp.tp_moe_combine(BF, N, H, cap, tok_ptr, tok_rows, row_weight, Yp, Y)
+    tp.tp_moe_combine_bwd(BF, N, H, cap, row_token, row_weight, dev["dY"], Yp, dYp, dw)
+    tp.tp_grouped_expert_bwd_devoff(desc, cap, offsets, Xp, dev["Wg"], dev["Wu"], dev["Wd"], Z,
+                                    Hh, dYp, dXp, *dW, ws, ws_bytes)
+    tp.tp_moe_combine(BF, N, H, cap, tok_ptr, tok_rows, None, dXp, dX)
+    torch.cuda.synchronize()
+
+    # the tables the device built are the host-built ones
+    assert np.array_equal(offsets.cpu().numpy(), off)
+    assert np.array_equal(row_token[:R].cpu().numpy(), ids)
+    assert bool((row_token[R:] == -1).all())
+    assert np.array_equal(row_weight[:R].cpu().numpy(), d["row_weight"].astype(np.float32))
+    assert np.array_equal(tok_ptr.cpu().numpy(), d["tok_ptr"].astype(np.int32))
+    assert np.array_equal(tok_rows[:R].cpu().numpy(), d["tok_rows"].astype(np.int32))
+    tol = TOL[BF]
+    Xp_ref = oracle.moe_permute(d["X"], ids)
+    g = oracle.grouped_fwd(Xp_ref, off, d["Wg"], d["Wu"], d["Wd"])
+    assert_close("Y", f64(to_host(Y)), oracle.moe_combine(g["Y"], ids, N, d["row_weight"]), tol)
+    dYp_ref, dw_ref = oracle.moe_combine_bwd(d["dY"], g["Y"], ids, d["row_weight"])
+    assert_close("d_weight", to_host(dw[:R]), dw_ref, tol)
+    # unrouted rows: zeros, although their Y_perm rows were never written
+    assert bool((dw[R:] == 0).all()) and bool((dYp[R:] == 0).all())
+    gb = oracle.grouped_bwd(Xp_ref, off, d["Wg"], d["Wu"], d["Wd"], dYp_ref, g)
+    assert_close("dX", f64(to_host(dX)), oracle.moe_combine(gb["dX"], ids, N), tol)
+    for name, got in zip(("dWg", "dWu", "dWd"), dW):
+        got = to_host(got)
+        for e in range(E):
+            assert_close(f"{name}[{e}]", got[e], gb[name][e], tol)
