@@ -349,10 +349,15 @@ int tp_grouped_expert_bwd_accum(const tp_expert_desc *desc, const int64_t *offse
  *   accumulate 0: weight gradients written (tp_grouped_expert_bwd);
  *            1: added to (tp_grouped_expert_bwd_accum)
  * The host cannot see the rows, so the row-tiled products launch for the
- * worst split of R rows (about E - 1 more tile rows than the most tiles the
- * offsets can need); workgroups without a tile exit at once.  Results are
- * those of the host-offset calls up to summation order (the host calls may
- * pick other tile shapes), bit-identical run to run.
+ * worst split of R rows (E - 1 more tile rows than R rows need at most);
+ * workgroups without a tile exit at once, so size R tightly: every spare
+ * workgroup holds a compute unit briefly.  The kernels make the host
+ * calls' choice among 256-row tiles, 256-row tiles with 32-row remainder
+ * tiles and 128-row tiles from the offsets themselves (not the 224-wide
+ * tiles, nor 128-row tiles whose worst-case grid exceeds one wave over the
+ * compute units): results equal the host-offset calls' bit for bit where
+ * both take the same tiling, and otherwise up to summation order; they are
+ * bit-identical run to run.
  * Errors: as the host-offset calls (the offsets' values are not checked).
  */
 int tp_grouped_expert_fwd_devoff(const tp_expert_desc *desc, int64_t R,
