@@ -101,3 +101,26 @@ def test_random_shard_shapes_derivative_in_loads(shape):
     assert_close("dB", to_host(pro.dB), b["dB"], tol)
     if act == wl.ACT_SWIGLU:
         assert_close("dA_up", to_host(pro.dA_up), b["dA_up"], tol)
+
+
+@st.composite
+def grouped_shapes_with_capacity(draw):
+    counts, H, F = draw(grouped_shapes())
+    return counts, H, F, draw(st.one_of(st.just(0), st.integers(1, 600)))
+
+
+@settings(max_examples=10, **SETTINGS)
+@given(grouped_shapes_with_capacity())
+def test_random_grouped_shapes_device_offsets(shape):
+    """The device-offset grouped calls on the same kind of ragged splits,
+    with buffers up to 600 rows larger than the routed rows: whole tensors
+    against the oracle, the unrouted rows untouched."""
+    from test_gpu_devoff import _check_oracle, _device_offsets, _inputs, _run
+    counts, H, F, slack = shape
+    if sum(counts) == 0:
+        counts = counts[:-1] + [1]
+    R = sum(counts) + slack
+    d = _inputs(counts, H, F, R=R, seed=700 + (sum(counts) + H + F + slack) % 300)
+    print(f"[gpu] sweep grouped device offsets counts={counts} H={H} F={F} R={R}", flush=True)
+    _, o = _run(d, H, F, _device_offsets(counts))
+    _check_oracle(d, d["offsets"], o, H, F)
