@@ -144,15 +144,20 @@ def lib() -> ctypes.CDLL:
     return L
 
 
-def _ptr(t, nbytes: Optional[int] = None, name: str = "tensor") -> Optional[int]:
+def _ptr(t, nbytes: Optional[int] = None, name: str = "tensor",
+         dtype: Optional[str] = None) -> Optional[int]:
     """Device address of a tensor, an int (a raw device address, passed as
     given), or None.  A tensor must be contiguous, live on the current GPU
     (a host tensor's address would reach a kernel as a device address) and,
-    when nbytes is given, hold at least that many bytes."""
+    when nbytes is given, hold at least that many bytes; tables and scale
+    buffers (dtype "int32" / "float32") must hold that element type, since
+    the library reads their bytes as such."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if dtype is not None and str(getattr(t, "dtype", "")) != f"torch.{dtype}":
+        raise ValueError(f"{name} must be a torch.{dtype} tensor, got {getattr(t, 'dtype', None)}")
     if not getattr(t, "is_cuda", False):
         raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
     import torch
@@ -167,9 +172,9 @@ def _ptr(t, nbytes: Optional[int] = None, name: str = "tensor") -> Optional[int]
     return t.data_ptr()
 
 
-def _sized(pairs):
-    """_ptr of each (tensor, bytes, name) triple."""
-    return [_ptr(t, n, name) for (t, n, name) in pairs]
+def _sized(items):
+    """_ptr of each (tensor, bytes, name) or (tensor, bytes, name, dtype)."""
+    return [_ptr(*it) for it in items]
 
 
 def _stream(stream) -> Optional[int]:
@@ -377,7 +382,7 @@ def tp_grouped_expert_fwd_devoff(desc, R: int, offsets, X_perm, Wg, Wu, Wd, Z_sa
     hold."""
     d = _edesc(desc)
     n = _expert_sizes(d, max(int(R), 0))
-    p = _sized([(offsets, 4 * (max(d.E, 0) + 1), "offsets"), (X_perm, n["X"], "X_perm"),
+    p = _sized([(offsets, 4 * (max(d.E, 0) + 1), "offsets", "int32"), (X_perm, n["X"], "X_perm"),
                 (Wg, n["W"], "Wg"), (Wu, n["W"], "Wu"), (Wd, n["W"], "Wd"),
                 (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"), (Y_perm, n["Y"], "Y_perm")])
     return _check(lib().tp_grouped_expert_fwd_devoff(ctypes.byref(d), int(R), *p,
@@ -396,7 +401,7 @@ def tp_grouped_expert_bwd_devoff(desc, R: int, offsets, X_perm, Wg, Wu, Wd, Z_sa
     int32 offsets, as tp_grouped_expert_fwd_devoff."""
     d = _edesc(desc)
     n = _expert_sizes(d, max(int(R), 0))
-    p = _sized([(offsets, 4 * (max(d.E, 0) + 1), "offsets"), (X_perm, n["X"], "X_perm"),
+    p = _sized([(offsets, 4 * (max(d.E, 0) + 1), "offsets", "int32"), (X_perm, n["X"], "X_perm"),
                 (Wg, n["W"], "Wg"), (Wu, n["W"], "Wu"), (Wd, n["W"], "Wd"),
                 (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"),
                 (dY_perm, n["Y"], "dY_perm"), (dX_perm, n["X"], "dX_perm"),
@@ -416,7 +421,7 @@ def tp_grouped_expert_bwd_accum(*args, **kw) -> int:
 
 def tp_moe_permute(dtype: int, N: int, H: int, R: int, row_token, X, X_perm, stream=None) -> int:
     e, n, h, r = _elt(dtype), max(int(N), 0), max(int(H), 0), max(int(R), 0)
-    p = _sized([(row_token, r * 4, "row_token"), (X, n * h * e, "X"),
+    p = _sized([(row_token, r * 4, "row_token", "int32"), (X, n * h * e, "X"),
                 (X_perm, r * h * e, "X_perm")])
     return _check(lib().tp_moe_permute(int(dtype), int(N), int(H), int(R), *p, _stream(stream)))
 
@@ -424,8 +429,8 @@ def tp_moe_permute(dtype: int, N: int, H: int, R: int, row_token, X, X_perm, str
 def tp_moe_combine(dtype: int, N: int, H: int, R: int, tok_ptr, tok_rows, row_weight, Y_perm, Y,
                    stream=None) -> int:
     e, n, h, r = _elt(dtype), max(int(N), 0), max(int(H), 0), max(int(R), 0)
-    p = _sized([(tok_ptr, (n + 1) * 4, "tok_ptr"), (tok_rows, r * 4, "tok_rows"),
-                (row_weight, r * 4, "row_weight"), (Y_perm, r * h * e, "Y_perm"),
+    p = _sized([(tok_ptr, (n + 1) * 4, "tok_ptr", "int32"), (tok_rows, r * 4, "tok_rows", "int32"),
+                (row_weight, r * 4, "row_weight", "float32"), (Y_perm, r * h * e, "Y_perm"),
                 (Y, n * h * e, "Y")])
     return _check(lib().tp_moe_combine(int(dtype), int(N), int(H), int(R), *p, _stream(stream)))
 
@@ -433,9 +438,9 @@ def tp_moe_combine(dtype: int, N: int, H: int, R: int, tok_ptr, tok_rows, row_we
 def tp_moe_combine_bwd(dtype: int, N: int, H: int, R: int, row_token, row_weight, dY, Y_perm,
                        dY_perm, d_weight, stream=None) -> int:
     e, n, h, r = _elt(dtype), max(int(N), 0), max(int(H), 0), max(int(R), 0)
-    p = _sized([(row_token, r * 4, "row_token"), (row_weight, r * 4, "row_weight"),
+    p = _sized([(row_token, r * 4, "row_token", "int32"), (row_weight, r * 4, "row_weight", "float32"),
                 (dY, n * h * e, "dY"), (Y_perm, r * h * e, "Y_perm"),
-                (dY_perm, r * h * e, "dY_perm"), (d_weight, r * 4, "d_weight")])
+                (dY_perm, r * h * e, "dY_perm"), (d_weight, r * 4, "d_weight", "float32")])
     return _check(lib().tp_moe_combine_bwd(int(dtype), int(N), int(H), int(R), *p,
                                            _stream(stream)))
 
@@ -443,7 +448,7 @@ def tp_moe_combine_bwd(dtype: int, N: int, H: int, R: int, row_token, row_weight
 def tp_fp8_quantize(fmt: int, transpose: bool, rows: int, cols: int, x, scale, q, amax=None,
                     stream=None) -> int:
     n = max(int(rows), 0) * max(int(cols), 0)
-    p = _sized([(x, n * 2, "x"), (scale, 4, "scale"), (q, n, "q"), (amax, 4, "amax")])
+    p = _sized([(x, n * 2, "x"), (scale, 4, "scale", "float32"), (q, n, "q"), (amax, 4, "amax", "float32")])
     return _check(lib().tp_fp8_quantize(int(fmt), int(bool(transpose)), int(rows), int(cols),
                                         *p, _stream(stream)))
 
@@ -454,8 +459,8 @@ def tp_mlp_shard_fwd_fp8(desc, Xq, Aq_t, Auq_t, Bq_t, scales, Z_save, H_act, H_q
     n = _shard_sizes(d)
     p = _sized([(Xq, n["X"] // 2, "Xq"), (Aq_t, n["A"] // 2, "Aq_t"),
                 (Auq_t, n["A"] // 2, "Auq_t"), (Bq_t, n["B"] // 2, "Bq_t"),
-                (scales, 5 * 4, "scales"), (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"),
-                (H_q, n["H"] // 2, "H_q"), (h_amax, 4, "h_amax"),
+                (scales, 5 * 4, "scales", "float32"), (Z_save, n["Z"], "Z_save"), (H_act, n["H"], "H_act"),
+                (H_q, n["H"] // 2, "H_q"), (h_amax, 4, "h_amax", "float32"),
                 (Y_partial, n["Y"], "Y_partial")])
     return _check(lib().tp_mlp_shard_fwd_fp8(ctypes.byref(d), *p, _stream(stream)))
 
@@ -470,9 +475,12 @@ def tp_fp8_scale_update(fmt: int, n: int, length: int, history, amax, scale, sca
                         margin: int = 0, stream=None) -> int:
     nb = max(int(n), 0) * 4
     return _check(lib().tp_fp8_scale_update(int(fmt), int(n), int(length),
-                                            _ptr(history, nb * max(int(length), 0), "history"),
-                                            _ptr(amax, nb, "amax"), _ptr(scale, nb, "scale"),
-                                            _ptr(scale_inv, nb, "scale_inv"), int(margin),
+                                            _ptr(history, nb * max(int(length), 0), "history",
+                                                 "float32"),
+                                            _ptr(amax, nb, "amax", "float32"),
+                                            _ptr(scale, nb, "scale", "float32"),
+                                            _ptr(scale_inv, nb, "scale_inv", "float32"),
+                                            int(margin),
                                             _stream(stream)))
 
 
@@ -484,8 +492,8 @@ def tp_mlp_shard_bwd_fp8(desc, dYq, dYq_t, Xq_t, Hq_t, Aq, Auq, Bq, Z_save, scal
     p = _sized([(dYq, n["Y"] // 2, "dYq"), (dYq_t, n["Y"] // 2, "dYq_t"),
                 (Xq_t, n["X"] // 2, "Xq_t"), (Hq_t, n["H"] // 2, "Hq_t"),
                 (Aq, n["A"] // 2, "Aq"), (Auq, n["A"] // 2, "Auq"), (Bq, n["B"] // 2, "Bq"),
-                (Z_save, n["Z"], "Z_save"), (scales, 7 * 4, "scales"),
+                (Z_save, n["Z"], "Z_save"), (scales, 7 * 4, "scales", "float32"),
                 (dX_partial, n["X"], "dX_partial"), (dA, n["dA"], "dA"),
                 (dA_up, n["dA"], "dA_up"), (dB, n["dB"], "dB"), (dZq, zq, "dZq"),
-                (dZq_t, zq, "dZq_t"), (dz_amax, 4, "dz_amax")])
+                (dZq_t, zq, "dZq_t"), (dz_amax, 4, "dz_amax", "float32")])
     return _check(lib().tp_mlp_shard_bwd_fp8(ctypes.byref(d), *p, _stream(stream)))

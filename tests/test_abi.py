@@ -480,3 +480,26 @@ def test_fp8_scale_update_argument_checks():
     assert su(inv=addr(4, 1)) == E_ALIGN
     assert su(s=addr(1, 16)) == E_ALIAS                # scale inside the history
     assert su(inv=addr(2, 4)) == E_ALIAS               # scale_inv overlapping amax
+
+
+def test_binding_checks_table_element_types():
+    """Index tables must be int32 and scale buffers float32: the library
+    reads their bytes as such (an int64 offsets tensor would be read as
+    pairs of int32)."""
+    import torch
+    d = dict(H=256, F=128, E=4, dtype=tp.TP_BF16)
+    with pytest.raises(ValueError, match="torch.int32"):
+        tp.tp_grouped_expert_fwd_devoff(d, 8, torch.zeros(5, dtype=torch.int64), addr(1),
+                                        addr(2), addr(3), addr(4), addr(5), addr(6), addr(7))
+    with pytest.raises(ValueError, match="torch.int32"):
+        tp.tp_moe_permute(tp.TP_BF16, 4, 8, 4, torch.zeros(4, dtype=torch.int64), addr(1),
+                          addr(2))
+    with pytest.raises(ValueError, match="torch.float32"):
+        tp.tp_moe_combine(tp.TP_BF16, 4, 8, 4, addr(1), addr(2),
+                          torch.zeros(4, dtype=torch.float64), addr(3), addr(4))
+    with pytest.raises(ValueError, match="torch.float32"):
+        tp.tp_fp8_scale_update(tp.TP_FP8_E4M3, 2, 4, torch.zeros(8, dtype=torch.float64),
+                               addr(2), addr(3))
+    with pytest.raises(ValueError, match="torch.float32"):
+        tp.tp_fp8_quantize(tp.TP_FP8_E4M3, 0, 16, 16, addr(1),
+                           torch.ones(1, dtype=torch.bfloat16), addr(3))
