@@ -497,6 +497,10 @@ int tp_fp8_transpose(int64_t rows, int64_t cols, const void *q, void *q_t, void 
  * correctly rounded fp32 operation.  scale_inv[t] = 1 / scale[t].
  *   fmt TP_FP8_E4M3 or TP_FP8_E5M2; 0 <= n <= 2^24; 1 <= len <= 1024;
  *   0 <= margin <= 16.  Nothing is allocated; no memset (capturable).
+ * Errors: TP_ERR_DTYPE (fmt), TP_ERR_SHAPE (n, len, margin), TP_ERR_NULL
+ * (history, amax or scale NULL with n > 0), TP_ERR_ALIGN (not 4-byte
+ * aligned), TP_ERR_ALIAS (two of the buffers overlap), TP_ERR_DEVICE,
+ * TP_ERR_HIP (launch); nothing is enqueued on an error.
  */
 int tp_fp8_scale_update(int32_t fmt, int32_t n, int32_t len, float *history, float *amax,
                         float *scale, float *scale_inv, int32_t margin, void *stream);
