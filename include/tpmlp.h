@@ -348,15 +348,16 @@ int tp_grouped_expert_bwd_accum(const tp_expert_desc *desc, const int64_t *offse
  *   workspace  tp_grouped_expert_devoff_workspace(desc, R) bytes ([R,2F] bf16)
  *   accumulate 0: weight gradients written (tp_grouped_expert_bwd);
  *            1: added to (tp_grouped_expert_bwd_accum)
- * The host cannot see the rows, so the row-tiled products launch for the
- * worst split of R rows (E - 1 more tile rows than R rows need at most);
- * workgroups without a tile exit at once, so size R tightly: every spare
- * workgroup holds a compute unit briefly.  The kernels make the host
+ * The host cannot see the rows, so the row-tiled products cover the worst
+ * split of R rows (E - 1 more tile rows than R rows need at most):
+ * workgroups without a tile exit at once, and where that worst case
+ * exceeds three waves over the compute units the launch instead loops over
+ * its tiles on one workgroup per compute unit.  The kernels make the host
  * calls' choice among 256-row tiles, 256-row tiles with 32-row remainder
  * tiles and 128-row tiles from the offsets themselves (not the 224-wide
- * tiles, nor 128-row tiles whose worst-case grid exceeds one wave over the
- * compute units): results equal the host-offset calls' bit for bit where
- * both take the same tiling, and otherwise up to summation order; they are
+ * tiles; 128-row tiles only where their grid fits one wave or the launch
+ * loops): results equal the host-offset calls' bit for bit where both take
+ * the same tiling, and otherwise up to summation order; they are
  * bit-identical run to run.
  * Errors: as the host-offset calls (the offsets' values are not checked).
  */

@@ -782,14 +782,14 @@ constexpr int lean_load_seq(int idx) {
   return idx < 2 * LA ? ((idx & 1) ? LA + (idx >> 1) : (idx >> 1)) : idx;
 }
 
+// One output tile of the hand-ordered kernel (its prologue, k loop and
+// epilogue) in the workgroup's shared memory `lds`.
 template <int TMR, bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT>
-__global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
-  gemm_wave_prio();
+__device__ __forceinline__ void lean_tile(const GemmArgs& g, const TileCoord& tc, bf16_t* lds) {
   using C = LeanCfg<TMR>;
   constexpr int FM = C::FM, FN = C::FN, WTM = C::WTM, WTN = C::WTN, NBUF = C::NBUF;
   constexpr int LA = C::LA, LB = C::LB, NL = C::NL;
   constexpr uint32_t A_BYTES = C::A_BYTES, STAGE = C::STAGE;
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[NBUF * STAGE / 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -797,8 +797,6 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
   const int wm = TMR == 256 ? wave >> 1 : 0, wn = TMR == 256 ? wave & 1 : wave;
   const int r_lane = lane & 31, c_lane = lane >> 5;
 
-  const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, TMR);
-  if (tc.e < 0) return;  // spare tile (device-resident offsets)
   const bf16_t* a0 = reinterpret_cast<const bf16_t*>(g.a.p0) + tc.e * g.a.bstride;
   const bf16_t* b0 = reinterpret_cast<const bf16_t*>(g.b.p0) + tc.e * g.b.bstride;
   const bf16_t* b1 = reinterpret_cast<const bf16_t*>(g.b.p1) + tc.e * g.b.bstride;
@@ -1045,10 +1043,38 @@ __global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
 
   // every wavefront's loads have landed and its reads are done before the
   // tile is staged through shared memory
-  static_assert(EQ_BYTES <= (int)sizeof(lds), "staging rows exceed shared memory");
+  static_assert(EQ_BYTES <= (int)(NBUF * STAGE), "staging rows exceed shared memory");
   __syncthreads();
   write_tile_staged<EPI, BMODE, OutT, FM, FN, WTM, WTN, LEAN_NT, 0, TMR / 64>(
       acc, ea, tc, wm, wn, lane, tid, Ncols, reinterpret_cast<float*>(lds));
+}
+
+// LOOP (row-ragged launches with device-resident offsets only): the grid,
+// at most one workgroup per compute unit and a multiple of 8 (so that tile
+// index b keeps running on XCD b mod 8), walks the tile indices b =
+// blockIdx.x, blockIdx.x + gridDim.x, ...; every workgroup stops at the
+// first index past the tiles the offsets call for, so no spare workgroup
+// is dispatched however far the worst-case tile count overshoots them.
+template <int TMR, bool A_KMAJOR, bool B_KMAJOR, int BMODE, int EPI, typename OutT,
+          bool LOOP = false>
+__global__ __launch_bounds__(LEAN_NT, 1) void gemm_lean(GemmArgs g) {
+  gemm_wave_prio();
+  using C = LeanCfg<TMR>;
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[C::NBUF * C::STAGE / 2];
+  if constexpr (!LOOP) {
+    const TileCoord tc = locate_tile(g, blockIdx.x, gridDim.x, TMR);
+    if (tc.e < 0) return;  // spare tile (device-resident offsets)
+    lean_tile<TMR, A_KMAJOR, B_KMAJOR, BMODE, EPI, OutT>(g, tc, lds);
+  } else {
+    for (int b = blockIdx.x;; b += gridDim.x) {
+      const TileCoord tc = locate_tile(g, b, 0, TMR);
+      if (tc.e < 0) return;
+      lean_tile<TMR, A_KMAJOR, B_KMAJOR, BMODE, EPI, OutT>(g, tc, lds);
+      // every wavefront is done with the epilogue's staging rows before
+      // the next tile's loads write shared memory
+      __syncthreads();
+    }
+  }
 }
 
 // ---- ring kernel: 4-stage shared-memory ring of 32-wide k tiles ------------
@@ -2382,13 +2408,13 @@ template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
 static hipError_t launch_256(GemmArgs& g, int blocks, hipStream_t stream);
 
 // Row-ragged grouped launches whose row offsets stay in device memory: the
-// host does not see the rows, so the launch takes 256 x 256 tiles for
+// host does not see the rows, so the launch covers 256 x 256 tiles for
 // every split of dev_rows rows into E problems, at most (dev_rows + E (BM -
-// 1)) / BM tile rows in all (the workgroups of spare tiles exit at once),
-// and queues the other tilings the host could pick beside it: 128-row
-// tiles, and a thin launch for remainders of at most THIN_MAX rows.  Every
-// workgroup takes the host's choice from the offsets; those of the
-// launches not chosen exit at once.  (A k-ragged launch's tiles do not
+// 1)) / BM tile rows in all, and queues the other tilings the host could
+// pick beside it: 128-row tiles, and a thin launch for remainders of at
+// most THIN_MAX rows.  Every workgroup takes the host's choice from the
+// offsets; those of the launches not chosen exit at once, as do those past
+// the tiles the offsets need.  (A k-ragged launch's tiles do not
 // depend on the rows: it takes the host's usual choice, and its kernels
 // read their k ranges from the device offsets.)
 template <int NW, bool AK, bool BK_, int BMODE, int EPI, typename OutT>
@@ -2406,25 +2432,42 @@ static hipError_t launch_devoff(GemmArgs& g, hipStream_t stream) {
   // the other tilings the host could pick (the kernels choose from the
   // offsets as the host would from host ones): remainders of at most
   // THIN_MAX rows on the thin kernel, at most THIN_MAX / THIN_M tile rows
-  // per problem; 128-row tiles on the hand-ordered kernel when their
-  // worst-case grid fits one wave over the compute units (every workgroup
-  // of a launch not chosen still holds a compute unit for ~2 us to find
-  // that out: on the grouped-expert workload a grid of 429 such workgroups
-  // added 7.5 us to FC1, where 128-row tiles do not pay)
+  // per problem; 128-row tiles on the hand-ordered kernel.
+  //
+  // A workgroup that only finds it has nothing to do still holds a compute
+  // unit for ~2 us.  Worst-case grids of more than three waves (R far above
+  // the rows routed) therefore run the hand-ordered launches as loops over
+  // their tiles on one workgroup per compute unit (their k loop is ~6 %
+  // slower: the loop's state spills scalar registers); smaller ones keep
+  // one tile per workgroup, the 128-row tiling only when its grid fits one
+  // wave (on the grouped-expert workload a grid of 429 idle workgroups
+  // added 7.5 us to FC1, where 128-row tiles do not pay).
   const int64_t b128 = ((int64_t)g.dev_rows + (int64_t)g.E * 127) / 128 * g.tiles_n;
-  const bool l128 = lean_ok<AK, BK_, BMODE>(g) && b128 <= (int64_t)device_cus();
+  const bool lean = lean_ok<AK, BK_, BMODE>(g);
   const bool thin = short_rows_ok<AK, BK_, BMODE>(g);
-  if (blocks > INT32_MAX || (l128 && b128 > INT32_MAX)) return hipErrorInvalidValue;
+  if (blocks > INT32_MAX || b128 > INT32_MAX) return hipErrorInvalidValue;
+  g.dev_cus = device_cus();
+  const int64_t loop_grid = std::max(8, g.dev_cus / 8 * 8);
+  const bool loop = lean && blocks > 3 * loop_grid;
+  const bool l128 = lean && (loop || b128 <= g.dev_cus);
   g.dev_thin = thin ? THIN_MAX : 0;
   g.dev_l128 = l128 ? (int)(TP_LEAN128_FACTOR * 1000 + 0.5) : 0;
-  g.dev_cus = device_cus();
-  hipError_t he = launch_256<NW, AK, BK_, BMODE, EPI, OutT>(g, (int)blocks, stream);
-  if (he != hipSuccess || blocks == 0) return he;
-  if (l128) {
-    hipLaunchKernelGGL((gemm_lean<128, AK, BK_, BMODE, EPI, OutT>), dim3((int)b128), dim3(LEAN_NT),
-                       0, stream, g);
-    if ((he = hipGetLastError()) != hipSuccess || !thin) return he;
+  if (blocks == 0) return hipSuccess;
+  hipError_t he;
+  if (loop) {
+    hipLaunchKernelGGL((gemm_lean<256, AK, BK_, BMODE, EPI, OutT, true>), dim3((int)loop_grid),
+                       dim3(LEAN_NT), 0, stream, g);
+    if ((he = hipGetLastError()) != hipSuccess) return he;
+    hipLaunchKernelGGL((gemm_lean<128, AK, BK_, BMODE, EPI, OutT, true>),
+                       dim3((int)std::min(b128, loop_grid)), dim3(LEAN_NT), 0, stream, g);
+  } else {
+    he = launch_256<NW, AK, BK_, BMODE, EPI, OutT>(g, (int)blocks, stream);
+    if (he != hipSuccess) return he;
+    if (l128)
+      hipLaunchKernelGGL((gemm_lean<128, AK, BK_, BMODE, EPI, OutT>), dim3((int)b128),
+                         dim3(LEAN_NT), 0, stream, g);
   }
+  if ((he = hipGetLastError()) != hipSuccess || !thin) return he;
   if (!thin) return hipSuccess;
   if constexpr (AK && !(BMODE == BMODE_PAIR32 && BK_)) {
     g.N = n_given;

@@ -228,6 +228,52 @@ def test_out_of_range_offsets_are_taken_clamped(vals):
     _check_oracle(d, _clamped(vals, R), o, H, F)
 
 
+def test_looped_launches_on_a_large_buffer():
+    """H = 4096 on a buffer of 20000 rows with 851 routed: the worst-case
+    grids of FC2 and dX (82 tile rows x 16) exceed three waves, so they run
+    as loops over their tiles on one workgroup per compute unit; whole
+    tensors against the oracle, the unrouted rows untouched."""
+    counts, H, F = [300, 0, 511, 40], 4096, 512
+    d = _inputs(counts, H, F, R=20000, seed=89)
+    _, o = _run(d, H, F, _device_offsets(counts))
+    _check_oracle(d, d["offsets"], o, H, F)
+
+
+def test_full_grouped_workload_on_capacity_buffers_bitwise():
+    """The full grouped workload on buffers of tokens x top-k = 32768 rows
+    (every row-ragged launch loops over its tiles): the offsets call for
+    the tilings the host-offset call picks (256-row tiles for FC1, 32-row
+    remainders for FC2 and dX, 128-row tiles for dH), and the looped
+    kernels compute each tile as the others do, so every output equals the
+    host-offset call's bit for bit."""
+    w = wl.WORKLOADS["c5_bf16_grouped_swiglu"]
+    g = wl.gen_grouped_inputs(w)
+    H, F, E = w.H, w.F, w.experts
+    off = g["offsets"]
+    R = int(off[-1])
+    cap = w.tokens * w.topk
+    d = {k: g[k] for k in ("Wg", "Wu", "Wd")}
+    d["R"] = cap
+    for k in ("X_perm", "dY_perm"):
+        full = np.zeros((cap, H), np.uint16)
+        full[:R] = g[k]
+        d[k] = full
+    dev, o = _run(d, H, F, _device_offsets(np.diff(off)))
+    desc = dict(H=H, F=F, E=E, dtype=wl.DT_BF16)
+    ref = ExpertBuffers(desc, off)
+    print("[gpu] host-offset grouped fwd+bwd", flush=True)
+    Xp, dYp = dev["X_perm"][:R].contiguous(), dev["dY_perm"][:R].contiguous()
+    tp.tp_grouped_expert_fwd(desc, off, Xp, dev["Wg"], dev["Wu"], dev["Wd"], ref.Z, ref.H, ref.Y)
+    tp.tp_grouped_expert_bwd(desc, off, Xp, dev["Wg"], dev["Wu"], dev["Wd"], ref.Z, ref.H, dYp,
+                             ref.dX, ref.dWg, ref.dWu, ref.dWd, ref.ws, ref.ws_bytes)
+    torch.cuda.synchronize()
+    for k in ("Z", "H", "Y", "dX"):
+        assert torch.equal(getattr(o, k)[:R], getattr(ref, k)), k
+        assert bool((getattr(o, k)[R:].view(torch.int16) == SENTINEL).all()), k
+    for k in ("dWg", "dWu", "dWd"):
+        assert torch.equal(getattr(o, k), getattr(ref, k)), k
+
+
 def test_sixty_four_experts():
     """E = 64 (the most a call takes: every lane of the offset scan holds an
     expert, the last reading the table's 65th entry), a third of them
